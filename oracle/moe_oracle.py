@@ -1,0 +1,329 @@
+"""Plain float64 CPU oracle for the forward pass of one sparse MoE FFN layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check of the graft entry point
+and the benchmark's CPU-baseline leg use it. It shares no code with the HIP
+library (no kernels, headers, tables or helpers) and imports nothing from it.
+
+Every step is the plain definition the pages give, in their order and
+notation, with numpy as the only primitive (matrix products, exp, a sort):
+
+  1. router logits  z_t = W_r h_t + b_r
+     [page "MOE 专家选择与路由机制" (wuhy-notes), §二 第一步;
+      page "MoE：router 怎样选 expert" (cooking-agi), first section]
+  2. scores: softmax p_t = exp(z_t) / sum_j exp(z_tj)            [§二 第二步]
+     or sigmoid s_t = 1/(1+exp(-z_t)) (DeepSeek-V3 style)
+     [cooking-agi, first section, the remark after the gate formula]
+  3. top-k selection S_t = TopK(score_t, k)                      [§二 第三步]
+  4. gates, three modes
+     A  g_i = p_i / sum_{j in S} p_j  (= softmax over the selected logits)
+        [wuhy-notes §二 第三步 gate formula; cooking-agi first section]
+     B  g_i = p_i, the full-softmax probability, no renormalisation
+        (Switch top-1; the route() snippet keeps top_probs for any k)
+        [cooking-agi first section, Switch remark; page pwwt.cn §2.1]
+     C  select on s + b_sel, g_i = s_i / sum_{j in S} s_j with the unbiased s
+        [cooking-agi first section; page "拆解 MoE：单个 Token 如何经过专家层"
+         (feinterview), load-balance section: where the bias acts is left to
+         the implementation; read here as selection only]
+  5. dispatch: stable regroup of the (token, slot) pairs by expert
+     [wuhy-notes §三 "Token Dispatch" table and bucket listing;
+      page "【大模型】MoE（专家混合模型）简介" (horizon.auto) §3 ② Dispatch]
+  6. experts: E_i(h) = W_down^(i) (SiLU(W_gate^(i) h) * W_up^(i) h)
+     [wuhy-notes §一, SwiGLU FFN and expert formulas]
+     shared expert: added to every token with weight 1  [wuhy-notes §八]
+  7. combine: y_t = sum_{i in S_t} g_ti E_i(h_t) (+ shared) -- a sum, never
+     an overwrite [cooking-agi "选好以后，token 怎么过去，输出怎么回来？";
+     horizon.auto §3 ④ Gather]
+  8. load statistics f_i, p_i and L_aux = alpha * N * sum_i f_i p_i
+     [feinterview, load-balance section; wuhy-notes §五 (garbled print)]
+  9. dense brute force: every expert on every token, unselected gates zero
+     [cooking-agi "怎么知道实现没把梯度弄丢？"]
+
+Readings where the pages are silent or garbled (each is listed in the design
+notes): ties in top-k go to the lower expert index; f_i = count_i / (T k);
+p_i in mode C averages s_ti / sum_j s_tj; the shared expert is ungated; the
+router bias is optional; SiLU(x) = x * sigmoid(x); expert linears have no
+bias; the layer output excludes the residual.
+
+Parity pins: every function here is pinned in tests/test_oracle_pins.py
+against the pages' worked examples, closed forms, brute force or library
+routines; tests/test_oracle_mutations.py plants plausible mistakes and shows
+a pin catches each.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+MODE_SOFTMAX_RENORM = 0
+MODE_SOFTMAX_FULL = 1
+MODE_SIGMOID_BIAS_RENORM = 2
+
+F64 = np.float64
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=F64)
+
+
+# ----------------------------------------------------------- 1. router logits
+def router_logits(h, w_router, b_router=None):
+    """z[t, i] = sum_c W_r[i, c] h[t, c] + b_r[i]; W_r is [N, d] (one row per
+    expert), h is [T, d]. The bias is optional (two of the pages omit it)."""
+    z = _f64(h) @ _f64(w_router).T
+    if b_router is not None:
+        z = z + _f64(b_router)[None, :]
+    return z
+
+
+# ------------------------------------------------------------------ 2. scores
+def softmax(z):
+    """p[t, i] = exp(z[t, i]) / sum_j exp(z[t, j]), evaluated as
+    exp(z - max) / sum exp(z - max) (same value, no overflow)."""
+    z = _f64(z)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def sigmoid(z):
+    """s = 1 / (1 + exp(-z))."""
+    return 1.0 / (1.0 + np.exp(-_f64(z)))
+
+
+# ------------------------------------------------------------------- 3. top-k
+def topk(sel, k):
+    """Top-k of each row of ``sel`` [T, N].
+
+    Experts are ordered by selection score descending, ties broken by the
+    lower expert index; the first k are the slots 0..k-1. Also returns the
+    gap between the k-th and (k+1)-th scores (+inf when k == N), used to
+    flag near-ties.
+    """
+    sel = _f64(sel)
+    T, N = sel.shape
+    if not 1 <= k <= N:
+        raise ValueError(f"need 1 <= k <= N, got k={k}, N={N}")
+    idx = np.broadcast_to(np.arange(N), sel.shape)
+    order = np.lexsort((idx, -sel), axis=-1)          # primary key: -score
+    ids = order[:, :k].astype(np.int64)
+    srt = np.take_along_axis(sel, order, axis=-1)
+    gap = srt[:, k - 1] - srt[:, k] if k < N else np.full(T, np.inf)
+    return ids, gap
+
+
+@dataclasses.dataclass
+class Routing:
+    ids: np.ndarray        # [T, k] int64, slot order = descending selection score
+    gates: np.ndarray      # [T, k] float64
+    z: np.ndarray          # [T, N] logits
+    sel: np.ndarray        # [T, N] selection score
+    gap: np.ndarray        # [T] k-th minus (k+1)-th selection score
+    stat_prob: np.ndarray  # [T, N] per-token probabilities averaged into p_i
+
+
+# ------------------------------------------------------------------- 4. gates
+def route(h, w_router, k, mode, b_router=None, b_select=None) -> Routing:
+    """Router logits, scores, top-k selection and gate values (steps 1-4)."""
+    z = router_logits(h, w_router, b_router)
+    if mode in (MODE_SOFTMAX_RENORM, MODE_SOFTMAX_FULL):
+        p = softmax(z)
+        sel = p                       # TopK(p_t, k)
+        ids, gap = topk(sel, k)
+        p_sel = np.take_along_axis(p, ids, axis=-1)
+        if mode == MODE_SOFTMAX_RENORM:
+            gates = p_sel / p_sel.sum(axis=-1, keepdims=True)
+        else:
+            gates = p_sel
+        stat_prob = p
+    elif mode == MODE_SIGMOID_BIAS_RENORM:
+        if b_select is None:
+            raise ValueError("mode C needs the selection bias")
+        s = sigmoid(z)
+        sel = s + _f64(b_select)[None, :]
+        ids, gap = topk(sel, k)
+        s_sel = np.take_along_axis(s, ids, axis=-1)   # unbiased scores
+        gates = s_sel / s_sel.sum(axis=-1, keepdims=True)
+        stat_prob = s / s.sum(axis=-1, keepdims=True)
+    else:
+        raise ValueError(f"unknown gate mode {mode}")
+    return Routing(ids, gates, z, sel, gap, stat_prob)
+
+
+# ---------------------------------------------------------------- 5. dispatch
+@dataclasses.dataclass
+class Dispatch:
+    counts: np.ndarray    # [N] rows per expert
+    offsets: np.ndarray   # [N+1] exclusive prefix of counts
+    perm_src: np.ndarray  # [T*k] bucket row -> flat slot t*k + j
+    row_of: np.ndarray    # [T*k] flat slot -> bucket row
+
+
+def dispatch(ids, N) -> Dispatch:
+    """Group the flat slots f = t*k + j by expert: expert 0's slots first,
+    then expert 1's, ...; within one expert in ascending f (token order)."""
+    flat = np.asarray(ids).reshape(-1)
+    buckets = [np.nonzero(flat == e)[0] for e in range(N)]
+    counts = np.array([len(b) for b in buckets], dtype=np.int64)
+    offsets = np.zeros(N + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm_src = (np.concatenate(buckets) if buckets else np.zeros(0)).astype(np.int64)
+    row_of = np.empty_like(perm_src)
+    row_of[perm_src] = np.arange(perm_src.size)
+    return Dispatch(counts, offsets, perm_src, row_of)
+
+
+# ----------------------------------------------------------------- 6. experts
+def silu(x):
+    """SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x))."""
+    x = _f64(x)
+    return x / (1.0 + np.exp(-x))
+
+
+def expert_ffn(x, w_gate, w_up, w_down):
+    """SwiGLU expert on rows x [n, d]: W_down (SiLU(W_gate x) * (W_up x)).
+    w_gate, w_up are [d_ff, d]; w_down is [d, d_ff] (out x in)."""
+    x = _f64(x)
+    g = x @ _f64(w_gate).T
+    u = x @ _f64(w_up).T
+    return (silu(g) * u) @ _f64(w_down).T
+
+
+WeightsOf = Callable[[int], Sequence[np.ndarray]]
+
+
+def weights_getter(w_gate, w_up, w_down) -> WeightsOf:
+    """Expert-weight provider over stacked [N, ...] arrays."""
+    return lambda e: (w_gate[e], w_up[e], w_down[e])
+
+
+def expert_rows(h, disp: Dispatch, k, weights_of: WeightsOf,
+                shared: Optional[Sequence[np.ndarray]] = None):
+    """Rows of expert outputs in bucket order: out[r] = E_e(h[perm_src[r] // k])
+    for the expert e whose bucket holds row r; then, with a shared expert,
+    out[T*k + t] = E_shared(h[t]). Streams one expert's weights at a time."""
+    h = _f64(h)
+    T = h.shape[0]
+    R = disp.perm_src.size
+    out = np.zeros((R + (T if shared is not None else 0), h.shape[1]))
+    for e in range(disp.counts.size):
+        lo, hi = disp.offsets[e], disp.offsets[e + 1]
+        if hi == lo:
+            continue
+        tok = disp.perm_src[lo:hi] // k
+        out[lo:hi] = expert_ffn(h[tok], *weights_of(e))
+    if shared is not None:
+        out[R:] = expert_ffn(h, *shared)
+    return out
+
+
+# ----------------------------------------------------------------- 7. combine
+def combine(out_rows, row_of, gates, has_shared=False):
+    """y[t] = out_rows[T*k + t] (shared, weight 1) + sum_j g[t, j] *
+    out_rows[row_of[t*k + j]]: every routed contribution is added."""
+    gates = _f64(gates)
+    T, k = gates.shape
+    out_rows = _f64(out_rows)
+    y = np.zeros((T, out_rows.shape[1]))
+    if has_shared:
+        y += out_rows[T * k:T * k + T]
+    rows = np.asarray(row_of).reshape(T, k)
+    for j in range(k):
+        y += gates[:, j:j + 1] * out_rows[rows[:, j]]
+    return y
+
+
+# ------------------------------------------------------------------- 8. stats
+def load_stats(counts, stat_prob, k, alpha):
+    """f_i = count_i / (T k); p_i = mean over tokens of the routing
+    probability; L_aux = alpha * N * sum_i f_i p_i."""
+    stat_prob = _f64(stat_prob)
+    T, N = stat_prob.shape
+    f = np.asarray(counts, dtype=F64) / (T * k) if T else np.zeros(N)
+    p = stat_prob.mean(axis=0) if T else np.zeros(N)
+    l_aux = alpha * N * float(np.sum(f * p))
+    return f, p, l_aux
+
+
+# --------------------------------------------------------------- whole layer
+@dataclasses.dataclass
+class LayerResult:
+    routing: Routing
+    disp: Dispatch
+    out_rows: np.ndarray
+    y: np.ndarray
+    f: np.ndarray
+    p: np.ndarray
+    l_aux: float
+
+
+def layer(h, w_router, k, mode, weights_of: WeightsOf, b_router=None,
+          b_select=None, shared=None, alpha=0.01) -> LayerResult:
+    """The whole forward pass, steps 1-8, on all tokens."""
+    N = np.asarray(w_router).shape[0]
+    r = route(h, w_router, k, mode, b_router, b_select)
+    disp = dispatch(r.ids, N)
+    out_rows = expert_rows(h, disp, k, weights_of, shared)
+    y = combine(out_rows, disp.row_of, r.gates, shared is not None)
+    f, p, l_aux = load_stats(disp.counts, r.stat_prob, k, alpha)
+    return LayerResult(r, disp, out_rows, y, f, p, l_aux)
+
+
+def layer_tokens(h, routing: Routing, tokens, weights_of: WeightsOf,
+                 shared=None):
+    """y for a subset of tokens only (tokens are independent: no step couples
+    two tokens), computed one token at a time: for each token, run each of
+    its selected experts on its row and add the gated outputs (+ shared)."""
+    h = _f64(h)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    y = np.zeros((tokens.size, h.shape[1]))
+    need = {}
+    for n, t in enumerate(tokens):
+        for j, e in enumerate(routing.ids[t]):
+            need.setdefault(int(e), []).append((n, t, j))
+    for e, items in sorted(need.items()):
+        wg, wu, wd = weights_of(e)
+        rows = np.array([t for _, t, _ in items])
+        o = expert_ffn(h[rows], wg, wu, wd)
+        for m, (n, t, j) in enumerate(items):
+            y[n] += routing.gates[t, j] * o[m]
+    if shared is not None:
+        y += expert_ffn(h[tokens], *shared)
+    return y
+
+
+def dense_layer(h, w_router, k, mode, weights_of: WeightsOf, b_router=None,
+                b_select=None, shared=None):
+    """Brute force: run every expert on every token, build the dense gate
+    matrix G (g on the selected experts, 0 elsewhere) and sum G[t,i] E_i(h_t),
+    plus the shared expert."""
+    h = _f64(h)
+    T = h.shape[0]
+    N = np.asarray(w_router).shape[0]
+    r = route(h, w_router, k, mode, b_router, b_select)
+    G = np.zeros((T, N))
+    np.put_along_axis(G, r.ids, r.gates, axis=-1)
+    y = np.zeros_like(h)
+    for e in range(N):
+        y += G[:, e:e + 1] * expert_ffn(h, *weights_of(e))
+    if shared is not None:
+        y += expert_ffn(h, *shared)
+    return y
+
+
+# ------------------------------------------------------ comparison helpers
+def near_tie_tokens(gap, threshold=1e-4):
+    """Tokens whose k-th and (k+1)-th selection scores are closer than the
+    threshold: their selected set may legitimately differ between two
+    correctly rounded implementations."""
+    return np.asarray(gap) < threshold
+
+
+def row_rel_err(y, y_ref):
+    """max over elements of |y - y_ref| divided by max |y_ref|, per row."""
+    y = _f64(y)
+    y_ref = _f64(y_ref)
+    num = np.abs(y - y_ref).max(axis=-1) if y.size else np.zeros(y.shape[0])
+    den = np.abs(y_ref).max(axis=-1) if y.size else np.ones(y.shape[0])
+    return num / np.where(den == 0, 1.0, den)

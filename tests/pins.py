@@ -1,0 +1,319 @@
+"""Pins of the float64 oracle to facts that do not come from the oracle.
+
+Each pin raises AssertionError when the oracle disagrees with what the pages
+print for a worked example, a closed form, a library routine, brute force on
+a tiny input, or an invariant of the mathematics. tests/test_oracle_pins.py
+runs every pin; tests/test_oracle_mutations.py plants plausible mistakes in
+the oracle and checks that at least one pin fails for each.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _rand_inputs(rng, T, d, N, d_ff, shared=False):
+    h = rng.standard_normal((T, d)) / math.sqrt(d)
+    wr = rng.standard_normal((N, d))
+    wg = rng.standard_normal((N, d_ff, d))
+    wu = rng.standard_normal((N, d_ff, d))
+    wd = rng.standard_normal((N, d, d_ff)) / math.sqrt(d_ff)
+    sh = None
+    if shared:
+        sh = (rng.standard_normal((d_ff + 3, d)), rng.standard_normal((d_ff + 3, d)),
+              rng.standard_normal((d, d_ff + 3)) / math.sqrt(d_ff))
+    return h, wr, wg, wu, wd, sh
+
+
+# --------------------------------------------------------- worked examples
+def pin_softmax_worked_example():
+    """Logits [2.2, 0.5, 1.8, -0.4] -> printed softmax (3 decimals); also
+    scipy's softmax. [wuhy-notes §二 numeric example]"""
+    g = golden("softmax_worked_example.json")
+    p = O.softmax(np.array([g["logits"]]))[0]
+    assert np.all(np.abs(p - g["softmax_printed"]) <= g["printed_tolerance"]), p
+    assert np.allclose(p, scipy.special.softmax(g["logits"]), rtol=0, atol=1e-15)
+
+
+def pin_top2_renorm_worked_example():
+    """Same logits, top-2 renormalised -> experts {0, 2}, printed gates.
+    Fed through the router with W_r = I and h = logits."""
+    g = golden("softmax_worked_example.json")
+    z = np.array([g["logits"]])
+    r = O.route(z, np.eye(4), 2, O.MODE_SOFTMAX_RENORM)
+    assert r.ids[0].tolist() == g["top2_experts"], r.ids
+    assert np.all(np.abs(r.gates[0] - g["top2_gates_printed"]) <= g["printed_tolerance"])
+
+
+def pin_top2_scores_example():
+    """Scores [2, 1, 0]: top-2 renormalised -> [0.731, 0.269]; closed form
+    sigmoid(1) = e/(1+e). Mode B keeps e^2/(e^2+e+1), e/(e^2+e+1).
+    [cooking-agi, first section]"""
+    g = golden("top2_renorm_example.json")
+    z = np.array([g["scores"]])
+    a = O.route(z, np.eye(3), 2, O.MODE_SOFTMAX_RENORM)
+    assert a.ids[0].tolist() == [0, 1]
+    assert np.all(np.abs(a.gates[0] - g["top2_gates_printed"]) <= g["printed_tolerance"])
+    e = math.e
+    assert abs(a.gates[0, 0] - e / (1 + e)) < 1e-15
+    b = O.route(z, np.eye(3), 2, O.MODE_SOFTMAX_FULL)
+    den = e * e + e + 1
+    assert np.allclose(b.gates[0], [e * e / den, e / den], rtol=0, atol=1e-15)
+
+
+def pin_dispatch_combine_example():
+    """2 tokens / 3 experts: buckets E0<-{t0}, E1<-{t1}, E2<-{t0,t1};
+    y0 = [1.5, 1], y1 = [2.6, 2.2] (a sum, not an overwrite).
+    [cooking-agi, dispatch/combine section]"""
+    g = golden("dispatch_combine_example.json")
+    ids = np.array(g["ids"])
+    disp = O.dispatch(ids, g["N"])
+    for e, toks in g["buckets_printed"].items():
+        lo, hi = disp.offsets[int(e)], disp.offsets[int(e) + 1]
+        assert (disp.perm_src[lo:hi] // g["k"]).tolist() == toks
+    eo = g["expert_outputs"]
+    by_slot = {(0, 0): eo["t0_e0"], (0, 1): eo["t0_e2"], (1, 0): eo["t1_e1"], (1, 1): eo["t1_e2"]}
+    out_rows = np.zeros((4, 2))
+    for (t, j), v in by_slot.items():
+        out_rows[disp.row_of[t * 2 + j]] = v
+    y = O.combine(out_rows, disp.row_of, np.array(g["gates"]))
+    assert np.allclose(y, g["y_printed"], rtol=0, atol=1e-12), y
+    assert not np.allclose(y, g["y_if_overwritten_by_last_expert"])
+
+
+def pin_dispatch_grouping_example():
+    """4 tokens, top-2: E0<-T0,T2; E1<-T1,T3; E2<-T0,T1,T3; E3<-T2.
+    [wuhy-notes §三 Token Dispatch]"""
+    g = golden("dispatch_grouping_example.json")
+    disp = O.dispatch(np.array(g["ids"]), g["N"])
+    for e, toks in g["buckets_printed"].items():
+        lo, hi = disp.offsets[int(e)], disp.offsets[int(e) + 1]
+        assert (disp.perm_src[lo:hi] // g["k"]).tolist() == toks
+    assert disp.counts.tolist() == [2, 2, 3, 1]
+    assert disp.perm_src.tolist() == [0, 4, 2, 7, 1, 3, 6, 5]
+
+
+# ------------------------------------------------------------ closed forms
+def pin_router_logits_integer():
+    """z = W_r h + b_r with W_r [N, d] = [[1,2,3],[4,5,6]], h = [1,1,1],
+    b_r = [1,-1] -> [7, 14]; non-square so a transpose cannot pass."""
+    z = O.router_logits(np.array([[1.0, 1.0, 1.0], [1.0, 0.0, 0.0]]),
+                        np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]]),
+                        np.array([1.0, -1.0]))
+    assert z.tolist() == [[7.0, 14.0], [2.0, 3.0]], z
+
+
+def pin_sigmoid_silu_closed_forms():
+    """sigmoid(ln a) = a/(1+a); SiLU(x) - SiLU(-x) = x; SiLU(0) = 0;
+    scipy's expit."""
+    for a in (0.25, 1.0, 3.0, 9.0):
+        assert abs(O.sigmoid(np.log(a)) - a / (1 + a)) < 1e-15
+        assert abs(O.silu(np.log(a)) - np.log(a) * a / (1 + a)) < 1e-15
+    x = np.linspace(-8, 8, 33)
+    assert np.allclose(O.silu(x) - O.silu(-x), x, rtol=0, atol=1e-13)
+    assert O.silu(0.0) == 0.0
+    assert np.allclose(O.sigmoid(x), scipy.special.expit(x), rtol=1e-15, atol=0)
+
+
+def pin_expert_ffn_integer():
+    """W_gate h = [40, 50, 60, -40] (SiLU ~ identity / ~0 there), W_up h =
+    [1, 2, 3, 7], W_down [2 x 4] -> [220, -80] up to e^-40 terms.
+    Non-square shapes: a transposed operand cannot pass."""
+    h = np.array([[1.0, 2.0]])
+    wg = np.array([[10.0, 15.0], [20.0, 15.0], [0.0, 30.0], [-40.0, 0.0]])
+    wu = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [7.0, 0.0]])
+    wd = np.array([[1.0, 0.0, 1.0, 1.0], [0.0, 1.0, -1.0, 1.0]])
+    y = O.expert_ffn(h, wg, wu, wd)
+    assert np.allclose(y, [[220.0, -80.0]], rtol=1e-12, atol=0), y
+
+
+def pin_topk_brute_force():
+    """Top-k equals the k-subset with the largest score sum (distinct
+    scores), listed by descending score; ties go to the lower index."""
+    rng = np.random.default_rng(7)
+    for N, k in [(5, 2), (6, 3), (7, 1), (4, 4)]:
+        s = rng.standard_normal((20, N))
+        ids, gap = O.topk(s, k)
+        for t in range(20):
+            best = max(itertools.combinations(range(N), k), key=lambda c: s[t, list(c)].sum())
+            assert sorted(ids[t].tolist()) == sorted(best)
+            assert np.all(np.diff(s[t, ids[t]]) < 0)
+            srt = np.sort(s[t])[::-1]
+            want = srt[k - 1] - srt[k] if k < N else np.inf
+            assert gap[t] == want
+    ids, _ = O.topk(np.array([[1.0, 3.0, 3.0, 2.0], [5.0, 5.0, 5.0, 5.0]]), 2)
+    assert ids.tolist() == [[1, 2], [0, 1]]
+    ids, _ = O.topk(np.array([[1.0, 3.0, 3.0, 2.0]]), 1)
+    assert ids.tolist() == [[1]]
+
+
+def pin_dispatch_stable_sort():
+    """perm_src is numpy's stable argsort of the flat expert ids; counts
+    its bincount; row_of its inverse."""
+    rng = np.random.default_rng(3)
+    for T, N, k in [(0, 4, 2), (1, 4, 4), (37, 9, 3), (200, 16, 1)]:
+        ids = np.stack([rng.permutation(N)[:k] for _ in range(T)]) if T else np.zeros((0, k), int)
+        disp = O.dispatch(ids, N)
+        flat = ids.reshape(-1)
+        assert disp.perm_src.tolist() == np.argsort(flat, kind="stable").tolist()
+        assert disp.counts.tolist() == np.bincount(flat, minlength=N).tolist()
+        assert disp.offsets[-1] == T * k
+        assert np.all(disp.perm_src[disp.row_of] == np.arange(T * k))
+
+
+def pin_mode_a_equivalence():
+    """Softmax over the selected logits equals the full softmax renormalised
+    over the selected experts. [cooking-agi, first section]"""
+    rng = np.random.default_rng(11)
+    z = rng.standard_normal((50, 9)) * 3
+    r = O.route(z, np.eye(9), 3, O.MODE_SOFTMAX_RENORM)
+    zs = np.take_along_axis(z, r.ids, axis=-1)
+    assert np.allclose(r.gates, scipy.special.softmax(zs, axis=-1), rtol=0, atol=1e-15)
+    full = scipy.special.softmax(z, axis=-1)
+    assert np.allclose(r.stat_prob, full, rtol=0, atol=1e-15)
+
+
+def pin_mode_b_top1():
+    """Mode B with k = 1: the gate is max_i p_ti and is below 1;
+    mode A with k = 1 gives gate 1."""
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal((30, 6))
+    b = O.route(z, np.eye(6), 1, O.MODE_SOFTMAX_FULL)
+    p = scipy.special.softmax(z, axis=-1)
+    assert np.allclose(b.gates[:, 0], p.max(axis=-1), rtol=0, atol=1e-15)
+    assert np.all(b.gates < 1)
+    assert b.ids[:, 0].tolist() == p.argmax(axis=-1).tolist()
+    a = O.route(z, np.eye(6), 1, O.MODE_SOFTMAX_RENORM)
+    assert np.all(a.gates == 1.0)
+
+
+def pin_mode_c_hand_case():
+    """sigmoid(z) = [0.60, 0.55, 0.50], b_sel = [-0.1, 0, 0.1], k = 2:
+    selection scores [0.50, 0.55, 0.60] -> experts [2, 1], gates from the
+    unbiased scores [0.50, 0.55] / 1.05."""
+    s = np.array([0.60, 0.55, 0.50])
+    z = np.log(s / (1 - s))[None, :]
+    r = O.route(z, np.eye(3), 2, O.MODE_SIGMOID_BIAS_RENORM,
+                b_select=np.array([-0.1, 0.0, 0.1]))
+    assert r.ids[0].tolist() == [2, 1]
+    assert np.allclose(r.gates[0], [0.50 / 1.05, 0.55 / 1.05], rtol=0, atol=1e-15)
+    assert np.allclose(r.stat_prob[0], s / s.sum(), rtol=0, atol=1e-15)
+
+
+def pin_load_stats_hand_case():
+    """T=2, N=2, k=1: logits [ln 3, 0] -> p = [0.75, 0.25]; logits [0, 0]
+    -> [0.5, 0.5], a tie taken by expert 0. counts [2, 0], f = [1, 0],
+    p = [0.625, 0.375], L_aux = alpha * 2 * 0.625."""
+    z = np.array([[math.log(3.0), 0.0], [0.0, 0.0]])
+    r = O.route(z, np.eye(2), 1, O.MODE_SOFTMAX_FULL)
+    assert r.ids[:, 0].tolist() == [0, 0]
+    d = O.dispatch(r.ids, 2)
+    f, p, l_aux = O.load_stats(d.counts, r.stat_prob, 1, 0.01)
+    assert d.counts.tolist() == [2, 0]
+    assert np.allclose(f, [1.0, 0.0], rtol=0, atol=0)
+    assert np.allclose(p, [0.625, 0.375], rtol=0, atol=1e-15)
+    assert abs(l_aux - 0.01 * 2 * 0.625) < 1e-15
+    # k = 2 normalisation: both experts always chosen -> f = [0.5, 0.5]
+    d2 = O.dispatch(O.route(z, np.eye(2), 2, O.MODE_SOFTMAX_RENORM).ids, 2)
+    f2, _, _ = O.load_stats(d2.counts, r.stat_prob, 2, 0.01)
+    assert np.allclose(f2, [0.5, 0.5], rtol=0, atol=0)
+
+
+def pin_balanced_cyclic_stats():
+    """Exactly balanced routing by construction: token t's logits are a
+    cyclic shift of one vector, T a multiple of N -> f_i = p_i = 1/N and
+    L_aux = alpha (Switch loss at perfect balance)."""
+    N, k, alpha = 8, 2, 0.05
+    base = np.array([3.0, 2.0, 1.5, 0.5, 0.0, -1.0, -2.0, -3.0])
+    z = np.stack([np.roll(base, t) for t in range(4 * N)])
+    for mode, bsel in ((O.MODE_SOFTMAX_RENORM, None), (O.MODE_SIGMOID_BIAS_RENORM, np.zeros(N))):
+        r = O.route(z, np.eye(N), k, mode, b_select=bsel)
+        d = O.dispatch(r.ids, N)
+        f, p, l_aux = O.load_stats(d.counts, r.stat_prob, k, alpha)
+        assert np.allclose(f, 1.0 / N, rtol=0, atol=1e-15)
+        assert np.allclose(p, 1.0 / N, rtol=0, atol=1e-15)
+        assert abs(l_aux - alpha) < 1e-14
+
+
+# ------------------------------------------------ whole-layer brute force
+def pin_sparse_equals_dense():
+    """Sparse dispatch + combine equals the dense brute force (all experts on
+    all tokens, gates zero off the selection), all modes, with and without a
+    shared expert. [cooking-agi, dense-oracle section]"""
+    rng = np.random.default_rng(21)
+    for mode in (O.MODE_SOFTMAX_RENORM, O.MODE_SOFTMAX_FULL, O.MODE_SIGMOID_BIAS_RENORM):
+        for shared in (False, True):
+            T, d, N, k, dff = 23, 6, 5, 2, 7
+            h, wr, wg, wu, wd, sh = _rand_inputs(rng, T, d, N, dff, shared)
+            br = rng.standard_normal(N)
+            bs = rng.uniform(-0.1, 0.1, N) if mode == O.MODE_SIGMOID_BIAS_RENORM else None
+            W = O.weights_getter(wg, wu, wd)
+            res = O.layer(h, wr, k, mode, W, br, bs, sh)
+            yd = O.dense_layer(h, wr, k, mode, W, br, bs, sh)
+            assert np.allclose(res.y, yd, rtol=0, atol=1e-12)
+            yt = O.layer_tokens(h, res.routing, [5, 0, 22], W, sh)
+            assert np.allclose(yt, res.y[[5, 0, 22]], rtol=0, atol=1e-12)
+
+
+def pin_identical_experts():
+    """All experts equal and gates summing to 1 (modes A, C) -> y = E(h),
+    a plain SwiGLU FFN evaluated directly here."""
+    rng = np.random.default_rng(8)
+    T, d, N, dff = 17, 5, 6, 4
+    h = rng.standard_normal((T, d))
+    wr = rng.standard_normal((N, d))
+    wg, wu, wd = rng.standard_normal((dff, d)), rng.standard_normal((dff, d)), rng.standard_normal((d, dff))
+    g = h @ wg.T
+    direct = ((g * scipy.special.expit(g)) * (h @ wu.T)) @ wd.T
+    for mode, bs in ((O.MODE_SOFTMAX_RENORM, None), (O.MODE_SIGMOID_BIAS_RENORM, rng.uniform(-.1, .1, N))):
+        res = O.layer(h, wr, 3, mode, lambda e: (wg, wu, wd), b_select=bs)
+        assert np.allclose(res.y, direct, rtol=0, atol=1e-12)
+
+
+def pin_soft_mixture_k_equals_n():
+    """Mode A with k = N: y_t = sum_i softmax(z_t)_i E_i(h_t)."""
+    rng = np.random.default_rng(9)
+    T, d, N, dff = 11, 4, 3, 5
+    h, wr, wg, wu, wd, _ = _rand_inputs(rng, T, d, N, dff)
+    P = scipy.special.softmax(h @ wr.T, axis=-1)
+    want = np.zeros((T, d))
+    for e in range(N):
+        g = h @ wg[e].T
+        want += P[:, e:e + 1] * (((g * scipy.special.expit(g)) * (h @ wu[e].T)) @ wd[e].T)
+    res = O.layer(h, wr, N, O.MODE_SOFTMAX_RENORM, O.weights_getter(wg, wu, wd))
+    assert np.allclose(res.y, want, rtol=0, atol=1e-12)
+
+
+def pin_permutation_symmetry():
+    """Permuting tokens permutes y; relabelling the experts (router rows,
+    expert weights and selection bias together) leaves y and gates alone."""
+    rng = np.random.default_rng(13)
+    T, d, N, k, dff = 19, 6, 7, 3, 5
+    h, wr, wg, wu, wd, sh = _rand_inputs(rng, T, d, N, dff, True)
+    bs = rng.uniform(-0.1, 0.1, N)
+    br = rng.standard_normal(N)
+    for mode in (O.MODE_SOFTMAX_RENORM, O.MODE_SIGMOID_BIAS_RENORM):
+        base = O.layer(h, wr, k, mode, O.weights_getter(wg, wu, wd), br, bs, sh)
+        tp = rng.permutation(T)
+        pt = O.layer(h[tp], wr, k, mode, O.weights_getter(wg, wu, wd), br, bs, sh)
+        assert np.allclose(pt.y, base.y[tp], rtol=0, atol=1e-12)
+        ep = rng.permutation(N)
+        pe = O.layer(h, wr[ep], k, mode, O.weights_getter(wg[ep], wu[ep], wd[ep]), br[ep], bs[ep], sh)
+        assert np.allclose(pe.y, base.y, rtol=0, atol=1e-12)
+        assert np.allclose(pe.routing.gates, base.routing.gates, rtol=0, atol=1e-15)
+        assert (ep[pe.routing.ids] == base.routing.ids).all()
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

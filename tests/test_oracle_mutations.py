@@ -1,0 +1,106 @@
+"""Plant a plausible mistake in the oracle (on the CPU) and check that at
+least one pin fails for it, so the pins constrain every step."""
+import numpy as np
+import pytest
+
+import pins
+from oracle import moe_oracle as O
+
+_orig = {n: getattr(O, n) for n in ("router_logits", "softmax", "sigmoid", "topk",
+                                     "dispatch", "silu", "expert_ffn", "combine",
+                                     "load_stats", "route")}
+
+
+def _route_no_renorm(h, w, k, mode, b_router=None, b_select=None):
+    r = _orig["route"](h, w, k, mode, b_router, b_select)
+    if mode == O.MODE_SOFTMAX_RENORM:
+        r.gates = np.take_along_axis(r.stat_prob, r.ids, axis=-1)
+    return r
+
+
+def _route_biased_gates(h, w, k, mode, b_router=None, b_select=None):
+    r = _orig["route"](h, w, k, mode, b_router, b_select)
+    if mode == O.MODE_SIGMOID_BIAS_RENORM:
+        s = np.take_along_axis(r.sel, r.ids, axis=-1)
+        r.gates = s / s.sum(axis=-1, keepdims=True)
+    return r
+
+
+def _logits_reversed(h, w, b=None):
+    return _orig["router_logits"](h, np.asarray(w, float)[::-1], b)
+
+
+def _topk_ascending(sel, k):
+    ids, gap = _orig["topk"](-np.asarray(sel, float), k)
+    return ids, gap
+
+
+def _topk_high_index_ties(sel, k):
+    sel = np.asarray(sel, float)
+    ids, gap = _orig["topk"](sel[:, ::-1], k)
+    return sel.shape[1] - 1 - ids, gap
+
+
+def _dispatch_reversed(ids, N):
+    d = _orig["dispatch"](ids, N)
+    for e in range(N):
+        lo, hi = d.offsets[e], d.offsets[e + 1]
+        d.perm_src[lo:hi] = d.perm_src[lo:hi][::-1].copy()
+    d.row_of[d.perm_src] = np.arange(d.perm_src.size)
+    return d
+
+
+def _combine_overwrite(out_rows, row_of, gates, has_shared=False):
+    gates = np.asarray(gates, float)
+    T, k = gates.shape
+    y = np.zeros((T, out_rows.shape[1]))
+    if has_shared:
+        y += out_rows[T * k:T * k + T]
+    rows = np.asarray(row_of).reshape(T, k)
+    for j in range(k):
+        y = gates[:, j:j + 1] * np.asarray(out_rows)[rows[:, j]]
+    return y
+
+
+def _combine_no_shared(out_rows, row_of, gates, has_shared=False):
+    return _orig["combine"](out_rows, row_of, gates, False)
+
+
+def _combine_slot0_gate(out_rows, row_of, gates, has_shared=False):
+    g = np.repeat(np.asarray(gates, float)[:, :1], np.asarray(gates).shape[1], axis=1)
+    return _orig["combine"](out_rows, row_of, g, has_shared)
+
+
+MUTATIONS = {
+    "logits_drop_bias": ("router_logits", lambda h, w, b=None: _orig["router_logits"](h, w, None)),
+    "logits_expert_index_reversed": ("router_logits", _logits_reversed),
+    "softmax_wrong_axis": ("softmax", lambda z: np.exp(np.asarray(z, float)) / np.exp(np.asarray(z, float)).sum(axis=0, keepdims=True)),
+    "sigmoid_sign": ("sigmoid", lambda z: 1.0 / (1.0 + np.exp(np.asarray(z, float)))),
+    "topk_ascending": ("topk", _topk_ascending),
+    "topk_ties_high_index": ("topk", _topk_high_index_ties),
+    "mode_a_no_renorm": ("route", _route_no_renorm),
+    "mode_c_biased_gates": ("route", _route_biased_gates),
+    "dispatch_unstable": ("dispatch", _dispatch_reversed),
+    "silu_is_relu": ("silu", lambda x: np.maximum(np.asarray(x, float), 0.0)),
+    "silu_is_sigmoid": ("silu", lambda x: 1.0 / (1.0 + np.exp(-np.asarray(x, float)))),
+    "ffn_gate_up_swapped": ("expert_ffn", lambda x, g, u, d: _orig["expert_ffn"](x, u, g, d)),
+    "ffn_no_up": ("expert_ffn", lambda x, g, u, d: O.silu(np.asarray(x, float) @ np.asarray(g, float).T) @ np.asarray(d, float).T),
+    "combine_overwrite": ("combine", _combine_overwrite),
+    "combine_drops_shared": ("combine", _combine_no_shared),
+    "combine_slot0_gate": ("combine", _combine_slot0_gate),
+    "stats_f_over_T": ("load_stats", lambda c, sp, k, a: _orig["load_stats"](c, sp, 1, a)),
+    "stats_no_N_factor": ("load_stats", lambda c, sp, k, a: (lambda f, p, l: (f, p, l / np.asarray(sp).shape[1]))(*_orig["load_stats"](c, sp, k, a))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except Exception:            # AssertionError, or a shape error
+            failed.append(pin.__name__)
+    assert failed, f"no pin fails with mutation {name}"
