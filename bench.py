@@ -1,0 +1,247 @@
+"""Benchmark of the MoE layer forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one moe_layer_fused call (route, dispatch, gate/up GEMM + SwiGLU,
+down GEMM, combine, load statistics) over one batch of synthetic tokens whose
+inputs are already resident in HBM. Prints ONE JSON line.
+
+  value     whole-layer tokens/s (T * K / wall time of K steps between two
+            device synchronisations)
+  roofline  the dominant kernel (the grouped gate/up GEMM) timed with HIP
+            events recorded by the library on its stream around that stage,
+            against the MI355X peak that bounds it: bf16 dense MFMA
+            2.5166 PFLOP/s when its rows per expert make it compute-bound,
+            HBM 8 TB/s when it streams weights (decode batches)
+  decode    the same layer at a decode batch (16 tokens) on the same
+            weights: tokens/s and HBM GB/s of the touched experts' weights
+  cpu_baseline  the float64 oracle on a bounded sample of the workload,
+            timed on this host's cores (a reported baseline, not a target)
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "MoE-layer tokens/sec at 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)"
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+# measured rocprofv3 FETCH_SIZE/WRITE_SIZE factors for a plain copy kernel
+# (bytes counted per byte moved); see profiles/. None until measured.
+TRAFFIC = None
+
+
+def hip_events(n):
+    """Create n hipEvent_t handles through the HIP runtime (the library
+    records them on its own stream)."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs.append(e.value)
+
+    def elapsed(a, b):
+        ms = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy():
+        for e in evs:
+            hip.hipEventDestroy(e)
+    return evs, elapsed, destroy
+
+
+def run_layer(M, torch, w, inp, steps, warmup, marked_steps):
+    s = M.Shape(w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.mode, w.aux_alpha)
+    layer = M.MoELayer(s)
+    args = dict(b_router=inp["b_router"], b_select=inp["b_select"], sh_gate=inp["sh_gate"],
+                sh_up=inp["sh_up"], sh_down=inp["sh_down"])
+    y = torch.empty_like(inp["h"])
+    res = None
+    for _ in range(warmup):
+        res = layer(inp["h"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                    out=y, **args)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        res = layer(inp["h"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                    out=y, **args)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # stage timing with events recorded by the library on its stream
+    evs, elapsed, destroy = hip_events(6 * marked_steps)
+    for i in range(marked_steps):
+        layer(inp["h"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], out=y,
+              events=evs[6 * i:6 * i + 6], **args)
+    torch.cuda.synchronize()
+    names = ["route", "dispatch", "gate_up", "down", "combine"]
+    stage = {n: 0.0 for n in names}
+    total = 0.0
+    for i in range(marked_steps):
+        e = evs[6 * i:6 * i + 6]
+        for j, n in enumerate(names):
+            stage[n] += elapsed(e[j], e[j + 1]) / marked_steps
+        total += elapsed(e[0], e[5]) / marked_steps
+    destroy()
+    counts = res["counts"].cpu().numpy()
+    return wall, stage, total, counts
+
+
+def gateup_work(w, counts):
+    """Algorithmic work of the gate/up stage: flops 4*d*d_ff per routed row
+    (+ 4*d*d_ff_shared per token); bytes: weights of the touched experts
+    once, the gathered token rows, the SwiGLU output."""
+    rows = int(counts.sum())
+    flops = 4.0 * w.d * w.d_ff * rows + 4.0 * w.d * w.d_ff_shared * w.T
+    touched = int((counts > 0).sum())
+    eb = 2 if w.dtype == W.DTYPE_BF16 else 4
+    wbytes = (touched * 2 * w.d_ff * w.d + (2 * w.d_ff_shared * w.d if w.d_ff_shared else 0)) * eb
+    act_bytes = (rows * w.d + rows * w.d_ff + (w.T * (w.d + w.d_ff_shared) if w.d_ff_shared else 0)) * eb
+    return flops, wbytes + act_bytes, touched
+
+
+def layer_work(w, counts):
+    rows = int(counts.sum())
+    flops = 6.0 * w.d * w.d_ff * rows + 6.0 * w.d * w.d_ff_shared * w.T
+    touched = int((counts > 0).sum())
+    eb = 2 if w.dtype == W.DTYPE_BF16 else 4
+    wbytes = (touched * 3 * w.d_ff * w.d + 3 * w.d_ff_shared * w.d) * eb
+    return flops, wbytes, touched
+
+
+def cpu_baseline(w, inp, sample_tokens):
+    """The float64 oracle on the first `sample_tokens` tokens (routing,
+    their experts, combine), timed on the host; inputs are copied to host
+    memory before the clock starts."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    S = min(sample_tokens, w.T)
+    h = inp["h"][:S].float().cpu().numpy()
+    wr = inp["w_router"].float().cpu().numpy()
+    br = None if inp["b_router"] is None else inp["b_router"].cpu().numpy()
+    bs = None if inp["b_select"] is None else inp["b_select"].cpu().numpy()
+    r0 = O.route(h, wr, w.k, w.mode, br, bs)
+    need = sorted(set(r0.ids.reshape(-1).tolist()))
+    host_w = {e: (inp["w_gate"][e].float().cpu().numpy(), inp["w_up"][e].float().cpu().numpy(),
+                  inp["w_down"][e].float().cpu().numpy()) for e in need}
+    sh = None
+    if inp["sh_gate"] is not None:
+        sh = tuple(inp[k_].float().cpu().numpy() for k_ in ("sh_gate", "sh_up", "sh_down"))
+    t0 = time.perf_counter()
+    r = O.route(h, wr, w.k, w.mode, br, bs)
+    d = O.dispatch(r.ids, w.N)
+    rows = O.expert_rows(h, d, w.k, lambda e: host_w[e], sh)
+    O.combine(rows, d.row_of, r.gates, sh is not None)
+    O.load_stats(d.counts, r.stat_prob, w.k, w.aux_alpha)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {w.T} tokens of {w.name} (route, dispatch, their "
+                      f"{len(need)} experts, combine, stats) in float64 numpy, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.MIXTRAL_PREFILL.name, choices=sorted(W.ALL))
+    ap.add_argument("--decode-tokens", type=int, default=16)
+    ap.add_argument("--cpu-sample", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this "
+              "single-GPU build (sharding is described in the design notes, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_mixture_experts_35_amd as M
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    M.lib()   # fail loudly if the HIP library is missing
+
+    w = W.ALL[a.workload]
+    inp = W.device_inputs(w)
+    torch.cuda.synchronize()
+    wall, stage, total_ev, counts = run_layer(M, torch, w, inp, a.steps, a.warmup, a.steps)
+    ms = wall / a.steps * 1e3
+    tok_s = w.T * a.steps / wall
+    flops_gu, bytes_gu, touched = gateup_work(w, counts)
+    lflops, lbytes, _ = layer_work(w, counts)
+    rows_per_expert = counts.sum() / max(touched, 1)
+    mfma_bound = rows_per_expert > 64
+    gu_s = stage["gate_up"] * 1e-3
+    if mfma_bound:
+        achieved = flops_gu / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": TRAFFIC,
+                "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",
+                "algorithmic_per_launch": flops_gu, "avg_launch_ms": stage["gate_up"]}
+    else:
+        achieved = bytes_gu / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": TRAFFIC,
+                "kernel": "skinny_gemm_kernel (gate/up + SwiGLU)",
+                "algorithmic_per_launch": bytes_gu, "avg_launch_ms": stage["gate_up"]}
+    out = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == W.DTYPE_BF16 else "f32",
+        "data": "synthetic (seeded random inputs and random-init weights of this shape)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "k": w.k, "d_ff": w.d_ff,
+                   "d_ff_shared": w.d_ff_shared, "gate_mode": w.mode,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"tflops": lflops / (ms * 1e-3) / 1e12,
+                  "frac_mfma_peak": lflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "weight_gbs": lbytes / (ms * 1e-3) / 1e9,
+                  "stages_ms": stage, "events_total_ms": total_ev,
+                  "experts_touched": touched, "max_rows": int(counts.max())},
+    }
+    if not a.no_decode and w.T > a.decode_tokens:
+        wd = w.replace(name=w.name.split("_T")[0] + f"_decode_T{a.decode_tokens}",
+                       T=a.decode_tokens)
+        dinp = dict(inp)
+        dinp["h"] = inp["h"][:a.decode_tokens].contiguous()
+        dwall, dstage, _, dcounts = run_layer(M, torch, wd, dinp, max(a.steps, 20), a.warmup,
+                                              max(a.steps, 20))
+        dsteps = max(a.steps, 20)
+        dms = dwall / dsteps * 1e3
+        _, dbytes, dtouched = layer_work(wd, dcounts)
+        out["decode"] = {"workload": wd.name, "tokens_per_s": wd.T * dsteps / dwall,
+                         "ms_per_step": dms, "experts_touched": dtouched,
+                         "weight_bytes": dbytes,
+                         "hbm_gbs_layer": dbytes / (dms * 1e-3) / 1e9,
+                         "frac_hbm_peak_layer": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "stages_ms": dstage}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * moe.h — C ABI of the HIP (gfx950 / MI355X) forward pass of one sparse
+ * Mixture-of-Experts FFN layer.
+ *
+ * The layer, as the pages define it:
+ *   router logits   z_t = W_r h_t (+ b_r)
+ *       [page "MOE 专家选择与路由机制" (wuhy-notes), §二 第一步;
+ *        page "MoE：router 怎样选 expert" (cooking-agi), first section]
+ *   scores          softmax over the N experts [wuhy-notes §二 第二步], or a
+ *                   sigmoid per expert [cooking-agi, first section]
+ *   top-k + gates   S_t = TopK(score_t, k) [wuhy-notes §二 第三步], with one of
+ *                   three gate modes (moe_gate_mode)
+ *   dispatch        stable regroup of the (token, slot) pairs by expert
+ *                   [wuhy-notes §三 "Token Dispatch";
+ *                    page "【大模型】MoE（专家混合模型）简介" (horizon.auto) §3 ②]
+ *   experts         E_i(h) = W_down^(i) (SiLU(W_gate^(i) h) ⊙ W_up^(i) h)
+ *                   [wuhy-notes §一], run as a grouped GEMM [wuhy-notes §十二
+ *                   "小矩阵问题"; horizon.auto §8 Kernel row], plus an optional
+ *                   always-on shared expert [wuhy-notes §八]
+ *   combine         y_t = Σ_{i∈S_t} g_ti E_i(h_t) (+ shared), a sum, never an
+ *                   overwrite [cooking-agi, "选好以后，token 怎么过去，输出怎么回来？"]
+ *   load statistics f_i, p_i, L_aux = α·N·Σ f_i p_i
+ *                   [page "拆解 MoE：单个 Token 如何经过专家层" (feinterview),
+ *                    load-balance section]
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless noted; `stream` is a hipStream_t
+ *    passed as void* (NULL = the default stream). Launches are asynchronous
+ *    on `stream`; results are valid once the caller synchronises it.
+ *  - The caller owns every buffer. The library never allocates, frees or
+ *    keeps a pointer after the call returns, and has no mutable global state
+ *    other than a per-thread error message and a per-device cache of the
+ *    compute-unit count.
+ *  - Tensors are contiguous and row-major. Activations (h, y, expert rows)
+ *    and weights have the element type `dtype` (fp32 or bf16); biases,
+ *    gates and statistics are fp32; indices are int32. Weights use the
+ *    [out, in] layout: w_router [N, d]; w_gate, w_up [N, d_ff, d];
+ *    w_down [N, d, d_ff]; shared sh_gate, sh_up [d_ff_shared, d],
+ *    sh_down [d, d_ff_shared].
+ *  - Every pointer that is read or written with vector loads (activations,
+ *    weights, expert rows, y) must be 16-byte aligned.
+ *  - Arithmetic: fp32 accumulation everywhere. On the bf16 path the SwiGLU
+ *    activations and the expert output rows are stored as bf16 (round to
+ *    nearest even) and y is rounded to bf16 at the end; the fp32 path
+ *    stores fp32 throughout. Ties in top-k go to the lower expert index.
+ *  - Errors: every error the host can detect is returned BEFORE anything is
+ *    launched, and no HIP call is made before argument validation succeeds:
+ *      MOE_ERR_INVALID_ARG  bad shape (T<0, d/N/k/d_ff<1, d_ff_shared<0),
+ *                           k > N (not enough candidates), unknown dtype or
+ *                           mode, a required pointer NULL, b_select given in
+ *                           modes A/B or missing in mode C, misaligned
+ *                           pointer, non-finite aux_alpha;
+ *      MOE_ERR_UNSUPPORTED  N > 512, k > 16, bf16 with d, d_ff or d_ff_shared
+ *                           not a multiple of 64, or sizes whose element
+ *                           counts exceed 2^31-1 per tensor;
+ *      MOE_ERR_WORKSPACE    ws_bytes below the size this call needs (or ws
+ *                           NULL when that size is non-zero);
+ *      MOE_ERR_HIP          a HIP launch or runtime error.
+ *    T = 0 is a valid no-op that still validates its arguments.
+ *    moe_last_error() returns a human-readable detail for the calling thread.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_TOPK 16
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  /* Mode A: top-k by softmax probability, gates renormalised over the k
+   * selected (equal to a softmax over the selected logits).
+   * [wuhy-notes §二 第三步 gate formula; cooking-agi, first section] */
+  MOE_GATE_SOFTMAX_RENORM = 0,
+  /* Mode B: top-k by softmax probability, each gate keeps its full-softmax
+   * probability, no renormalisation (Switch Transformer top-1; any k).
+   * [cooking-agi, first section (Switch remark); pwwt.cn §2.1 route()] */
+  MOE_GATE_SOFTMAX_FULL = 1,
+  /* Mode C: s = sigmoid(z); select the top-k of s + b_select; gates are the
+   * UNBIASED s of the selected, renormalised to sum 1. The bias acts on
+   * selection only. [cooking-agi, first section (DeepSeek-V3 remark);
+   * feinterview load-balance section (bias placement left open)] */
+  MOE_GATE_SIGMOID_BIAS_RENORM = 2
+} moe_gate_mode;
+
+/* Host struct describing one layer call. */
+typedef struct {
+  int32_t T;            /* tokens (rows of h)                                  */
+  int32_t d;            /* model width                                         */
+  int32_t N;            /* routed experts, 1..512                              */
+  int32_t k;            /* experts selected per token, 1..min(N,16)            */
+  int32_t d_ff;         /* routed expert hidden width                          */
+  int32_t d_ff_shared;  /* shared expert hidden width, 0 = no shared expert    */
+  int32_t dtype;        /* moe_dtype of activations and weights               */
+  int32_t mode;         /* moe_gate_mode                                       */
+  float aux_alpha;      /* α of L_aux = α·N·Σ f_i p_i                          */
+} moe_shape;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static string for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if
+ * none). Valid until the next call on this thread. */
+const char* moe_last_error(void);
+
+/* Host, pure: workspace bytes that suffice for EVERY call below with this
+ * shape (the fused layer needs the most). 0 for an invalid shape. The
+ * individual calls need: moe_route — T·N + blocks·N + N floats;
+ * moe_dispatch — none; moe_expert_ffn — the SwiGLU activations
+ * (T·k·d_ff + T·d_ff_shared elements); moe_combine — none. */
+size_t moe_workspace_bytes(const moe_shape* s);
+
+/* Router: logits, scores, top-k and gates (steps 1-4).
+ *   h          [T, d]   dtype
+ *   w_router   [N, d]   dtype
+ *   b_router   [N] fp32, nullable (router bias b_r)
+ *   b_select   [N] fp32, mode C only (must be NULL in modes A and B)
+ *   topk_ids   [T, k] int32 out: slot j holds the (j+1)-th best expert
+ *   topk_gates [T, k] fp32  out: gate of that slot
+ *   p_mean     [N] fp32 out, nullable: p_i = mean_t P_ti (modes A/B: the
+ *              softmax probability; mode C: s_ti / Σ_j s_tj), reduced in a
+ *              fixed order (bit-reproducible).
+ * [wuhy-notes §二 第一步–第三步; cooking-agi first section] */
+moe_status moe_route(const moe_shape* s, const void* h, const void* w_router,
+                     const float* b_router, const float* b_select,
+                     int32_t* topk_ids, float* topk_gates, float* p_mean,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: stable regroup of the T·k flat slots f = t·k + j by expert.
+ *   topk_ids [T, k] int32 in, every id in [0, N) (precondition; not checked
+ *            on the device)
+ *   counts   [N]   int32 out: rows per expert
+ *   offsets  [N+1] int32 out: exclusive prefix of counts (offsets[N] = T·k)
+ *   perm_src [T·k] int32 out: bucket row r -> flat slot; expert e's rows are
+ *            offsets[e]..offsets[e+1]-1, in ascending slot (= token) order
+ *   row_of   [T·k] int32 out: flat slot -> bucket row (inverse of perm_src)
+ *   p_mean   [N] fp32 in, nullable (needed only for l_aux)
+ *   f_out    [N] fp32 out, nullable: f_i = counts_i / (T·k)
+ *   l_aux    [1] fp32 out, nullable (requires p_mean): α·N·Σ f_i p_i
+ * Deterministic: no atomic decides any order or any float sum.
+ * [wuhy-notes §三 Token Dispatch; horizon.auto §3 ②; feinterview
+ *  load-balance section] */
+moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids,
+                        int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                        int32_t* row_of, const float* p_mean, float* f_out,
+                        float* l_aux, void* ws, size_t ws_bytes, void* stream);
+
+/* Experts: grouped SwiGLU FFN over the dispatched rows (steps 5-6).
+ *   out_rows [T·k (+T if d_ff_shared), d] dtype out:
+ *     out_rows[r] = E_e(h[perm_src[r] / k]) for bucket row r of expert e;
+ *     out_rows[T·k + t] = E_shared(h[t]) when a shared expert is present.
+ *   sh_gate/sh_up/sh_down must be given iff d_ff_shared > 0.
+ * [wuhy-notes §一 expert formula, §八 shared expert, §十二 小矩阵问题] */
+moe_status moe_expert_ffn(const moe_shape* s, const void* h,
+                          const int32_t* perm_src, const int32_t* offsets,
+                          const void* w_gate, const void* w_up,
+                          const void* w_down, const void* sh_gate,
+                          const void* sh_up, const void* sh_down,
+                          void* out_rows, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Combine: y[t] = out_rows[T·k + t] (shared, if any) +
+ *          Σ_{j<k} topk_gates[t, j] · out_rows[row_of[t·k + j]],
+ * accumulated in fp32 in that order, stored as dtype.
+ * [cooking-agi, "选好以后，token 怎么过去，输出怎么回来？"; horizon.auto §3 ④] */
+moe_status moe_combine(const moe_shape* s, const void* out_rows,
+                       const int32_t* row_of, const float* topk_gates,
+                       void* y, void* stream);
+
+/* The whole layer in one call (route, dispatch, experts, combine, stats),
+ * no host synchronisation inside.
+ *   y [T, d] dtype out (required).
+ *   topk_ids, topk_gates, counts, f_out, p_out, l_aux: nullable outputs
+ *   (the workspace holds whatever is not returned). */
+moe_status moe_layer_fused(const moe_shape* s, const void* h,
+                           const void* w_router, const float* b_router,
+                           const float* b_select, const void* w_gate,
+                           const void* w_up, const void* w_down,
+                           const void* sh_gate, const void* sh_up,
+                           const void* sh_down, void* y, int32_t* topk_ids,
+                           float* topk_gates, int32_t* counts, float* f_out,
+                           float* p_out, float* l_aux, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* moe_layer_fused that also records caller-created hipEvent_t handles on
+ * `stream` at the stage boundaries, for timing: events[0] before routing,
+ * [1] after routing, [2] after dispatch, [3] after the gate/up GEMM
+ * (SwiGLU), [4] after the down GEMM, [5] after combine. `events` is a host
+ * array of 6 hipEvent_t (as void*), all non-NULL. */
+moe_status moe_layer_fused_marked(const moe_shape* s, const void* h,
+                                  const void* w_router, const float* b_router,
+                                  const float* b_select, const void* w_gate,
+                                  const void* w_up, const void* w_down,
+                                  const void* sh_gate, const void* sh_up,
+                                  const void* sh_down, void* y,
+                                  int32_t* topk_ids, float* topk_gates,
+                                  int32_t* counts, float* f_out, float* p_out,
+                                  float* l_aux, void* ws, size_t ws_bytes,
+                                  void* stream, void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

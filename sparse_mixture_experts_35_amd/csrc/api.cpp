@@ -1,0 +1,448 @@
+// C ABI of the MoE layer: argument validation, workspace layout and the
+// launch sequence route -> dispatch -> expert GEMMs -> combine. Every check
+// runs before the first HIP call, so invalid arguments never reach the GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+constexpr int64_t kI32Max = 2147483647LL;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+size_t esize(const moe_shape* s) { return s->dtype == MOE_BF16 ? 2 : 4; }
+
+// ------------------------------------------------------------ validation
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+  if (s->d < 1 || s->N < 1 || s->k < 1 || s->d_ff < 1)
+    return fail(MOE_ERR_INVALID_ARG, "d, N, k and d_ff must be >= 1");
+  if (s->d_ff_shared < 0) return fail(MOE_ERR_INVALID_ARG, "d_ff_shared < 0");
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (s->mode < MOE_GATE_SOFTMAX_RENORM || s->mode > MOE_GATE_SIGMOID_BIAS_RENORM)
+    return fail(MOE_ERR_INVALID_ARG, "unknown gate mode");
+  if (!std::isfinite(s->aux_alpha)) return fail(MOE_ERR_INVALID_ARG, "aux_alpha is not finite");
+  if (s->k > s->N) return fail(MOE_ERR_INVALID_ARG, "k > N: not enough candidate experts");
+  if (s->N > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "N > 512");
+  if (s->k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k > 16");
+  if (s->dtype == MOE_BF16 &&
+      (s->d % 64 || s->d_ff % 64 || s->d_ff_shared % 64))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d, d_ff and d_ff_shared multiples of 64");
+  const int64_t T = s->T, R = T * s->k, Rt = R + (s->d_ff_shared ? T : 0);
+  const int64_t lim[] = {R, Rt * s->d, R * s->d_ff, T * s->d_ff_shared, T * s->d,
+                         (int64_t)s->d_ff * s->d, (int64_t)s->d_ff_shared * s->d,
+                         (int64_t)s->N * s->d, T * s->N * moe::kRouterMaxSplits};
+  for (int64_t v : lim)
+    if (v > kI32Max) return fail(MOE_ERR_UNSUPPORTED, "a tensor exceeds 2^31-1 elements");
+  return MOE_OK;
+}
+
+moe_status need(const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  return MOE_OK;
+}
+moe_status need16(const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+  return MOE_OK;
+}
+moe_status need4(const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned4(p)) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is not 4-byte aligned");
+  return MOE_OK;
+}
+moe_status opt4(const void* p, const char* name) {
+  if (p && !aligned4(p)) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is not 4-byte aligned");
+  return MOE_OK;
+}
+
+#define TRY(x)                      \
+  do {                              \
+    const moe_status _st = (x);     \
+    if (_st != MOE_OK) return _st;  \
+  } while (0)
+
+moe_status check_bias(const moe_shape* s, const float* b_router, const float* b_select) {
+  TRY(opt4(b_router, "b_router"));
+  if (s->mode == MOE_GATE_SIGMOID_BIAS_RENORM) {
+    TRY(need4(b_select, "b_select (mode C)"));
+  } else if (b_select) {
+    return fail(MOE_ERR_INVALID_ARG, "b_select must be NULL in the softmax gate modes");
+  }
+  return MOE_OK;
+}
+
+moe_status check_shared(const moe_shape* s, const void* sg, const void* su, const void* sd) {
+  if (s->d_ff_shared) {
+    TRY(need16(sg, "sh_gate"));
+    TRY(need16(su, "sh_up"));
+    TRY(need16(sd, "sh_down"));
+  } else if (sg || su || sd) {
+    return fail(MOE_ERR_INVALID_ARG, "shared-expert weights given but d_ff_shared = 0");
+  }
+  return MOE_OK;
+}
+
+// ------------------------------------------------------- workspace layout
+struct RouteWs {
+  size_t z, p_part, end;
+};
+RouteWs route_ws(const moe_shape* s, size_t base) {
+  RouteWs w;
+  w.z = base;
+  w.p_part = align_up(w.z + sizeof(float) * (size_t)moe::kRouterMaxSplits * s->T * s->N);
+  w.end = align_up(w.p_part + sizeof(float) * (size_t)moe::route_select_blocks(s->T) * s->N);
+  return w;
+}
+size_t act_bytes(const moe_shape* s) {
+  const size_t R = (size_t)s->T * s->k;
+  return esize(s) * (R * s->d_ff + (size_t)s->T * s->d_ff_shared);
+}
+struct FusedWs {
+  RouteWs r;
+  size_t p_mean, ids, gates, counts, offsets, perm, row_of, f, act, rows, end;
+};
+FusedWs fused_ws(const moe_shape* s) {
+  FusedWs w;
+  w.r = route_ws(s, 0);
+  const size_t T = s->T, N = s->N, R = T * s->k;
+  w.p_mean = w.r.end;
+  w.ids = align_up(w.p_mean + 4 * N);
+  w.gates = align_up(w.ids + 4 * R);
+  w.counts = align_up(w.gates + 4 * R);
+  w.offsets = align_up(w.counts + 4 * N);
+  w.perm = align_up(w.offsets + 4 * (N + 1));
+  w.row_of = align_up(w.perm + 4 * R);
+  w.f = align_up(w.row_of + 4 * R);
+  w.act = align_up(w.f + 4 * N + 4);
+  w.rows = align_up(w.act + act_bytes(s));
+  w.end = align_up(w.rows + esize(s) * (R + (s->d_ff_shared ? T : 0)) * s->d);
+  return w;
+}
+
+moe_status check_ws(void* ws, size_t ws_bytes, size_t need_bytes) {
+  if (need_bytes == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < need_bytes)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_bytes) +
+                                       " bytes, got " + std::to_string(ws_bytes));
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------- device info
+int num_cu() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 64 && cache[dev]) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+moe_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// ------------------------------------------------------------ stage impls
+moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
+                      const float* b_router, const float* b_select, int32_t* ids,
+                      float* gates, float* p_mean, float* z_part, float* p_part,
+                      hipStream_t st) {
+  int splits = 1;
+  if (s->dtype == MOE_BF16) {
+    splits = moe::router_splits(s->T, s->d, s->N);
+    TRY(hip_check(moe::launch_router_gemm_bf16(h, w_router, z_part, s->T, s->d, s->N, splits, st),
+                  "router GEMM"));
+  } else {
+    TRY(hip_check(moe::launch_router_logits_f32(static_cast<const float*>(h),
+                                                static_cast<const float*>(w_router), z_part,
+                                                s->T, s->d, s->N, st),
+                  "router logits"));
+  }
+  TRY(hip_check(moe::launch_route_select(z_part, splits, b_router, b_select, ids, gates,
+                                         p_mean ? p_part : nullptr, s->T, s->N, s->k, s->mode,
+                                         st),
+                "route select"));
+  if (p_mean)
+    TRY(hip_check(moe::launch_p_reduce(p_part, p_mean, moe::route_select_blocks(s->T), s->T,
+                                       s->N, st),
+                  "p reduce"));
+  return MOE_OK;
+}
+
+moe_status dispatch_impl(const moe_shape* s, const int32_t* ids, int32_t* counts,
+                         int32_t* offsets, int32_t* perm_src, int32_t* row_of,
+                         const float* p_mean, float* f_out, float* l_aux, hipStream_t st) {
+  return hip_check(moe::launch_dispatch(ids, s->T, s->k, s->N, counts, offsets, perm_src, row_of,
+                                        p_mean, f_out, l_aux, s->aux_alpha, st),
+                   "dispatch");
+}
+
+moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32_t* perm_src,
+                     const int32_t* offsets, const void* w_gate, const void* w_up,
+                     const void* w_down, const void* sh_gate, const void* sh_up,
+                     const void* sh_down, void* out_rows, void* act, hipStream_t st) {
+  const int T = s->T, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
+  const int R = T * s->k;
+  const bool bf16 = s->dtype == MOE_BF16;
+  const int ncu = bf16 ? num_cu() : 0;
+  void* act_sh = static_cast<char*>(act) + esize(s) * (size_t)R * dff;
+  auto run = [&](const moe::GroupedProblem& p, bool gu) -> hipError_t {
+    if (bf16) return gu ? moe::launch_gateup_bf16(p, ncu, st) : moe::launch_down_bf16(p, ncu, st);
+    return gu ? moe::launch_gateup_f32(p, st) : moe::launch_down_f32(p, st);
+  };
+  moe::GroupedProblem p{};
+  if (gateup) {
+    p = moe::GroupedProblem{h, d, perm_src, s->k, offsets, s->N, R, T, w_gate, w_up,
+                            (int64_t)dff * d, d, dff, d, act, dff, 0};
+    TRY(hip_check(run(p, true), "gate/up GEMM"));
+    if (dfs) {
+      p = moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d, dfs, d,
+                              act_sh, dfs, 0};
+      TRY(hip_check(run(p, true), "shared gate/up GEMM"));
+    }
+  } else {
+    p = moe::GroupedProblem{act, dff, nullptr, 1, offsets, s->N, R, T, w_down, nullptr,
+                            (int64_t)d * dff, dff, d, dff, out_rows, d, 0};
+    TRY(hip_check(run(p, false), "down GEMM"));
+    if (dfs) {
+      p = moe::GroupedProblem{act_sh, dfs, nullptr, 1, nullptr, 1, T, T, sh_down, nullptr, 0,
+                              dfs, d, dfs, out_rows, d, (int64_t)R};
+      TRY(hip_check(run(p, false), "shared down GEMM"));
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status combine_impl(const moe_shape* s, const void* out_rows, const int32_t* row_of,
+                        const float* gates, void* y, hipStream_t st) {
+  return hip_check(moe::launch_combine(out_rows, row_of, gates, y, s->T, s->k, s->d,
+                                       s->d_ff_shared ? 1 : 0, s->dtype == MOE_BF16, st),
+                   "combine");
+}
+
+moe_status mark(void* const* events, int i, hipStream_t st) {
+  if (!events) return MOE_OK;
+  return hip_check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st), "event record");
+}
+
+moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
+                      const float* b_router, const float* b_select, const void* w_gate,
+                      const void* w_up, const void* w_down, const void* sh_gate,
+                      const void* sh_up, const void* sh_down, void* y, int32_t* topk_ids,
+                      float* topk_gates, int32_t* counts, float* f_out, float* p_out,
+                      float* l_aux, void* ws, size_t ws_bytes, void* stream,
+                      void* const* events) {
+  TRY(check_shape(s));
+  TRY(need16(h, "h"));
+  TRY(need16(w_router, "w_router"));
+  TRY(check_bias(s, b_router, b_select));
+  TRY(need16(w_gate, "w_gate"));
+  TRY(need16(w_up, "w_up"));
+  TRY(need16(w_down, "w_down"));
+  TRY(check_shared(s, sh_gate, sh_up, sh_down));
+  TRY(need16(y, "y"));
+  TRY(opt4(topk_ids, "topk_ids"));
+  TRY(opt4(topk_gates, "topk_gates"));
+  TRY(opt4(counts, "counts"));
+  TRY(opt4(f_out, "f_out"));
+  TRY(opt4(p_out, "p_out"));
+  TRY(opt4(l_aux, "l_aux"));
+  if (events)
+    for (int i = 0; i < 6; ++i)
+      if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[] holds a NULL event");
+  const FusedWs L = fused_ws(s);
+  TRY(check_ws(ws, ws_bytes, L.end));
+  if (s->T == 0) return MOE_OK;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = topk_gates ? topk_gates : at<float>(ws, L.gates);
+  int32_t* cnt = counts ? counts : at<int32_t>(ws, L.counts);
+  const bool want_p = p_out || l_aux;
+  float* p_mean = want_p ? (p_out ? p_out : at<float>(ws, L.p_mean)) : nullptr;
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* row_of = at<int32_t>(ws, L.row_of);
+  void* act = at<char>(ws, L.act);
+  void* rows = at<char>(ws, L.rows);
+
+  TRY(mark(events, 0, st));
+  TRY(route_impl(s, h, w_router, b_router, b_select, ids, gates, p_mean, at<float>(ws, L.r.z),
+                 at<float>(ws, L.r.p_part), st));
+  TRY(mark(events, 1, st));
+  TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, st));
+  TRY(mark(events, 2, st));
+  TRY(ffn_stage(s, true, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
+                act, st));
+  TRY(mark(events, 3, st));
+  TRY(ffn_stage(s, false, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
+                act, st));
+  TRY(mark(events, 4, st));
+  TRY(combine_impl(s, rows, row_of, gates, y, st));
+  TRY(mark(events, 5, st));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return fused_ws(s).end;
+}
+
+moe_status moe_route(const moe_shape* s, const void* h, const void* w_router,
+                     const float* b_router, const float* b_select, int32_t* topk_ids,
+                     float* topk_gates, float* p_mean, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  TRY(check_shape(s));
+  TRY(need16(h, "h"));
+  TRY(need16(w_router, "w_router"));
+  TRY(check_bias(s, b_router, b_select));
+  TRY(need4(topk_ids, "topk_ids"));
+  TRY(need4(topk_gates, "topk_gates"));
+  TRY(opt4(p_mean, "p_mean"));
+  const RouteWs L = route_ws(s, 0);
+  TRY(check_ws(ws, ws_bytes, L.end));
+  if (s->T == 0) return MOE_OK;
+  return route_impl(s, h, w_router, b_router, b_select, topk_ids, topk_gates, p_mean,
+                    at<float>(ws, L.z), at<float>(ws, L.p_part), static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids, int32_t* counts,
+                        int32_t* offsets, int32_t* perm_src, int32_t* row_of,
+                        const float* p_mean, float* f_out, float* l_aux, void* ws,
+                        size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  g_err.clear();
+  TRY(check_shape(s));
+  TRY(need4(topk_ids, "topk_ids"));
+  TRY(need4(counts, "counts"));
+  TRY(need4(offsets, "offsets"));
+  TRY(need4(perm_src, "perm_src"));
+  TRY(need4(row_of, "row_of"));
+  TRY(opt4(p_mean, "p_mean"));
+  TRY(opt4(f_out, "f_out"));
+  TRY(opt4(l_aux, "l_aux"));
+  if (l_aux && !p_mean) return fail(MOE_ERR_INVALID_ARG, "l_aux requested without p_mean");
+  if (s->T == 0) return MOE_OK;
+  return dispatch_impl(s, topk_ids, counts, offsets, perm_src, row_of, p_mean, f_out, l_aux,
+                       static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn(const moe_shape* s, const void* h, const int32_t* perm_src,
+                          const int32_t* offsets, const void* w_gate, const void* w_up,
+                          const void* w_down, const void* sh_gate, const void* sh_up,
+                          const void* sh_down, void* out_rows, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_err.clear();
+  TRY(check_shape(s));
+  TRY(need16(h, "h"));
+  TRY(need4(perm_src, "perm_src"));
+  TRY(need4(offsets, "offsets"));
+  TRY(need16(w_gate, "w_gate"));
+  TRY(need16(w_up, "w_up"));
+  TRY(need16(w_down, "w_down"));
+  TRY(check_shared(s, sh_gate, sh_up, sh_down));
+  TRY(need16(out_rows, "out_rows"));
+  TRY(check_ws(ws, ws_bytes, align_up(act_bytes(s))));
+  if (s->T == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY(ffn_stage(s, true, h, perm_src, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
+                out_rows, ws, st));
+  return ffn_stage(s, false, h, perm_src, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
+                   out_rows, ws, st);
+}
+
+moe_status moe_combine(const moe_shape* s, const void* out_rows, const int32_t* row_of,
+                       const float* topk_gates, void* y, void* stream) {
+  g_err.clear();
+  TRY(check_shape(s));
+  TRY(need16(out_rows, "out_rows"));
+  TRY(need4(row_of, "row_of"));
+  TRY(need4(topk_gates, "topk_gates"));
+  TRY(need16(y, "y"));
+  if (s->T == 0) return MOE_OK;
+  return combine_impl(s, out_rows, row_of, topk_gates, y, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_layer_fused(const moe_shape* s, const void* h, const void* w_router,
+                           const float* b_router, const float* b_select, const void* w_gate,
+                           const void* w_up, const void* w_down, const void* sh_gate,
+                           const void* sh_up, const void* sh_down, void* y, int32_t* topk_ids,
+                           float* topk_gates, int32_t* counts, float* f_out, float* p_out,
+                           float* l_aux, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
+                    sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, ws, ws_bytes,
+                    stream, nullptr);
+}
+
+moe_status moe_layer_fused_marked(const moe_shape* s, const void* h, const void* w_router,
+                                  const float* b_router, const float* b_select,
+                                  const void* w_gate, const void* w_up, const void* w_down,
+                                  const void* sh_gate, const void* sh_up, const void* sh_down,
+                                  void* y, int32_t* topk_ids, float* topk_gates,
+                                  int32_t* counts, float* f_out, float* p_out, float* l_aux,
+                                  void* ws, size_t ws_bytes, void* stream,
+                                  void* const* events) {
+  g_err.clear();
+  if (!events) return fail(MOE_ERR_INVALID_ARG, "events is NULL");
+  return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
+                    sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, ws, ws_bytes,
+                    stream, events);
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Host-side launchers of the MoE HIP kernels (one translation unit each).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- routing
+constexpr int kRouterMaxSplits = 8;
+// Split-K partial logits z_part[s][T][N] (fp32) = h[:, K_s] · w_router[:, K_s]^T,
+// s < router_splits(T, d, N) (bf16), or one slice with the fp32 kernel.
+int router_splits(int T, int d, int N);
+hipError_t launch_router_gemm_bf16(const void* h, const void* w_router,
+                                   float* z_part, int T, int d, int N,
+                                   int splits, hipStream_t st);
+hipError_t launch_router_logits_f32(const float* h, const float* w_router,
+                                    float* z, int T, int d, int N,
+                                    hipStream_t st);
+// z = sum of the partial slices + b_router; scores, top-k, gates, and
+// per-block sums of the routing probabilities
+int route_select_blocks(int T);
+hipError_t launch_route_select(const float* z_part, int splits,
+                               const float* b_router, const float* b_select,
+                               int32_t* ids, float* gates, float* p_part,
+                               int T, int N, int k, int mode, hipStream_t st);
+hipError_t launch_p_reduce(const float* p_part, float* p_mean, int blocks,
+                           int T, int N, hipStream_t st);
+
+// --------------------------------------------------------------- dispatch
+hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N,
+                           int32_t* counts, int32_t* offsets,
+                           int32_t* perm_src, int32_t* row_of,
+                           const float* p_mean, float* f_out, float* l_aux,
+                           float alpha, hipStream_t st);
+
+// ---------------------------------------------------------------- experts
+// One grouped problem: rows of A gathered through perm (token = perm[r] /
+// kdiv, or r when perm is NULL), groups given by offsets (NULL: one group
+// of M rows), B rows of group g at B + g*b_gstride.
+struct GroupedProblem {
+  const void* A;
+  int lda;
+  const int32_t* perm;
+  int kdiv;
+  const int32_t* offsets;
+  int groups;
+  int M;          // rows when offsets == NULL; upper bound of rows otherwise
+  int max_rows;   // upper bound on the rows of any one group
+  const void* B0;
+  const void* B1;  // up projection (gate/up GEMM only)
+  int64_t b_gstride;
+  int ldb;
+  int Ncols;
+  int K;
+  void* C;
+  int ldc;
+  int64_t c_row0;
+};
+
+// Act = SiLU(A·B0^T) ⊙ (A·B1^T)   (bf16 in/out, fp32 accumulate)
+hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu,
+                              hipStream_t st);
+// C = A·B0^T                        (bf16 in/out, fp32 accumulate)
+hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu,
+                            hipStream_t st);
+// fp32 versions (plain FMA kernels)
+hipError_t launch_gateup_f32(const GroupedProblem& p, hipStream_t st);
+hipError_t launch_down_f32(const GroupedProblem& p, hipStream_t st);
+
+// ---------------------------------------------------------------- combine
+hipError_t launch_combine(const void* out_rows, const int32_t* row_of,
+                          const float* gates, void* y, int T, int k, int d,
+                          int has_shared, int bf16, hipStream_t st);
+
+}  // namespace moe

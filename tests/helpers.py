@@ -1,0 +1,89 @@
+"""Shared helpers of the GPU parity tests: moving seeded host inputs to the
+device in the library's dtypes, reading results back, and the comparison
+rules (near-tie exclusion, per-row relative error)."""
+import numpy as np
+
+import workloads as W
+from oracle import moe_oracle as O
+
+TOL = {W.DTYPE_F32: 1e-4, W.DTYPE_BF16: 2e-2}
+NEAR_TIE = 1e-4
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev(a, dtype, device="cuda"):
+    """numpy array (fp32 values; bf16-representable when dtype is bf16) ->
+    device tensor of that dtype, bit-exact."""
+    if a is None:
+        return None
+    t = torch()
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == W.DTYPE_BF16:
+        bits = W.bf16_bits(a).view(np.int16)
+        return t.from_numpy(bits.copy()).to(device).view(t.bfloat16)
+    return t.from_numpy(a.copy()).to(device)
+
+
+def dev_f32(a, device="cuda"):
+    return None if a is None else torch().from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def host(t):
+    """device tensor -> float64 (or int64) numpy array."""
+    tt = torch()
+    t = t.detach().cpu()
+    if t.dtype in (tt.int32, tt.int64):
+        return t.numpy().astype(np.int64)
+    return t.float().numpy().astype(np.float64)
+
+
+def tdtype(dtype):
+    t = torch()
+    return t.bfloat16 if dtype == W.DTYPE_BF16 else t.float32
+
+
+def oracle_weights(inp):
+    return O.weights_getter(inp["w_gate"], inp["w_up"], inp["w_down"])
+
+
+def oracle_shared(inp):
+    if inp.get("sh_gate") is None:
+        return None
+    return (inp["sh_gate"], inp["sh_up"], inp["sh_down"])
+
+
+def check_ids(gpu_ids, oracle_routing, k):
+    """Selected experts must match exactly for every token whose k-th and
+    (k+1)-th selection scores are at least NEAR_TIE apart. For near-tie
+    tokens the GPU's selection must still be a valid top-k within that
+    margin. Returns the near-tie mask."""
+    near = O.near_tie_tokens(oracle_routing.gap, NEAR_TIE)
+    ok = ~near
+    assert np.array_equal(gpu_ids[ok], oracle_routing.ids[ok]), \
+        np.nonzero((gpu_ids != oracle_routing.ids).any(axis=1) & ok)[0][:10]
+    for t in np.nonzero(near)[0]:
+        sel = oracle_routing.sel[t]
+        kth = np.sort(sel)[::-1][k - 1]
+        assert len(set(gpu_ids[t].tolist())) == k
+        assert np.all(sel[gpu_ids[t]] >= kth - NEAR_TIE)
+    return near
+
+
+def check_close_rows(y, y_ref, tol, mask=None, what="y"):
+    err = O.row_rel_err(y, y_ref)
+    if mask is not None:
+        err = err[mask]
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, f"{what}: max per-row relative error {worst:.3e} > {tol:.1e}"
+    return worst
+
+
+def check_gates(g, g_ref, tol, mask):
+    err = np.abs(g - g_ref) / np.maximum(np.abs(g_ref), 1e-30)
+    worst = float(err[mask].max()) if mask.any() else 0.0
+    assert worst <= tol, f"gates: max relative error {worst:.3e} > {tol:.1e}"
+    return worst
