@@ -112,7 +112,7 @@ RouteWs route_ws(const moe_shape* s, size_t base) {
   RouteWs w;
   w.z = base;
   w.p_part = align_up(w.z + sizeof(float) * (size_t)moe::kRouterMaxSplits * s->T * s->N);
-  w.end = align_up(w.p_part + sizeof(float) * (size_t)moe::route_select_blocks(s->T) * s->N);
+  w.end = align_up(w.p_part + sizeof(float) * (size_t)moe::route_select_blocks(s->T, s->N) * s->N);
   return w;
 }
 size_t act_bytes(const moe_shape* s) {
@@ -198,7 +198,7 @@ moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
                                          st),
                 "route select"));
   if (p_mean)
-    TRY(hip_check(moe::launch_p_reduce(p_part, p_mean, moe::route_select_blocks(s->T), s->T,
+    TRY(hip_check(moe::launch_p_reduce(p_part, p_mean, moe::route_select_blocks(s->T, s->N), s->T,
                                        s->N, st),
                   "p reduce"));
   return MOE_OK;
@@ -220,6 +220,7 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
   const int R = T * s->k;
   const bool bf16 = s->dtype == MOE_BF16;
   const int ncu = bf16 ? num_cu() : 0;
+  const size_t esz = esize(s);
   void* act_sh = static_cast<char*>(act) + esize(s) * (size_t)R * dff;
   auto run = [&](const moe::GroupedProblem& p, bool gu) -> hipError_t {
     if (bf16) return gu ? moe::launch_gateup_bf16(p, ncu, st) : moe::launch_down_bf16(p, ncu, st);
@@ -228,20 +229,20 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
   moe::GroupedProblem p{};
   if (gateup) {
     p = moe::GroupedProblem{h, d, perm_src, s->k, offsets, s->N, R, T, w_gate, w_up,
-                            (int64_t)dff * d, d, dff, d, act, dff, 0};
+                            (int64_t)dff * d, d, dff, d, act, dff, 0, (uint32_t)(esz * T * d)};
     TRY(hip_check(run(p, true), "gate/up GEMM"));
     if (dfs) {
       p = moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d, dfs, d,
-                              act_sh, dfs, 0};
+                              act_sh, dfs, 0, (uint32_t)(esz * T * d)};
       TRY(hip_check(run(p, true), "shared gate/up GEMM"));
     }
   } else {
     p = moe::GroupedProblem{act, dff, nullptr, 1, offsets, s->N, R, T, w_down, nullptr,
-                            (int64_t)d * dff, dff, d, dff, out_rows, d, 0};
+                            (int64_t)d * dff, dff, d, dff, out_rows, d, 0, (uint32_t)(esz * R * dff)};
     TRY(hip_check(run(p, false), "down GEMM"));
     if (dfs) {
       p = moe::GroupedProblem{act_sh, dfs, nullptr, 1, nullptr, 1, T, T, sh_down, nullptr, 0,
-                              dfs, d, dfs, out_rows, d, (int64_t)R};
+                              dfs, d, dfs, out_rows, d, (int64_t)R, (uint32_t)(esz * T * dfs)};
       TRY(hip_check(run(p, false), "shared down GEMM"));
     }
   }

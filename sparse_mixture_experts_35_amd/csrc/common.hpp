@@ -15,6 +15,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Raw buffer resource over [base, base + bytes): 32-bit offsets, reads past
+// the extent return zero. Dword 3 selects the 32-bit data format used for
+// untyped buffer access on this architecture.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(const Rsrc& r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -63,8 +75,9 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b,
       __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// SiLU(x) = x·sigmoid(x) with the hardware exp and reciprocal (bf16 path).
 __device__ __forceinline__ float silu_fast(float x) {
-  return x / (1.0f + __expf(-x));
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
 __device__ __forceinline__ float silu_precise(float x) {

@@ -48,24 +48,22 @@ struct TileCfg {
   static_assert(FM >= 1 && FN >= 1, "tile too small");
 };
 
+enum Epi { EPI_SWIGLU = 0, EPI_STORE_BF16 = 1 };
+
 // Global -> registers for one BK slab. Thread tid loads 16-byte chunk
 // (tid & 7) of rows (tid >> 3) + 32 i: eight lanes cover one 128-byte row
-// segment, so every load instruction is fully coalesced.
+// segment, so every load instruction is fully coalesced. Raw buffer loads:
+// a 32-bit per-lane byte offset, the K position as a scalar offset, and the
+// buffer's extent in the descriptor (reads past it return zero).
 template <class C>
 __device__ __forceinline__ void load_slab(u32x4 (&ra)[C::ACH], u32x4 (&rb)[C::BCH],
-                                          const bf16_t* __restrict__ A,
-                                          const int32_t (&aoff)[C::ACH],
-                                          const bf16_t* __restrict__ B0,
-                                          const bf16_t* __restrict__ B1,
-                                          const int32_t (&boff)[C::BCH], int k0) {
+                                          const Rsrc& A, const uint32_t (&aoff)[C::ACH],
+                                          const Rsrc& B0, const Rsrc& B1,
+                                          const uint32_t (&boff)[C::BCH], int kbytes) {
 #pragma unroll
-  for (int i = 0; i < C::ACH; ++i)
-    ra[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + k0);
+  for (int i = 0; i < C::ACH; ++i) ra[i] = buffer_load16(A, aoff[i], kbytes);
 #pragma unroll
-  for (int i = 0; i < C::BCH; ++i) {
-    const bf16_t* B = (i < C::BCH0) ? B0 : B1;
-    rb[i] = *reinterpret_cast<const u32x4*>(B + boff[i] + k0);
-  }
+  for (int i = 0; i < C::BCH; ++i) rb[i] = buffer_load16((i < C::BCH0) ? B0 : B1, boff[i], kbytes);
 }
 
 template <class C>
@@ -116,28 +114,97 @@ __device__ __forceinline__ void mma_slab(const char* __restrict__ stage,
 }
 
 // acc += A[rows] · B[cols]^T over k in [k_begin, k_begin + k_len), k_len a
-// multiple of 64. One __syncthreads per K step; LDS double buffered.
+// multiple of 64. Two register stages of global loads are in flight: the
+// slab for step kt+2 is issued when step kt starts and reaches LDS at the
+// end of step kt+1, so a load has two steps of MFMA work to arrive. LDS is
+// double buffered; one __syncthreads per step.
 template <class C>
-__device__ __forceinline__ void mainloop(char* __restrict__ lds,
-                                         const bf16_t* __restrict__ A,
-                                         const int32_t (&aoff)[C::ACH],
-                                         const bf16_t* __restrict__ B0,
-                                         const bf16_t* __restrict__ B1,
-                                         const int32_t (&boff)[C::BCH],
+__device__ __forceinline__ void mainloop(char* __restrict__ lds, const Rsrc& A,
+                                         const uint32_t (&aoff)[C::ACH], const Rsrc& B0,
+                                         const Rsrc& B1, const uint32_t (&boff)[C::BCH],
                                          int k_begin, int k_len,
                                          f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  constexpr int STEP = C::BK * 2;  // bytes per slab along K
   const int KT = k_len / C::BK;
-  u32x4 ra[C::ACH], rb[C::BCH];
-  load_slab<C>(ra, rb, A, aoff, B0, B1, boff, k_begin);
-  store_slab<C>(lds, ra, rb);
+  const int kb = k_begin * 2;
+  char* L0 = lds;
+  char* L1 = lds + C::STAGE;
+  u32x4 ra0[C::ACH], rb0[C::BCH], ra1[C::ACH], rb1[C::BCH];
+  load_slab<C>(ra0, rb0, A, aoff, B0, B1, boff, kb);
+  if (KT > 1) load_slab<C>(ra1, rb1, A, aoff, B0, B1, boff, kb + STEP);
+  store_slab<C>(L0, ra0, rb0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) load_slab<C>(ra, rb, A, aoff, B0, B1, boff, k_begin + (kt + 1) * C::BK);
-    mma_slab<C>(lds + (kt & 1) * C::STAGE, acc);
-    if (more) store_slab<C>(lds + ((kt + 1) & 1) * C::STAGE, ra, rb);
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    // even step: L0 holds slab kt, registers 1 hold slab kt+1
+    if (kt + 2 < KT) load_slab<C>(ra0, rb0, A, aoff, B0, B1, boff, kb + (kt + 2) * STEP);
+    mma_slab<C>(L0, acc);
+    store_slab<C>(L1, ra1, rb1);
+    __syncthreads();
+    // odd step: L1 holds slab kt+1, registers 0 hold slab kt+2
+    if (kt + 3 < KT) load_slab<C>(ra1, rb1, A, aoff, B0, B1, boff, kb + (kt + 3) * STEP);
+    mma_slab<C>(L1, acc);
+    if (kt + 2 < KT) store_slab<C>(L0, ra0, rb0);
     __syncthreads();
   }
+  if (kt < KT) {   // odd number of steps: the last slab is in L0
+    mma_slab<C>(L0, acc);
+    __syncthreads();
+  }
+}
+
+// Write the tile's outputs through LDS so that global stores are 16-byte,
+// row-contiguous. Each lane holds one column of 16 rows per 32x32 block;
+// neighbouring lanes swap values so every LDS write carries two adjacent
+// columns. EPI_SWIGLU stores SiLU(gate)·up, EPI_STORE_BF16 stores acc.
+template <class C, int EPI>
+__device__ __forceinline__ void epilogue_bf16(char* __restrict__ lds,
+                                              const f32x16 (&acc)[C::NB][C::FM][C::FN],
+                                              bf16_t* __restrict__ Cout, int64_t ldc,
+                                              int64_t row0_out, int rows_valid, int n0,
+                                              int Ncols) {
+  constexpr int PITCH = C::BN * 2 + 16;   // bytes per LDS output row
+  static_assert(C::BM * PITCH <= C::LDS, "output tile does not fit in LDS");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const bool odd = lane & 1;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int col = wn * C::TN + fn * 32 + lr;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        float v0, v1;
+        if (EPI == EPI_SWIGLU) {
+          v0 = silu_fast(acc[0][fm][fn][i]) * acc[C::NB - 1][fm][fn][i];
+          v1 = silu_fast(acc[0][fm][fn][i + 1]) * acc[C::NB - 1][fm][fn][i + 1];
+        } else {
+          v0 = acc[0][fm][fn][i];
+          v1 = acc[0][fm][fn][i + 1];
+        }
+        // even lane keeps row i (cols lr, lr+1); odd lane keeps row i+1 (cols lr-1, lr)
+        const float send = odd ? v0 : v1;
+        const float recv = __shfl_xor(send, 1, 64);
+        const int ii = odd ? i + 1 : i;
+        const int r = wm * C::TM + fm * 32 + 8 * (ii >> 2) + 4 * lh + (ii & 3);
+        const uint32_t packed = odd ? pack_bf16x2(recv, v1) : pack_bf16x2(v0, recv);
+        *reinterpret_cast<uint32_t*>(lds + r * PITCH + (col & ~1) * 2) = packed;
+      }
+    }
+  __syncthreads();
+  constexpr int CPR = C::BN / 8;            // 16-byte chunks per row
+  for (int c = tid; c < C::BM * CPR; c += kThreads) {
+    const int r = c / CPR, ch = c % CPR;
+    const int col = n0 + ch * 8;
+    if (r < rows_valid && col < Ncols) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * PITCH + ch * 16);
+      *reinterpret_cast<u32x4*>(Cout + (row0_out + r) * ldc + col) = v;
+    }
+  }
+  __syncthreads();
 }
 
 template <class C>
@@ -161,8 +228,6 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   }
   return v;
 }
-
-enum Epi { EPI_SWIGLU = 0, EPI_STORE_BF16 = 1 };
 
 // Persistent grouped GEMM. Every block first builds the exclusive prefix of
 // m-tiles per group in LDS, then walks its share of the tile list:
@@ -222,11 +287,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedProble
     t_step = nblk;
   }
 
-  const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
+  const Rsrc rA = make_rsrc(p.A, p.a_bytes);
   const int row0 = tid >> 3, c16 = tid & 7;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int lr = lane & 31, lh = lane >> 5;
   constexpr int GN = 8;
 
   for (int64_t t = t_begin; t < t_end; t += t_step) {
@@ -250,48 +312,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedProble
     const int m_end = min(m0 + C::BM, gend);
     const int n0 = nt * C::BN;
 
-    int32_t aoff[C::ACH];
+    uint32_t aoff[C::ACH];
 #pragma unroll
     for (int i = 0; i < C::ACH; ++i) {
       const int r = min(m0 + row0 + 32 * i, m_end - 1);
       const int src = p.perm ? p.perm[r] / p.kdiv : r;
-      aoff[i] = src * p.lda + c16 * 8;
+      aoff[i] = (uint32_t)(src * p.lda + c16 * 8) * 2u;
     }
-    int32_t boff[C::BCH];
+    uint32_t boff[C::BCH];
 #pragma unroll
     for (int i = 0; i < C::BCH; ++i) {
       const int rr = (row0 + 32 * i) % C::BN;
       const int col = min(n0 + rr, p.Ncols - 1);
-      boff[i] = col * p.ldb + c16 * 8;
+      boff[i] = (uint32_t)(col * p.ldb + c16 * 8) * 2u;
     }
-    const bf16_t* B0 = static_cast<const bf16_t*>(p.B0) + (int64_t)g * p.b_gstride;
-    const bf16_t* B1 = C::DUAL ? static_cast<const bf16_t*>(p.B1) + (int64_t)g * p.b_gstride : B0;
+    const uint32_t bbytes = (uint32_t)((int64_t)p.Ncols * p.ldb * 2);
+    const Rsrc rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)g * p.b_gstride, bbytes);
+    const Rsrc rB1 = C::DUAL ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)g * p.b_gstride, bbytes) : rB0;
 
     f32x16 acc[C::NB][C::FM][C::FN];
     zero_acc<C>(acc);
-    mainloop<C>(lds, A, aoff, B0, B1, boff, 0, p.K, acc);
+    mainloop<C>(lds, rA, aoff, rB0, rB1, boff, 0, p.K, acc);
 
-    // ---- epilogue
-    bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int col = n0 + wn * C::TN + fn * 32 + lr;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = m0 + wm * C::TM + fm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if (r < m_end && col < p.Ncols) {
-            float v;
-            if (EPI == EPI_SWIGLU) {
-              v = silu_fast(acc[0][fm][fn][i]) * acc[C::NB - 1][fm][fn][i];
-            } else {
-              v = acc[0][fm][fn][i];
-            }
-            Cout[(p.c_row0 + r) * (int64_t)p.ldc + col] = (bf16_t)f32_to_bf16(v);
-          }
-        }
-      }
+    epilogue_bf16<C, EPI>(lds, acc, static_cast<bf16_t*>(p.C), p.ldc, p.c_row0 + m0,
+                          m_end - m0, n0, p.Ncols);
   }
 }
 
@@ -310,15 +354,17 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(
   const int k_begin = (kt * s / splits) * C::BK;
   const int k_len = (kt * (s + 1) / splits) * C::BK - k_begin;
   const int row0 = tid >> 3, c16 = tid & 7;
-  int32_t aoff[C::ACH];
+  uint32_t aoff[C::ACH];
 #pragma unroll
-  for (int i = 0; i < C::ACH; ++i) aoff[i] = min(m0 + row0 + 32 * i, T - 1) * d + c16 * 8;
-  int32_t boff[C::BCH];
+  for (int i = 0; i < C::ACH; ++i) aoff[i] = (uint32_t)(min(m0 + row0 + 32 * i, T - 1) * d + c16 * 8) * 2u;
+  uint32_t boff[C::BCH];
 #pragma unroll
-  for (int i = 0; i < C::BCH; ++i) boff[i] = min(n0 + row0 + 32 * i, N - 1) * d + c16 * 8;
+  for (int i = 0; i < C::BCH; ++i) boff[i] = (uint32_t)(min(n0 + row0 + 32 * i, N - 1) * d + c16 * 8) * 2u;
   f32x16 acc[C::NB][C::FM][C::FN];
   zero_acc<C>(acc);
-  mainloop<C>(lds, h, aoff, w, w, boff, k_begin, k_len, acc);
+  const Rsrc rh = make_rsrc(h, (uint32_t)((int64_t)T * d * 2));
+  const Rsrc rw = make_rsrc(w, (uint32_t)((int64_t)N * d * 2));
+  mainloop<C>(lds, rh, aoff, rw, rw, boff, k_begin, k_len, acc);
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lr = lane & 31, lh = lane >> 5;

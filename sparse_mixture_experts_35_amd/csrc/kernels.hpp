@@ -19,7 +19,7 @@ hipError_t launch_router_logits_f32(const float* h, const float* w_router,
                                     hipStream_t st);
 // z = sum of the partial slices + b_router; scores, top-k, gates, and
 // per-block sums of the routing probabilities
-int route_select_blocks(int T);
+int route_select_blocks(int T, int N);
 hipError_t launch_route_select(const float* z_part, int splits,
                                const float* b_router, const float* b_select,
                                int32_t* ids, float* gates, float* p_part,
@@ -56,6 +56,7 @@ struct GroupedProblem {
   void* C;
   int ldc;
   int64_t c_row0;
+  uint32_t a_bytes;  // extent of A in bytes (rows of A times lda times element size)
 };
 
 // Act = SiLU(A·B0^T) ⊙ (A·B1^T)   (bf16 in/out, fp32 accumulate)

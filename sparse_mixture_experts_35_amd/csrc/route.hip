@@ -9,10 +9,10 @@
 //   S_t = TopK(score_t, k) + gates   [wuhy-notes §二 第三步; cooking-agi first
 //                                     section; pwwt.cn §2.1 route()]
 //
-// One wavefront per token. Lane l holds experts l, l+64, ... (N <= 512, so
-// at most eight per lane, in registers). Top-k is k rounds of a wave-wide
-// argmax (butterfly over __shfl_xor) on (score, index) with the lower index
-// winning ties. In the softmax modes the selection runs on z, which orders
+// A group of lanes per token (8 lanes when N <= 8, up to a whole wavefront
+// for N > 32; each lane holds up to eight experts in registers, N <= 512).
+// Top-k is k rounds of a group-wide argmax (butterfly over __shfl_xor) on
+// (score, index) with the lower index winning ties. In the softmax modes the selection runs on z, which orders
 // the experts exactly as the softmax does. Per-block sums of the routing
 // probabilities go to p_part in a fixed order, never through float atomics.
 #include <math.h>
@@ -24,8 +24,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokensPerBlock = 64;   // 16 per wave
-constexpr int kMaxPerLane = 8;        // 512 experts / 64 lanes
 constexpr int kMaxK = 16;
 
 __global__ void router_logits_f32_kernel(const float* __restrict__ h,
@@ -45,47 +43,53 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
-template <int MODE>
+// A group of LPT lanes routes one token (LPT = 8/16/32 for N up to that
+// many experts, else 64); lane li of the group holds experts li, li+LPT, ...
+// (VPL values). All reductions stay inside the group (xor offsets < LPT).
+template <int LPT, int VPL, int MODE, int ITER>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
     const float* __restrict__ b_select, int32_t* __restrict__ ids,
     float* __restrict__ gates, float* __restrict__ p_part, int T, int N, int k) {
-  __shared__ float s_p[4][512];
+  constexpr int TPW = 64 / LPT;               // tokens per wave per iteration
+  constexpr int TPB = 4 * TPW * ITER;         // tokens per block
+  __shared__ float s_p[4][64][VPL];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = lane / LPT, li = lane % LPT;
   const int64_t TN = (int64_t)T * N;
 
-  float pacc[kMaxPerLane];
+  float pacc[VPL];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) pacc[i] = 0.0f;
+  for (int i = 0; i < VPL; ++i) pacc[i] = 0.0f;
 
-  const int tw0 = blockIdx.x * kTokensPerBlock + w * (kTokensPerBlock / 4);
-  for (int tt = 0; tt < kTokensPerBlock / 4; ++tt) {
-    const int t = tw0 + tt;
-    if (t >= T) break;
-    // ---- logits (sum of split-K slices in order, then the router bias)
-    float zv[kMaxPerLane], sel[kMaxPerLane], aux[kMaxPerLane];
-    bool cand[kMaxPerLane];
+  for (int it = 0; it < ITER; ++it) {
+    const int t = blockIdx.x * TPB + (it * 4 + w) * TPW + grp;
+    const bool tok = t < T;
+    // ---- logits: split-K slices summed in order, then the router bias
+    float zv[VPL], sel[VPL], aux[VPL];
+    bool cand[VPL];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + 64 * i;
-      cand[i] = e < N;
+    for (int i = 0; i < VPL; ++i) {
+      const int e = li + LPT * i;
+      const bool in = tok && e < N;
+      cand[i] = in;
       float v = 0.0f;
-      if (cand[i]) {
+      if (in) {
         const float* zp = z_part + (int64_t)t * N + e;
         for (int s = 0; s < splits; ++s) v += zp[s * TN];
         if (b_router) v += b_router[e];
       }
       zv[i] = v;
       if (MODE == 2) {
-        const float s = 1.0f / (1.0f + expf(-v));   // sigmoid score
-        aux[i] = s;
-        sel[i] = cand[i] ? s + b_select[e] : 0.0f;
+        const float sg = 1.0f / (1.0f + expf(-v));   // sigmoid score
+        aux[i] = sg;
+        sel[i] = in ? sg + b_select[e] : 0.0f;
       } else {
         aux[i] = v;
         sel[i] = v;
       }
     }
-    // ---- top-k: k rounds of a wave argmax
+    // ---- top-k: k rounds of a group-wide argmax, lower index wins ties
     int win_id[kMaxK];
     float win_aux[kMaxK];
 #pragma unroll
@@ -97,8 +101,8 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
       float bv = -INFINITY, ba = 0.0f;
       int bi = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
+      for (int i = 0; i < VPL; ++i) {
+        const int e = li + LPT * i;
         if (cand[i] && better(sel[i], e, bv, bi)) {
           bv = sel[i];
           bi = e;
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
         }
       }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
+      for (int o = LPT / 2; o >= 1; o >>= 1) {
         const float ov = __shfl_xor(bv, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
         const float oa = __shfl_xor(ba, o, 64);
@@ -116,11 +120,10 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
           ba = oa;
         }
       }
-      // every lane now holds the same winner; its owner drops it
-      if ((bi & 63) == lane) {
+      if (bi % LPT == li) {                  // the owner drops the winner
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-          if (i == (bi >> 6)) cand[i] = false;
+        for (int i = 0; i < VPL; ++i)
+          if (i == bi / LPT) cand[i] = false;
       }
 #pragma unroll
       for (int jj = 0; jj < kMaxK; ++jj)
@@ -129,21 +132,26 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
           win_aux[jj] = ba;
         }
     }
-    // ---- gates
-    float zmax = -INFINITY, denom_all = 0.0f;
+    // ---- full-softmax max and denominator (mode B gates, p statistics)
+    float zmax = 0.0f, denom_all = 1.0f;
     const bool need_full = (MODE == 1) || (p_part != nullptr);
     if (MODE != 2 && need_full) {
       float m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
-        if (lane + 64 * i < N) m = fmaxf(m, zv[i]);
-      zmax = wave_max(m);
-      float s = 0.0f;
+      for (int i = 0; i < VPL; ++i)
+        if (li + LPT * i < N) m = fmaxf(m, zv[i]);
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
-        if (lane + 64 * i < N) s += expf(zv[i] - zmax);
-      denom_all = wave_sum(s);
+      for (int o = LPT / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      zmax = m;
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (li + LPT * i < N) sum += expf(zv[i] - zmax);
+#pragma unroll
+      for (int o = LPT / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      denom_all = sum;
     }
+    // ---- gates
     float gsel[kMaxK];
     if (MODE == 0) {
       // softmax over the selected logits; win_aux[0] is the largest
@@ -172,51 +180,103 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
     float my_g = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      if (j == lane) {
+      if (j == li) {
         my_id = win_id[j];
         my_g = gsel[j];
       }
-    if (lane < k) {
-      ids[(int64_t)t * k + lane] = my_id;
-      gates[(int64_t)t * k + lane] = my_g;
+    if (tok && li < k) {
+      ids[(int64_t)t * k + li] = my_id;
+      gates[(int64_t)t * k + li] = my_g;
     }
     // ---- routing probabilities for p_i
     if (p_part) {
       if (MODE == 2) {
-        float s = 0.0f;
+        float sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-          if (lane + 64 * i < N) s += aux[i];
-        const float inv = 1.0f / wave_sum(s);
+        for (int i = 0; i < VPL; ++i)
+          if (li + LPT * i < N) sum += aux[i];
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-          if (lane + 64 * i < N) pacc[i] += aux[i] * inv;
+        for (int o = LPT / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+          if (tok && li + LPT * i < N) pacc[i] += aux[i] * inv;
       } else {
         const float inv = 1.0f / denom_all;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-          if (lane + 64 * i < N) pacc[i] += expf(zv[i] - zmax) * inv;
+        for (int i = 0; i < VPL; ++i)
+          if (tok && li + LPT * i < N) pacc[i] += expf(zv[i] - zmax) * inv;
       }
     }
   }
   if (p_part) {
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (lane + 64 * i < N) s_p[w][lane + 64 * i] = pacc[i];
+    for (int i = 0; i < VPL; ++i) s_p[w][lane][i] = pacc[i];
     __syncthreads();
-    for (int e = tid; e < N; e += kThreads)
-      p_part[(int64_t)blockIdx.x * N + e] = ((s_p[0][e] + s_p[1][e]) + s_p[2][e]) + s_p[3][e];
+    // block sum per expert: waves in order, token groups in order
+    for (int e = tid; e < N; e += kThreads) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww)
+#pragma unroll
+        for (int g = 0; g < TPW; ++g) sum += s_p[ww][g * LPT + e % LPT][e / LPT];
+      p_part[(int64_t)blockIdx.x * N + e] = sum;
+    }
   }
 }
 
-// p_mean[e] = (sum over blocks, in block order, of p_part[b][e]) / T
-__global__ void p_reduce_kernel(const float* __restrict__ p_part, float* __restrict__ p_mean,
-                                int blocks, int T, int N) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= N) return;
-  float s = 0.0f;
-  for (int b = 0; b < blocks; ++b) s += p_part[(int64_t)b * N + e];
-  p_mean[e] = s / (float)T;
+// p_mean[e] = (sum over blocks of p_part[b][e]) / T: one block per expert,
+// thread i sums blocks i, i+256, ... in order, then a fixed tree.
+__global__ __launch_bounds__(kThreads) void p_reduce_kernel(const float* __restrict__ p_part,
+                                                            float* __restrict__ p_mean,
+                                                            int blocks, int T, int N) {
+  __shared__ float s[kThreads];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  float v = 0.0f;
+  for (int b = tid; b < blocks; b += kThreads) v += p_part[(int64_t)b * N + e];
+  s[tid] = v;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) s[tid] += s[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) p_mean[e] = s[0] / (float)T;
+}
+
+// Launch configuration of route_select for N experts.
+struct SelectCfg {
+  int lpt, vpl, iter, tpb;
+};
+SelectCfg select_cfg(int N) {
+  SelectCfg c;
+  c.lpt = N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : 64;
+  c.vpl = (N + c.lpt - 1) / c.lpt;
+  if (c.vpl > 1) c.vpl = c.vpl <= 2 ? 2 : c.vpl <= 4 ? 4 : 8;
+  const int tpw = 64 / c.lpt;
+  c.iter = (4 * tpw >= 16) ? 1 : 16 / (4 * tpw);
+  c.tpb = 4 * tpw * c.iter;
+  return c;
+}
+
+template <int LPT, int VPL, int ITER>
+hipError_t launch_select_t(const float* z_part, int splits, const float* b_router,
+                           const float* b_select, int32_t* ids, float* gates, float* p_part,
+                           int T, int N, int k, int mode, int blocks, hipStream_t st) {
+  switch (mode) {
+    case 0:
+      hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 0, ITER>), dim3(blocks), dim3(kThreads),
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k);
+      break;
+    case 1:
+      hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 1, ITER>), dim3(blocks), dim3(kThreads),
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k);
+      break;
+    default:
+      hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 2, ITER>), dim3(blocks), dim3(kThreads),
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k);
+      break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -230,35 +290,37 @@ hipError_t launch_router_logits_f32(const float* h, const float* w, float* z, in
   return hipGetLastError();
 }
 
-int route_select_blocks(int T) { return (T + kTokensPerBlock - 1) / kTokensPerBlock; }
+int route_select_blocks(int T, int N) {
+  const SelectCfg c = select_cfg(N);
+  return (T + c.tpb - 1) / c.tpb;
+}
 
 hipError_t launch_route_select(const float* z_part, int splits, const float* b_router,
                                const float* b_select, int32_t* ids, float* gates,
                                float* p_part, int T, int N, int k, int mode, hipStream_t st) {
-  const int blocks = route_select_blocks(T);
+  const SelectCfg c = select_cfg(N);
+  const int blocks = (T + c.tpb - 1) / c.tpb;
   if (blocks == 0) return hipSuccess;
-  switch (mode) {
-    case 0:
-      hipLaunchKernelGGL(route_select_kernel<0>, dim3(blocks), dim3(kThreads), 0, st, z_part,
-                         splits, b_router, b_select, ids, gates, p_part, T, N, k);
-      break;
-    case 1:
-      hipLaunchKernelGGL(route_select_kernel<1>, dim3(blocks), dim3(kThreads), 0, st, z_part,
-                         splits, b_router, b_select, ids, gates, p_part, T, N, k);
-      break;
-    default:
-      hipLaunchKernelGGL(route_select_kernel<2>, dim3(blocks), dim3(kThreads), 0, st, z_part,
-                         splits, b_router, b_select, ids, gates, p_part, T, N, k);
-      break;
-  }
-  return hipGetLastError();
+#define MOE_SEL(L, V, I)                                                                    \
+  if (c.lpt == L && c.vpl == V)                                                             \
+    return launch_select_t<L, V, I>(z_part, splits, b_router, b_select, ids, gates, p_part, \
+                                    T, N, k, mode, blocks, st);
+  MOE_SEL(8, 1, 1)
+  MOE_SEL(16, 1, 1)
+  MOE_SEL(32, 1, 2)
+  MOE_SEL(64, 1, 4)
+  MOE_SEL(64, 2, 4)
+  MOE_SEL(64, 4, 4)
+  MOE_SEL(64, 8, 4)
+#undef MOE_SEL
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_p_reduce(const float* p_part, float* p_mean, int blocks, int T, int N,
                            hipStream_t st) {
   if (T == 0 || N == 0) return hipSuccess;
-  hipLaunchKernelGGL(p_reduce_kernel, dim3((N + 255) / 256), dim3(256), 0, st, p_part, p_mean,
-                     blocks, T, N);
+  hipLaunchKernelGGL(p_reduce_kernel, dim3(N), dim3(kThreads), 0, st, p_part, p_mean, blocks,
+                     T, N);
   return hipGetLastError();
 }
 
