@@ -23,7 +23,7 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
-__device__ __forceinline__ u32x4 buffer_load16(const Rsrc& r, uint32_t voff, int soff) {
+__device__ __forceinline__ u32x4 buffer_load16(Rsrc r, uint32_t voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
@@ -41,6 +41,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 pair (lo, hi) with the hardware converter (round to
+// nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2_t));
 }
 
 // Unpack 8 bf16 (one 16-byte vector) to fp32.

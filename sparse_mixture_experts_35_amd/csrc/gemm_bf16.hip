@@ -28,182 +28,173 @@ constexpr int kMaxGroups = 512;
 constexpr int kXcds = 8;   // MI355X: 8 XCDs; block b runs on XCD b % 8
 
 // ---------------------------------------------------------------- tiling
-template <int BM_, int BN_, bool DUAL_>
+// Block tile BM rows x BN output columns (gate and up columns both when
+// DUAL), four waves in a 2x2 grid, each wave TM x TN with 32x32x16 MFMAs.
+// K advances in slabs of BK = 32. A slab of the block tile lives in LDS as
+// BM + BROWS rows of 64 bytes (A rows, then B rows), 16-byte chunks XOR-
+// swizzled per row so that the fragment reads of 8 or 16 consecutive rows
+// hit distinct banks. STAGES such stages form a ring; OCC blocks share a CU
+// (two blocks: two waves per SIMD, each hides the other's waits).
+template <int BM_, int BN_, bool DUAL_, int STAGES_, int OCC_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, BK = 32;
   static constexpr bool DUAL = DUAL_;
+  static constexpr int STAGES = STAGES_;             // LDS ring depth (3 or 4)
+  static constexpr int OCC = OCC_;                   // blocks per CU (1 or 2)
   static constexpr int NB = DUAL ? 2 : 1;           // gate and up, or one B
   static constexpr int WM = 2, WN = 2;              // 2x2 waves
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
-  static constexpr int BROWS = BN * NB;             // B rows staged per K step
-  static constexpr int ROWB = BK * 2 + 16;          // LDS row pitch (bytes), +16 pad
+  static constexpr int BROWS = BN * NB;             // B rows staged per slab
+  static constexpr int ROWB = BK * 2;               // 64 bytes per staged row
   static constexpr int A_BYTES = BM * ROWB;
-  static constexpr int B_BYTES = BROWS * ROWB;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int ACH = BM / 32;               // 16B chunks per thread (A)
-  static constexpr int BCH = BROWS / 32;            // 16B chunks per thread (B)
-  static constexpr int BCH0 = BN / 32;              // chunks that come from B0
+  static constexpr int STAGE = (BM + BROWS) * ROWB;
+  static constexpr int NAW = BM / 64;               // A blocks (16 rows, 1 KiB) per wave
+  static constexpr int NBW = BROWS / 64;            // B blocks per wave
+  static constexpr int NLW = NAW + NBW;             // direct-to-LDS loads per wave per slab
   static_assert(FM >= 1 && FN >= 1, "tile too small");
+  static_assert(BM % 64 == 0 && BROWS % 64 == 0, "tile rows must be multiples of 64");
 };
 
-enum Epi { EPI_SWIGLU = 0, EPI_STORE_BF16 = 1 };
+// Chunk swizzle of staged row r: logical 16-byte chunk c lives at c ^ swz(r).
+// For rows r..r+7 (r a multiple of 8) the pairs (r & 1, chunk) are distinct,
+// and for rows r..r+15 the pairs (r & 3, chunk) are, so reads of 8 or 16
+// consecutive rows are conflict-free with 128- or 256-byte wide LDS.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
 
-// Global -> registers for one BK slab. Thread tid loads 16-byte chunk
-// (tid & 7) of rows (tid >> 3) + 32 i: eight lanes cover one 128-byte row
-// segment, so every load instruction is fully coalesced. Raw buffer loads:
-// a 32-bit per-lane byte offset, the K position as a scalar offset, and the
-// buffer's extent in the descriptor (reads past it return zero).
-template <class C>
-__device__ __forceinline__ void load_slab(u32x4 (&ra)[C::ACH], u32x4 (&rb)[C::BCH],
-                                          const Rsrc& A, const uint32_t (&aoff)[C::ACH],
-                                          const Rsrc& B0, const Rsrc& B1,
-                                          const uint32_t (&boff)[C::BCH], int kbytes) {
-#pragma unroll
-  for (int i = 0; i < C::ACH; ++i) ra[i] = buffer_load16(A, aoff[i], kbytes);
-#pragma unroll
-  for (int i = 0; i < C::BCH; ++i) rb[i] = buffer_load16((i < C::BCH0) ? B0 : B1, boff[i], kbytes);
-}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Issue the direct-to-LDS loads of one slab (byte offset kbytes along K)
+// into stage `st`. Wave w fills A blocks w, w+4, ... and B blocks w, w+4, ...;
+// lane l of a block writes bytes [16 l, 16 l + 16) of the block, i.e. row
+// l / 4, physical chunk l % 4, so it loads logical chunk (l % 4) ^ swz(row).
 template <class C>
-__device__ __forceinline__ void store_slab(char* __restrict__ stage,
-                                           const u32x4 (&ra)[C::ACH],
-                                           const u32x4 (&rb)[C::BCH]) {
-  const int tid = threadIdx.x;
-  char* a = stage + (tid >> 3) * C::ROWB + (tid & 7) * 16;
-  char* b = a + C::A_BYTES;
+__device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const uint32_t* aoff,
+                                         Rsrc B0, Rsrc B1, const uint32_t* boff, int kbytes) {
+  const int w = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < C::ACH; ++i)
-    *reinterpret_cast<u32x4*>(a + i * 32 * C::ROWB) = ra[i];
+  for (int j = 0; j < C::NAW; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(A, (lds_ptr_t)(st + (w + 4 * j) * 1024), 16,
+                                             aoff[j], kbytes, 0, 0);
 #pragma unroll
-  for (int i = 0; i < C::BCH; ++i)
-    *reinterpret_cast<u32x4*>(b + i * 32 * C::ROWB) = rb[i];
-}
-
-template <class C>
-__device__ __forceinline__ void mma_slab(const char* __restrict__ stage,
-                                         f32x16 (&acc)[C::NB][C::FM][C::FN]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int lr = lane & 31, lh = lane >> 5;
-  const char* a = stage + (wm * C::TM + lr) * C::ROWB + lh * 16;
-  const char* b = stage + C::A_BYTES + (wn * C::TN + lr) * C::ROWB + lh * 16;
-#pragma unroll
-  for (int ks = 0; ks < C::BK / 16; ++ks) {
-    u32x4 af[C::FM];
-    u32x4 bfr[C::NB][C::FN];
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-      af[fm] = *reinterpret_cast<const u32x4*>(a + fm * 32 * C::ROWB + ks * 32);
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-        bfr[nb][fn] = *reinterpret_cast<const u32x4*>(
-            b + (nb * C::BN + fn * 32) * C::ROWB + ks * 32);
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-          acc[nb][fm][fn] = mfma_32x32x16(af[fm], bfr[nb][fn], acc[nb][fm][fn]);
+  for (int j = 0; j < C::NBW; ++j) {
+    const bool up = C::DUAL && (4 * j) >= C::BN / 16;   // B block w + 4j is an up row block
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? B1 : B0,
+                                             (lds_ptr_t)(st + C::A_BYTES + (w + 4 * j) * 1024),
+                                             16, boff[j], kbytes, 0, 0);
   }
 }
 
-// acc += A[rows] · B[cols]^T over k in [k_begin, k_begin + k_len), k_len a
-// multiple of 64. Two register stages of global loads are in flight: the
-// slab for step kt+2 is issued when step kt starts and reaches LDS at the
-// end of step kt+1, so a load has two steps of MFMA work to arrive. LDS is
-// double buffered; one __syncthreads per step.
 template <class C>
-__device__ __forceinline__ void mainloop(char* __restrict__ lds, const Rsrc& A,
-                                         const uint32_t (&aoff)[C::ACH], const Rsrc& B0,
-                                         const Rsrc& B1, const uint32_t (&boff)[C::BCH],
-                                         int k_begin, int k_len,
-                                         f32x16 (&acc)[C::NB][C::FM][C::FN]) {
-  constexpr int STEP = C::BK * 2;  // bytes per slab along K
-  const int KT = k_len / C::BK;
-  const int kb = k_begin * 2;
-  char* L0 = lds;
-  char* L1 = lds + C::STAGE;
-  u32x4 ra0[C::ACH], rb0[C::BCH], ra1[C::ACH], rb1[C::BCH];
-  load_slab<C>(ra0, rb0, A, aoff, B0, B1, boff, kb);
-  if (KT > 1) load_slab<C>(ra1, rb1, A, aoff, B0, B1, boff, kb + STEP);
-  store_slab<C>(L0, ra0, rb0);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    // even step: L0 holds slab kt, registers 1 hold slab kt+1
-    if (kt + 2 < KT) load_slab<C>(ra0, rb0, A, aoff, B0, B1, boff, kb + (kt + 2) * STEP);
-    mma_slab<C>(L0, acc);
-    store_slab<C>(L1, ra1, rb1);
-    __syncthreads();
-    // odd step: L1 holds slab kt+1, registers 0 hold slab kt+2
-    if (kt + 3 < KT) load_slab<C>(ra1, rb1, A, aoff, B0, B1, boff, kb + (kt + 3) * STEP);
-    mma_slab<C>(L1, acc);
-    if (kt + 2 < KT) store_slab<C>(L0, ra0, rb0);
-    __syncthreads();
-  }
-  if (kt < KT) {   // odd number of steps: the last slab is in L0
-    mma_slab<C>(L0, acc);
-    __syncthreads();
-  }
-}
+struct Frags {
+  u32x4 a[C::FM];
+  u32x4 b[C::NB][C::FN];
+};
 
-// Write the tile's outputs through LDS so that global stores are 16-byte,
-// row-contiguous. Each lane holds one column of 16 rows per 32x32 block;
-// neighbouring lanes swap values so every LDS write carries two adjacent
-// columns. EPI_SWIGLU stores SiLU(gate)·up, EPI_STORE_BF16 stores acc.
-template <class C, int EPI>
-__device__ __forceinline__ void epilogue_bf16(char* __restrict__ lds,
-                                              const f32x16 (&acc)[C::NB][C::FM][C::FN],
-                                              bf16_t* __restrict__ Cout, int64_t ldc,
-                                              int64_t row0_out, int rows_valid, int n0,
-                                              int Ncols) {
-  constexpr int PITCH = C::BN * 2 + 16;   // bytes per LDS output row
-  static_assert(C::BM * PITCH <= C::LDS, "output tile does not fit in LDS");
+// Fragments of MFMA k-step ks (0 or 1) of the slab in stage `st`.
+template <class C>
+__device__ __forceinline__ void read_frags(const char* __restrict__ st, int ks, Frags<C>& f) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lr = lane & 31, lh = lane >> 5;
-  const bool odd = lane & 1;
+  const int co = (((ks * 2 + lh) ^ swz(lr)) << 4);
+  const char* a = st + (wm * C::TM + lr) * C::ROWB + co;
+  const char* b = st + C::A_BYTES + (wn * C::TN + lr) * C::ROWB + co;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
+    f.a[fm] = *reinterpret_cast<const u32x4*>(a + fm * 32 * C::ROWB);
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) {
-      const int col = wn * C::TN + fn * 32 + lr;
+  for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float v0, v1;
-        if (EPI == EPI_SWIGLU) {
-          v0 = silu_fast(acc[0][fm][fn][i]) * acc[C::NB - 1][fm][fn][i];
-          v1 = silu_fast(acc[0][fm][fn][i + 1]) * acc[C::NB - 1][fm][fn][i + 1];
-        } else {
-          v0 = acc[0][fm][fn][i];
-          v1 = acc[0][fm][fn][i + 1];
-        }
-        // even lane keeps row i (cols lr, lr+1); odd lane keeps row i+1 (cols lr-1, lr)
-        const float send = odd ? v0 : v1;
-        const float recv = __shfl_xor(send, 1, 64);
-        const int ii = odd ? i + 1 : i;
-        const int r = wm * C::TM + fm * 32 + 8 * (ii >> 2) + 4 * lh + (ii & 3);
-        const uint32_t packed = odd ? pack_bf16x2(recv, v1) : pack_bf16x2(v0, recv);
-        *reinterpret_cast<uint32_t*>(lds + r * PITCH + (col & ~1) * 2) = packed;
-      }
+    for (int fn = 0; fn < C::FN; ++fn)
+      f.b[nb][fn] = *reinterpret_cast<const u32x4*>(b + (nb * C::BN + fn * 32) * C::ROWB);
+}
+
+template <class C>
+__device__ __forceinline__ void mma(const Frags<C>& f, f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        acc[nb][fm][fn] = mfma_32x32x16(f.a[fm], f.b[nb][fn], acc[nb][fm][fn]);
+}
+
+// s_waitcnt vmcnt(n) (n < 64) leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 15));
+}
+
+// One K step k on stage S[j]: frags f0 (k-step 0) are already in registers.
+//  1. issue the loads of slab k+STAGES-1 (clamped to the last slab) into the
+//     stage slab k-1 occupied
+//  2. read frags f1 (k-step 1) of S[j]
+//  3. MFMAs on f0
+//  4. wait until this wave's loads of slab k+1 are done, barrier: slab k+1
+//     is complete in its stage and every wave has read all of S[j]
+//  5. read frags f0 of slab k+1, then MFMAs on f1
+template <class C>
+__device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict__ nxt,
+                                       char* __restrict__ dst, int kload_bytes,
+                                       Frags<C>& f0, Frags<C>& f1, Rsrc A,
+                                       const uint32_t* aoff, Rsrc B0, Rsrc B1,
+                                       const uint32_t* boff,
+                                       f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  dma_slab<C>(dst, A, aoff, B0, B1, boff, kload_bytes);
+  read_frags<C>(cur, 1, f1);
+  mma<C>(f0, acc);
+  wait_vmcnt<(C::STAGES - 2) * C::NLW>();
+  __builtin_amdgcn_s_barrier();
+  read_frags<C>(nxt, 0, f0);
+  mma<C>(f1, acc);
+}
+
+// acc += A[rows] · B[cols]^T over k in [k_begin, k_begin + k_len) (k_len a
+// multiple of 32). Loads run STAGES-1 slabs ahead of the MFMAs through a
+// ring of LDS stages; the loop is unrolled by STAGES so that every stage is
+// a distinct LDS object. Loads past the last slab re-load the last slab, so
+// every step issues the same number of loads and the vmcnt accounting holds.
+template <class C>
+__device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict__ S1,
+                                         char* __restrict__ S2, char* __restrict__ S3,
+                                         Rsrc A, const uint32_t* aoff, Rsrc B0, Rsrc B1,
+                                         const uint32_t* boff, int k_begin, int k_len,
+                                         f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  constexpr int STEP = C::BK * 2;
+  const int KT = k_len / C::BK;
+  const int kb = k_begin * 2;
+  auto kbyte = [&](int k) { return kb + min(k, KT - 1) * STEP; };
+  Frags<C> f0, f1;
+  if constexpr (C::STAGES == 4) {
+    dma_slab<C>(S0, A, aoff, B0, B1, boff, kbyte(0));
+    dma_slab<C>(S1, A, aoff, B0, B1, boff, kbyte(1));
+    dma_slab<C>(S2, A, aoff, B0, B1, boff, kbyte(2));
+    wait_vmcnt<2 * C::NLW>();
+    __builtin_amdgcn_s_barrier();
+    read_frags<C>(S0, 0, f0);
+    for (int k = 0; k < KT; k += 4) {
+      k_step<C>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+      if (k + 1 < KT) k_step<C>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+      if (k + 2 < KT) k_step<C>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
+      if (k + 3 < KT) k_step<C>(S3, S0, S2, kbyte(k + 6), f0, f1, A, aoff, B0, B1, boff, acc);
     }
-  __syncthreads();
-  constexpr int CPR = C::BN / 8;            // 16-byte chunks per row
-  for (int c = tid; c < C::BM * CPR; c += kThreads) {
-    const int r = c / CPR, ch = c % CPR;
-    const int col = n0 + ch * 8;
-    if (r < rows_valid && col < Ncols) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * PITCH + ch * 16);
-      *reinterpret_cast<u32x4*>(Cout + (row0_out + r) * ldc + col) = v;
+  } else {
+    dma_slab<C>(S0, A, aoff, B0, B1, boff, kbyte(0));
+    dma_slab<C>(S1, A, aoff, B0, B1, boff, kbyte(1));
+    wait_vmcnt<C::NLW>();
+    __builtin_amdgcn_s_barrier();
+    read_frags<C>(S0, 0, f0);
+    for (int k = 0; k < KT; k += 3) {
+      k_step<C>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+      if (k + 1 < KT) k_step<C>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+      if (k + 2 < KT) k_step<C>(S2, S0, S1, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
     }
   }
+  wait_vmcnt<0>();
   __syncthreads();
 }
 
@@ -219,6 +210,64 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[C::NB][C::FM][C::FN]) {
         for (int i = 0; i < 16; ++i) acc[nb][fm][fn][i] = 0.0f;
 }
 
+enum Epi { EPI_SWIGLU = 0, EPI_STORE_BF16 = 1 };
+
+// Output column of MFMA block fn, lane column lr, in a wave's TN-wide strip:
+// B rows are staged so that blocks 2j and 2j+1 hold the even and odd columns
+// of the 64-column group j. Each lane then owns two adjacent output columns
+// of the same rows, stored as one packed bf16 pair.
+__device__ __forceinline__ int strip_col(int fn, int lr) {
+  return (fn >> 1) * 64 + 2 * lr + (fn & 1);
+}
+
+// Epilogue: SiLU(gate)·up (SWIGLU) or the accumulator, rounded to bf16
+// (hardware round-to-nearest-even), stored straight from registers as 4-byte
+// column pairs: a store instruction writes two full 128-byte row segments.
+// Raw buffer stores over the tile's valid rows: rows past the group's end
+// fall outside the descriptor and are dropped, columns past Ncols get an
+// out-of-range offset, so there are no branches.
+template <class C, int EPI>
+__device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][C::FN],
+                                              bf16_t* __restrict__ Cout, int64_t ldc,
+                                              int64_t row0_out, int rows_valid, int n0,
+                                              int Ncols) {
+  static_assert(C::FN % 2 == 0, "column pairs need an even number of MFMA blocks");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int lr = lane & 31, lh = lane >> 5;
+  // Row stride in bytes, made opaque so the compiler recomputes the row
+  // offsets per tile instead of hoisting (and spilling) all of them.
+  int ldc2 = (int)ldc * 2;
+  asm volatile("" : "+s"(ldc2));
+  const Rsrc out = make_rsrc(Cout + row0_out * ldc, (uint32_t)rows_valid * (uint32_t)ldc2);
+  const uint32_t lane_row = (uint32_t)(4 * lh) * (uint32_t)ldc2;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int rb = wm * C::TM + fm * 32;
+    if (rb >= rows_valid) break;             // the rest of this wave's rows are padding
+#pragma unroll
+    for (int fe = 0; fe < C::FN; fe += 2) {
+      const int col = n0 + wn * C::TN + strip_col(fe, lr);
+      const uint32_t voff = col < Ncols ? lane_row + (uint32_t)col * 2u : 0xC0000000u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rrow = rb + 8 * (i >> 2) + (i & 3);   // + 4*lh (in voff)
+        float v0, v1;
+        if (EPI == EPI_SWIGLU) {
+          v0 = silu_fast(acc[0][fm][fe][i]) * acc[C::NB - 1][fm][fe][i];
+          v1 = silu_fast(acc[0][fm][fe + 1][i]) * acc[C::NB - 1][fm][fe + 1][i];
+        } else {
+          v0 = acc[0][fm][fe][i];
+          v1 = acc[0][fm][fe + 1][i];
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2_hw(v0, v1), out, voff,
+                                              rrow * ldc2, 0);
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -229,6 +278,31 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Per-lane load offsets of the DMA blocks of wave w: A block w + 4j holds
+// tile rows 16(w + 4j) .. +15; lane l loads row 16(w+4j) + l/4, logical chunk
+// (l % 4) ^ swz(row). Rows past the group's end re-read its last row.
+template <class C>
+__device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (&boff)[C::NBW],
+                                            const int32_t* perm, int kdiv, int lda, int m0,
+                                            int m_end, int ldb, int n0, int Ncols) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rl = lane >> 2;
+#pragma unroll
+  for (int j = 0; j < C::NAW; ++j) {
+    const int row = 16 * (w + 4 * j) + rl;
+    const int r = min(m0 + row, m_end - 1);
+    const int src = perm ? perm[r] / kdiv : r;
+    aoff[j] = (uint32_t)(src * lda * 2 + (((lane & 3) ^ swz(row)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < C::NBW; ++j) {
+    const int row = 16 * (w + 4 * j) + rl;      // B row within the stage's B part
+    const int q = row % C::BN;                  // staged row -> output column (strip_col)
+    const int col = min(n0 + (q & ~63) + 2 * (q & 31) + ((q >> 5) & 1), Ncols - 1);
+    boff[j] = (uint32_t)(col * ldb * 2 + (((lane & 3) ^ swz(C::BM + row)) << 4));
+  }
+}
+
 // Persistent grouped GEMM. Every block first builds the exclusive prefix of
 // m-tiles per group in LDS, then walks its share of the tile list:
 //  * XCD-aware split: block b runs on XCD b % 8, and XCD x takes the
@@ -237,8 +311,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 //  * tile order: groups of 8 n-tiles, m-tiles (all experts) inside, so 4
 //    m-tiles × 8 n-tiles run together.
 template <class C, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedProblem p) {
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+__global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedProblem p) {
+  __shared__ __attribute__((aligned(1024))) char S0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S3[C::STAGES == 4 ? C::STAGE : 1024];
   __shared__ int s_pref[kMaxGroups + 1];
   const int tid = threadIdx.x;
   const int G = p.offsets ? p.groups : 1;
@@ -269,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedProble
   }
   __syncthreads();
 
-  const int total_mt = s_pref[G];
+  const int total_mt = __builtin_amdgcn_readfirstlane(s_pref[G]);
   const int nt_n = (p.Ncols + C::BN - 1) / C::BN;
   const int64_t total = (int64_t)total_mt * nt_n;
   if (total == 0) return;
@@ -288,7 +365,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedProble
   }
 
   const Rsrc rA = make_rsrc(p.A, p.a_bytes);
-  const int row0 = tid >> 3, c16 = tid & 7;
   constexpr int GN = 8;
 
   for (int64_t t = t_begin; t < t_end; t += t_step) {
@@ -305,37 +381,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedProble
       const int mid = (lo + hi) >> 1;
       if (s_pref[mid] <= mt) lo = mid; else hi = mid;
     }
-    const int g = lo;
-    const int gbase = p.offsets ? p.offsets[g] : 0;
-    const int gend = p.offsets ? p.offsets[g + 1] : p.M;
-    const int m0 = gbase + (mt - s_pref[g]) * C::BM;
+    // every lane computed the same values from LDS; say so to the compiler,
+    // so that descriptors and bounds live in scalar registers
+    const int g = __builtin_amdgcn_readfirstlane(lo);
+    const int gbase = p.offsets ? __builtin_amdgcn_readfirstlane(p.offsets[g]) : 0;
+    const int gend = p.offsets ? __builtin_amdgcn_readfirstlane(p.offsets[g + 1]) : p.M;
+    const int m0 = gbase + (mt - __builtin_amdgcn_readfirstlane(s_pref[g])) * C::BM;
     const int m_end = min(m0 + C::BM, gend);
     const int n0 = nt * C::BN;
 
-    uint32_t aoff[C::ACH];
-#pragma unroll
-    for (int i = 0; i < C::ACH; ++i) {
-      const int r = min(m0 + row0 + 32 * i, m_end - 1);
-      const int src = p.perm ? p.perm[r] / p.kdiv : r;
-      aoff[i] = (uint32_t)(src * p.lda + c16 * 8) * 2u;
-    }
-    uint32_t boff[C::BCH];
-#pragma unroll
-    for (int i = 0; i < C::BCH; ++i) {
-      const int rr = (row0 + 32 * i) % C::BN;
-      const int col = min(n0 + rr, p.Ncols - 1);
-      boff[i] = (uint32_t)(col * p.ldb + c16 * 8) * 2u;
-    }
+    uint32_t aoff[C::NAW], boff[C::NBW];
+    dma_offsets<C>(aoff, boff, p.perm, p.kdiv, p.lda, m0, m_end, p.ldb, n0, p.Ncols);
     const uint32_t bbytes = (uint32_t)((int64_t)p.Ncols * p.ldb * 2);
     const Rsrc rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)g * p.b_gstride, bbytes);
     const Rsrc rB1 = C::DUAL ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)g * p.b_gstride, bbytes) : rB0;
 
     f32x16 acc[C::NB][C::FM][C::FN];
     zero_acc<C>(acc);
-    mainloop<C>(lds, rA, aoff, rB0, rB1, boff, 0, p.K, acc);
-
-    epilogue_bf16<C, EPI>(lds, acc, static_cast<bf16_t*>(p.C), p.ldc, p.c_row0 + m0,
-                          m_end - m0, n0, p.Ncols);
+    mainloop<C>(S0, S1, S2, S3, rA, aoff, rB0, rB1, boff, 0, p.K, acc);
+    epilogue_bf16<C, EPI>(acc, static_cast<bf16_t*>(p.C), p.ldc, p.c_row0 + m0, m_end - m0, n0,
+                          p.Ncols);
   }
 }
 
@@ -345,26 +410,24 @@ template <class C>
 __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(
     const bf16_t* __restrict__ h, const bf16_t* __restrict__ w, float* __restrict__ z_part,
     int T, int d, int N, int splits) {
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  __shared__ __attribute__((aligned(1024))) char S0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S3[C::STAGES == 4 ? C::STAGE : 1024];
   const int tid = threadIdx.x;
   const int m0 = blockIdx.x * C::BM, n0 = blockIdx.y * C::BN, s = blockIdx.z;
-  // split s covers K steps [kt*s/splits, kt*(s+1)/splits): never empty when
+  // split s covers K slabs [kt*s/splits, kt*(s+1)/splits): never empty when
   // kt >= splits, so every partial slice is written
   const int kt = d / C::BK;
   const int k_begin = (kt * s / splits) * C::BK;
   const int k_len = (kt * (s + 1) / splits) * C::BK - k_begin;
-  const int row0 = tid >> 3, c16 = tid & 7;
-  uint32_t aoff[C::ACH];
-#pragma unroll
-  for (int i = 0; i < C::ACH; ++i) aoff[i] = (uint32_t)(min(m0 + row0 + 32 * i, T - 1) * d + c16 * 8) * 2u;
-  uint32_t boff[C::BCH];
-#pragma unroll
-  for (int i = 0; i < C::BCH; ++i) boff[i] = (uint32_t)(min(n0 + row0 + 32 * i, N - 1) * d + c16 * 8) * 2u;
-  f32x16 acc[C::NB][C::FM][C::FN];
-  zero_acc<C>(acc);
+  uint32_t aoff[C::NAW], boff[C::NBW];
+  dma_offsets<C>(aoff, boff, nullptr, 1, d, m0, T, d, n0, N);
   const Rsrc rh = make_rsrc(h, (uint32_t)((int64_t)T * d * 2));
   const Rsrc rw = make_rsrc(w, (uint32_t)((int64_t)N * d * 2));
-  mainloop<C>(lds, rh, aoff, rw, rw, boff, k_begin, k_len, acc);
+  f32x16 acc[C::NB][C::FM][C::FN];
+  zero_acc<C>(acc);
+  mainloop<C>(S0, S1, S2, S3, rh, aoff, rw, rw, boff, k_begin, k_len, acc);
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lr = lane & 31, lh = lane >> 5;
@@ -373,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      const int col = n0 + wn * C::TN + fn * 32 + lr;
+      const int col = n0 + wn * C::TN + strip_col(fn, lr);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = m0 + wm * C::TM + fm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
@@ -531,7 +594,7 @@ hipError_t launch_grouped(const GroupedProblem& p, int num_cu, hipStream_t st) {
   const int G = p.offsets ? p.groups : 1;
   const int64_t mt_bound = (int64_t)(p.M + C::BM - 1) / C::BM + (p.offsets ? G : 0);
   const int64_t tiles = mt_bound * ((p.Ncols + C::BN - 1) / C::BN);
-  int nblk = num_cu;
+  int nblk = num_cu * C::OCC;
   if (tiles < nblk) nblk = (int)tiles;
   if (nblk >= kXcds) nblk -= nblk % kXcds;
   if (nblk <= 0) return hipSuccess;
@@ -541,27 +604,32 @@ hipError_t launch_grouped(const GroupedProblem& p, int num_cu, hipStream_t st) {
 
 }  // namespace
 
-// Rows per expert at most 64: weight streaming. Otherwise tiles of 256 rows
-// when experts average at least 1024 rows, else 128.
+// Tile configurations of the prefill kernels.
+using GateUp256 = TileCfg<256, 128, true, 4, 1>;    // 256 rows, 1 block per CU
+using GateUp128 = TileCfg<128, 128, true, 3, 2>;    // 128 rows, 2 blocks per CU
+using Down128 = TileCfg<128, 256, false, 3, 2>;
+using Router = TileCfg<128, 128, false, 4, 1>;
+
+// Rows per expert at most 64: weight streaming. Gate/up: 256-row tiles (one
+// block per CU) when experts average at least 1024 rows, else 128-row tiles
+// (two blocks per CU); down: 128-row tiles.
 hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
   if (p.max_rows <= 64) return launch_skinny_any<true>(p, st);
   const int G = p.offsets ? p.groups : 1;
-  if (p.M >= 1024 * G) return launch_grouped<TileCfg<256, 128, true>, EPI_SWIGLU>(p, num_cu, st);
-  return launch_grouped<TileCfg<128, 128, true>, EPI_SWIGLU>(p, num_cu, st);
+  if (p.M >= 1024 * G) return launch_grouped<GateUp256, EPI_SWIGLU>(p, num_cu, st);
+  return launch_grouped<GateUp128, EPI_SWIGLU>(p, num_cu, st);
 }
 
 hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
   if (p.max_rows <= 64) return launch_skinny_any<false>(p, st);
-  const int G = p.offsets ? p.groups : 1;
-  if (p.M >= 1024 * G) return launch_grouped<TileCfg<256, 256, false>, EPI_STORE_BF16>(p, num_cu, st);
-  return launch_grouped<TileCfg<128, 256, false>, EPI_STORE_BF16>(p, num_cu, st);
+  return launch_grouped<Down128, EPI_STORE_BF16>(p, num_cu, st);
 }
 
 // Split-K factor of the router GEMM: enough blocks to fill about 256 CUs,
 // at least four K steps per split, at most kRouterMaxSplits. It depends on
 // the shape only, so results do not depend on the device.
 int router_splits(int T, int d, int N) {
-  using C = TileCfg<128, 128, false>;
+  using C = Router;
   const int64_t tiles = (int64_t)((T + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
   int s = 1;
   while (s < kRouterMaxSplits && tiles * s * 2 <= 256 && (d / 64) >= s * 2 * 4) s *= 2;
@@ -570,7 +638,7 @@ int router_splits(int T, int d, int N) {
 
 hipError_t launch_router_gemm_bf16(const void* h, const void* w, float* z_part, int T, int d,
                                    int N, int splits, hipStream_t st) {
-  using C = TileCfg<128, 128, false>;
+  using C = Router;
   dim3 grid((T + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, splits);
   hipLaunchKernelGGL((router_gemm_kernel<C>), grid, dim3(kThreads), 0, st,
                      static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(w), z_part, T, d,
