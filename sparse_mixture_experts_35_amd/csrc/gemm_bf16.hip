@@ -147,10 +147,28 @@ __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict_
   dma_slab<C>(dst, A, aoff, B0, B1, boff, kload_bytes);
   read_frags<C>(cur, 1, f1);
   mma<C>(f0, acc);
+  // One wave per SIMD: spread the loads and fragment reads through the MFMA
+  // stream (the MFMAs of one k-step use distinct accumulators, any order).
+  constexpr int NMF = C::NB * C::FM * C::FN;      // MFMAs per k-step
+  constexpr int NRD = C::FM + C::NB * C::FN;      // fragment reads per k-step
+#pragma unroll
+  for (int i = 0; i < NMF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+    if (i * C::NLW / NMF != (i + 1) * C::NLW / NMF)
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                    // load
+    if (i * NRD / NMF != (i + 1) * NRD / NMF)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // LDS read
+  }
   wait_vmcnt<(C::STAGES - 2) * C::NLW>();
   __builtin_amdgcn_s_barrier();
   read_frags<C>(nxt, 0, f0);
   mma<C>(f1, acc);
+#pragma unroll
+  for (int i = 0; i < NMF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+    if (i * NRD / NMF != (i + 1) * NRD / NMF)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // LDS read
+  }
 }
 
 // acc += A[rows] · B[cols]^T over k in [k_begin, k_begin + k_len) (k_len a
