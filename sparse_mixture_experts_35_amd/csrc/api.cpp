@@ -3,6 +3,7 @@
 // runs before the first HIP call, so invalid arguments never reach the GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -119,9 +120,34 @@ size_t act_bytes(const moe_shape* s) {
   const size_t R = (size_t)s->T * s->k;
   return esize(s) * (R * s->d_ff + (size_t)s->T * s->d_ff_shared);
 }
+// Expert stage: SwiGLU activations, then (bf16) the split-K partial sums
+// and arrival counters of the grouped GEMMs.
+int64_t split_floats(const moe_shape* s) {
+  if (s->dtype != MOE_BF16) return 0;
+  const int64_t R = (int64_t)s->T * s->k;
+  int64_t f = std::max(moe::split_part_floats(R, s->N, s->d_ff, true),
+                       moe::split_part_floats(R, s->N, s->d, false));
+  if (s->d_ff_shared)
+    f = std::max(f, std::max(moe::split_part_floats(s->T, 1, s->d_ff_shared, true),
+                             moe::split_part_floats(s->T, 1, s->d, false)));
+  return f;
+}
+struct FfnWs {
+  size_t act, part, cnt, end;
+};
+FfnWs ffn_ws(const moe_shape* s, size_t base) {
+  FfnWs w;
+  w.act = base;
+  w.part = align_up(w.act + act_bytes(s));
+  const int64_t f = split_floats(s);
+  w.cnt = align_up(w.part + sizeof(float) * (size_t)f);
+  w.end = f ? align_up(w.cnt + sizeof(int32_t) * moe::kSplitCounters) : w.cnt;
+  return w;
+}
 struct FusedWs {
   RouteWs r;
-  size_t p_mean, ids, gates, counts, offsets, perm, row_of, f, act, rows, end;
+  FfnWs x;
+  size_t p_mean, ids, gates, counts, offsets, perm, row_of, f, rows, end;
 };
 FusedWs fused_ws(const moe_shape* s) {
   FusedWs w;
@@ -135,8 +161,8 @@ FusedWs fused_ws(const moe_shape* s) {
   w.perm = align_up(w.offsets + 4 * (N + 1));
   w.row_of = align_up(w.perm + 4 * R);
   w.f = align_up(w.row_of + 4 * R);
-  w.act = align_up(w.f + 4 * N + 4);
-  w.rows = align_up(w.act + act_bytes(s));
+  w.x = ffn_ws(s, align_up(w.f + 4 * N + 4));
+  w.rows = w.x.end;
   w.end = align_up(w.rows + esize(s) * (R + (s->d_ff_shared ? T : 0)) * s->d);
   return w;
 }
@@ -215,8 +241,13 @@ moe_status dispatch_impl(const moe_shape* s, const int32_t* ids, int32_t* counts
 moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32_t* perm_src,
                      const int32_t* offsets, const void* w_gate, const void* w_up,
                      const void* w_down, const void* sh_gate, const void* sh_up,
-                     const void* sh_down, void* out_rows, void* act, hipStream_t st) {
+                     const void* sh_down, void* out_rows, void* ws, const FfnWs& W,
+                     hipStream_t st) {
   const int T = s->T, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
+  void* act = at<char>(ws, W.act);
+  float* part = W.cnt > W.part ? at<float>(ws, W.part) : nullptr;
+  int32_t* part_cnt = part ? at<int32_t>(ws, W.cnt) : nullptr;
+  const int64_t part_floats = part ? (int64_t)((W.cnt - W.part) / sizeof(float)) : 0;
   const int R = T * s->k;
   const bool bf16 = s->dtype == MOE_BF16;
   const int ncu = bf16 ? num_cu() : 0;
@@ -229,20 +260,24 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
   moe::GroupedProblem p{};
   if (gateup) {
     p = moe::GroupedProblem{h, d, perm_src, s->k, offsets, s->N, R, T, w_gate, w_up,
-                            (int64_t)dff * d, d, dff, d, act, dff, 0, (uint32_t)(esz * T * d)};
+                            (int64_t)dff * d, d, dff, d, act, dff, 0, (uint32_t)(esz * T * d),
+                            part, part_cnt, part_floats};
     TRY(hip_check(run(p, true), "gate/up GEMM"));
     if (dfs) {
       p = moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d, dfs, d,
-                              act_sh, dfs, 0, (uint32_t)(esz * T * d)};
+                              act_sh, dfs, 0, (uint32_t)(esz * T * d),
+                              part, part_cnt, part_floats};
       TRY(hip_check(run(p, true), "shared gate/up GEMM"));
     }
   } else {
     p = moe::GroupedProblem{act, dff, nullptr, 1, offsets, s->N, R, T, w_down, nullptr,
-                            (int64_t)d * dff, dff, d, dff, out_rows, d, 0, (uint32_t)(esz * R * dff)};
+                            (int64_t)d * dff, dff, d, dff, out_rows, d, 0, (uint32_t)(esz * R * dff),
+                            part, part_cnt, part_floats};
     TRY(hip_check(run(p, false), "down GEMM"));
     if (dfs) {
       p = moe::GroupedProblem{act_sh, dfs, nullptr, 1, nullptr, 1, T, T, sh_down, nullptr, 0,
-                              dfs, d, dfs, out_rows, d, (int64_t)R, (uint32_t)(esz * T * dfs)};
+                              dfs, d, dfs, out_rows, d, (int64_t)R, (uint32_t)(esz * T * dfs),
+                              part, part_cnt, part_floats};
       TRY(hip_check(run(p, false), "shared down GEMM"));
     }
   }
@@ -299,7 +334,6 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm = at<int32_t>(ws, L.perm);
   int32_t* row_of = at<int32_t>(ws, L.row_of);
-  void* act = at<char>(ws, L.act);
   void* rows = at<char>(ws, L.rows);
 
   TRY(mark(events, 0, st));
@@ -309,10 +343,10 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, st));
   TRY(mark(events, 2, st));
   TRY(ffn_stage(s, true, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
-                act, st));
+                ws, L.x, st));
   TRY(mark(events, 3, st));
   TRY(ffn_stage(s, false, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
-                act, st));
+                ws, L.x, st));
   TRY(mark(events, 4, st));
   TRY(combine_impl(s, rows, row_of, gates, y, st));
   TRY(mark(events, 5, st));
@@ -398,13 +432,14 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* h, const int32_t* perm
   TRY(need16(w_down, "w_down"));
   TRY(check_shared(s, sh_gate, sh_up, sh_down));
   TRY(need16(out_rows, "out_rows"));
-  TRY(check_ws(ws, ws_bytes, align_up(act_bytes(s))));
+  const FfnWs W = ffn_ws(s, 0);
+  TRY(check_ws(ws, ws_bytes, W.end));
   if (s->T == 0) return MOE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   TRY(ffn_stage(s, true, h, perm_src, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
-                out_rows, ws, st));
+                out_rows, ws, W, st));
   return ffn_stage(s, false, h, perm_src, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
-                   out_rows, ws, st);
+                   out_rows, ws, W, st);
 }
 
 moe_status moe_combine(const moe_shape* s, const void* out_rows, const int32_t* row_of,

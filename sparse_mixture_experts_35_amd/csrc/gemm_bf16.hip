@@ -321,13 +321,154 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (
   }
 }
 
+// Tile t of the tile list -> expert g, rows [m0, m_end), first column n0.
+// Tile order: groups of GN = 8 n-tiles, m-tiles (all experts) inside, so
+// 4 m-tiles x 8 n-tiles of neighbouring tiles share A rows and B columns.
+struct TileInfo {
+  int g, m0, m_end, n0;
+};
+template <class C>
+__device__ __forceinline__ TileInfo tile_info(const GroupedProblem& p, const int* s_pref, int G,
+                                              int total_mt, int nt_n, int64_t t) {
+  constexpr int GN = 8;
+  const int64_t sg = (int64_t)total_mt * GN;
+  const int nsup = (int)(t / sg);
+  const int within = (int)(t - (int64_t)nsup * sg);
+  const int width = min(GN, nt_n - nsup * GN);
+  const int mt = within / width;
+  const int nt = nsup * GN + within % width;
+  // m-tile -> group (binary search in the prefix)
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= mt) lo = mid; else hi = mid;
+  }
+  // every lane computed the same values from LDS; say so to the compiler,
+  // so that descriptors and bounds live in scalar registers
+  TileInfo ti;
+  ti.g = __builtin_amdgcn_readfirstlane(lo);
+  const int gbase = p.offsets ? __builtin_amdgcn_readfirstlane(p.offsets[ti.g]) : 0;
+  const int gend = p.offsets ? __builtin_amdgcn_readfirstlane(p.offsets[ti.g + 1]) : p.M;
+  ti.m0 = gbase + (mt - __builtin_amdgcn_readfirstlane(s_pref[ti.g])) * C::BM;
+  ti.m_end = min(ti.m0 + C::BM, gend);
+  ti.n0 = nt * C::BN;
+  return ti;
+}
+
+// acc = A[tile rows] · B[tile columns]^T over k in [k_begin, k_begin + k_len).
+template <class C>
+__device__ __forceinline__ void tile_mainloop(const GroupedProblem& p, const TileInfo& ti, Rsrc rA,
+                                              char* S0, char* S1, char* S2, char* S3,
+                                              int k_begin, int k_len,
+                                              f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  uint32_t aoff[C::NAW], boff[C::NBW];
+  dma_offsets<C>(aoff, boff, p.perm, p.kdiv, p.lda, ti.m0, ti.m_end, p.ldb, ti.n0, p.Ncols);
+  const uint32_t bbytes = (uint32_t)((int64_t)p.Ncols * p.ldb * 2);
+  const Rsrc rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)ti.g * p.b_gstride, bbytes);
+  const Rsrc rB1 = C::DUAL ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)ti.g * p.b_gstride, bbytes) : rB0;
+  zero_acc<C>(acc);
+  mainloop<C>(S0, S1, S2, S3, rA, aoff, rB0, rB1, boff, k_begin, k_len, acc);
+}
+
+// A tile's fp32 partial sums in the split-K workspace, element-major
+// ([element][thread]) so that every wave instruction covers 1 KiB. Splits of
+// one tile may run on different XCDs, each with its own L2, so partials are
+// written and read with agent-scope coherent accesses (sc1, the form of a
+// relaxed agent-scope atomic load or store): no cache-wide write-back or
+// invalidate is needed, only the completion of the stores before the
+// arrival counter (an agent-scope atomic) is bumped.
+constexpr int kSc1 = 16;   // buffer cache-policy bit: agent-scope coherent
+template <class C>
+struct Partial {
+  static constexpr int FLOATS = C::BM * C::BN * C::NB;
+};
+template <class C>
+__device__ __forceinline__ void store_partial(Rsrc r, int soff,
+                                              const f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  int e = 0;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 16; i += 4, ++e) {
+          const f32x4 v = {acc[nb][fm][fn][i], acc[nb][fm][fn][i + 1], acc[nb][fm][fn][i + 2],
+                           acc[nb][fm][fn][i + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r,
+                                                 threadIdx.x * 16u, soff + e * kThreads * 16,
+                                                 kSc1);
+        }
+}
+// acc = partial (FIRST) or acc += partial, element by element.
+template <class C, bool FIRST>
+__device__ __forceinline__ void add_partial(Rsrc r, int soff, f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  int e = 0;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 16; i += 4, ++e) {
+          const f32x4 v = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, threadIdx.x * 16u,
+                                                           soff + e * kThreads * 16, kSc1));
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[nb][fm][fn][i + c] = FIRST ? v[c] : acc[nb][fm][fn][i + c] + v[c];
+        }
+}
+
+constexpr int kMaxSplit = 8;        // K splits of one tail tile
+constexpr int kMinSplitSlabs = 64;  // K slabs (of 32) per split at least
+constexpr int kQueueCounters = (kSplitCounters - kXcds) / kXcds;   // tail tiles per queue
+
+// Work plan of one queue: n tiles for B blocks. The tiles past the last
+// full round (n mod B of them) are cut into S K-ranges each, so that the
+// last round is made of short units instead of a few whole tiles.
+struct QueuePlan {
+  int64_t base, n, dp, items;   // first tile, tiles, whole tiles, work items
+  int S;
+};
+template <class C>
+__device__ __forceinline__ QueuePlan queue_plan(int64_t total, int x, int Q, int B, int KT,
+                                                int64_t cap_floats) {
+  QueuePlan q;
+  q.base = total * x / Q;
+  q.n = total * (x + 1) / Q - q.base;
+  q.dp = q.n;
+  q.S = 1;
+  const int rem = (int)(q.n % B);
+  if (rem > 0 && rem <= kQueueCounters) {
+    int sp = min(B / rem, min(KT / kMinSplitSlabs, kMaxSplit));
+    sp = (int)min((int64_t)sp, cap_floats / ((int64_t)Partial<C>::FLOATS * rem));
+    if (sp >= 2) {
+      q.S = sp;
+      q.dp = q.n - rem;
+    }
+  }
+  q.items = q.dp + (q.n - q.dp) * q.S;
+  return q;
+}
+
 // Persistent grouped GEMM. Every block first builds the exclusive prefix of
-// m-tiles per group in LDS, then walks its share of the tile list:
-//  * XCD-aware split: block b runs on XCD b % 8, and XCD x takes the
+// m-tiles per group in LDS, then takes work from queues:
+//  * XCD-aware queues: block b runs on XCD b % 8, and queue x holds the
 //    contiguous tile range [x·n/8, (x+1)·n/8), so the ~32 tiles in flight
-//    on one XCD share A rows and B columns in that XCD's L2;
-//  * tile order: groups of 8 n-tiles, m-tiles (all experts) inside, so 4
-//    m-tiles × 8 n-tiles run together.
+//    on one XCD share A rows and B columns in that XCD's L2. A block takes
+//    the next item of its own queue with an atomic counter, and once that
+//    queue is empty, items of the other queues; tile speed varies from CU
+//    to CU, and dynamic assignment evens it out.
+//  * split-K tail: each queue's last partial round of tiles is cut into S
+//    K-ranges per tile. Every split stores its fp32 partial sums; the block
+//    that arrives last at the tile's counter adds the S partials in split
+//    order and runs the epilogue. No block waits on another, and each tile's
+//    arithmetic is the same whichever blocks run it, so results do not
+//    depend on timing.
+// Without a workspace (p.part == NULL) the blocks walk a static schedule.
 template <class C, int EPI>
 __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedProblem p) {
   __shared__ __attribute__((aligned(1024))) char S0[C::STAGE];
@@ -335,6 +476,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
   __shared__ __attribute__((aligned(1024))) char S2[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char S3[C::STAGES == 4 ? C::STAGE : 1024];
   __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_item;
+  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int G = p.offsets ? p.groups : 1;
 
@@ -370,56 +513,102 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
   if (total == 0) return;
 
   const int nblk = gridDim.x, b = blockIdx.x;
-  int64_t t_begin, t_end, t_step;
-  if (nblk >= kXcds && nblk % kXcds == 0) {
+  const bool xcd_split = nblk >= kXcds && nblk % kXcds == 0;
+  const Rsrc rA = make_rsrc(p.A, p.a_bytes);
+  const bool dynamic = p.part != nullptr;
+  const int Q = xcd_split ? kXcds : 1;
+  const int BQ = nblk / Q;                       // blocks per queue
+  const int KT = p.K / C::BK;
+  const int64_t cap_q = p.part_floats / Q;       // partial floats per queue
+  constexpr int64_t TF = Partial<C>::FLOATS;
+
+  // static schedule: block b takes tiles t_next, t_next + t_step, ... < t_end
+  int64_t t_next = b, t_end = total, t_step = nblk;
+  if (xcd_split) {
     const int xcd = b % kXcds;
-    t_begin = total * xcd / kXcds + b / kXcds;
+    t_next = total * xcd / kXcds + b / kXcds;
     t_end = total * (xcd + 1) / kXcds;
     t_step = nblk / kXcds;
-  } else {
-    t_begin = b;
-    t_end = total;
-    t_step = nblk;
   }
-
-  const Rsrc rA = make_rsrc(p.A, p.a_bytes);
-  constexpr int GN = 8;
-
-  for (int64_t t = t_begin; t < t_end; t += t_step) {
-    // ---- tile -> (m-tile, n-tile)
-    const int64_t sg = (int64_t)total_mt * GN;
-    const int nsup = (int)(t / sg);
-    const int within = (int)(t - (int64_t)nsup * sg);
-    const int width = min(GN, nt_n - nsup * GN);
-    const int mt = within / width;
-    const int nt = nsup * GN + within % width;
-    // ---- m-tile -> group (binary search in the prefix)
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= mt) lo = mid; else hi = mid;
+  // dynamic schedule: the next item of queue x is fetched with one atomic,
+  // issued for item i+1 before item i's epilogue so that its latency hides
+  // behind the stores
+  int qi = 0, x = b % Q;
+  QueuePlan q;
+  int64_t it = 0;
+  if (dynamic) {
+    q = queue_plan<C>(total, x, Q, BQ, KT, cap_q);
+    if (tid == 0) s_item = atomicAdd(p.part_cnt + x, 1);
+    __syncthreads();
+    it = __builtin_amdgcn_readfirstlane(s_item);
+  }
+  for (;;) {
+    // ---- work item: tile t over K range [k0, k1); split s of S
+    int64_t t;
+    int S = 1, s = 0, j = 0;
+    if (dynamic) {
+      while (it >= q.items && qi < Q) {          // queue x is empty: next queue
+        if (++qi == Q) break;
+        x = (b % Q + qi) % Q;
+        q = queue_plan<C>(total, x, Q, BQ, KT, cap_q);
+        __syncthreads();                         // every thread has read s_item
+        if (tid == 0) s_item = atomicAdd(p.part_cnt + x, 1);
+        __syncthreads();
+        it = __builtin_amdgcn_readfirstlane(s_item);
+      }
+      if (qi == Q) break;
+      if (it < q.dp) {
+        t = q.base + it;
+      } else {
+        const int u = (int)(it - q.dp);
+        S = q.S;
+        j = u / S;
+        s = u - j * S;
+        t = q.base + q.dp + j;
+      }
+    } else {
+      if (t_next >= t_end) break;
+      t = t_next;
+      t_next += t_step;
     }
-    // every lane computed the same values from LDS; say so to the compiler,
-    // so that descriptors and bounds live in scalar registers
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int gbase = p.offsets ? __builtin_amdgcn_readfirstlane(p.offsets[g]) : 0;
-    const int gend = p.offsets ? __builtin_amdgcn_readfirstlane(p.offsets[g + 1]) : p.M;
-    const int m0 = gbase + (mt - __builtin_amdgcn_readfirstlane(s_pref[g])) * C::BM;
-    const int m_end = min(m0 + C::BM, gend);
-    const int n0 = nt * C::BN;
+    const int k0 = (KT * s / S) * C::BK, k1 = (KT * (s + 1) / S) * C::BK;
 
-    uint32_t aoff[C::NAW], boff[C::NBW];
-    dma_offsets<C>(aoff, boff, p.perm, p.kdiv, p.lda, m0, m_end, p.ldb, n0, p.Ncols);
-    const uint32_t bbytes = (uint32_t)((int64_t)p.Ncols * p.ldb * 2);
-    const Rsrc rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)g * p.b_gstride, bbytes);
-    const Rsrc rB1 = C::DUAL ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)g * p.b_gstride, bbytes) : rB0;
-
+    const TileInfo ti = tile_info<C>(p, s_pref, G, total_mt, nt_n, t);
     f32x16 acc[C::NB][C::FM][C::FN];
-    zero_acc<C>(acc);
-    mainloop<C>(S0, S1, S2, S3, rA, aoff, rB0, rB1, boff, 0, p.K, acc);
-    epilogue_bf16<C, EPI>(acc, static_cast<bf16_t*>(p.C), p.ldc, p.c_row0 + m0, m_end - m0, n0,
-                          p.Ncols);
+    tile_mainloop<C>(p, ti, rA, S0, S1, S2, S3, k0, k1 - k0, acc);
+    int nxt = 0;
+    if (dynamic && tid == 0) nxt = atomicAdd(p.part_cnt + x, 1);
+    bool write = true;
+    if (S > 1) {
+      // store this split's partial; the last split of the tile to arrive
+      // sums all of them in split order and writes the tile
+      const Rsrc rp = make_rsrc(p.part + (int64_t)x * cap_q + (int64_t)j * S * TF,
+                                (uint32_t)(S * TF * sizeof(float)));
+      store_partial<C>(rp, s * (int)(TF * sizeof(float)), acc);
+      wait_vmcnt<0>();                 // this wave's partial stores are complete
+      __syncthreads();
+      if (tid == 0) s_last = atomicAdd(p.part_cnt + kXcds + x * kQueueCounters + j, 1) == S - 1;
+      __syncthreads();
+      write = __builtin_amdgcn_readfirstlane(s_last);
+      if (write) {
+        add_partial<C, true>(rp, 0, acc);
+        for (int r = 1; r < S; ++r) add_partial<C, false>(rp, r * (int)(TF * sizeof(float)), acc);
+      }
+    }
+    if (write)
+      epilogue_bf16<C, EPI>(acc, static_cast<bf16_t*>(p.C), p.ldc, p.c_row0 + ti.m0,
+                            ti.m_end - ti.m0, ti.n0, p.Ncols);
+    if (dynamic) {
+      __syncthreads();                 // every thread has read s_item / s_last
+      if (tid == 0) s_item = nxt;
+      __syncthreads();
+      it = __builtin_amdgcn_readfirstlane(s_item);
+    }
   }
+}
+
+__global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
 // Router logits as a split-K GEMM: z_part[s][T][N] = h[:, Ks] · W_r[:, Ks]^T.
@@ -612,10 +801,17 @@ hipError_t launch_grouped(const GroupedProblem& p, int num_cu, hipStream_t st) {
   const int G = p.offsets ? p.groups : 1;
   const int64_t mt_bound = (int64_t)(p.M + C::BM - 1) / C::BM + (p.offsets ? G : 0);
   const int64_t tiles = mt_bound * ((p.Ncols + C::BN - 1) / C::BN);
+  // with a split-K workspace, small problems may use more blocks than tiles
+  const int64_t units = p.part ? tiles * kMaxSplit : tiles;
   int nblk = num_cu * C::OCC;
-  if (tiles < nblk) nblk = (int)tiles;
+  if (units < nblk) nblk = (int)units;
   if (nblk >= kXcds) nblk -= nblk % kXcds;
   if (nblk <= 0) return hipSuccess;
+  if (p.part) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(kThreads), 0, st, p.part_cnt, kSplitCounters);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((grouped_gemm_kernel<C, EPI>), dim3(nblk), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
@@ -626,11 +822,12 @@ hipError_t launch_grouped(const GroupedProblem& p, int num_cu, hipStream_t st) {
 using GateUp256 = TileCfg<256, 128, true, 4, 1>;    // 256 rows, 1 block per CU
 using GateUp128 = TileCfg<128, 128, true, 3, 2>;    // 128 rows, 2 blocks per CU
 using Down128 = TileCfg<128, 256, false, 3, 2>;
+using Down256 = TileCfg<256, 256, false, 4, 1>;
 using Router = TileCfg<128, 128, false, 4, 1>;
 
 // Rows per expert at most 64: weight streaming. Gate/up: 256-row tiles (one
 // block per CU) when experts average at least 1024 rows, else 128-row tiles
-// (two blocks per CU); down: 128-row tiles.
+// (two blocks per CU); down likewise with 256 x 256 or 128 x 256 tiles.
 hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
   if (p.max_rows <= 64) return launch_skinny_any<true>(p, st);
   const int G = p.offsets ? p.groups : 1;
@@ -640,7 +837,18 @@ hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu, hipStream_t s
 
 hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
   if (p.max_rows <= 64) return launch_skinny_any<false>(p, st);
+  const int G = p.offsets ? p.groups : 1;
+  if (p.M >= 1024 * G) return launch_grouped<Down256, EPI_STORE_BF16>(p, num_cu, st);
   return launch_grouped<Down128, EPI_STORE_BF16>(p, num_cu, st);
+}
+
+int64_t split_part_floats(int64_t M, int G, int Ncols, bool dual) {
+  // kMaxSplit partial tiles per tile at most (tiles of up to 256 rows and
+  // 256 columns); the cap covers one 256 KiB partial per block of a launch
+  // on 256 CUs
+  const int64_t cols = ((int64_t)Ncols + 255) / 256 * 256;
+  const int64_t f = (M + (int64_t)G * 256) * cols * (dual ? 2 : 1) * kMaxSplit;
+  return f < kSplitMaxFloats ? f : kSplitMaxFloats;
 }
 
 // Split-K factor of the router GEMM: enough blocks to fill about 256 CUs,

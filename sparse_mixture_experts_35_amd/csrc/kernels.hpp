@@ -57,7 +57,22 @@ struct GroupedProblem {
   int ldc;
   int64_t c_row0;
   uint32_t a_bytes;  // extent of A in bytes (rows of A times lda times element size)
+  // Work queues and split-K of the last, partial round of tiles (bf16
+  // prefill kernels; NULL: static schedule, no split). part holds
+  // part_floats fp32 partial sums, part_cnt kSplitCounters queue heads and
+  // arrival counters, zeroed by the launcher before every launch.
+  float* part;
+  int32_t* part_cnt;
+  int64_t part_floats;
 };
+
+constexpr int kSplitCounters = 1024;
+constexpr int64_t kSplitMaxFloats = int64_t(16) << 20;   // 64 MiB of partials
+// fp32 partial-sum capacity for the split-K tail of a grouped launch over
+// at most M rows in G groups and Ncols output columns (gate and up both
+// when dual), capped at kSplitMaxFloats. The kernel never uses more than it
+// is given: it lowers the split count to fit.
+int64_t split_part_floats(int64_t M, int G, int Ncols, bool dual);
 
 // Act = SiLU(A·B0^T) ⊙ (A·B1^T)   (bf16 in/out, fp32 accumulate)
 hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu,

@@ -136,6 +136,11 @@ CASES = [
     ("bf16_prefill_many_experts", 520, 128, 64, 8, 128, 0, W.DTYPE_BF16, 0),
     ("bf16_k16_N512", 200, 64, 512, 16, 64, 0, W.DTYPE_BF16, 0),
     ("bf16_N1_k1", 100, 64, 1, 1, 64, 64, W.DTYPE_BF16, 0),
+    # K of 4096 and more: the tiles past the last full round of a work queue
+    # (here: every tile) are split along K and summed by the last split
+    ("bf16_split_k4096", 256, 4096, 2, 1, 256, 0, W.DTYPE_BF16, 0),
+    ("bf16_split_down_k8192", 256, 256, 2, 1, 8192, 0, W.DTYPE_BF16, 1),
+    ("bf16_split_shared_k4096", 128, 4096, 4, 1, 128, 4096, W.DTYPE_BF16, 2),
 ]
 
 
@@ -262,10 +267,13 @@ def test_dispatch_random(T, N, k):
     assert abs(float(host(la)[0]) - 0.01 * N * np.sum(d.counts / (T * k) / N)) < 1e-6
 
 
-def test_deterministic_repeat():
-    """Same inputs twice: ids, permutation-dependent outputs and y identical."""
-    inp = W.random_small(520, 128, 64, 8, 128, 128, W.DTYPE_BF16, 2, seed=5)
-    s = shape_of(520, 128, 64, 8, 128, 128, W.DTYPE_BF16, 2)
+@pytest.mark.parametrize("T,d,N,k,dff,dfs", [(520, 128, 64, 8, 128, 128),
+                                              (256, 256, 2, 1, 8192, 0)])
+def test_deterministic_repeat(T, d, N, k, dff, dfs):
+    """Same inputs twice: ids, permutation-dependent outputs and y identical
+    (the second shape takes the split-K tail of the grouped GEMMs)."""
+    inp = W.random_small(T, d, N, k, dff, dfs, W.DTYPE_BF16, 2, seed=5)
+    s = shape_of(T, d, N, k, dff, dfs, W.DTYPE_BF16, 2)
     a = run_steps(s, inp)
     b = run_steps(s, inp)
     for key in ("ids", "gates", "perm", "row_of", "out_rows", "y", "p", "l_aux"):
