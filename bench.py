@@ -1,18 +1,23 @@
 """Benchmark of the MoE layer forward pass on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-calibration    # plain 1 GiB copy, for counter scaling
 
 A step is one moe_layer_fused call (route, dispatch, gate/up GEMM + SwiGLU,
 down GEMM, combine, load statistics) over one batch of synthetic tokens whose
 inputs are already resident in HBM. Prints ONE JSON line.
 
-  value     whole-layer tokens/s (T * K / wall time of K steps between two
-            device synchronisations)
-  roofline  the dominant kernel (the grouped gate/up GEMM) timed with HIP
-            events recorded by the library on its stream around that stage,
-            against the MI355X peak that bounds it: bf16 dense MFMA
-            2.5166 PFLOP/s when its rows per expert make it compute-bound,
-            HBM 8 TB/s when it streams weights (decode batches)
+  value     whole-layer tokens/s (T * K / wall time of the K timed steps
+            between two device synchronisations)
+  roofline  the dominant kernel (the grouped gate/up GEMM), timed with HIP
+            events that the library records on its own stream around that
+            stage in each of the K timed steps, against the MI355X peak that
+            bounds it: bf16 dense MFMA 2.5166 PFLOP/s when its rows per
+            expert make it compute-bound, HBM 8 TB/s when it streams weights
+            (decode batches). traffic: HBM bytes per launch from rocprofv3
+            FETCH_SIZE / WRITE_SIZE counters scaled by a plain copy's
+            readings (a committed summary under profiles/), reported only
+            while the kernel sources match the ones that were counted
   decode    the same layer at a decode batch (16 tokens) on the same
             weights: tokens/s and HBM GB/s of the touched experts' weights
   cpu_baseline  the float64 oracle on a bounded sample of the workload,
@@ -20,6 +25,7 @@ inputs are already resident in HBM. Prints ONE JSON line.
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -36,9 +42,53 @@ import workloads as W  # noqa: E402
 METRIC = "MoE-layer tokens/sec at 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)"
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
-# measured rocprofv3 FETCH_SIZE/WRITE_SIZE factors for a plain copy kernel
-# (bytes counted per byte moved); see profiles/. None until measured.
-TRAFFIC = None
+PROFILES = os.path.join(ROOT, "profiles")
+GEMM_SOURCES = ("gemm_bf16.hip", "common.hpp", "kernels.hpp")
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_35_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, or None when there is none or the kernel sources have
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, gib=1, reps=5):
+    """A plain device copy of a known size: its FETCH_SIZE / WRITE_SIZE
+    readings per dispatch give the bytes-per-count scale of the counters."""
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps,
+                      "ms_per_copy": dt * 1e3, "gb_s": 2 * n / dt / 1e9}), flush=True)
 
 
 def hip_events(n):
@@ -68,7 +118,9 @@ def hip_events(n):
     return evs, elapsed, destroy
 
 
-def run_layer(M, torch, w, inp, steps, warmup, marked_steps):
+def run_layer(M, torch, w, inp, steps, warmup):
+    """warmup untimed steps, then `steps` timed steps; the library records
+    six HIP events per timed step on its stream at the stage boundaries."""
     s = M.Shape(w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.mode, w.aux_alpha)
     layer = M.MoELayer(s)
     args = dict(b_router=inp["b_router"], b_select=inp["b_select"], sh_gate=inp["sh_gate"],
@@ -78,27 +130,22 @@ def run_layer(M, torch, w, inp, steps, warmup, marked_steps):
     for _ in range(warmup):
         res = layer(inp["h"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
                     out=y, **args)
+    evs, elapsed, destroy = hip_events(6 * steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
         res = layer(inp["h"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
-                    out=y, **args)
+                    out=y, events=evs[6 * i:6 * i + 6], **args)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # stage timing with events recorded by the library on its stream
-    evs, elapsed, destroy = hip_events(6 * marked_steps)
-    for i in range(marked_steps):
-        layer(inp["h"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], out=y,
-              events=evs[6 * i:6 * i + 6], **args)
-    torch.cuda.synchronize()
     names = ["route", "dispatch", "gate_up", "down", "combine"]
     stage = {n: 0.0 for n in names}
     total = 0.0
-    for i in range(marked_steps):
+    for i in range(steps):
         e = evs[6 * i:6 * i + 6]
         for j, n in enumerate(names):
-            stage[n] += elapsed(e[j], e[j + 1]) / marked_steps
-        total += elapsed(e[0], e[5]) / marked_steps
+            stage[n] += elapsed(e[j], e[j + 1]) / steps
+        total += elapsed(e[0], e[5]) / steps
     destroy()
     counts = res["counts"].cpu().numpy()
     return wall, stage, total, counts
@@ -167,9 +214,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=W.MIXTRAL_PREFILL.name, choices=sorted(W.ALL))
     ap.add_argument("--decode-tokens", type=int, default=16)
-    ap.add_argument("--cpu-sample", type=int, default=128)
+    ap.add_argument("--cpu-sample", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration) and exit")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this "
@@ -182,12 +231,15 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if a.copy_calibration:
+        copy_calibration(torch)
+        return
     M.lib()   # fail loudly if the HIP library is missing
 
     w = W.ALL[a.workload]
     inp = W.device_inputs(w)
     torch.cuda.synchronize()
-    wall, stage, total_ev, counts = run_layer(M, torch, w, inp, a.steps, a.warmup, a.steps)
+    wall, stage, total_ev, counts = run_layer(M, torch, w, inp, a.steps, a.warmup)
     ms = wall / a.steps * 1e3
     tok_s = w.T * a.steps / wall
     flops_gu, bytes_gu, touched = gateup_work(w, counts)
@@ -198,13 +250,15 @@ def main():
     if mfma_bound:
         achieved = flops_gu / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": TRAFFIC,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(w.name, "grouped_gemm_gateup"),
                 "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",
                 "algorithmic_per_launch": flops_gu, "avg_launch_ms": stage["gate_up"]}
     else:
         achieved = bytes_gu / gu_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": TRAFFIC,
+                "frac": achieved / PEAK_HBM_GBS,
+                "traffic": measured_traffic(w.name, "skinny_gemm_gateup"),
                 "kernel": "skinny_gemm_kernel (gate/up + SwiGLU)",
                 "algorithmic_per_launch": bytes_gu, "avg_launch_ms": stage["gate_up"]}
     out = {
@@ -227,8 +281,7 @@ def main():
                        T=a.decode_tokens)
         dinp = dict(inp)
         dinp["h"] = inp["h"][:a.decode_tokens].contiguous()
-        dwall, dstage, _, dcounts = run_layer(M, torch, wd, dinp, max(a.steps, 20), a.warmup,
-                                              max(a.steps, 20))
+        dwall, dstage, _, dcounts = run_layer(M, torch, wd, dinp, max(a.steps, 20), a.warmup)
         dsteps = max(a.steps, 20)
         dms = dwall / dsteps * 1e3
         _, dbytes, dtouched = layer_work(wd, dcounts)

@@ -123,10 +123,15 @@ const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 
 /* Host, pure: workspace bytes that suffice for EVERY call below with this
- * shape (the fused layer needs the most). 0 for an invalid shape. The
- * individual calls need: moe_route — T·N + blocks·N + N floats;
- * moe_dispatch — none; moe_expert_ffn — the SwiGLU activations
- * (T·k·d_ff + T·d_ff_shared elements); moe_combine — none. */
+ * shape (the fused layer needs the most). 0 for an invalid shape.
+ * moe_dispatch and moe_combine use no workspace. moe_route keeps the
+ * router's partial logits and per-block probability sums there;
+ * moe_expert_ffn keeps the SwiGLU activations (T·k·d_ff + T·d_ff_shared
+ * elements) and, on the bf16 path, up to 64 MiB of fp32 split-K partial
+ * sums plus 4 KiB of work-queue counters. The workspace needs no
+ * initialisation, its contents are undefined after a call, and one
+ * workspace serves one call at a time (calls in flight on different
+ * streams need separate workspaces). */
 size_t moe_workspace_bytes(const moe_shape* s);
 
 /* Router: logits, scores, top-k and gates (steps 1-4).
@@ -169,6 +174,11 @@ moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids,
  *     out_rows[r] = E_e(h[perm_src[r] / k]) for bucket row r of expert e;
  *     out_rows[T·k + t] = E_shared(h[t]) when a shared expert is present.
  *   sh_gate/sh_up/sh_down must be given iff d_ff_shared > 0.
+ *   offsets [N+1] as written by moe_dispatch (non-decreasing, offsets[0] = 0,
+ *   offsets[N] = T·k; precondition, not checked on the device).
+ * Bitwise reproducible: work is spread over the GPU dynamically, but every
+ * output element is computed by the same sequence of operations; K-split
+ * partial sums are added in split order. */
  * [wuhy-notes §一 expert formula, §八 shared expert, §十二 小矩阵问题] */
 moe_status moe_expert_ffn(const moe_shape* s, const void* h,
                           const int32_t* perm_src, const int32_t* offsets,
