@@ -178,7 +178,7 @@ moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids,
  *   offsets[N] = T·k; precondition, not checked on the device).
  * Bitwise reproducible: work is spread over the GPU dynamically, but every
  * output element is computed by the same sequence of operations; K-split
- * partial sums are added in split order. */
+ * partial sums are added in split order.
  * [wuhy-notes §一 expert formula, §八 shared expert, §十二 小矩阵问题] */
 moe_status moe_expert_ffn(const moe_shape* s, const void* h,
                           const int32_t* perm_src, const int32_t* offsets,

@@ -142,3 +142,17 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(M, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(M.MoEError):
         M.lib()
+
+
+@pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
+def test_header_compiles(lang, compiler, tmp_path):
+    """include/moe.h is a self-contained C and C++ header."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not available")
+    src = tmp_path / ("use.c" if lang == "c" else "use.cpp")
+    src.write_text('#include "moe.h"\nint main(void) { return (int)moe_abi_version(); }\n')
+    r = subprocess.run([compiler, "-fsyntax-only", "-Wall", "-Werror", "-I", os.path.dirname(HDR),
+                        str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
