@@ -71,7 +71,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 template <class C>
 __device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const uint32_t* aoff,
                                          Rsrc B0, Rsrc B1, const uint32_t* boff, int kbytes) {
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS address in SALU
 #pragma unroll
   for (int j = 0; j < C::NAW; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(A, (lds_ptr_t)(st + (w + 4 * j) * 1024), 16,
@@ -147,17 +147,17 @@ __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict_
   dma_slab<C>(dst, A, aoff, B0, B1, boff, kload_bytes);
   read_frags<C>(cur, 1, f1);
   mma<C>(f0, acc);
-  // One wave per SIMD: spread the loads and fragment reads through the MFMA
-  // stream (the MFMAs of one k-step use distinct accumulators, any order).
+  // One wave per SIMD: weave the fragment reads (needed first, by the next
+  // half-step) into the first MFMAs and the loads into the rest (the MFMAs
+  // of one k-step use distinct accumulators, any order).
   constexpr int NMF = C::NB * C::FM * C::FN;      // MFMAs per k-step
   constexpr int NRD = C::FM + C::NB * C::FN;      // fragment reads per k-step
 #pragma unroll
   for (int i = 0; i < NMF; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
-    if (i * C::NLW / NMF != (i + 1) * C::NLW / NMF)
+    if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+    else if ((i - NRD) * C::NLW / (NMF - NRD) != (i - NRD + 1) * C::NLW / (NMF - NRD))
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                    // load
-    if (i * NRD / NMF != (i + 1) * NRD / NMF)
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // LDS read
   }
   wait_vmcnt<(C::STAGES - 2) * C::NLW>();
   __builtin_amdgcn_s_barrier();
@@ -166,8 +166,7 @@ __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict_
 #pragma unroll
   for (int i = 0; i < NMF; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
-    if (i * NRD / NMF != (i + 1) * NRD / NMF)
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // LDS read
+    if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
   }
 }
 
@@ -194,23 +193,30 @@ __device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict
     wait_vmcnt<2 * C::NLW>();
     __builtin_amdgcn_s_barrier();
     read_frags<C>(S0, 0, f0);
-    for (int k = 0; k < KT; k += 4) {
+    int k = 0;
+    for (; k + 4 <= KT; k += 4) {
       k_step<C>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
-      if (k + 1 < KT) k_step<C>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
-      if (k + 2 < KT) k_step<C>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
-      if (k + 3 < KT) k_step<C>(S3, S0, S2, kbyte(k + 6), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C>(S3, S0, S2, kbyte(k + 6), f0, f1, A, aoff, B0, B1, boff, acc);
     }
+    if (k < KT) k_step<C>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k + 1 < KT) k_step<C>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k + 2 < KT) k_step<C>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
   } else {
     dma_slab<C>(S0, A, aoff, B0, B1, boff, kbyte(0));
     dma_slab<C>(S1, A, aoff, B0, B1, boff, kbyte(1));
     wait_vmcnt<C::NLW>();
     __builtin_amdgcn_s_barrier();
     read_frags<C>(S0, 0, f0);
-    for (int k = 0; k < KT; k += 3) {
+    int k = 0;
+    for (; k + 3 <= KT; k += 3) {
       k_step<C>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
-      if (k + 1 < KT) k_step<C>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
-      if (k + 2 < KT) k_step<C>(S2, S0, S1, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C>(S2, S0, S1, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
     }
+    if (k < KT) k_step<C>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k + 1 < KT) k_step<C>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -251,9 +257,18 @@ __device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][
                                               int Ncols) {
   static_assert(C::FN % 2 == 0, "column pairs need an even number of MFMA blocks");
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // wave index, tile origin and extent are uniform: keep them scalar (they
+  // can come back from spill slots as vector values, and a buffer store with
+  // a vector descriptor or soffset turns into a loop over lanes)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lr = lane & 31, lh = lane >> 5;
+  rows_valid = __builtin_amdgcn_readfirstlane(rows_valid);
+  n0 = __builtin_amdgcn_readfirstlane(n0);
+  const uint32_t r0lo = __builtin_amdgcn_readfirstlane((uint32_t)row0_out);
+  const uint32_t r0hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)row0_out >> 32));
+  row0_out = (int64_t)(((uint64_t)r0hi << 32) | r0lo);
   // Row stride in bytes, made opaque so the compiler recomputes the row
   // offsets per tile instead of hoisting (and spilling) all of them.
   int ldc2 = (int)ldc * 2;
