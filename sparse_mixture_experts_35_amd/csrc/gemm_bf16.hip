@@ -32,9 +32,10 @@ constexpr int kXcds = 8;   // MI355X: 8 XCDs; block b runs on XCD b % 8
 // DUAL), four waves in a 2x2 grid, each wave TM x TN with 32x32x16 MFMAs.
 // K advances in slabs of BK = 32. A slab of the block tile lives in LDS as
 // BM + BROWS rows of 64 bytes (A rows, then B rows), 16-byte chunks XOR-
-// swizzled per row so that the fragment reads of 8 or 16 consecutive rows
-// hit distinct banks. STAGES such stages form a ring; OCC blocks share a CU
+// swizzled per row. STAGES such stages form a ring; OCC blocks share a CU
 // (two blocks: two waves per SIMD, each hides the other's waits).
+// (64-deep slabs, whose loads cover whole cache lines, were measured too:
+// they halve the L1-to-L2 requests but did not make the kernel faster.)
 template <int BM_, int BN_, bool DUAL_, int STAGES_, int OCC_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 32;
@@ -47,27 +48,35 @@ struct TileCfg {
   static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
   static constexpr int BROWS = BN * NB;             // B rows staged per slab
   static constexpr int ROWB = BK * 2;               // 64 bytes per staged row
+  static constexpr int CH = ROWB / 16;              // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;               // rows per 1 KiB load instruction
   static constexpr int A_BYTES = BM * ROWB;
   static constexpr int STAGE = (BM + BROWS) * ROWB;
-  static constexpr int NAW = BM / 64;               // A blocks (16 rows, 1 KiB) per wave
-  static constexpr int NBW = BROWS / 64;            // B blocks per wave
+  static constexpr int NAW = BM / (4 * RPI);        // A load blocks per wave
+  static constexpr int NBW = BROWS / (4 * RPI);     // B load blocks per wave
   static constexpr int NLW = NAW + NBW;             // direct-to-LDS loads per wave per slab
   static_assert(FM >= 1 && FN >= 1, "tile too small");
-  static_assert(BM % 64 == 0 && BROWS % 64 == 0, "tile rows must be multiples of 64");
+  static_assert(BM % (4 * RPI) == 0 && BROWS % (4 * RPI) == 0, "tile rows vs load blocks");
+  static_assert(STAGES == 3 || STAGES == 4, "pipeline shape");
 };
 
 // Chunk swizzle of staged row r: logical 16-byte chunk c lives at c ^ swz(r).
-// For rows r..r+7 (r a multiple of 8) the pairs (r & 1, chunk) are distinct,
-// and for rows r..r+15 the pairs (r & 3, chunk) are, so reads of 8 or 16
-// consecutive rows are conflict-free with 128- or 256-byte wide LDS.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
+// ds_read_b128 serves 16 consecutive lanes per pass from 64 four-byte banks.
+// A fragment read has lane = row and one logical chunk, so a lane's bank
+// quad is (r & 3, chunk), and (r & 3, (r >> 2) & 3) is distinct over any 16
+// consecutive rows. Measured conflict-free with the LDS bank-conflict
+// counter on gfx950 (where ((r >> 1) + (r >> 3)) & 3, for instance, still
+// costs 4 stall cycles per read).
+template <class C>
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Issue the direct-to-LDS loads of one slab (byte offset kbytes along K)
-// into stage `st`. Wave w fills A blocks w, w+4, ... and B blocks w, w+4, ...;
-// lane l of a block writes bytes [16 l, 16 l + 16) of the block, i.e. row
-// l / 4, physical chunk l % 4, so it loads logical chunk (l % 4) ^ swz(row).
+// into stage `st`. Wave w fills A blocks w, w+4, ... and B blocks w, w+4, ...
+// (RPI rows, 1 KiB each); lane l of a block writes bytes [16 l, 16 l + 16)
+// of the block, i.e. row l / CH, physical chunk l % CH, so it loads logical
+// chunk (l % CH) ^ swz(row).
 template <class C>
 __device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const uint32_t* aoff,
                                          Rsrc B0, Rsrc B1, const uint32_t* boff, int kbytes) {
@@ -78,7 +87,7 @@ __device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const ui
                                              aoff[j], kbytes, 0, 0);
 #pragma unroll
   for (int j = 0; j < C::NBW; ++j) {
-    const bool up = C::DUAL && (4 * j) >= C::BN / 16;   // B block w + 4j is an up row block
+    const bool up = C::DUAL && 4 * j * C::RPI >= C::BN;   // B block w + 4j holds up rows
     __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? B1 : B0,
                                              (lds_ptr_t)(st + C::A_BYTES + (w + 4 * j) * 1024),
                                              16, boff[j], kbytes, 0, 0);
@@ -98,7 +107,7 @@ __device__ __forceinline__ void read_frags(const char* __restrict__ st, int ks, 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lr = lane & 31, lh = lane >> 5;
-  const int co = (((ks * 2 + lh) ^ swz(lr)) << 4);
+  const int co = (((ks * 2 + lh) ^ swz<C>(lr)) << 4);
   const char* a = st + (wm * C::TM + lr) * C::ROWB + co;
   const char* b = st + C::A_BYTES + (wn * C::TN + lr) * C::ROWB + co;
 #pragma unroll
@@ -129,6 +138,37 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 15));
 }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0): also every LDS read of this wave is done,
+// so that once all waves pass the following barrier, a stage they read can
+// be overwritten by loads.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0x0 << 8) | (0x7 << 4) | (N & 15));
+}
+
+// Scheduling hints for one MFMA k-step (one wave per SIMD): the next
+// k-step's fragment reads go between the first MFMAs, then `LOADS`
+// direct-to-LDS loads are spread over the remaining ones (or over all of
+// them when the k-step has no reads). The MFMAs of a k-step use distinct
+// accumulators, so any order is valid.
+template <class C, int LOADS, bool READS>
+__device__ __forceinline__ void weave() {
+  constexpr int NMF = C::NB * C::FM * C::FN;      // MFMAs per k-step
+  constexpr int NRD = READS ? C::FM + C::NB * C::FN : 0;
+  constexpr int FIRST = (LOADS > 0 && NRD < NMF) ? NRD : 0;   // first slot with loads
+#pragma unroll
+  for (int i = 0; i < NMF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+    if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+    if (LOADS > 0 && i >= FIRST) {
+      const int n = (i - FIRST + 1) * LOADS / (NMF - FIRST) - (i - FIRST) * LOADS / (NMF - FIRST);
+#pragma unroll
+      for (int q = 0; q < n; ++q) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // load
+    }
+  }
+}
+
 // One K step k on stage S[j]: frags f0 (k-step 0) are already in registers.
 //  1. issue the loads of slab k+STAGES-1 (clamped to the last slab) into the
 //     stage slab k-1 occupied
@@ -147,27 +187,12 @@ __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict_
   dma_slab<C>(dst, A, aoff, B0, B1, boff, kload_bytes);
   read_frags<C>(cur, 1, f1);
   mma<C>(f0, acc);
-  // One wave per SIMD: weave the fragment reads (needed first, by the next
-  // half-step) into the first MFMAs and the loads into the rest (the MFMAs
-  // of one k-step use distinct accumulators, any order).
-  constexpr int NMF = C::NB * C::FM * C::FN;      // MFMAs per k-step
-  constexpr int NRD = C::FM + C::NB * C::FN;      // fragment reads per k-step
-#pragma unroll
-  for (int i = 0; i < NMF; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
-    if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
-    else if ((i - NRD) * C::NLW / (NMF - NRD) != (i - NRD + 1) * C::NLW / (NMF - NRD))
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                    // load
-  }
-  wait_vmcnt<(C::STAGES - 2) * C::NLW>();
+  weave<C, C::NLW, true>();
+  wait_vmcnt_lds<(C::STAGES - 2) * C::NLW>();
   __builtin_amdgcn_s_barrier();
   read_frags<C>(nxt, 0, f0);
   mma<C>(f1, acc);
-#pragma unroll
-  for (int i = 0; i < NMF; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
-    if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
-  }
+  weave<C, 0, true>();
 }
 
 // acc += A[rows] · B[cols]^T over k in [k_begin, k_begin + k_len) (k_len a
@@ -312,27 +337,27 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // Per-lane load offsets of the DMA blocks of wave w: A block w + 4j holds
-// tile rows 16(w + 4j) .. +15; lane l loads row 16(w+4j) + l/4, logical chunk
-// (l % 4) ^ swz(row). Rows past the group's end re-read its last row.
+// tile rows RPI(w + 4j) .. +RPI-1; lane l loads row RPI(w+4j) + l/CH, logical
+// chunk (l % CH) ^ swz(row). Rows past the group's end re-read its last row.
 template <class C>
 __device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (&boff)[C::NBW],
                                             const int32_t* perm, int kdiv, int lda, int m0,
                                             int m_end, int ldb, int n0, int Ncols) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rl = lane >> 2;
+  const int rl = lane / C::CH, ch = lane % C::CH;
 #pragma unroll
   for (int j = 0; j < C::NAW; ++j) {
-    const int row = 16 * (w + 4 * j) + rl;
+    const int row = C::RPI * (w + 4 * j) + rl;
     const int r = min(m0 + row, m_end - 1);
     const int src = perm ? perm[r] / kdiv : r;
-    aoff[j] = (uint32_t)(src * lda * 2 + (((lane & 3) ^ swz(row)) << 4));
+    aoff[j] = (uint32_t)(src * lda * 2 + ((ch ^ swz<C>(row)) << 4));
   }
 #pragma unroll
   for (int j = 0; j < C::NBW; ++j) {
-    const int row = 16 * (w + 4 * j) + rl;      // B row within the stage's B part
+    const int row = C::RPI * (w + 4 * j) + rl;  // B row within the stage's B part
     const int q = row % C::BN;                  // staged row -> output column (strip_col)
     const int col = min(n0 + (q & ~63) + 2 * (q & 31) + ((q >> 5) & 1), Ncols - 1);
-    boff[j] = (uint32_t)(col * ldb * 2 + (((lane & 3) ^ swz(C::BM + row)) << 4));
+    boff[j] = (uint32_t)(col * ldb * 2 + ((ch ^ swz<C>(C::BM + row)) << 4));
   }
 }
 
@@ -438,7 +463,7 @@ __device__ __forceinline__ void add_partial(Rsrc r, int soff, f32x16 (&acc)[C::N
 }
 
 constexpr int kMaxSplit = 8;        // K splits of one tail tile
-constexpr int kMinSplitSlabs = 64;  // K slabs (of 32) per split at least
+constexpr int kMinSplitK = 2048;    // K per split at least
 constexpr int kQueueCounters = (kSplitCounters - kXcds) / kXcds;   // tail tiles per queue
 
 // Work plan of one queue: n tiles for B blocks. The tiles past the last
@@ -458,7 +483,7 @@ __device__ __forceinline__ QueuePlan queue_plan(int64_t total, int x, int Q, int
   q.S = 1;
   const int rem = (int)(q.n % B);
   if (rem > 0 && rem <= kQueueCounters) {
-    int sp = min(B / rem, min(KT / kMinSplitSlabs, kMaxSplit));
+    int sp = min(B / rem, min(KT / (kMinSplitK / C::BK), kMaxSplit));
     sp = (int)min((int64_t)sp, cap_floats / ((int64_t)Partial<C>::FLOATS * rem));
     if (sp >= 2) {
       q.S = sp;
@@ -533,7 +558,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
   const bool dynamic = p.part != nullptr;
   const int Q = xcd_split ? kXcds : 1;
   const int BQ = nblk / Q;                       // blocks per queue
-  const int KT = p.K / C::BK;
+  const int KT = p.K / C::BK;                    // K slabs
   const int64_t cap_q = p.part_floats / Q;       // partial floats per queue
   constexpr int64_t TF = Partial<C>::FLOATS;
 
