@@ -77,20 +77,25 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // (RPI rows, 1 KiB each); lane l of a block writes bytes [16 l, 16 l + 16)
 // of the block, i.e. row l / CH, physical chunk l % CH, so it loads logical
 // chunk (l % CH) ^ swz(row).
-template <class C>
+// PART selects the loads: all of them (-1), or the first (0) or second (1)
+// half of the wave's list (A blocks, then B blocks).
+template <class C, int PART = -1>
 __device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const uint32_t* aoff,
                                          Rsrc B0, Rsrc B1, const uint32_t* boff, int kbytes) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS address in SALU
 #pragma unroll
-  for (int j = 0; j < C::NAW; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(A, (lds_ptr_t)(st + (w + 4 * j) * 1024), 16,
-                                             aoff[j], kbytes, 0, 0);
-#pragma unroll
-  for (int j = 0; j < C::NBW; ++j) {
-    const bool up = C::DUAL && 4 * j * C::RPI >= C::BN;   // B block w + 4j holds up rows
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? B1 : B0,
-                                             (lds_ptr_t)(st + C::A_BYTES + (w + 4 * j) * 1024),
-                                             16, boff[j], kbytes, 0, 0);
+  for (int q = 0; q < C::NLW; ++q) {
+    if (PART >= 0 && (q < C::NLW / 2) != (PART == 0)) continue;
+    if (q < C::NAW) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(A, (lds_ptr_t)(st + (w + 4 * q) * 1024), 16,
+                                               aoff[q], kbytes, 0, 0);
+    } else {
+      const int j = q - C::NAW;
+      const bool up = C::DUAL && 4 * j * C::RPI >= C::BN;   // B block w + 4j holds up rows
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? B1 : B0,
+                                               (lds_ptr_t)(st + C::A_BYTES + (w + 4 * j) * 1024),
+                                               16, boff[j], kbytes, 0, 0);
+    }
   }
 }
 
@@ -148,15 +153,17 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 }
 
 // Scheduling hints for one MFMA k-step (one wave per SIMD): the next
-// k-step's fragment reads go between the first MFMAs, then `LOADS`
-// direct-to-LDS loads are spread over the remaining ones (or over all of
-// them when the k-step has no reads). The MFMAs of a k-step use distinct
-// accumulators, so any order is valid.
-template <class C, int LOADS, bool READS>
+// k-step's fragment reads go between the first MFMAs, and `LOADS`
+// direct-to-LDS loads are spread evenly over all MFMAs (SPREAD) or over the
+// ones after the reads. A wave that issues loads back to back waits behind
+// the other waves' loads at the CU's load unit and leaves its MFMA pipe idle;
+// one load every few MFMAs measured fastest. The MFMAs of a k-step use
+// distinct accumulators, so any order is valid.
+template <class C, int LOADS, bool READS, bool SPREAD = false>
 __device__ __forceinline__ void weave() {
   constexpr int NMF = C::NB * C::FM * C::FN;      // MFMAs per k-step
   constexpr int NRD = READS ? C::FM + C::NB * C::FN : 0;
-  constexpr int FIRST = (LOADS > 0 && NRD < NMF) ? NRD : 0;   // first slot with loads
+  constexpr int FIRST = (!SPREAD && LOADS > 0 && NRD < NMF) ? NRD : 0;   // first slot with loads
 #pragma unroll
   for (int i = 0; i < NMF; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
@@ -170,13 +177,15 @@ __device__ __forceinline__ void weave() {
 }
 
 // One K step k on stage S[j]: frags f0 (k-step 0) are already in registers.
-//  1. issue the loads of slab k+STAGES-1 (clamped to the last slab) into the
-//     stage slab k-1 occupied
-//  2. read frags f1 (k-step 1) of S[j]
-//  3. MFMAs on f0
-//  4. wait until this wave's loads of slab k+1 are done, barrier: slab k+1
-//     is complete in its stage and every wave has read all of S[j]
-//  5. read frags f0 of slab k+1, then MFMAs on f1
+//  1. read frags f1 (k-step 1) of S[j]; MFMAs on f0, with the first half of
+//     the loads of slab k+STAGES-1 (clamped to the last slab) into the stage
+//     slab k-1 occupied (free since the previous barrier)
+//  2. wait until this wave's loads of slab k+1 are done and its LDS reads
+//     too; barrier: slab k+1 is complete in its stage and every wave has
+//     read all of S[j]
+//  3. read frags f0 of slab k+1; MFMAs on f1, with the second half of the
+//     loads. Spreading the loads over both halves keeps any one wave from
+//     queueing several loads behind the other waves' between two MFMAs.
 template <class C>
 __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict__ nxt,
                                        char* __restrict__ dst, int kload_bytes,
@@ -184,15 +193,16 @@ __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict_
                                        const uint32_t* aoff, Rsrc B0, Rsrc B1,
                                        const uint32_t* boff,
                                        f32x16 (&acc)[C::NB][C::FM][C::FN]) {
-  dma_slab<C>(dst, A, aoff, B0, B1, boff, kload_bytes);
   read_frags<C>(cur, 1, f1);
   mma<C>(f0, acc);
-  weave<C, C::NLW, true>();
-  wait_vmcnt_lds<(C::STAGES - 2) * C::NLW>();
+  dma_slab<C, 0>(dst, A, aoff, B0, B1, boff, kload_bytes);
+  weave<C, C::NLW / 2, true, true>();
+  wait_vmcnt_lds<(C::STAGES - 2) * C::NLW - C::NLW / 2>();
   __builtin_amdgcn_s_barrier();
   read_frags<C>(nxt, 0, f0);
   mma<C>(f1, acc);
-  weave<C, 0, true>();
+  dma_slab<C, 1>(dst, A, aoff, B0, B1, boff, kload_bytes);
+  weave<C, C::NLW - C::NLW / 2, true, true>();
 }
 
 // acc += A[rows] · B[cols]^T over k in [k_begin, k_begin + k_len) (k_len a
