@@ -105,9 +105,11 @@ struct Frags {
   u32x4 b[C::NB][C::FN];
 };
 
-// Fragments of MFMA k-step ks (0 or 1) of the slab in stage `st`.
-template <class C>
+// Fragments of MFMA k-step ks (0 or 1) of the slab in stage `st`, for the
+// first V of the wave's FM row blocks (the others hold only padding rows).
+template <class C, int V>
 __device__ __forceinline__ void read_frags(const char* __restrict__ st, int ks, Frags<C>& f) {
+  if constexpr (V == 0) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -116,7 +118,7 @@ __device__ __forceinline__ void read_frags(const char* __restrict__ st, int ks, 
   const char* a = st + (wm * C::TM + lr) * C::ROWB + co;
   const char* b = st + C::A_BYTES + (wn * C::TN + lr) * C::ROWB + co;
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
+  for (int fm = 0; fm < V; ++fm)
     f.a[fm] = *reinterpret_cast<const u32x4*>(a + fm * 32 * C::ROWB);
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb)
@@ -125,12 +127,12 @@ __device__ __forceinline__ void read_frags(const char* __restrict__ st, int ks, 
       f.b[nb][fn] = *reinterpret_cast<const u32x4*>(b + (nb * C::BN + fn * 32) * C::ROWB);
 }
 
-template <class C>
+template <class C, int V>
 __device__ __forceinline__ void mma(const Frags<C>& f, f32x16 (&acc)[C::NB][C::FM][C::FN]) {
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
+    for (int fm = 0; fm < V; ++fm)
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
         acc[nb][fm][fn] = mfma_32x32x16(f.a[fm], f.b[nb][fn], acc[nb][fm][fn]);
@@ -159,10 +161,11 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 // the other waves' loads at the CU's load unit and leaves its MFMA pipe idle;
 // one load every few MFMAs measured fastest. The MFMAs of a k-step use
 // distinct accumulators, so any order is valid.
-template <class C, int LOADS, bool READS, bool SPREAD = false>
+template <class C, int V, int LOADS, bool READS, bool SPREAD = false>
 __device__ __forceinline__ void weave() {
-  constexpr int NMF = C::NB * C::FM * C::FN;      // MFMAs per k-step
-  constexpr int NRD = READS ? C::FM + C::NB * C::FN : 0;
+  constexpr int NMF = C::NB * V * C::FN;          // MFMAs per k-step
+  constexpr int NRD = READS && V > 0 ? V + C::NB * C::FN : 0;
+  if constexpr (NMF == 0) return;
   constexpr int FIRST = (!SPREAD && LOADS > 0 && NRD < NMF) ? NRD : 0;   // first slot with loads
 #pragma unroll
   for (int i = 0; i < NMF; ++i) {
@@ -186,23 +189,23 @@ __device__ __forceinline__ void weave() {
 //  3. read frags f0 of slab k+1; MFMAs on f1, with the second half of the
 //     loads. Spreading the loads over both halves keeps any one wave from
 //     queueing several loads behind the other waves' between two MFMAs.
-template <class C>
+template <class C, int V>
 __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict__ nxt,
                                        char* __restrict__ dst, int kload_bytes,
                                        Frags<C>& f0, Frags<C>& f1, Rsrc A,
                                        const uint32_t* aoff, Rsrc B0, Rsrc B1,
                                        const uint32_t* boff,
                                        f32x16 (&acc)[C::NB][C::FM][C::FN]) {
-  read_frags<C>(cur, 1, f1);
-  mma<C>(f0, acc);
+  read_frags<C, V>(cur, 1, f1);
+  mma<C, V>(f0, acc);
   dma_slab<C, 0>(dst, A, aoff, B0, B1, boff, kload_bytes);
-  weave<C, C::NLW / 2, true, true>();
+  weave<C, V, C::NLW / 2, true, true>();
   wait_vmcnt_lds<(C::STAGES - 2) * C::NLW - C::NLW / 2>();
   __builtin_amdgcn_s_barrier();
-  read_frags<C>(nxt, 0, f0);
-  mma<C>(f1, acc);
+  read_frags<C, V>(nxt, 0, f0);
+  mma<C, V>(f1, acc);
   dma_slab<C, 1>(dst, A, aoff, B0, B1, boff, kload_bytes);
-  weave<C, C::NLW - C::NLW / 2, true, true>();
+  weave<C, V, C::NLW - C::NLW / 2, true, true>();
 }
 
 // acc += A[rows] · B[cols]^T over k in [k_begin, k_begin + k_len) (k_len a
@@ -210,7 +213,7 @@ __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict_
 // ring of LDS stages; the loop is unrolled by STAGES so that every stage is
 // a distinct LDS object. Loads past the last slab re-load the last slab, so
 // every step issues the same number of loads and the vmcnt accounting holds.
-template <class C>
+template <class C, int V = C::FM>
 __device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict__ S1,
                                          char* __restrict__ S2, char* __restrict__ S3,
                                          Rsrc A, const uint32_t* aoff, Rsrc B0, Rsrc B1,
@@ -227,31 +230,31 @@ __device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict
     dma_slab<C>(S2, A, aoff, B0, B1, boff, kbyte(2));
     wait_vmcnt<2 * C::NLW>();
     __builtin_amdgcn_s_barrier();
-    read_frags<C>(S0, 0, f0);
+    read_frags<C, V>(S0, 0, f0);
     int k = 0;
     for (; k + 4 <= KT; k += 4) {
-      k_step<C>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C>(S3, S0, S2, kbyte(k + 6), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S3, S0, S2, kbyte(k + 6), f0, f1, A, aoff, B0, B1, boff, acc);
     }
-    if (k < KT) k_step<C>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
-    if (k + 1 < KT) k_step<C>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
-    if (k + 2 < KT) k_step<C>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k < KT) k_step<C, V>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k + 1 < KT) k_step<C, V>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k + 2 < KT) k_step<C, V>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
   } else {
     dma_slab<C>(S0, A, aoff, B0, B1, boff, kbyte(0));
     dma_slab<C>(S1, A, aoff, B0, B1, boff, kbyte(1));
     wait_vmcnt<C::NLW>();
     __builtin_amdgcn_s_barrier();
-    read_frags<C>(S0, 0, f0);
+    read_frags<C, V>(S0, 0, f0);
     int k = 0;
     for (; k + 3 <= KT; k += 3) {
-      k_step<C>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C>(S2, S0, S1, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S2, S0, S1, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
     }
-    if (k < KT) k_step<C>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
-    if (k + 1 < KT) k_step<C>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k < KT) k_step<C, V>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k + 1 < KT) k_step<C, V>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -348,7 +351,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // Per-lane load offsets of the DMA blocks of wave w: A block w + 4j holds
 // tile rows RPI(w + 4j) .. +RPI-1; lane l loads row RPI(w+4j) + l/CH, logical
-// chunk (l % CH) ^ swz(row). Rows past the group's end re-read its last row.
+// chunk (l % CH) ^ swz(row). Rows past the group's end load zeros: their
+// MFMAs then work on zero operands, which draws less power than repeating a
+// real row (the GEMMs run at the power limit), and they are never stored.
 template <class C>
 __device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (&boff)[C::NBW],
                                             const int32_t* perm, int kdiv, int lda, int m0,
@@ -358,9 +363,13 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (
 #pragma unroll
   for (int j = 0; j < C::NAW; ++j) {
     const int row = C::RPI * (w + 4 * j) + rl;
-    const int r = min(m0 + row, m_end - 1);
-    const int src = perm ? perm[r] / kdiv : r;
-    aoff[j] = (uint32_t)(src * lda * 2 + ((ch ^ swz<C>(row)) << 4));
+    const int r = m0 + row;
+    if (r >= m_end) {
+      aoff[j] = 0x80000000u;    // past the descriptor's extent: the load returns zeros
+    } else {
+      const int src = perm ? perm[r] / kdiv : r;
+      aoff[j] = (uint32_t)(src * lda * 2 + ((ch ^ swz<C>(row)) << 4));
+    }
   }
 #pragma unroll
   for (int j = 0; j < C::NBW; ++j) {
@@ -405,6 +414,20 @@ __device__ __forceinline__ TileInfo tile_info(const GroupedProblem& p, const int
   return ti;
 }
 
+// mainloop<C, v> for the run-time v in [0, W] (a wave-uniform branch).
+template <class C, int W>
+__device__ __forceinline__ void mainloop_rows(int v, char* S0, char* S1, char* S2, char* S3,
+                                              Rsrc A, const uint32_t* aoff, Rsrc B0, Rsrc B1,
+                                              const uint32_t* boff, int k_begin, int k_len,
+                                              f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  if (v == W || W == 0) {
+    mainloop<C, W>(S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+    return;
+  }
+  if constexpr (W > 0)
+    mainloop_rows<C, W - 1>(v, S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+}
+
 // acc = A[tile rows] · B[tile columns]^T over k in [k_begin, k_begin + k_len).
 template <class C>
 __device__ __forceinline__ void tile_mainloop(const GroupedProblem& p, const TileInfo& ti, Rsrc rA,
@@ -417,7 +440,11 @@ __device__ __forceinline__ void tile_mainloop(const GroupedProblem& p, const Til
   const Rsrc rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)ti.g * p.b_gstride, bbytes);
   const Rsrc rB1 = C::DUAL ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)ti.g * p.b_gstride, bbytes) : rB0;
   zero_acc<C>(acc);
-  mainloop<C>(S0, S1, S2, S3, rA, aoff, rB0, rB1, boff, k_begin, k_len, acc);
+  // row blocks of this wave that hold rows of the group: the MFMAs of the
+  // others would only multiply padding (zeros), so they are not issued
+  const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / C::WN;
+  const int v = min(max((ti.m_end - ti.m0 - wm * C::TM + 31) / 32, 0), C::FM);
+  mainloop_rows<C, C::FM>(v, S0, S1, S2, S3, rA, aoff, rB0, rB1, boff, k_begin, k_len, acc);
 }
 
 // A tile's fp32 partial sums in the split-K workspace, element-major
