@@ -15,6 +15,9 @@ notation, with numpy as the only primitive (matrix products, exp, a sort):
      or sigmoid s_t = 1/(1+exp(-z_t)) (DeepSeek-V3 style)
      [cooking-agi, first section, the remark after the gate formula]
   3. top-k selection S_t = TopK(score_t, k)                      [§二 第三步]
+     optionally over group-limited candidates: the best groups of experts
+     by the sum of their top-m scores first, the rest masked to -inf
+     [cooking-agi, section on choosing groups first across devices]
   4. gates, three modes
      A  g_i = p_i / sum_{j in S} p_j  (= softmax over the selected logits)
         [wuhy-notes §二 第三步 gate formula; cooking-agi first section]
@@ -113,6 +116,35 @@ def topk(sel, k):
     return ids, gap
 
 
+# ------------------------------------------------- 3b. group-limited top-k
+def group_limit(sel, n_groups, topk_groups, topm):
+    """Group-limited candidates [cooking-agi, section on choosing groups
+    first across devices]: the N experts form n_groups contiguous groups of
+    N / n_groups; a group's score is the sum of its topm largest selection
+    scores (topm = 1: the group's maximum); the topk_groups best groups (ties
+    to the lower group index) keep their experts as candidates and every
+    other expert gets -inf, not 0, so that a negative score cannot lose to a
+    masked expert. Returns the masked scores and the gap between the
+    topk_groups-th and the next group score (+inf when every group is kept)."""
+    sel = _f64(sel)
+    T, N = sel.shape
+    if n_groups < 1 or N % n_groups:
+        raise ValueError(f"{N} experts do not split into {n_groups} equal groups")
+    gs = N // n_groups
+    if not 1 <= topk_groups <= n_groups:
+        raise ValueError(f"need 1 <= topk_groups <= n_groups, got {topk_groups}")
+    if not 1 <= topm <= gs:
+        raise ValueError(f"need 1 <= topm <= group size {gs}, got {topm}")
+    per_group = sel.reshape(T, n_groups, gs)
+    best_m = -np.sort(-per_group, axis=-1)[:, :, :topm]
+    gscore = best_m.sum(axis=-1)                                   # [T, G]
+    gids, ggap = topk(gscore, topk_groups)
+    keep = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(keep, gids, True, axis=-1)
+    masked = np.where(np.repeat(keep, gs, axis=1), sel, -np.inf)
+    return masked, ggap
+
+
 @dataclasses.dataclass
 class Routing:
     ids: np.ndarray        # [T, k] int64, slot order = descending selection score
@@ -124,13 +156,29 @@ class Routing:
 
 
 # ------------------------------------------------------------------- 4. gates
-def route(h, w_router, k, mode, b_router=None, b_select=None) -> Routing:
-    """Router logits, scores, top-k selection and gate values (steps 1-4)."""
+def _select(sel, k, groups):
+    """Top-k of sel, over the group-limited candidates when ``groups`` is
+    (n_groups, topk_groups, topm); the near-tie gap is then the smaller of
+    the expert and the group gaps."""
+    if not groups:
+        return topk(sel, k)
+    n_groups, topk_groups, topm = groups
+    if topk_groups * (sel.shape[1] // n_groups) < k:
+        raise ValueError("fewer candidate experts than k in the kept groups")
+    masked, ggap = group_limit(sel, n_groups, topk_groups, topm)
+    ids, gap = topk(masked, k)
+    return ids, np.minimum(gap, ggap)
+
+
+def route(h, w_router, k, mode, b_router=None, b_select=None, groups=None) -> Routing:
+    """Router logits, scores, top-k selection and gate values (steps 1-4).
+    ``groups`` = (n_groups, topk_groups, topm) limits the candidates to the
+    best groups first (group_limit); None selects over all experts."""
     z = router_logits(h, w_router, b_router)
     if mode in (MODE_SOFTMAX_RENORM, MODE_SOFTMAX_FULL):
         p = softmax(z)
         sel = p                       # TopK(p_t, k)
-        ids, gap = topk(sel, k)
+        ids, gap = _select(sel, k, groups)
         p_sel = np.take_along_axis(p, ids, axis=-1)
         if mode == MODE_SOFTMAX_RENORM:
             gates = p_sel / p_sel.sum(axis=-1, keepdims=True)
@@ -142,7 +190,7 @@ def route(h, w_router, k, mode, b_router=None, b_select=None) -> Routing:
             raise ValueError("mode C needs the selection bias")
         s = sigmoid(z)
         sel = s + _f64(b_select)[None, :]
-        ids, gap = topk(sel, k)
+        ids, gap = _select(sel, k, groups)
         s_sel = np.take_along_axis(s, ids, axis=-1)   # unbiased scores
         gates = s_sel / s_sel.sum(axis=-1, keepdims=True)
         stat_prob = s / s.sum(axis=-1, keepdims=True)
@@ -259,10 +307,10 @@ class LayerResult:
 
 
 def layer(h, w_router, k, mode, weights_of: WeightsOf, b_router=None,
-          b_select=None, shared=None, alpha=0.01) -> LayerResult:
+          b_select=None, shared=None, alpha=0.01, groups=None) -> LayerResult:
     """The whole forward pass, steps 1-8, on all tokens."""
     N = np.asarray(w_router).shape[0]
-    r = route(h, w_router, k, mode, b_router, b_select)
+    r = route(h, w_router, k, mode, b_router, b_select, groups)
     disp = dispatch(r.ids, N)
     out_rows = expert_rows(h, disp, k, weights_of, shared)
     y = combine(out_rows, disp.row_of, r.gates, shared is not None)
@@ -294,14 +342,14 @@ def layer_tokens(h, routing: Routing, tokens, weights_of: WeightsOf,
 
 
 def dense_layer(h, w_router, k, mode, weights_of: WeightsOf, b_router=None,
-                b_select=None, shared=None):
+                b_select=None, shared=None, groups=None):
     """Brute force: run every expert on every token, build the dense gate
     matrix G (g on the selected experts, 0 elsewhere) and sum G[t,i] E_i(h_t),
     plus the shared expert."""
     h = _f64(h)
     T = h.shape[0]
     N = np.asarray(w_router).shape[0]
-    r = route(h, w_router, k, mode, b_router, b_select)
+    r = route(h, w_router, k, mode, b_router, b_select, groups)
     G = np.zeros((T, N))
     np.put_along_axis(G, r.ids, r.gates, axis=-1)
     y = np.zeros_like(h)

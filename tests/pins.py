@@ -316,4 +316,80 @@ def pin_permutation_symmetry():
         assert (ep[pe.routing.ids] == base.routing.ids).all()
 
 
+# ------------------------------------------------- group-limited selection
+def pin_group_limited_worked_example():
+    """Groups A = [0.90, 0.10], B = [0.80, 0.79], k = 2: unrestricted ->
+    {0, 2}; keep the group with the larger maximum -> {0, 1}; keep the group
+    with the larger top-2 sum -> {2, 3}. Run as mode C selection scores
+    (sigmoid(z) = score, no bias) and as mode A (softmax probabilities
+    proportional to the scores). [cooking-agi, group-limited routing]"""
+    g = golden("group_limited_example.json")
+    sc = np.array(g["scores"])
+    G, k = g["n_groups"], g["k"]
+    for mode, z, b in ((O.MODE_SIGMOID_BIAS_RENORM, np.log(sc / (1 - sc)), np.zeros(4)),
+                       (O.MODE_SOFTMAX_RENORM, np.log(sc), None)):
+        z = z[None, :]
+        for groups, want in ((None, g["unrestricted"]), ((G, 1, 1), g["keep_1_group_by_max"]),
+                             ((G, 1, 2), g["keep_1_group_by_top2_sum"])):
+            r = O.route(z, np.eye(4), k, mode, b_select=b, groups=groups)
+            assert r.ids[0].tolist() == want, (mode, groups, r.ids)
+            if mode == O.MODE_SIGMOID_BIAS_RENORM:
+                assert np.allclose(r.gates[0], sc[want] / sc[want].sum(), rtol=0, atol=1e-15)
+        _, ggap = O.group_limit(sc[None, :], G, 1, 2)
+        assert abs(ggap[0] - (g["group_scores_by_top2_sum"][1] - g["group_scores_by_top2_sum"][0])) < 1e-12
+
+
+def pin_group_limit_brute_force():
+    """On tiny random inputs (distinct scores), the kept groups are a set K
+    of topk_groups groups with no outside group scoring higher (ties to the
+    lower index), a group's score being the largest sum over topm of its
+    experts (enumerated); the picks are the best k-subset of K's experts."""
+    rng = np.random.default_rng(11)
+    for N, G in ((6, 2), (6, 3), (8, 4), (12, 3), (12, 6)):
+        gs = N // G
+        for gk in range(1, G + 1):
+            for m in range(1, gs + 1):
+                for k in range(1, min(gk * gs, 4) + 1):
+                    sel = rng.permutation(N)[None, :].astype(float) / N + rng.random(N)[None, :] * 1e-3
+                    score = [max(sum(c) for c in itertools.combinations(sel[0, g * gs:(g + 1) * gs], m))
+                             for g in range(G)]
+                    best = None
+                    for K in itertools.combinations(range(G), gk):
+                        out = [g for g in range(G) if g not in K]
+                        if all(score[a] > score[b] or (score[a] == score[b] and a < b)
+                               for a in K for b in out):
+                            best = K
+                    cand = [e for e in range(N) if e // gs in best]
+                    pick = max(itertools.combinations(cand, k), key=lambda c: sum(sel[0, list(c)]))
+                    masked, _ = O.group_limit(sel, G, gk, m)
+                    ids, _ = O.topk(masked, k)
+                    assert sorted(ids[0].tolist()) == sorted(pick), (N, G, gk, m, k)
+                    assert all(sel[0, ids[0][i]] > sel[0, ids[0][i + 1]] for i in range(k - 1))
+
+
+def pin_group_limit_trivial_cases():
+    """One group, or keeping every group, selects exactly as without a
+    group limit."""
+    rng = np.random.default_rng(12)
+    h, wr, *_ = _rand_inputs(rng, 30, 8, 8, 4)
+    for mode in (O.MODE_SOFTMAX_RENORM, O.MODE_SOFTMAX_FULL, O.MODE_SIGMOID_BIAS_RENORM):
+        b = rng.uniform(-0.1, 0.1, 8) if mode == O.MODE_SIGMOID_BIAS_RENORM else None
+        ref = O.route(h, wr, 3, mode, b_select=b)
+        for groups in ((1, 1, 1), (4, 4, 2), (2, 2, 1)):
+            r = O.route(h, wr, 3, mode, b_select=b, groups=groups)
+            assert np.array_equal(r.ids, ref.ids) and np.allclose(r.gates, ref.gates, rtol=0, atol=0)
+
+
+def pin_group_mask_is_minus_infinity():
+    """Mode C selection scores can be negative: with sel = [0.9, -0.05, 0.5,
+    0.4] in groups {0, 1} and {2, 3}, keeping one group by its maximum keeps
+    the first and must pick experts 0 and 1 (a zero mask would pick 2)."""
+    s = np.array([0.8, 0.05, 0.45, 0.35])
+    b = np.array([0.1, -0.1, 0.05, 0.05])
+    r = O.route(np.log(s / (1 - s))[None, :], np.eye(4), 2, O.MODE_SIGMOID_BIAS_RENORM,
+                b_select=b, groups=(2, 1, 1))
+    assert r.ids[0].tolist() == [0, 1]
+    assert np.allclose(r.gates[0], s[[0, 1]] / s[[0, 1]].sum(), rtol=0, atol=1e-15)
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

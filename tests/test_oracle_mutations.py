@@ -6,7 +6,7 @@ import pytest
 import pins
 from oracle import moe_oracle as O
 
-_orig = {n: getattr(O, n) for n in ("router_logits", "softmax", "sigmoid", "topk",
+_orig = {n: getattr(O, n) for n in ("router_logits", "softmax", "sigmoid", "topk", "group_limit",
                                      "dispatch", "silu", "expert_ffn", "combine",
                                      "load_stats", "route")}
 
@@ -71,6 +71,20 @@ def _combine_slot0_gate(out_rows, row_of, gates, has_shared=False):
     return _orig["combine"](out_rows, row_of, g, has_shared)
 
 
+def _group_mask_zero(sel, n_groups, topk_groups, topm):
+    masked, gap = _orig["group_limit"](sel, n_groups, topk_groups, topm)
+    return np.where(np.isinf(masked), 0.0, masked), gap
+
+
+def _group_score_max(sel, n_groups, topk_groups, topm):
+    return _orig["group_limit"](sel, n_groups, topk_groups, 1)
+
+
+def _group_keep_worst(sel, n_groups, topk_groups, topm):
+    return _orig["group_limit"](-np.asarray(sel, float), n_groups, topk_groups, topm)[0] * -1.0, \
+        np.full(np.asarray(sel).shape[0], np.inf)
+
+
 MUTATIONS = {
     "logits_drop_bias": ("router_logits", lambda h, w, b=None: _orig["router_logits"](h, w, None)),
     "logits_expert_index_reversed": ("router_logits", _logits_reversed),
@@ -88,6 +102,9 @@ MUTATIONS = {
     "combine_overwrite": ("combine", _combine_overwrite),
     "combine_drops_shared": ("combine", _combine_no_shared),
     "combine_slot0_gate": ("combine", _combine_slot0_gate),
+    "group_mask_zero": ("group_limit", _group_mask_zero),
+    "group_score_max_only": ("group_limit", _group_score_max),
+    "group_keep_worst": ("group_limit", _group_keep_worst),
     "stats_f_over_T": ("load_stats", lambda c, sp, k, a: _orig["load_stats"](c, sp, 1, a)),
     "stats_no_N_factor": ("load_stats", lambda c, sp, k, a: (lambda f, p, l: (f, p, l / np.asarray(sp).shape[1]))(*_orig["load_stats"](c, sp, k, a))),
 }
