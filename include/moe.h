@@ -46,11 +46,14 @@
  *  - Errors: every error the host can detect is returned BEFORE anything is
  *    launched, and no HIP call is made before argument validation succeeds:
  *      MOE_ERR_INVALID_ARG  bad shape (T<0, d/N/k/d_ff<1, d_ff_shared<0),
- *                           k > N (not enough candidates), unknown dtype or
+ *                           k > N or k above the kept groups' experts (not
+ *                           enough candidates), a group limit that does not
+ *                           fit N (see moe_shape), unknown dtype or
  *                           mode, a required pointer NULL, b_select given in
  *                           modes A/B or missing in mode C, misaligned
  *                           pointer, non-finite aux_alpha;
- *      MOE_ERR_UNSUPPORTED  N > 512, k > 16, bf16 with d, d_ff or d_ff_shared
+ *      MOE_ERR_UNSUPPORTED  N > 512, k > 16, more than 64 groups or a group
+ *                           score over more than 8 experts, bf16 with d, d_ff or d_ff_shared
  *                           not a multiple of 64, or sizes whose element
  *                           counts exceed 2^31-1 per tensor;
  *      MOE_ERR_WORKSPACE    ws_bytes below the size this call needs (or ws
@@ -69,9 +72,11 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
+#define MOE_MAX_GROUPS 64
+#define MOE_MAX_GROUP_TOPM 8
 
 typedef enum {
   MOE_OK = 0,
@@ -110,6 +115,17 @@ typedef struct {
   int32_t dtype;        /* moe_dtype of activations and weights               */
   int32_t mode;         /* moe_gate_mode                                       */
   float aux_alpha;      /* α of L_aux = α·N·Σ f_i p_i                          */
+  /* Group-limited selection [cooking-agi, section on choosing groups first
+   * across devices]: the N experts form n_groups contiguous groups of
+   * N / n_groups; a group's score is the sum of its group_topm largest
+   * selection scores (softmax probability in modes A/B, sigmoid + b_select
+   * in mode C; group_topm = 1 is the group maximum); only the topk_groups
+   * best groups (ties to the lower group index) keep their experts as
+   * candidates for the top-k. Gates and statistics are unchanged (mode B
+   * still uses the full softmax). All three 0 = no group limit. */
+  int32_t n_groups;     /* 0, or 1..64 dividing N                              */
+  int32_t topk_groups;  /* 1..n_groups, with topk_groups·N/n_groups >= k      */
+  int32_t group_topm;   /* 1..min(8, N/n_groups)                               */
 } moe_shape;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION). */

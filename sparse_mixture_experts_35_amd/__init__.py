@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_hip.so")
 F32, BF16 = 0, 1
 SOFTMAX_RENORM, SOFTMAX_FULL, SIGMOID_BIAS_RENORM = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-MAX_EXPERTS, MAX_TOPK = 512, 16
+MAX_EXPERTS, MAX_TOPK, MAX_GROUPS, MAX_GROUP_TOPM = 512, 16, 64, 8
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_fused",
@@ -32,14 +32,20 @@ class MoEError(RuntimeError):
 
 
 class Shape(ctypes.Structure):
+    """moe_shape: sizes, dtype, gate mode, L_aux alpha and the optional group
+    limit (n_groups contiguous expert groups, the topk_groups best by the sum
+    of their group_topm largest selection scores stay candidates)."""
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("mode", ctypes.c_int32), ("aux_alpha", ctypes.c_float)]
+                ("mode", ctypes.c_int32), ("aux_alpha", ctypes.c_float),
+                ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
+                ("group_topm", ctypes.c_int32)]
 
     def __init__(self, T, d, N, k, d_ff, d_ff_shared=0, dtype=BF16, mode=SOFTMAX_RENORM,
-                 aux_alpha=0.01):
-        super().__init__(T, d, N, k, d_ff, d_ff_shared, dtype, mode, aux_alpha)
+                 aux_alpha=0.01, n_groups=0, topk_groups=0, group_topm=0):
+        super().__init__(T, d, N, k, d_ff, d_ff_shared, dtype, mode, aux_alpha, n_groups,
+                         topk_groups, group_topm)
 
 
 _lib = None

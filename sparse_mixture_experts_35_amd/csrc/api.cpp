@@ -47,6 +47,22 @@ moe_status check_shape(const moe_shape* s) {
   if (s->k > s->N) return fail(MOE_ERR_INVALID_ARG, "k > N: not enough candidate experts");
   if (s->N > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "N > 512");
   if (s->k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k > 16");
+  if (s->n_groups == 0) {
+    if (s->topk_groups != 0 || s->group_topm != 0)
+      return fail(MOE_ERR_INVALID_ARG, "topk_groups and group_topm need n_groups > 0");
+  } else {
+    if (s->n_groups < 0 || s->N % s->n_groups)
+      return fail(MOE_ERR_INVALID_ARG, "n_groups must divide N");
+    if (s->n_groups > MOE_MAX_GROUPS) return fail(MOE_ERR_UNSUPPORTED, "n_groups > 64");
+    const int gs = s->N / s->n_groups;
+    if (s->topk_groups < 1 || s->topk_groups > s->n_groups)
+      return fail(MOE_ERR_INVALID_ARG, "need 1 <= topk_groups <= n_groups");
+    if (s->group_topm < 1 || s->group_topm > gs)
+      return fail(MOE_ERR_INVALID_ARG, "need 1 <= group_topm <= N / n_groups");
+    if (s->group_topm > MOE_MAX_GROUP_TOPM) return fail(MOE_ERR_UNSUPPORTED, "group_topm > 8");
+    if ((int64_t)s->topk_groups * gs < s->k)
+      return fail(MOE_ERR_INVALID_ARG, "the kept groups hold fewer than k experts");
+  }
   if (s->dtype == MOE_BF16 &&
       (s->d % 64 || s->d_ff % 64 || s->d_ff_shared % 64))
     return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d, d_ff and d_ff_shared multiples of 64");
@@ -219,9 +235,12 @@ moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
                                                 s->T, s->d, s->N, st),
                   "router logits"));
   }
+  // a group limit that keeps every group changes nothing
+  const bool grouped = s->n_groups > 1 && s->topk_groups < s->n_groups;
+  const moe::GroupLimit gl{grouped ? s->n_groups : 0, s->topk_groups, s->group_topm};
   TRY(hip_check(moe::launch_route_select(z_part, splits, b_router, b_select, ids, gates,
                                          p_mean ? p_part : nullptr, s->T, s->N, s->k, s->mode,
-                                         st),
+                                         gl, st),
                 "route select"));
   if (p_mean)
     TRY(hip_check(moe::launch_p_reduce(p_part, p_mean, moe::route_select_blocks(s->T, s->N), s->T,

@@ -17,13 +17,19 @@ hipError_t launch_router_gemm_bf16(const void* h, const void* w_router,
 hipError_t launch_router_logits_f32(const float* h, const float* w_router,
                                     float* z, int T, int d, int N,
                                     hipStream_t st);
+// Group-limited candidates: n_groups contiguous groups (0 = no limit), the
+// keep best by the sum of their topm largest selection scores.
+struct GroupLimit {
+  int n_groups, keep, topm;
+};
 // z = sum of the partial slices + b_router; scores, top-k, gates, and
 // per-block sums of the routing probabilities
 int route_select_blocks(int T, int N);
 hipError_t launch_route_select(const float* z_part, int splits,
                                const float* b_router, const float* b_select,
                                int32_t* ids, float* gates, float* p_part,
-                               int T, int N, int k, int mode, hipStream_t st);
+                               int T, int N, int k, int mode, GroupLimit gl,
+                               hipStream_t st);
 hipError_t launch_p_reduce(const float* p_part, float* p_mean, int blocks,
                            int T, int N, hipStream_t st);
 

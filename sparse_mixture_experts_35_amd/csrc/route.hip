@@ -12,9 +12,16 @@
 // A group of lanes per token (8 lanes when N <= 8, up to a whole wavefront
 // for N > 32; each lane holds up to eight experts in registers, N <= 512).
 // Top-k is k rounds of a group-wide argmax (butterfly over __shfl_xor) on
-// (score, index) with the lower index winning ties. In the softmax modes the selection runs on z, which orders
-// the experts exactly as the softmax does. Per-block sums of the routing
-// probabilities go to p_part in a fixed order, never through float atomics.
+// (score, index) with the lower index winning ties. In the softmax modes the
+// selection runs on z, which orders the experts exactly as the softmax does.
+// Per-block sums of the routing probabilities go to p_part in a fixed order,
+// never through float atomics.
+//
+// With a group limit [cooking-agi, section on choosing groups first across
+// devices] the token's group scores (sum of each expert group's top-m
+// selection scores) are formed from a copy of its scores in LDS, the best
+// groups are kept by a few more rounds of argmax, and the other groups'
+// experts leave the candidate set before the top-k.
 #include <math.h>
 
 #include "common.hpp"
@@ -50,10 +57,13 @@ template <int LPT, int VPL, int MODE, int ITER>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
     const float* __restrict__ b_select, int32_t* __restrict__ ids,
-    float* __restrict__ gates, float* __restrict__ p_part, int T, int N, int k) {
+    float* __restrict__ gates, float* __restrict__ p_part, int T, int N, int k,
+    GroupLimit gl) {
   constexpr int TPW = 64 / LPT;               // tokens per wave per iteration
   constexpr int TPB = 4 * TPW * ITER;         // tokens per block
+  constexpr int GPL = 64 / LPT;               // groups per lane at most (64 groups)
   __shared__ float s_p[4][64][VPL];
+  __shared__ float s_g[4][64 * VPL];          // group scoring values of the wave's tokens
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane / LPT, li = lane % LPT;
   const int64_t TN = (int64_t)T * N;
@@ -88,6 +98,84 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
         aux[i] = v;
         sel[i] = v;
       }
+    }
+    // ---- group limit: keep the gl.keep best expert groups as candidates
+    if (gl.n_groups > 0) {
+      // scoring values: the selection score (mode C), or exp(z - zmax),
+      // which is the softmax probability up to the token's common factor
+      float zm = 0.0f;
+      if (MODE != 2) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+          if (li + LPT * i < N) m = fmaxf(m, zv[i]);
+#pragma unroll
+        for (int o = LPT / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        zm = m;
+      }
+      float* gv = &s_g[w][grp * N];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = li + LPT * i;
+        if (e < N) gv[e] = MODE == 2 ? sel[i] : expf(zv[i] - zm);
+      }
+      __syncthreads();
+      const int gsz = N / gl.n_groups;
+      float gsc[GPL];
+#pragma unroll
+      for (int q = 0; q < GPL; ++q) {
+        const int g = li + LPT * q;
+        gsc[q] = -INFINITY;
+        if (g < gl.n_groups) {
+          float top[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) top[j] = -INFINITY;
+          for (int x = 0; x < gsz; ++x) {          // insert into the sorted top-m
+            float v = gv[g * gsz + x];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (j < gl.topm && v > top[j]) {
+                const float t0 = top[j];
+                top[j] = v;
+                v = t0;
+              }
+          }
+          float sum = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (j < gl.topm) sum += top[j];
+          gsc[q] = sum;
+        }
+      }
+      uint64_t kept = 0;
+      for (int r = 0; r < gl.keep; ++r) {
+        float bv = -INFINITY;
+        int bg = 0x7fffffff;
+#pragma unroll
+        for (int q = 0; q < GPL; ++q) {
+          const int g = li + LPT * q;
+          if (g < gl.n_groups && !((kept >> g) & 1) && better(gsc[q], g, bv, bg)) {
+            bv = gsc[q];
+            bg = g;
+          }
+        }
+#pragma unroll
+        for (int o = LPT / 2; o >= 1; o >>= 1) {
+          const float ov = __shfl_xor(bv, o, 64);
+          const int og = __shfl_xor(bg, o, 64);
+          if (better(ov, og, bv, bg)) {
+            bv = ov;
+            bg = og;
+          }
+        }
+        kept |= 1ull << bg;
+      }
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = li + LPT * i;
+        if (e < N && !((kept >> (e / gsz)) & 1)) cand[i] = false;
+      }
+      __syncthreads();                       // before the next tokens reuse s_g
     }
     // ---- top-k: k rounds of a group-wide argmax, lower index wins ties
     int win_id[kMaxK];
@@ -261,19 +349,20 @@ SelectCfg select_cfg(int N) {
 template <int LPT, int VPL, int ITER>
 hipError_t launch_select_t(const float* z_part, int splits, const float* b_router,
                            const float* b_select, int32_t* ids, float* gates, float* p_part,
-                           int T, int N, int k, int mode, int blocks, hipStream_t st) {
+                           int T, int N, int k, int mode, GroupLimit gl, int blocks,
+                           hipStream_t st) {
   switch (mode) {
     case 0:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 0, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k, gl);
       break;
     case 1:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 1, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k, gl);
       break;
     default:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 2, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k, gl);
       break;
   }
   return hipGetLastError();
@@ -297,14 +386,15 @@ int route_select_blocks(int T, int N) {
 
 hipError_t launch_route_select(const float* z_part, int splits, const float* b_router,
                                const float* b_select, int32_t* ids, float* gates,
-                               float* p_part, int T, int N, int k, int mode, hipStream_t st) {
+                               float* p_part, int T, int N, int k, int mode, GroupLimit gl,
+                               hipStream_t st) {
   const SelectCfg c = select_cfg(N);
   const int blocks = (T + c.tpb - 1) / c.tpb;
   if (blocks == 0) return hipSuccess;
 #define MOE_SEL(L, V, I)                                                                    \
   if (c.lpt == L && c.vpl == V)                                                             \
     return launch_select_t<L, V, I>(z_part, splits, b_router, b_select, ids, gates, p_part, \
-                                    T, N, k, mode, blocks, st);
+                                    T, N, k, mode, gl, blocks, st);
   MOE_SEL(8, 1, 1)
   MOE_SEL(16, 1, 1)
   MOE_SEL(32, 1, 2)

@@ -56,20 +56,23 @@ def oracle_shared(inp):
     return (inp["sh_gate"], inp["sh_up"], inp["sh_down"])
 
 
-def check_ids(gpu_ids, oracle_routing, k):
+def check_ids(gpu_ids, oracle_routing, k, grouped=False):
     """Selected experts must match exactly for every token whose k-th and
-    (k+1)-th selection scores are at least NEAR_TIE apart. For near-tie
-    tokens the GPU's selection must still be a valid top-k within that
-    margin. Returns the near-tie mask."""
+    (k+1)-th selection scores (and, with a group limit, its last kept and
+    first dropped group scores) are at least NEAR_TIE apart. For near-tie
+    tokens the GPU's selection must still be k distinct experts, and without
+    a group limit a valid top-k within that margin. Returns the near-tie
+    mask."""
     near = O.near_tie_tokens(oracle_routing.gap, NEAR_TIE)
     ok = ~near
     assert np.array_equal(gpu_ids[ok], oracle_routing.ids[ok]), \
         np.nonzero((gpu_ids != oracle_routing.ids).any(axis=1) & ok)[0][:10]
     for t in np.nonzero(near)[0]:
-        sel = oracle_routing.sel[t]
-        kth = np.sort(sel)[::-1][k - 1]
         assert len(set(gpu_ids[t].tolist())) == k
-        assert np.all(sel[gpu_ids[t]] >= kth - NEAR_TIE)
+        if not grouped:
+            sel = oracle_routing.sel[t]
+            kth = np.sort(sel)[::-1][k - 1]
+            assert np.all(sel[gpu_ids[t]] >= kth - NEAR_TIE)
     return near
 
 

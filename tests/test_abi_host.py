@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(M.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -83,6 +83,14 @@ def fused(s, **over):
     (dict(mode=3), M.ERR_INVALID_ARG, "mode"),
     (dict(aux_alpha=float("nan")), M.ERR_INVALID_ARG, "aux_alpha"),
     (dict(T=1 << 28, d=4096), M.ERR_UNSUPPORTED, "2^31"),
+    (dict(topk_groups=1), M.ERR_INVALID_ARG, "need n_groups > 0"),
+    (dict(n_groups=3, topk_groups=1, group_topm=1), M.ERR_INVALID_ARG, "divide N"),
+    (dict(n_groups=4, topk_groups=0, group_topm=1), M.ERR_INVALID_ARG, "topk_groups"),
+    (dict(n_groups=4, topk_groups=5, group_topm=1), M.ERR_INVALID_ARG, "topk_groups"),
+    (dict(n_groups=4, topk_groups=2, group_topm=3), M.ERR_INVALID_ARG, "group_topm"),
+    (dict(n_groups=8, topk_groups=1, group_topm=1), M.ERR_INVALID_ARG, "fewer than k"),
+    (dict(N=256, n_groups=128, topk_groups=8, group_topm=1), M.ERR_UNSUPPORTED, "n_groups > 64"),
+    (dict(N=256, n_groups=8, topk_groups=4, group_topm=9), M.ERR_UNSUPPORTED, "group_topm > 8"),
 ])
 def test_bad_shapes(kw, want, msg):
     st, err = fused(shape(**kw))

@@ -38,8 +38,14 @@ def f32(n):
     return t.empty(n, dtype=t.float32, device="cuda")
 
 
-def shape_of(T, d, N, k, d_ff, d_ff_shared=0, dtype=W.DTYPE_BF16, mode=0, alpha=0.01):
-    return M.Shape(T, d, N, k, d_ff, d_ff_shared, dtype, mode, alpha)
+def shape_of(T, d, N, k, d_ff, d_ff_shared=0, dtype=W.DTYPE_BF16, mode=0, alpha=0.01,
+             groups=None):
+    g = groups or (0, 0, 0)
+    return M.Shape(T, d, N, k, d_ff, d_ff_shared, dtype, mode, alpha, *g)
+
+
+def groups_of(s):
+    return (s.n_groups, s.topk_groups, s.group_topm) if s.n_groups else None
 
 
 def workspace(s):
@@ -87,8 +93,9 @@ def run_steps(s, inp):
 
 def check_all(s, inp, res, alpha=0.01):
     tol = TOL[s.dtype]
-    r = O.route(inp["h"], inp["w_router"], s.k, s.mode, inp["b_router"], inp["b_select"])
-    near = check_ids(res["ids"], r, s.k)
+    r = O.route(inp["h"], inp["w_router"], s.k, s.mode, inp["b_router"], inp["b_select"],
+                groups_of(s))
+    near = check_ids(res["ids"], r, s.k, grouped=groups_of(s) is not None)
     ok = ~near
     check_gates(res["gates"], r.gates, 1e-4, ok)
     # dispatch: bit-exact against the oracle's dispatch of the GPU's own ids
@@ -110,7 +117,7 @@ def check_all(s, inp, res, alpha=0.01):
     check_close_rows(res["y"], y_comb, tol, what="combine")
     # end to end against the oracle's own routing (non-near-tie tokens)
     ref = O.layer(inp["h"], inp["w_router"], s.k, s.mode, oracle_weights(inp), inp["b_router"],
-                  inp["b_select"], oracle_shared(inp), alpha)
+                  inp["b_select"], oracle_shared(inp), alpha, groups_of(s))
     worst = check_close_rows(res["y"], ref.y, tol, ok, what="y")
     # the fused call is the same kernels: identical bits
     fz = res["fused"]
@@ -153,6 +160,52 @@ def test_layer_parity(case):
     res = run_steps(s, inp)
     worst, near = check_all(s, inp, res)
     print(f"{name}: worst row rel err {worst:.2e}, near-ties {near}")
+
+
+GROUPED_CASES = [
+    # name, T, d, N, k, d_ff, d_ff_shared, dtype, mode, (n_groups, topk_groups, group_topm)
+    ("bf16_grouped_C_8x4_top2sum", 300, 128, 64, 8, 128, 128, W.DTYPE_BF16, 2, (8, 4, 2)),
+    ("bf16_grouped_A_groupmax", 257, 192, 16, 2, 128, 0, W.DTYPE_BF16, 0, (4, 1, 1)),
+    ("bf16_grouped_B_top2sum", 200, 128, 32, 4, 128, 0, W.DTYPE_BF16, 1, (8, 2, 2)),
+    ("f32_grouped_C_shared", 64, 32, 12, 3, 40, 24, W.DTYPE_F32, 2, (3, 2, 2)),
+    ("bf16_grouped_N256_64groups", 150, 64, 256, 8, 64, 0, W.DTYPE_BF16, 0, (64, 8, 4)),
+    ("bf16_grouped_N512_16groups", 100, 64, 512, 16, 64, 0, W.DTYPE_BF16, 2, (16, 3, 8)),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_CASES, ids=[c[0] for c in GROUPED_CASES])
+def test_layer_parity_grouped(case):
+    """Group-limited selection through every call and the fused layer."""
+    name, T, d, N, k, dff, dfs, dt, mode, groups = case
+    inp = W.random_small(T, d, N, k, dff, dfs, dt, mode, seed=len(name), router_bias=(T % 2 == 0))
+    s = shape_of(T, d, N, k, dff, dfs, dt, mode, groups=groups)
+    print(f"case {name}", flush=True)
+    res = run_steps(s, inp)
+    worst, near = check_all(s, inp, res)
+    print(f"{name}: worst row rel err {worst:.2e}, near-ties {near}")
+
+
+def test_route_group_limited_worked_example_on_gpu():
+    """Groups A = [0.90, 0.10], B = [0.80, 0.79], k = 2 (fp32, W_r = I):
+    no limit -> {0, 2}; keep the group with the larger maximum -> {0, 1};
+    keep the group with the larger top-2 sum -> {2, 3}; as sigmoid scores
+    (mode C, zero bias) and as softmax probabilities (mode A)."""
+    import pins
+    g = pins.golden("group_limited_example.json")
+    sc = np.array(g["scores"])
+    G = g["n_groups"]
+    for mode, z, b in ((2, np.log(sc / (1 - sc)), np.zeros(4)), (0, np.log(sc), None)):
+        for groups, want in ((None, g["unrestricted"]), ((G, 1, 1), g["keep_1_group_by_max"]),
+                             ((G, 1, 2), g["keep_1_group_by_top2_sum"])):
+            s = shape_of(1, 4, 4, 2, 64, 0, W.DTYPE_F32, mode, groups=groups)
+            ws, nws = workspace(s)
+            ids, gates = i32(2), f32(2)
+            M.route(s, dev_f32(z[None, :]), dev_f32(np.eye(4)), None, dev_f32(b), ids, gates, None,
+                    ws, nws)
+            torch().cuda.synchronize()
+            assert host(ids).tolist() == want, (mode, groups)
+            if mode == 2:
+                assert np.allclose(host(gates), sc[want] / sc[want].sum(), rtol=1e-6, atol=0)
 
 
 def test_tiny_workloads_exact_recipe():
