@@ -38,7 +38,9 @@ notation, with numpy as the only primitive (matrix products, exp, a sort):
      an overwrite [cooking-agi "选好以后，token 怎么过去，输出怎么回来？";
      horizon.auto §3 ④ Gather]
   8. load statistics f_i, p_i and L_aux = alpha * N * sum_i f_i p_i
-     [feinterview, load-balance section; wuhy-notes §五 (garbled print)]
+     [feinterview, load-balance section; wuhy-notes §五 (garbled print)];
+     router z-loss (mean squared log-sum-exp of the logits) and the mean
+     routing entropy [wuhy-notes §五 and its monitoring list]
   9. dense brute force: every expert on every token, unselected gates zero
      [cooking-agi "怎么知道实现没把梯度弄丢？"]
 
@@ -292,6 +294,32 @@ def load_stats(counts, stat_prob, k, alpha):
     p = stat_prob.mean(axis=0) if T else np.zeros(N)
     l_aux = alpha * N * float(np.sum(f * p))
     return f, p, l_aux
+
+
+# ------------------------------------------------- router z-loss, entropy
+def router_z_loss(z):
+    """L_z = (1/T) sum_t (log sum_i exp z_ti)^2: the mean squared
+    log-sum-exp of the router logits [wuhy-notes §五 Router z-loss (the
+    extracted formula is garbled; this is its plain reading)]."""
+    z = _f64(z)
+    if z.shape[0] == 0:
+        return 0.0
+    m = z.max(axis=-1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(z - m).sum(axis=-1))
+    return float(np.mean(lse ** 2))
+
+
+def routing_entropy(stat_prob):
+    """Mean over tokens of the entropy -sum_i q_ti log q_ti of the routing
+    distribution q_t (the rows that p_i averages: the softmax in modes A/B,
+    the normalised sigmoid scores in mode C) [wuhy-notes, monitoring list:
+    router probability distribution and routing entropy]."""
+    q = _f64(stat_prob)
+    if q.shape[0] == 0:
+        return 0.0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        terms = np.where(q > 0, -q * np.log(q), 0.0)
+    return float(np.mean(terms.sum(axis=-1)))
 
 
 # --------------------------------------------------------------- whole layer

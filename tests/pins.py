@@ -392,4 +392,34 @@ def pin_group_mask_is_minus_infinity():
     assert np.allclose(r.gates[0], s[[0, 1]] / s[[0, 1]].sum(), rtol=0, atol=1e-15)
 
 
+# ------------------------------------------------ z-loss and routing entropy
+def pin_z_loss_closed_forms():
+    """z-loss of the worked-example logits [2.2, 0.5, 1.8, -0.4] is
+    (ln(e^2.2 + e^0.5 + e^1.8 + e^-0.4))^2 (scipy's logsumexp); all-zero
+    logits over N experts give (ln N)^2; a shift by c adds c to every
+    log-sum-exp; the mean is over tokens."""
+    z = np.array([[2.2, 0.5, 1.8, -0.4]])
+    want = math.log(math.exp(2.2) + math.exp(0.5) + math.exp(1.8) + math.exp(-0.4)) ** 2
+    assert abs(O.router_z_loss(z) - want) < 1e-12
+    assert abs(O.router_z_loss(z) - scipy.special.logsumexp(z[0]) ** 2) < 1e-12
+    assert abs(O.router_z_loss(np.zeros((3, 8))) - math.log(8) ** 2) < 1e-12
+    two = np.vstack([z, z + 1.5])
+    l0 = scipy.special.logsumexp(z[0])
+    assert abs(O.router_z_loss(two) - (l0 ** 2 + (l0 + 1.5) ** 2) / 2) < 1e-12
+
+
+def pin_routing_entropy_closed_forms():
+    """Uniform routing over N experts has entropy ln N; a one-hot row has 0;
+    random rows match scipy.stats.entropy (natural log), averaged over
+    tokens."""
+    import scipy.stats
+    assert abs(O.routing_entropy(np.full((2, 8), 1 / 8)) - math.log(8)) < 1e-12
+    assert O.routing_entropy(np.eye(4)) == 0.0
+    rng = np.random.default_rng(13)
+    q = rng.random((5, 7))
+    q /= q.sum(axis=1, keepdims=True)
+    want = np.mean([scipy.stats.entropy(r) for r in q])
+    assert abs(O.routing_entropy(q) - want) < 1e-12
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -1,6 +1,9 @@
 """Plant a plausible mistake in the oracle (on the CPU) and check that at
 least one pin fails for it, so the pins constrain every step."""
+import math
+
 import numpy as np
+import scipy.special
 import pytest
 
 import pins
@@ -8,7 +11,7 @@ from oracle import moe_oracle as O
 
 _orig = {n: getattr(O, n) for n in ("router_logits", "softmax", "sigmoid", "topk", "group_limit",
                                      "dispatch", "silu", "expert_ffn", "combine",
-                                     "load_stats", "route")}
+                                     "load_stats", "route", "router_z_loss", "routing_entropy")}
 
 
 def _route_no_renorm(h, w, k, mode, b_router=None, b_select=None):
@@ -105,6 +108,9 @@ MUTATIONS = {
     "group_mask_zero": ("group_limit", _group_mask_zero),
     "group_score_max_only": ("group_limit", _group_score_max),
     "group_keep_worst": ("group_limit", _group_keep_worst),
+    "z_loss_not_squared": ("router_z_loss", lambda z: float(np.mean(scipy.special.logsumexp(np.asarray(z, float), axis=-1)))),
+    "z_loss_sum_not_mean": ("router_z_loss", lambda z: _orig["router_z_loss"](z) * np.asarray(z).shape[0]),
+    "entropy_log2": ("routing_entropy", lambda q: _orig["routing_entropy"](q) / math.log(2)),
     "stats_f_over_T": ("load_stats", lambda c, sp, k, a: _orig["load_stats"](c, sp, 1, a)),
     "stats_no_N_factor": ("load_stats", lambda c, sp, k, a: (lambda f, p, l: (f, p, l / np.asarray(sp).shape[1]))(*_orig["load_stats"](c, sp, k, a))),
 }
