@@ -160,11 +160,18 @@ size_t moe_workspace_bytes(const moe_shape* s);
  *   p_mean     [N] fp32 out, nullable: p_i = mean_t P_ti (modes A/B: the
  *              softmax probability; mode C: s_ti / Σ_j s_tj), reduced in a
  *              fixed order (bit-reproducible).
+ *   z_loss     [1] fp32 out, nullable: router z-loss (1/T) Σ_t (log Σ_i e^z_ti)²
+ *              over the logits z (with b_r) [wuhy-notes §五 Router z-loss]
+ *   entropy    [1] fp32 out, nullable: (1/T) Σ_t −Σ_i P_ti log P_ti, the mean
+ *              entropy of the routing distribution P (as for p_mean)
+ *              [wuhy-notes, monitoring list: routing entropy]
+ *   Both scalars are reduced in a fixed order (bit-reproducible).
  * [wuhy-notes §二 第一步–第三步; cooking-agi first section] */
 moe_status moe_route(const moe_shape* s, const void* h, const void* w_router,
                      const float* b_router, const float* b_select,
                      int32_t* topk_ids, float* topk_gates, float* p_mean,
-                     void* ws, size_t ws_bytes, void* stream);
+                     float* z_loss, float* entropy, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* Dispatch: stable regroup of the T·k flat slots f = t·k + j by expert.
  *   topk_ids [T, k] int32 in, every id in [0, N) (precondition; not checked
@@ -215,8 +222,9 @@ moe_status moe_combine(const moe_shape* s, const void* out_rows,
 /* The whole layer in one call (route, dispatch, experts, combine, stats),
  * no host synchronisation inside.
  *   y [T, d] dtype out (required).
- *   topk_ids, topk_gates, counts, f_out, p_out, l_aux: nullable outputs
- *   (the workspace holds whatever is not returned). */
+ *   topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss, entropy:
+ *   nullable outputs as in moe_route / moe_dispatch (the workspace holds
+ *   whatever is not returned). */
 moe_status moe_layer_fused(const moe_shape* s, const void* h,
                            const void* w_router, const float* b_router,
                            const float* b_select, const void* w_gate,
@@ -224,8 +232,9 @@ moe_status moe_layer_fused(const moe_shape* s, const void* h,
                            const void* sh_gate, const void* sh_up,
                            const void* sh_down, void* y, int32_t* topk_ids,
                            float* topk_gates, int32_t* counts, float* f_out,
-                           float* p_out, float* l_aux, void* ws,
-                           size_t ws_bytes, void* stream);
+                           float* p_out, float* l_aux, float* z_loss,
+                           float* entropy, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* moe_layer_fused that also records caller-created hipEvent_t handles on
  * `stream` at the stage boundaries, for timing: events[0] before routing,
@@ -240,8 +249,9 @@ moe_status moe_layer_fused_marked(const moe_shape* s, const void* h,
                                   const void* sh_down, void* y,
                                   int32_t* topk_ids, float* topk_gates,
                                   int32_t* counts, float* f_out, float* p_out,
-                                  float* l_aux, void* ws, size_t ws_bytes,
-                                  void* stream, void* const* events);
+                                  float* l_aux, float* z_loss, float* entropy,
+                                  void* ws, size_t ws_bytes, void* stream,
+                                  void* const* events);
 
 #ifdef __cplusplus
 }

@@ -55,12 +55,12 @@ _SIG = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
-    "moe_route": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 7 + [_P, ctypes.c_size_t, _P]),
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 9 + [_P, ctypes.c_size_t, _P]),
     "moe_dispatch": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]),
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 10 + [_P, ctypes.c_size_t, _P]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 5),
-    "moe_layer_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 17 + [_P, ctypes.c_size_t, _P]),
-    "moe_layer_fused_marked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 17
+    "moe_layer_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 19 + [_P, ctypes.c_size_t, _P]),
+    "moe_layer_fused_marked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 19
                                + [_P, ctypes.c_size_t, _P, _P]),
 }
 
@@ -113,10 +113,11 @@ def workspace_bytes(shape: Shape) -> int:
 
 
 def route(shape, h, w_router, b_router, b_select, topk_ids, topk_gates, p_mean, ws,
-          ws_bytes, stream=None):
+          ws_bytes, stream=None, z_loss=None, entropy=None):
     _check(lib().moe_route(ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router),
                            _ptr(b_select), _ptr(topk_ids), _ptr(topk_gates), _ptr(p_mean),
-                           _ptr(ws), ws_bytes, _stream(stream)), "moe_route")
+                           _ptr(z_loss), _ptr(entropy), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_route")
 
 
 def dispatch(shape, topk_ids, counts, offsets, perm_src, row_of, p_mean=None, f_out=None,
@@ -141,11 +142,12 @@ def combine(shape, out_rows, row_of, topk_gates, y, stream=None):
 
 def layer_fused(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                 sh_down, y, topk_ids=None, topk_gates=None, counts=None, f_out=None,
-                p_out=None, l_aux=None, ws=None, ws_bytes=0, stream=None, events=None):
+                p_out=None, l_aux=None, ws=None, ws_bytes=0, stream=None, events=None,
+                z_loss=None, entropy=None):
     args = (ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(b_select),
             _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),
             _ptr(y), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _ptr(f_out), _ptr(p_out),
-            _ptr(l_aux), _ptr(ws), ws_bytes, _stream(stream))
+            _ptr(l_aux), _ptr(z_loss), _ptr(entropy), _ptr(ws), ws_bytes, _stream(stream))
     if events is None:
         _check(lib().moe_layer_fused(*args), "moe_layer_fused")
     else:
@@ -178,9 +180,11 @@ class MoELayer:
                        counts=torch.empty(s.N, dtype=torch.int32, device=dev),
                        f=torch.empty(s.N, dtype=torch.float32, device=dev),
                        p=torch.empty(s.N, dtype=torch.float32, device=dev),
-                       l_aux=torch.empty(1, dtype=torch.float32, device=dev))
+                       l_aux=torch.empty(1, dtype=torch.float32, device=dev),
+                       z_loss=torch.empty(1, dtype=torch.float32, device=dev),
+                       entropy=torch.empty(1, dtype=torch.float32, device=dev))
         layer_fused(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                     sh_down, y, res.get("topk_ids"), res.get("topk_gates"), res.get("counts"),
                     res.get("f"), res.get("p"), res.get("l_aux"), self.ws, self.ws_bytes,
-                    events=events)
+                    events=events, z_loss=res.get("z_loss"), entropy=res.get("entropy"))
         return res

@@ -123,13 +123,15 @@ moe_status check_shared(const moe_shape* s, const void* sg, const void* su, cons
 
 // ------------------------------------------------------- workspace layout
 struct RouteWs {
-  size_t z, p_part, end;
+  size_t z, p_part, zl_part, end;
 };
 RouteWs route_ws(const moe_shape* s, size_t base) {
   RouteWs w;
+  const size_t blocks = (size_t)moe::route_select_blocks(s->T, s->N);
   w.z = base;
   w.p_part = align_up(w.z + sizeof(float) * (size_t)moe::kRouterMaxSplits * s->T * s->N);
-  w.end = align_up(w.p_part + sizeof(float) * (size_t)moe::route_select_blocks(s->T, s->N) * s->N);
+  w.zl_part = align_up(w.p_part + sizeof(float) * blocks * s->N);
+  w.end = align_up(w.zl_part + sizeof(float) * blocks * 2);
   return w;
 }
 size_t act_bytes(const moe_shape* s) {
@@ -222,8 +224,11 @@ T* at(void* ws, size_t off) {
 // ------------------------------------------------------------ stage impls
 moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
                       const float* b_router, const float* b_select, int32_t* ids,
-                      float* gates, float* p_mean, float* z_part, float* p_part,
-                      hipStream_t st) {
+                      float* gates, float* p_mean, float* z_loss, float* entropy,
+                      const RouteWs& W, void* ws, hipStream_t st) {
+  float* z_part = at<float>(ws, W.z);
+  float* p_part = at<float>(ws, W.p_part);
+  float* zl_part = (z_loss || entropy) ? at<float>(ws, W.zl_part) : nullptr;
   int splits = 1;
   if (s->dtype == MOE_BF16) {
     splits = moe::router_splits(s->T, s->d, s->N);
@@ -239,12 +244,12 @@ moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
   const bool grouped = s->n_groups > 1 && s->topk_groups < s->n_groups;
   const moe::GroupLimit gl{grouped ? s->n_groups : 0, s->topk_groups, s->group_topm};
   TRY(hip_check(moe::launch_route_select(z_part, splits, b_router, b_select, ids, gates,
-                                         p_mean ? p_part : nullptr, s->T, s->N, s->k, s->mode,
-                                         gl, st),
+                                         p_mean ? p_part : nullptr, zl_part, s->T, s->N, s->k,
+                                         s->mode, gl, st),
                 "route select"));
-  if (p_mean)
-    TRY(hip_check(moe::launch_p_reduce(p_part, p_mean, moe::route_select_blocks(s->T, s->N), s->T,
-                                       s->N, st),
+  if (p_mean || zl_part)
+    TRY(hip_check(moe::launch_p_reduce(p_part, p_mean, zl_part, z_loss, entropy,
+                                       moe::route_select_blocks(s->T, s->N), s->T, s->N, st),
                   "p reduce"));
   return MOE_OK;
 }
@@ -320,8 +325,8 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
                       const void* w_up, const void* w_down, const void* sh_gate,
                       const void* sh_up, const void* sh_down, void* y, int32_t* topk_ids,
                       float* topk_gates, int32_t* counts, float* f_out, float* p_out,
-                      float* l_aux, void* ws, size_t ws_bytes, void* stream,
-                      void* const* events) {
+                      float* l_aux, float* z_loss, float* entropy, void* ws, size_t ws_bytes,
+                      void* stream, void* const* events) {
   TRY(check_shape(s));
   TRY(need16(h, "h"));
   TRY(need16(w_router, "w_router"));
@@ -337,6 +342,8 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   TRY(opt4(f_out, "f_out"));
   TRY(opt4(p_out, "p_out"));
   TRY(opt4(l_aux, "l_aux"));
+  TRY(opt4(z_loss, "z_loss"));
+  TRY(opt4(entropy, "entropy"));
   if (events)
     for (int i = 0; i < 6; ++i)
       if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[] holds a NULL event");
@@ -356,8 +363,8 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   void* rows = at<char>(ws, L.rows);
 
   TRY(mark(events, 0, st));
-  TRY(route_impl(s, h, w_router, b_router, b_select, ids, gates, p_mean, at<float>(ws, L.r.z),
-                 at<float>(ws, L.r.p_part), st));
+  TRY(route_impl(s, h, w_router, b_router, b_select, ids, gates, p_mean, z_loss, entropy, L.r,
+                 ws, st));
   TRY(mark(events, 1, st));
   TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, st));
   TRY(mark(events, 2, st));
@@ -398,7 +405,8 @@ size_t moe_workspace_bytes(const moe_shape* s) {
 
 moe_status moe_route(const moe_shape* s, const void* h, const void* w_router,
                      const float* b_router, const float* b_select, int32_t* topk_ids,
-                     float* topk_gates, float* p_mean, void* ws, size_t ws_bytes, void* stream) {
+                     float* topk_gates, float* p_mean, float* z_loss, float* entropy, void* ws,
+                     size_t ws_bytes, void* stream) {
   g_err.clear();
   TRY(check_shape(s));
   TRY(need16(h, "h"));
@@ -407,11 +415,13 @@ moe_status moe_route(const moe_shape* s, const void* h, const void* w_router,
   TRY(need4(topk_ids, "topk_ids"));
   TRY(need4(topk_gates, "topk_gates"));
   TRY(opt4(p_mean, "p_mean"));
+  TRY(opt4(z_loss, "z_loss"));
+  TRY(opt4(entropy, "entropy"));
   const RouteWs L = route_ws(s, 0);
   TRY(check_ws(ws, ws_bytes, L.end));
   if (s->T == 0) return MOE_OK;
-  return route_impl(s, h, w_router, b_router, b_select, topk_ids, topk_gates, p_mean,
-                    at<float>(ws, L.z), at<float>(ws, L.p_part), static_cast<hipStream_t>(stream));
+  return route_impl(s, h, w_router, b_router, b_select, topk_ids, topk_gates, p_mean, z_loss,
+                    entropy, L, ws, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids, int32_t* counts,
@@ -478,11 +488,12 @@ moe_status moe_layer_fused(const moe_shape* s, const void* h, const void* w_rout
                            const void* w_up, const void* w_down, const void* sh_gate,
                            const void* sh_up, const void* sh_down, void* y, int32_t* topk_ids,
                            float* topk_gates, int32_t* counts, float* f_out, float* p_out,
-                           float* l_aux, void* ws, size_t ws_bytes, void* stream) {
+                           float* l_aux, float* z_loss, float* entropy, void* ws,
+                           size_t ws_bytes, void* stream) {
   g_err.clear();
   return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
-                    sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, ws, ws_bytes,
-                    stream, nullptr);
+                    sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss,
+                    entropy, ws, ws_bytes, stream, nullptr);
 }
 
 moe_status moe_layer_fused_marked(const moe_shape* s, const void* h, const void* w_router,
@@ -491,13 +502,13 @@ moe_status moe_layer_fused_marked(const moe_shape* s, const void* h, const void*
                                   const void* sh_gate, const void* sh_up, const void* sh_down,
                                   void* y, int32_t* topk_ids, float* topk_gates,
                                   int32_t* counts, float* f_out, float* p_out, float* l_aux,
-                                  void* ws, size_t ws_bytes, void* stream,
-                                  void* const* events) {
+                                  float* z_loss, float* entropy, void* ws, size_t ws_bytes,
+                                  void* stream, void* const* events) {
   g_err.clear();
   if (!events) return fail(MOE_ERR_INVALID_ARG, "events is NULL");
   return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
-                    sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, ws, ws_bytes,
-                    stream, events);
+                    sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss,
+                    entropy, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -25,13 +25,17 @@ struct GroupLimit {
 // z = sum of the partial slices + b_router; scores, top-k, gates, and
 // per-block sums of the routing probabilities
 int route_select_blocks(int T, int N);
+// (zl_part, when given: per-block sums of the squared log-sum-exp of the
+// logits and of the routing entropy, 2 floats per block)
 hipError_t launch_route_select(const float* z_part, int splits,
                                const float* b_router, const float* b_select,
                                int32_t* ids, float* gates, float* p_part,
-                               int T, int N, int k, int mode, GroupLimit gl,
-                               hipStream_t st);
-hipError_t launch_p_reduce(const float* p_part, float* p_mean, int blocks,
-                           int T, int N, hipStream_t st);
+                               float* zl_part, int T, int N, int k, int mode,
+                               GroupLimit gl, hipStream_t st);
+// p_mean (nullable) from p_part; z_loss / entropy (nullable) from zl_part
+hipError_t launch_p_reduce(const float* p_part, float* p_mean,
+                           const float* zl_part, float* z_loss, float* entropy,
+                           int blocks, int T, int N, hipStream_t st);
 
 // --------------------------------------------------------------- dispatch
 hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N,

@@ -57,13 +57,14 @@ template <int LPT, int VPL, int MODE, int ITER>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
     const float* __restrict__ b_select, int32_t* __restrict__ ids,
-    float* __restrict__ gates, float* __restrict__ p_part, int T, int N, int k,
-    GroupLimit gl) {
+    float* __restrict__ gates, float* __restrict__ p_part, float* __restrict__ zl_part, int T,
+    int N, int k, GroupLimit gl) {
   constexpr int TPW = 64 / LPT;               // tokens per wave per iteration
   constexpr int TPB = 4 * TPW * ITER;         // tokens per block
   constexpr int GPL = 64 / LPT;               // groups per lane at most (64 groups)
   __shared__ float s_p[4][64][VPL];
   __shared__ float s_g[4][64 * VPL];          // group scoring values of the wave's tokens
+  __shared__ float s_zl[4][64][2];            // per-lane sums of lse^2 and entropy
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane / LPT, li = lane % LPT;
   const int64_t TN = (int64_t)T * N;
@@ -71,6 +72,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   float pacc[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) pacc[i] = 0.0f;
+  float zl_acc = 0.0f, ent_acc = 0.0f;        // this lane's tokens (lane li == 0)
 
   for (int it = 0; it < ITER; ++it) {
     const int t = blockIdx.x * TPB + (it * 4 + w) * TPW + grp;
@@ -220,10 +222,11 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
           win_aux[jj] = ba;
         }
     }
-    // ---- full-softmax max and denominator (mode B gates, p statistics)
+    // ---- full-softmax max and denominator (mode B gates, p statistics,
+    //      z-loss)
     float zmax = 0.0f, denom_all = 1.0f;
-    const bool need_full = (MODE == 1) || (p_part != nullptr);
-    if (MODE != 2 && need_full) {
+    const bool need_full = (MODE == 1) || (p_part != nullptr) || (zl_part != nullptr);
+    if (need_full) {
       float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
@@ -238,6 +241,41 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
 #pragma unroll
       for (int o = LPT / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
       denom_all = sum;
+    }
+    // ---- router z-loss term (log-sum-exp of the logits)^2 and the entropy
+    //      of the routing distribution [wuhy-notes §五 Router z-loss]
+    if (zl_part) {
+      const float lse = zmax + logf(denom_all);
+      float ent;
+      if (MODE != 2) {
+        // H = lse - sum_i p_i z_i
+        float pz = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+          if (li + LPT * i < N) pz += expf(zv[i] - zmax) * zv[i];
+#pragma unroll
+        for (int o = LPT / 2; o >= 1; o >>= 1) pz += __shfl_xor(pz, o, 64);
+        ent = lse - pz / denom_all;
+      } else {
+        // q = s / S: H = log S - sum_i s_i log s_i / S
+        float ss = 0.0f, sls = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+          if (li + LPT * i < N) {
+            ss += aux[i];
+            sls += aux[i] > 0.0f ? aux[i] * logf(aux[i]) : 0.0f;
+          }
+#pragma unroll
+        for (int o = LPT / 2; o >= 1; o >>= 1) {
+          ss += __shfl_xor(ss, o, 64);
+          sls += __shfl_xor(sls, o, 64);
+        }
+        ent = logf(ss) - sls / ss;
+      }
+      if (tok && li == 0) {
+        zl_acc += lse * lse;
+        ent_acc += ent;
+      }
     }
     // ---- gates
     float gsel[kMaxK];
@@ -297,6 +335,20 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
       }
     }
   }
+  if (zl_part) {
+    // block sums in a fixed order: waves, then token groups
+    s_zl[w][lane][0] = zl_acc;
+    s_zl[w][lane][1] = ent_acc;
+    __syncthreads();
+    if (tid < 2) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww)
+#pragma unroll
+        for (int g = 0; g < TPW; ++g) sum += s_zl[ww][g * LPT][tid];
+      zl_part[(int64_t)blockIdx.x * 2 + tid] = sum;
+    }
+  }
   if (p_part) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) s_p[w][lane][i] = pacc[i];
@@ -315,20 +367,45 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
 
 // p_mean[e] = (sum over blocks of p_part[b][e]) / T: one block per expert,
 // thread i sums blocks i, i+256, ... in order, then a fixed tree.
+// Blocks past the first n_p (when zl_part is given): z_loss and entropy as
+// the sums of the per-block partials over T, by the same fixed tree.
 __global__ __launch_bounds__(kThreads) void p_reduce_kernel(const float* __restrict__ p_part,
                                                             float* __restrict__ p_mean,
+                                                            const float* __restrict__ zl_part,
+                                                            float* __restrict__ z_loss,
+                                                            float* __restrict__ entropy, int n_p,
                                                             int blocks, int T, int N) {
-  __shared__ float s[kThreads];
-  const int e = blockIdx.x, tid = threadIdx.x;
-  float v = 0.0f;
-  for (int b = tid; b < blocks; b += kThreads) v += p_part[(int64_t)b * N + e];
-  s[tid] = v;
+  __shared__ float s[2][kThreads];
+  const int tid = threadIdx.x;
+  const bool scalars = (int)blockIdx.x >= n_p;
+  const int e = blockIdx.x;
+  float v0 = 0.0f, v1 = 0.0f;
+  for (int b = tid; b < blocks; b += kThreads) {
+    if (scalars) {
+      v0 += zl_part[(int64_t)b * 2];
+      v1 += zl_part[(int64_t)b * 2 + 1];
+    } else {
+      v0 += p_part[(int64_t)b * N + e];
+    }
+  }
+  s[0][tid] = v0;
+  s[1][tid] = v1;
   __syncthreads();
   for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) s[tid] += s[tid + o];
+    if (tid < o) {
+      s[0][tid] += s[0][tid + o];
+      s[1][tid] += s[1][tid + o];
+    }
     __syncthreads();
   }
-  if (tid == 0) p_mean[e] = s[0] / (float)T;
+  if (tid == 0) {
+    if (!scalars) {
+      p_mean[e] = s[0][0] / (float)T;
+    } else {
+      if (z_loss) *z_loss = s[0][0] / (float)T;
+      if (entropy) *entropy = s[1][0] / (float)T;
+    }
+  }
 }
 
 // Launch configuration of route_select for N experts.
@@ -349,20 +426,20 @@ SelectCfg select_cfg(int N) {
 template <int LPT, int VPL, int ITER>
 hipError_t launch_select_t(const float* z_part, int splits, const float* b_router,
                            const float* b_select, int32_t* ids, float* gates, float* p_part,
-                           int T, int N, int k, int mode, GroupLimit gl, int blocks,
-                           hipStream_t st) {
+                           float* zl_part, int T, int N, int k, int mode, GroupLimit gl,
+                           int blocks, hipStream_t st) {
   switch (mode) {
     case 0:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 0, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k, gl);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl);
       break;
     case 1:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 1, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k, gl);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl);
       break;
     default:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 2, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, T, N, k, gl);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl);
       break;
   }
   return hipGetLastError();
@@ -386,15 +463,15 @@ int route_select_blocks(int T, int N) {
 
 hipError_t launch_route_select(const float* z_part, int splits, const float* b_router,
                                const float* b_select, int32_t* ids, float* gates,
-                               float* p_part, int T, int N, int k, int mode, GroupLimit gl,
-                               hipStream_t st) {
+                               float* p_part, float* zl_part, int T, int N, int k, int mode,
+                               GroupLimit gl, hipStream_t st) {
   const SelectCfg c = select_cfg(N);
   const int blocks = (T + c.tpb - 1) / c.tpb;
   if (blocks == 0) return hipSuccess;
 #define MOE_SEL(L, V, I)                                                                    \
   if (c.lpt == L && c.vpl == V)                                                             \
     return launch_select_t<L, V, I>(z_part, splits, b_router, b_select, ids, gates, p_part, \
-                                    T, N, k, mode, gl, blocks, st);
+                                    zl_part, T, N, k, mode, gl, blocks, st);
   MOE_SEL(8, 1, 1)
   MOE_SEL(16, 1, 1)
   MOE_SEL(32, 1, 2)
@@ -406,11 +483,15 @@ hipError_t launch_route_select(const float* z_part, int splits, const float* b_r
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_p_reduce(const float* p_part, float* p_mean, int blocks, int T, int N,
+hipError_t launch_p_reduce(const float* p_part, float* p_mean, const float* zl_part,
+                           float* z_loss, float* entropy, int blocks, int T, int N,
                            hipStream_t st) {
   if (T == 0 || N == 0) return hipSuccess;
-  hipLaunchKernelGGL(p_reduce_kernel, dim3(N), dim3(kThreads), 0, st, p_part, p_mean, blocks,
-                     T, N);
+  const int n_p = p_mean ? N : 0;
+  const int grid = n_p + ((z_loss || entropy) ? 1 : 0);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(p_reduce_kernel, dim3(grid), dim3(kThreads), 0, st, p_part, p_mean,
+                     zl_part, z_loss, entropy, n_p, blocks, T, N);
   return hipGetLastError();
 }
 

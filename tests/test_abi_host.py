@@ -63,8 +63,8 @@ def fused(s, **over):
     st = lib.moe_layer_fused(ctypes.byref(s), args["h"], args["w_router"], args["b_router"],
                              args["b_select"], args["w_gate"], args["w_up"], args["w_down"],
                              args["sh_gate"], args["sh_up"], args["sh_down"], args["y"],
-                             None, None, None, None, None, None, args["ws"], args["ws_bytes"],
-                             None)
+                             None, None, None, None, None, None, None, None, args["ws"],
+                             args["ws_bytes"], None)
     return st, lib.moe_last_error().decode()
 
 
@@ -126,13 +126,15 @@ def test_zero_tokens_is_a_noop():
 def test_other_entry_points_validate():
     lib = M.lib()
     s = shape(k=9)
-    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE,
-                         1 << 40, None) == M.ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, FAKE, None, None, None,
+                         FAKE, 1 << 40, None) == M.ERR_INVALID_ARG
     s = shape()
-    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, None, None, None, FAKE, None, FAKE,
-                         1 << 40, None) == M.ERR_INVALID_ARG
-    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE,
-                         16, None) == M.ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, None, None, None, FAKE, None, None, None,
+                         FAKE, 1 << 40, None) == M.ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, FAKE, None, None, None,
+                         FAKE, 16, None) == M.ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE + 2,
+                         None, FAKE, 1 << 40, None) == M.ERR_INVALID_ARG   # misaligned z_loss
     assert lib.moe_dispatch(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
                             None, 0, None) == M.ERR_INVALID_ARG     # l_aux without p_mean
     assert lib.moe_dispatch(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, None, None, None,
@@ -141,7 +143,7 @@ def test_other_entry_points_validate():
                               None, FAKE, FAKE, 8, None) == M.ERR_WORKSPACE
     assert lib.moe_combine(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE + 4, None) == M.ERR_INVALID_ARG
     assert lib.moe_layer_fused_marked(ctypes.byref(s), *([FAKE] * 3), None, *([FAKE] * 3),
-                                      None, None, None, FAKE, *([None] * 6), FAKE, 1 << 40, None,
+                                      None, None, None, FAKE, *([None] * 8), FAKE, 1 << 40, None,
                                       None) == M.ERR_INVALID_ARG
 
 

@@ -110,6 +110,10 @@ def test_full_size_layer(w):
     assert np.allclose(host(fo), f_ref, rtol=1e-6, atol=0)
     assert np.allclose(host(p), p_ref, rtol=1e-4, atol=1e-7)
     assert abs(float(host(la)[0]) - l_ref) <= 1e-4 * abs(l_ref) + 1e-9
+    zl_ref, ent_ref = O.router_z_loss(r.z), O.routing_entropy(r.stat_prob)
+    zl, ent = float(host(res["z_loss"])[0]), float(host(res["entropy"])[0])
+    assert abs(zl - zl_ref) <= 1e-4 * abs(zl_ref) + 1e-6, (zl, zl_ref)
+    assert abs(ent - ent_ref) <= 1e-4 * abs(ent_ref) + 1e-6, (ent, ent_ref)
     print(f"[{w.name}] routing/dispatch/stats exact; near-tie tokens {int(near.sum())} of {T}; "
           f"rows per expert min/max {d.counts.min()}/{d.counts.max()}", flush=True)
 

@@ -66,7 +66,8 @@ def run_steps(s, inp):
     ws, nws = workspace(s)
     T, k, N = s.T, s.k, s.N
     ids, gates, p = i32(T * k), f32(T * k), f32(N)
-    M.route(s, h, wr, br, bs, ids, gates, p, ws, nws)
+    zl, ent = f32(1), f32(1)
+    M.route(s, h, wr, br, bs, ids, gates, p, ws, nws, z_loss=zl, entropy=ent)
     counts, offsets, perm, row_of = i32(N), i32(N + 1), i32(T * k), i32(T * k)
     fo, la = f32(N), f32(1)
     M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la)
@@ -80,14 +81,18 @@ def run_steps(s, inp):
     t.cuda.synchronize()
     res = dict(ids=host(ids).reshape(T, k), gates=host(gates).reshape(T, k), p=host(p),
                counts=host(counts), offsets=host(offsets), perm=host(perm), row_of=host(row_of),
-               f=host(fo), l_aux=float(host(la)[0]), out_rows=host(out_rows), y=host(y))
+               f=host(fo), l_aux=float(host(la)[0]), out_rows=host(out_rows), y=host(y),
+               z_loss=float(host(zl)[0]), entropy=float(host(ent)[0]))
     # the fused call on the same inputs must agree bit for bit
     y2 = t.empty_like(y)
     ids2, g2, c2, f2, p2, l2 = i32(T * k), f32(T * k), i32(N), f32(N), f32(N), f32(1)
-    M.layer_fused(s, h, wr, br, bs, wg, wu, wd, sg, su, sd, y2, ids2, g2, c2, f2, p2, l2, ws, nws)
+    zl2, ent2 = f32(1), f32(1)
+    M.layer_fused(s, h, wr, br, bs, wg, wu, wd, sg, su, sd, y2, ids2, g2, c2, f2, p2, l2, ws, nws,
+                  z_loss=zl2, entropy=ent2)
     t.cuda.synchronize()
     res["fused"] = dict(y=host(y2), ids=host(ids2).reshape(T, k), gates=host(g2).reshape(T, k),
-                        counts=host(c2), f=host(f2), p=host(p2), l_aux=float(host(l2)[0]))
+                        counts=host(c2), f=host(f2), p=host(p2), l_aux=float(host(l2)[0]),
+                        z_loss=float(host(zl2)[0]), entropy=float(host(ent2)[0]))
     return res
 
 
@@ -109,6 +114,10 @@ def check_all(s, inp, res, alpha=0.01):
     assert np.allclose(res["f"], f, rtol=1e-6, atol=0)
     assert np.allclose(res["p"], p, rtol=1e-4, atol=1e-7)
     assert abs(res["l_aux"] - l_aux) <= 1e-4 * abs(l_aux) + 1e-9
+    # router z-loss and routing entropy over every token (fp32 on the GPU)
+    zl_ref, ent_ref = O.router_z_loss(r.z), O.routing_entropy(r.stat_prob)
+    assert abs(res["z_loss"] - zl_ref) <= 1e-4 * abs(zl_ref) + 1e-6, (res["z_loss"], zl_ref)
+    assert abs(res["entropy"] - ent_ref) <= 1e-4 * abs(ent_ref) + 1e-6, (res["entropy"], ent_ref)
     # expert rows: oracle experts on the GPU's dispatch
     rows_ref = O.expert_rows(inp["h"], d, s.k, oracle_weights(inp), oracle_shared(inp))
     check_close_rows(res["out_rows"], rows_ref, tol, what="out_rows")
@@ -126,6 +135,7 @@ def check_all(s, inp, res, alpha=0.01):
     assert np.array_equal(fz["gates"], res["gates"])
     assert np.array_equal(fz["counts"], res["counts"])
     assert np.array_equal(fz["p"], res["p"]) and fz["l_aux"] == res["l_aux"]
+    assert fz["z_loss"] == res["z_loss"] and fz["entropy"] == res["entropy"]
     return worst, int(near.sum())
 
 
