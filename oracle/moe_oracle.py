@@ -31,6 +31,9 @@ notation, with numpy as the only primitive (matrix products, exp, a sort):
   5. dispatch: stable regroup of the (token, slot) pairs by expert
      [wuhy-notes §三 "Token Dispatch" table and bucket listing;
       page "【大模型】MoE（专家混合模型）简介" (horizon.auto) §3 ② Dispatch]
+     optionally with an expert capacity C = ceil(factor * T k / N): each
+     expert keeps its first C slots in token order, later ones are dropped
+     [wuhy-notes §六 Expert Capacity]; usage and drop fraction are reported
   6. experts: E_i(h) = W_down^(i) (SiLU(W_gate^(i) h) * W_up^(i) h)
      [wuhy-notes §一, SwiGLU FFN and expert formulas]
      shared expert: added to every token with weight 1  [wuhy-notes §八]
@@ -48,7 +51,9 @@ Readings where the pages are silent or garbled (each is listed in the design
 notes): ties in top-k go to the lower expert index; f_i = count_i / (T k);
 p_i in mode C averages s_ti / sum_j s_tj; the shared expert is ungated; the
 router bias is optional; SiLU(x) = x * sigmoid(x); expert linears have no
-bias; the layer output excludes the residual.
+bias; the layer output excludes the residual; with a capacity, slots past C
+are dropped in token order (latest first), contribute nothing to y and still
+count in f_i (f_i is the routing decision, not what was computed).
 
 Parity pins: every function here is pinned in tests/test_oracle_pins.py
 against the pages' worked examples, closed forms, brute force or library
@@ -58,6 +63,7 @@ a pin catches each.
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Callable, Optional, Sequence
 
 import numpy as np
@@ -204,24 +210,48 @@ def route(h, w_router, k, mode, b_router=None, b_select=None, groups=None) -> Ro
 # ---------------------------------------------------------------- 5. dispatch
 @dataclasses.dataclass
 class Dispatch:
-    counts: np.ndarray    # [N] rows per expert
-    offsets: np.ndarray   # [N+1] exclusive prefix of counts
-    perm_src: np.ndarray  # [T*k] bucket row -> flat slot t*k + j
-    row_of: np.ndarray    # [T*k] flat slot -> bucket row
+    counts: np.ndarray    # [N] slots routed to each expert
+    offsets: np.ndarray   # [N+1] exclusive prefix of the kept counts
+    perm_src: np.ndarray  # [sum kept] bucket row -> flat slot t*k + j
+    row_of: np.ndarray    # [T*k] flat slot -> bucket row, -1 if dropped
+    kept: np.ndarray      # [N] slots each expert keeps (= counts without a capacity)
 
 
-def dispatch(ids, N) -> Dispatch:
+def expert_capacity(capacity_factor, T, k, N):
+    """C = ceil(capacity_factor * T * k / N) [wuhy-notes §六 Expert Capacity],
+    evaluated in double precision on the float32 factor the library gets."""
+    return int(math.ceil(float(np.float32(capacity_factor)) * (T * k) / N))
+
+
+def dispatch(ids, N, capacity=None) -> Dispatch:
     """Group the flat slots f = t*k + j by expert: expert 0's slots first,
-    then expert 1's, ...; within one expert in ascending f (token order)."""
+    then expert 1's, ...; within one expert in ascending f (token order).
+    With a capacity C each expert keeps its first C slots in that order and
+    the later ones are dropped (row_of = -1) [wuhy-notes §六: what happens to
+    overflow depends on the implementation; here it is dropped]."""
     flat = np.asarray(ids).reshape(-1)
     buckets = [np.nonzero(flat == e)[0] for e in range(N)]
     counts = np.array([len(b) for b in buckets], dtype=np.int64)
+    if capacity is not None:
+        buckets = [b[:capacity] for b in buckets]
+    kept = np.array([len(b) for b in buckets], dtype=np.int64)
     offsets = np.zeros(N + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum(counts)
+    offsets[1:] = np.cumsum(kept)
     perm_src = (np.concatenate(buckets) if buckets else np.zeros(0)).astype(np.int64)
-    row_of = np.empty_like(perm_src)
+    row_of = np.full(flat.size, -1, dtype=np.int64)
     row_of[perm_src] = np.arange(perm_src.size)
-    return Dispatch(counts, offsets, perm_src, row_of)
+    return Dispatch(counts, offsets, perm_src, row_of, kept)
+
+
+def capacity_stats(disp: Dispatch, capacity):
+    """Capacity usage sum_e kept_e / (N C) and the fraction of routed slots
+    dropped [wuhy-notes, monitoring list: expert capacity usage and dropped
+    token ratio]."""
+    N = disp.counts.size
+    routed = int(disp.counts.sum())
+    kept = int(disp.kept.sum())
+    usage = kept / (N * capacity) if capacity else 0.0
+    return usage, ((routed - kept) / routed if routed else 0.0)
 
 
 # ----------------------------------------------------------------- 6. experts
@@ -255,7 +285,7 @@ def expert_rows(h, disp: Dispatch, k, weights_of: WeightsOf,
     out[T*k + t] = E_shared(h[t]). Streams one expert's weights at a time."""
     h = _f64(h)
     T = h.shape[0]
-    R = disp.perm_src.size
+    R = disp.row_of.size                     # T*k: shared rows follow at T*k + t
     out = np.zeros((R + (T if shared is not None else 0), h.shape[1]))
     for e in range(disp.counts.size):
         lo, hi = disp.offsets[e], disp.offsets[e + 1]
@@ -271,7 +301,8 @@ def expert_rows(h, disp: Dispatch, k, weights_of: WeightsOf,
 # ----------------------------------------------------------------- 7. combine
 def combine(out_rows, row_of, gates, has_shared=False):
     """y[t] = out_rows[T*k + t] (shared, weight 1) + sum_j g[t, j] *
-    out_rows[row_of[t*k + j]]: every routed contribution is added."""
+    out_rows[row_of[t*k + j]]: every routed contribution is added; a dropped
+    slot (row_of = -1) adds nothing."""
     gates = _f64(gates)
     T, k = gates.shape
     out_rows = _f64(out_rows)
@@ -280,7 +311,8 @@ def combine(out_rows, row_of, gates, has_shared=False):
         y += out_rows[T * k:T * k + T]
     rows = np.asarray(row_of).reshape(T, k)
     for j in range(k):
-        y += gates[:, j:j + 1] * out_rows[rows[:, j]]
+        keep = rows[:, j] >= 0
+        y[keep] += gates[keep, j:j + 1] * out_rows[rows[keep, j]]
     return y
 
 
@@ -335,11 +367,15 @@ class LayerResult:
 
 
 def layer(h, w_router, k, mode, weights_of: WeightsOf, b_router=None,
-          b_select=None, shared=None, alpha=0.01, groups=None) -> LayerResult:
-    """The whole forward pass, steps 1-8, on all tokens."""
+          b_select=None, shared=None, alpha=0.01, groups=None,
+          capacity_factor=None) -> LayerResult:
+    """The whole forward pass, steps 1-8, on all tokens (dropless, or with
+    the expert capacity of ``capacity_factor``)."""
     N = np.asarray(w_router).shape[0]
+    T = np.asarray(h).shape[0]
     r = route(h, w_router, k, mode, b_router, b_select, groups)
-    disp = dispatch(r.ids, N)
+    cap = expert_capacity(capacity_factor, T, k, N) if capacity_factor else None
+    disp = dispatch(r.ids, N, cap)
     out_rows = expert_rows(h, disp, k, weights_of, shared)
     y = combine(out_rows, disp.row_of, r.gates, shared is not None)
     f, p, l_aux = load_stats(disp.counts, r.stat_prob, k, alpha)
@@ -347,16 +383,20 @@ def layer(h, w_router, k, mode, weights_of: WeightsOf, b_router=None,
 
 
 def layer_tokens(h, routing: Routing, tokens, weights_of: WeightsOf,
-                 shared=None):
-    """y for a subset of tokens only (tokens are independent: no step couples
-    two tokens), computed one token at a time: for each token, run each of
-    its selected experts on its row and add the gated outputs (+ shared)."""
+                 shared=None, row_of=None):
+    """y for a subset of tokens only (without a capacity no step couples two
+    tokens), computed one token at a time: for each token, run each of its
+    selected experts on its row and add the gated outputs (+ shared). With a
+    capacity, pass the dispatch's row_of: dropped slots are skipped."""
     h = _f64(h)
     tokens = np.asarray(tokens, dtype=np.int64)
     y = np.zeros((tokens.size, h.shape[1]))
+    k = routing.ids.shape[1]
     need = {}
     for n, t in enumerate(tokens):
         for j, e in enumerate(routing.ids[t]):
+            if row_of is not None and row_of[t * k + j] < 0:
+                continue
             need.setdefault(int(e), []).append((n, t, j))
     for e, items in sorted(need.items()):
         wg, wu, wd = weights_of(e)
@@ -370,16 +410,26 @@ def layer_tokens(h, routing: Routing, tokens, weights_of: WeightsOf,
 
 
 def dense_layer(h, w_router, k, mode, weights_of: WeightsOf, b_router=None,
-                b_select=None, shared=None, groups=None):
+                b_select=None, shared=None, groups=None, capacity_factor=None):
     """Brute force: run every expert on every token, build the dense gate
     matrix G (g on the selected experts, 0 elsewhere) and sum G[t,i] E_i(h_t),
-    plus the shared expert."""
+    plus the shared expert. With a capacity C, walking the tokens in order,
+    an expert's (C+1)-th and later slots get gate 0."""
     h = _f64(h)
     T = h.shape[0]
     N = np.asarray(w_router).shape[0]
     r = route(h, w_router, k, mode, b_router, b_select, groups)
     G = np.zeros((T, N))
     np.put_along_axis(G, r.ids, r.gates, axis=-1)
+    if capacity_factor:
+        cap = expert_capacity(capacity_factor, T, k, N)
+        seen = np.zeros(N, dtype=np.int64)
+        for t in range(T):
+            for j in range(k):
+                e = int(r.ids[t, j])
+                seen[e] += 1
+                if seen[e] > cap:
+                    G[t, e] = 0.0
     y = np.zeros_like(h)
     for e in range(N):
         y += G[:, e:e + 1] * expert_ffn(h, *weights_of(e))

@@ -422,4 +422,59 @@ def pin_routing_entropy_closed_forms():
     assert abs(O.routing_entropy(q) - want) < 1e-12
 
 
+# ------------------------------------------------------- expert capacity
+def pin_capacity_closed_form():
+    """C = ceil(capacity_factor * T * k / N) [wuhy-notes §六 Expert
+    Capacity]: T = 4, k = 2, N = 4 gives T k / N = 2, so factor 1 -> 2,
+    1.25 -> 3 (2.5 rounds up), 0.5 -> 1; T = 10, k = 2, N = 4, factor 1.25
+    -> ceil(6.25) = 7."""
+    assert O.expert_capacity(1.0, 4, 2, 4) == 2
+    assert O.expert_capacity(1.25, 4, 2, 4) == 3
+    assert O.expert_capacity(0.5, 4, 2, 4) == 1
+    assert O.expert_capacity(1.25, 10, 2, 4) == 7
+
+
+def pin_capacity_grouping_example():
+    """The 4-token top-2 grouping example (E0<-T0,T2; E1<-T1,T3;
+    E2<-T0,T1,T3; E3<-T2) with capacity factor 1 (C = 2): E2's third slot,
+    the latest token T3, is dropped; every other slot is kept. Worked by
+    hand from the page's listing and the capacity formula."""
+    g = golden("dispatch_grouping_example.json")
+    ids = np.array(g["ids"])
+    d = O.dispatch(ids, 4, O.expert_capacity(1.0, 4, 2, 4))
+    assert d.counts.tolist() == [2, 2, 3, 1]
+    assert d.kept.tolist() == [2, 2, 2, 1]
+    assert d.offsets.tolist() == [0, 2, 4, 6, 7]
+    dropped = [f for f in range(8) if d.row_of[f] < 0]
+    assert dropped == [6] and ids.reshape(-1)[6] == 2 and 6 // 2 == 3
+    assert d.perm_src.tolist() == [0, 4, 2, 7, 1, 3, 5]
+    for e, toks in g["buckets_printed"].items():     # kept tokens: the printed ones, C at most
+        kept = [int(f) // 2 for f in d.perm_src[d.offsets[int(e)]:d.offsets[int(e) + 1]]]
+        assert kept == toks[:2]
+    usage, drop = O.capacity_stats(d, 2)
+    assert usage == 7 / 8 and drop == 1 / 8
+    y = O.combine(np.arange(7.0)[:, None] + 1.0, d.row_of, np.ones((4, 2)))
+    assert y[:, 0].tolist() == [1 + 5, 3 + 6, 2 + 7, 4]   # token 3 keeps only its E1 row
+
+
+def pin_capacity_dense_equivalence():
+    """With a capacity, the sparse layer equals the dense brute force whose
+    gates are zeroed on each expert's slots past C (in token order), for all
+    gate modes, with and without a shared expert; a capacity that no expert
+    reaches changes nothing."""
+    rng = np.random.default_rng(14)
+    for mode, shared, cf in ((O.MODE_SOFTMAX_RENORM, False, 0.75), (O.MODE_SOFTMAX_FULL, True, 1.0),
+                             (O.MODE_SIGMOID_BIAS_RENORM, True, 0.5)):
+        h, wr, wg, wu, wd, sh = _rand_inputs(rng, 24, 6, 5, 7, shared)
+        b = rng.uniform(-0.1, 0.1, 5) if mode == O.MODE_SIGMOID_BIAS_RENORM else None
+        W_ = O.weights_getter(wg, wu, wd)
+        sparse = O.layer(h, wr, 2, mode, W_, b_select=b, shared=sh, capacity_factor=cf)
+        dense = O.dense_layer(h, wr, 2, mode, W_, b_select=b, shared=sh, capacity_factor=cf)
+        assert np.allclose(sparse.y, dense, rtol=0, atol=1e-12)
+        assert (sparse.disp.row_of < 0).any()
+        free = O.layer(h, wr, 2, mode, W_, b_select=b, shared=sh)
+        big = O.layer(h, wr, 2, mode, W_, b_select=b, shared=sh, capacity_factor=5.0)
+        assert np.array_equal(big.y, free.y)
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

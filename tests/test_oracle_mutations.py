@@ -10,7 +10,7 @@ import pins
 from oracle import moe_oracle as O
 
 _orig = {n: getattr(O, n) for n in ("router_logits", "softmax", "sigmoid", "topk", "group_limit",
-                                     "dispatch", "silu", "expert_ffn", "combine",
+                                     "dispatch", "expert_capacity", "silu", "expert_ffn", "combine",
                                      "load_stats", "route", "router_z_loss", "routing_entropy")}
 
 
@@ -88,6 +88,34 @@ def _group_keep_worst(sel, n_groups, topk_groups, topm):
         np.full(np.asarray(sel).shape[0], np.inf)
 
 
+def _dispatch_drop_earliest(ids, N, capacity=None):
+    d = _orig["dispatch"](ids, N, None)
+    if capacity is None:
+        return d
+    flat = np.asarray(ids).reshape(-1)
+    buckets = [np.nonzero(flat == e)[0] for e in range(N)]
+    buckets = [b[max(0, len(b) - capacity):] for b in buckets]
+    kept = np.array([len(b) for b in buckets])
+    offsets = np.concatenate([[0], np.cumsum(kept)])
+    perm = np.concatenate(buckets).astype(np.int64)
+    row_of = np.full(flat.size, -1)
+    row_of[perm] = np.arange(perm.size)
+    return O.Dispatch(d.counts, offsets, perm, row_of, kept)
+
+
+def _combine_negative_row(out_rows, row_of, gates, has_shared=False):
+    gates = np.asarray(gates, float)
+    T, k = gates.shape
+    out_rows = np.asarray(out_rows, float)
+    y = np.zeros((T, out_rows.shape[1]))
+    if has_shared:
+        y += out_rows[T * k:T * k + T]
+    rows = np.asarray(row_of).reshape(T, k)
+    for j in range(k):
+        y += gates[:, j:j + 1] * out_rows[rows[:, j]]
+    return y
+
+
 MUTATIONS = {
     "logits_drop_bias": ("router_logits", lambda h, w, b=None: _orig["router_logits"](h, w, None)),
     "logits_expert_index_reversed": ("router_logits", _logits_reversed),
@@ -111,6 +139,9 @@ MUTATIONS = {
     "z_loss_not_squared": ("router_z_loss", lambda z: float(np.mean(scipy.special.logsumexp(np.asarray(z, float), axis=-1)))),
     "z_loss_sum_not_mean": ("router_z_loss", lambda z: _orig["router_z_loss"](z) * np.asarray(z).shape[0]),
     "entropy_log2": ("routing_entropy", lambda q: _orig["routing_entropy"](q) / math.log(2)),
+    "capacity_drops_earliest": ("dispatch", _dispatch_drop_earliest),
+    "capacity_floor": ("expert_capacity", lambda cf, T, k, N: int(math.floor(float(np.float32(cf)) * (T * k) / N))),
+    "combine_dropped_slot_wraps": ("combine", _combine_negative_row),
     "stats_f_over_T": ("load_stats", lambda c, sp, k, a: _orig["load_stats"](c, sp, 1, a)),
     "stats_no_N_factor": ("load_stats", lambda c, sp, k, a: (lambda f, p, l: (f, p, l / np.asarray(sp).shape[1]))(*_orig["load_stats"](c, sp, k, a))),
 }
