@@ -20,6 +20,11 @@ inputs are already resident in HBM. Prints ONE JSON line.
             while the kernel sources match the ones that were counted
   decode    the same layer at a decode batch (16 tokens) on the same
             weights: tokens/s and HBM GB/s of the touched experts' weights
+  variants  the fine-grained skewed layer (128 experts, top-8) dropless and
+            with expert capacity 1.25 (capacity usage, dropped fraction),
+            and the DeepSeek-V3-shaped layer without and with group-limited
+            selection: tokens/s, stage times, gate/up MFMA rate over the rows
+            computed, router z-loss and routing entropy
   cpu_baseline  the float64 oracle on a bounded sample of the workload,
             timed on this host's cores (a reported baseline, not a target)
 """
@@ -44,6 +49,7 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 GEMM_SOURCES = ("gemm_bf16.hip", "common.hpp", "kernels.hpp")
+VARIANTS = (W.QWEN3_30B, W.QWEN3_30B_CAP, W.DEEPSEEK_V3, W.DEEPSEEK_V3_GROUPED)
 
 
 def gemm_source_hash():
@@ -121,7 +127,9 @@ def hip_events(n):
 def run_layer(M, torch, w, inp, steps, warmup):
     """warmup untimed steps, then `steps` timed steps; the library records
     six HIP events per timed step on its stream at the stage boundaries."""
-    s = M.Shape(w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.mode, w.aux_alpha)
+    g = w.groups or (0, 0, 0)
+    s = M.Shape(w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.mode, w.aux_alpha, *g,
+                capacity_factor=w.capacity_factor)
     layer = M.MoELayer(s)
     args = dict(b_router=inp["b_router"], b_select=inp["b_select"], sh_gate=inp["sh_gate"],
                 sh_up=inp["sh_up"], sh_down=inp["sh_down"])
@@ -148,6 +156,8 @@ def run_layer(M, torch, w, inp, steps, warmup):
         total += elapsed(e[0], e[5]) / steps
     destroy()
     counts = res["counts"].cpu().numpy()
+    run_layer.last = {k_: v.cpu().numpy() for k_, v in res.items()
+                      if k_ in ("cap_stats", "z_loss", "entropy", "l_aux")}
     return wall, stage, total, counts
 
 
@@ -172,6 +182,40 @@ def layer_work(w, counts):
     wbytes = (touched * 3 * w.d_ff * w.d + 3 * w.d_ff_shared * w.d) * eb
     return flops, wbytes, touched
 
+
+
+def kept_counts(w, counts):
+    """Rows each expert computes: all routed slots, or at most C of them."""
+    if not w.capacity_factor:
+        return counts
+    C = math.ceil(float(np.float32(w.capacity_factor)) * (w.T * w.k) / w.N)
+    return np.minimum(counts, C)
+
+
+def run_variant(M, torch, w, steps, warmup):
+    """One workload of the variant list: whole-layer throughput, stage times
+    and the gate/up GEMM's MFMA rate over the rows it computes."""
+    inp = W.device_inputs(w)
+    torch.cuda.synchronize()
+    wall, stage, _, counts = run_layer(M, torch, w, inp, steps, warmup)
+    extra = run_layer.last
+    kept = kept_counts(w, counts)
+    flops_gu, _, touched = gateup_work(w, kept)
+    gu = flops_gu / (stage["gate_up"] * 1e-3) / 1e12
+    out = {"workload": w.name, "tokens_per_s": w.T * steps / wall,
+           "ms_per_step": wall / steps * 1e3, "stages_ms": stage,
+           "gate_up_tflops": gu, "gate_up_frac_mfma_peak": gu / PEAK_BF16_TFLOPS,
+           "rows_computed": int(kept.sum()), "experts_touched": touched,
+           "z_loss": float(extra["z_loss"][0]), "entropy": float(extra["entropy"][0])}
+    if w.capacity_factor:
+        out.update(capacity_factor=w.capacity_factor, capacity_usage=float(extra["cap_stats"][0]),
+                   dropped_fraction=float(extra["cap_stats"][1]))
+    if w.groups:
+        out["groups"] = {"n_groups": w.groups[0], "topk_groups": w.groups[1],
+                         "group_topm": w.groups[2]}
+    del inp
+    torch.cuda.empty_cache()
+    return out
 
 def cpu_baseline(w, inp, sample_tokens, min_seconds=10.0, max_reps=5):
     """The float64 oracle on the first `sample_tokens` tokens (routing,
@@ -225,6 +269,8 @@ def main():
                     help="tokens of the workload the CPU baseline runs (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the capacity / group-limited / fine-grained variant workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     a = ap.parse_args()
@@ -299,6 +345,11 @@ def main():
                          "hbm_gbs_layer": dbytes / (dms * 1e-3) / 1e9,
                          "frac_hbm_peak_layer": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "stages_ms": dstage}
+    if not a.no_variants:
+        del inp
+        torch.cuda.empty_cache()
+        out["variants"] = [run_variant(M, torch, v, a.steps, a.warmup) for v in VARIANTS]
+        inp = W.device_inputs(w)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_sample)
     print(json.dumps(out), flush=True)

@@ -22,6 +22,9 @@
  *   load statistics f_i, p_i, L_aux = α·N·Σ f_i p_i
  *                   [page "拆解 MoE：单个 Token 如何经过专家层" (feinterview),
  *                    load-balance section]
+ *   capacity        optional: each expert keeps at most C = ⌈cf·T·k/N⌉ slots,
+ *                   the earliest in token order; the rest are dropped
+ *                   [wuhy-notes §六 Expert Capacity]
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless noted; `stream` is a hipStream_t
@@ -51,7 +54,8 @@
  *                           fit N (see moe_shape), unknown dtype or
  *                           mode, a required pointer NULL, b_select given in
  *                           modes A/B or missing in mode C, misaligned
- *                           pointer, non-finite aux_alpha;
+ *                           pointer, non-finite aux_alpha, capacity_factor
+ *                           not finite or outside [0, N];
  *      MOE_ERR_UNSUPPORTED  N > 512, k > 16, more than 64 groups or a group
  *                           score over more than 8 experts, bf16 with d, d_ff or d_ff_shared
  *                           not a multiple of 64, or sizes whose element
@@ -72,7 +76,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_GROUPS 64
@@ -126,6 +130,13 @@ typedef struct {
   int32_t n_groups;     /* 0, or 1..64 dividing N                              */
   int32_t topk_groups;  /* 1..n_groups, with topk_groups·N/n_groups >= k      */
   int32_t group_topm;   /* 1..min(8, N/n_groups)                               */
+  /* Expert capacity [wuhy-notes §六 Expert Capacity]: 0 = dropless; else
+   * each expert keeps at most C = ceil(capacity_factor·T·k/N) slots
+   * (evaluated in double precision), the first C in token order, and
+   * the later slots are dropped: they get no expert row and add nothing to
+   * y. f_i, p_i and L_aux still describe the routing (dropped slots count
+   * in f_i). Must lie in [0, N]; any factor >= N/k keeps every slot. */
+  float capacity_factor;
 } moe_shape;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION). */
@@ -176,29 +187,40 @@ moe_status moe_route(const moe_shape* s, const void* h, const void* w_router,
 /* Dispatch: stable regroup of the T·k flat slots f = t·k + j by expert.
  *   topk_ids [T, k] int32 in, every id in [0, N) (precondition; not checked
  *            on the device)
- *   counts   [N]   int32 out: rows per expert
- *   offsets  [N+1] int32 out: exclusive prefix of counts (offsets[N] = T·k)
- *   perm_src [T·k] int32 out: bucket row r -> flat slot; expert e's rows are
- *            offsets[e]..offsets[e+1]-1, in ascending slot (= token) order
- *   row_of   [T·k] int32 out: flat slot -> bucket row (inverse of perm_src)
+ *   counts   [N]   int32 out: slots routed to each expert (before capacity)
+ *   offsets  [N+1] int32 out: exclusive prefix of the KEPT counts
+ *            kept_e = min(counts_e, C) (no capacity: kept = counts and
+ *            offsets[N] = T·k)
+ *   perm_src [T·k] int32 out: bucket row r -> flat slot for r < offsets[N];
+ *            expert e's rows are offsets[e]..offsets[e+1]-1, in ascending
+ *            slot (= token) order; entries from offsets[N] on are untouched
+ *   row_of   [T·k] int32 out: flat slot -> bucket row (inverse of perm_src),
+ *            -1 for a slot dropped by the capacity
  *   p_mean   [N] fp32 in, nullable (needed only for l_aux)
  *   f_out    [N] fp32 out, nullable: f_i = counts_i / (T·k)
  *   l_aux    [1] fp32 out, nullable (requires p_mean): α·N·Σ f_i p_i
+ *   cap_stats [2] fp32 out, nullable: capacity usage Σ_e kept_e / (N·C) and
+ *            the dropped fraction (T·k − Σ_e kept_e) / (T·k), each the fp32
+ *            rounding of the exact ratio; both 0 without a capacity
+ *            [wuhy-notes, monitoring list: capacity usage, dropped tokens]
  * Deterministic: no atomic decides any order or any float sum.
- * [wuhy-notes §三 Token Dispatch; horizon.auto §3 ②; feinterview
- *  load-balance section] */
+ * [wuhy-notes §三 Token Dispatch, §六 Expert Capacity; horizon.auto §3 ②;
+ *  feinterview load-balance section] */
 moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src,
                         int32_t* row_of, const float* p_mean, float* f_out,
-                        float* l_aux, void* ws, size_t ws_bytes, void* stream);
+                        float* l_aux, float* cap_stats, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* Experts: grouped SwiGLU FFN over the dispatched rows (steps 5-6).
  *   out_rows [T·k (+T if d_ff_shared), d] dtype out:
  *     out_rows[r] = E_e(h[perm_src[r] / k]) for bucket row r of expert e;
  *     out_rows[T·k + t] = E_shared(h[t]) when a shared expert is present.
  *   sh_gate/sh_up/sh_down must be given iff d_ff_shared > 0.
- *   offsets [N+1] as written by moe_dispatch (non-decreasing, offsets[0] = 0,
- *   offsets[N] = T·k; precondition, not checked on the device).
+ *   offsets [N+1] as written by moe_dispatch with the same shape
+ *   (non-decreasing, offsets[0] = 0, offsets[N] <= T·k, at most min(T, C)
+ *   rows per expert; precondition, not checked on the device). Rows from
+ *   offsets[N] to T·k−1 of out_rows are not written.
  * Bitwise reproducible: work is spread over the GPU dynamically, but every
  * output element is computed by the same sequence of operations; K-split
  * partial sums are added in split order.
@@ -213,7 +235,8 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* h,
 
 /* Combine: y[t] = out_rows[T·k + t] (shared, if any) +
  *          Σ_{j<k} topk_gates[t, j] · out_rows[row_of[t·k + j]],
- * accumulated in fp32 in that order, stored as dtype.
+ * accumulated in fp32 in that order, stored as dtype; a slot with
+ * row_of = -1 (dropped by the capacity) adds nothing.
  * [cooking-agi, "选好以后，token 怎么过去，输出怎么回来？"; horizon.auto §3 ④] */
 moe_status moe_combine(const moe_shape* s, const void* out_rows,
                        const int32_t* row_of, const float* topk_gates,
@@ -222,9 +245,9 @@ moe_status moe_combine(const moe_shape* s, const void* out_rows,
 /* The whole layer in one call (route, dispatch, experts, combine, stats),
  * no host synchronisation inside.
  *   y [T, d] dtype out (required).
- *   topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss, entropy:
- *   nullable outputs as in moe_route / moe_dispatch (the workspace holds
- *   whatever is not returned). */
+ *   topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss, entropy,
+ *   cap_stats: nullable outputs as in moe_route / moe_dispatch (the
+ *   workspace holds whatever is not returned). */
 moe_status moe_layer_fused(const moe_shape* s, const void* h,
                            const void* w_router, const float* b_router,
                            const float* b_select, const void* w_gate,
@@ -233,8 +256,8 @@ moe_status moe_layer_fused(const moe_shape* s, const void* h,
                            const void* sh_down, void* y, int32_t* topk_ids,
                            float* topk_gates, int32_t* counts, float* f_out,
                            float* p_out, float* l_aux, float* z_loss,
-                           float* entropy, void* ws, size_t ws_bytes,
-                           void* stream);
+                           float* entropy, float* cap_stats, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* moe_layer_fused that also records caller-created hipEvent_t handles on
  * `stream` at the stage boundaries, for timing: events[0] before routing,
@@ -250,8 +273,8 @@ moe_status moe_layer_fused_marked(const moe_shape* s, const void* h,
                                   int32_t* topk_ids, float* topk_gates,
                                   int32_t* counts, float* f_out, float* p_out,
                                   float* l_aux, float* z_loss, float* entropy,
-                                  void* ws, size_t ws_bytes, void* stream,
-                                  void* const* events);
+                                  float* cap_stats, void* ws, size_t ws_bytes,
+                                  void* stream, void* const* events);
 
 #ifdef __cplusplus
 }

@@ -32,20 +32,21 @@ class MoEError(RuntimeError):
 
 
 class Shape(ctypes.Structure):
-    """moe_shape: sizes, dtype, gate mode, L_aux alpha and the optional group
+    """moe_shape: sizes, dtype, gate mode, L_aux alpha, the optional group
     limit (n_groups contiguous expert groups, the topk_groups best by the sum
-    of their group_topm largest selection scores stay candidates)."""
+    of their group_topm largest selection scores stay candidates) and the
+    optional expert capacity factor (0 = dropless)."""
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("aux_alpha", ctypes.c_float),
                 ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
-                ("group_topm", ctypes.c_int32)]
+                ("group_topm", ctypes.c_int32), ("capacity_factor", ctypes.c_float)]
 
     def __init__(self, T, d, N, k, d_ff, d_ff_shared=0, dtype=BF16, mode=SOFTMAX_RENORM,
-                 aux_alpha=0.01, n_groups=0, topk_groups=0, group_topm=0):
+                 aux_alpha=0.01, n_groups=0, topk_groups=0, group_topm=0, capacity_factor=0.0):
         super().__init__(T, d, N, k, d_ff, d_ff_shared, dtype, mode, aux_alpha, n_groups,
-                         topk_groups, group_topm)
+                         topk_groups, group_topm, capacity_factor)
 
 
 _lib = None
@@ -56,11 +57,11 @@ _SIG = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 9 + [_P, ctypes.c_size_t, _P]),
-    "moe_dispatch": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]),
+    "moe_dispatch": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 9 + [_P, ctypes.c_size_t, _P]),
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 10 + [_P, ctypes.c_size_t, _P]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 5),
-    "moe_layer_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 19 + [_P, ctypes.c_size_t, _P]),
-    "moe_layer_fused_marked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 19
+    "moe_layer_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 20 + [_P, ctypes.c_size_t, _P]),
+    "moe_layer_fused_marked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 20
                                + [_P, ctypes.c_size_t, _P, _P]),
 }
 
@@ -121,10 +122,11 @@ def route(shape, h, w_router, b_router, b_select, topk_ids, topk_gates, p_mean, 
 
 
 def dispatch(shape, topk_ids, counts, offsets, perm_src, row_of, p_mean=None, f_out=None,
-             l_aux=None, ws=None, ws_bytes=0, stream=None):
+             l_aux=None, ws=None, ws_bytes=0, stream=None, cap_stats=None):
     _check(lib().moe_dispatch(ctypes.byref(shape), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
                               _ptr(perm_src), _ptr(row_of), _ptr(p_mean), _ptr(f_out),
-                              _ptr(l_aux), _ptr(ws), ws_bytes, _stream(stream)), "moe_dispatch")
+                              _ptr(l_aux), _ptr(cap_stats), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_dispatch")
 
 
 def expert_ffn(shape, h, perm_src, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
@@ -143,11 +145,12 @@ def combine(shape, out_rows, row_of, topk_gates, y, stream=None):
 def layer_fused(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                 sh_down, y, topk_ids=None, topk_gates=None, counts=None, f_out=None,
                 p_out=None, l_aux=None, ws=None, ws_bytes=0, stream=None, events=None,
-                z_loss=None, entropy=None):
+                z_loss=None, entropy=None, cap_stats=None):
     args = (ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(b_select),
             _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),
             _ptr(y), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _ptr(f_out), _ptr(p_out),
-            _ptr(l_aux), _ptr(z_loss), _ptr(entropy), _ptr(ws), ws_bytes, _stream(stream))
+            _ptr(l_aux), _ptr(z_loss), _ptr(entropy), _ptr(cap_stats), _ptr(ws), ws_bytes,
+            _stream(stream))
     if events is None:
         _check(lib().moe_layer_fused(*args), "moe_layer_fused")
     else:
@@ -182,9 +185,11 @@ class MoELayer:
                        p=torch.empty(s.N, dtype=torch.float32, device=dev),
                        l_aux=torch.empty(1, dtype=torch.float32, device=dev),
                        z_loss=torch.empty(1, dtype=torch.float32, device=dev),
-                       entropy=torch.empty(1, dtype=torch.float32, device=dev))
+                       entropy=torch.empty(1, dtype=torch.float32, device=dev),
+                       cap_stats=torch.empty(2, dtype=torch.float32, device=dev))
         layer_fused(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                     sh_down, y, res.get("topk_ids"), res.get("topk_gates"), res.get("counts"),
                     res.get("f"), res.get("p"), res.get("l_aux"), self.ws, self.ws_bytes,
-                    events=events, z_loss=res.get("z_loss"), entropy=res.get("entropy"))
+                    events=events, z_loss=res.get("z_loss"), entropy=res.get("entropy"),
+                    cap_stats=res.get("cap_stats"))
         return res

@@ -44,6 +44,9 @@ moe_status check_shape(const moe_shape* s) {
   if (s->mode < MOE_GATE_SOFTMAX_RENORM || s->mode > MOE_GATE_SIGMOID_BIAS_RENORM)
     return fail(MOE_ERR_INVALID_ARG, "unknown gate mode");
   if (!std::isfinite(s->aux_alpha)) return fail(MOE_ERR_INVALID_ARG, "aux_alpha is not finite");
+  if (!std::isfinite(s->capacity_factor) || s->capacity_factor < 0.0f ||
+      s->capacity_factor > (float)s->N)
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite and in [0, N]");
   if (s->k > s->N) return fail(MOE_ERR_INVALID_ARG, "k > N: not enough candidate experts");
   if (s->N > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "N > 512");
   if (s->k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k > 16");
@@ -73,6 +76,16 @@ moe_status check_shape(const moe_shape* s) {
   for (int64_t v : lim)
     if (v > kI32Max) return fail(MOE_ERR_UNSUPPORTED, "a tensor exceeds 2^31-1 elements");
   return MOE_OK;
+}
+
+// Expert capacity C = ceil(capacity_factor * T * k / N) in double precision,
+// 0 for dropless [wuhy-notes §六 Expert Capacity]. capacity_factor <= N keeps
+// C <= T * k.
+int expert_capacity(const moe_shape* s) {
+  if (s->capacity_factor == 0.0f) return 0;
+  const double c = std::ceil((double)s->capacity_factor * (double)((int64_t)s->T * s->k) /
+                             (double)s->N);
+  return (int)c;
 }
 
 moe_status need(const void* p, const char* name) {
@@ -256,9 +269,11 @@ moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
 
 moe_status dispatch_impl(const moe_shape* s, const int32_t* ids, int32_t* counts,
                          int32_t* offsets, int32_t* perm_src, int32_t* row_of,
-                         const float* p_mean, float* f_out, float* l_aux, hipStream_t st) {
+                         const float* p_mean, float* f_out, float* l_aux, float* cap_stats,
+                         hipStream_t st) {
   return hip_check(moe::launch_dispatch(ids, s->T, s->k, s->N, counts, offsets, perm_src, row_of,
-                                        p_mean, f_out, l_aux, s->aux_alpha, st),
+                                        p_mean, f_out, l_aux, s->aux_alpha, expert_capacity(s),
+                                        cap_stats, st),
                    "dispatch");
 }
 
@@ -273,6 +288,11 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
   int32_t* part_cnt = part ? at<int32_t>(ws, W.cnt) : nullptr;
   const int64_t part_floats = part ? (int64_t)((W.cnt - W.part) / sizeof(float)) : 0;
   const int R = T * s->k;
+  // bounds on the routed rows: all of them and T per expert, or what the
+  // capacity keeps
+  const int C = expert_capacity(s);
+  const int rows_all = C ? (int)std::min<int64_t>(R, (int64_t)s->N * C) : R;
+  const int rows_max = C ? std::min(T, C) : T;
   const bool bf16 = s->dtype == MOE_BF16;
   const int ncu = bf16 ? num_cu() : 0;
   const size_t esz = esize(s);
@@ -283,8 +303,8 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
   };
   moe::GroupedProblem p{};
   if (gateup) {
-    p = moe::GroupedProblem{h, d, perm_src, s->k, offsets, s->N, R, T, w_gate, w_up,
-                            (int64_t)dff * d, d, dff, d, act, dff, 0, (uint32_t)(esz * T * d),
+    p = moe::GroupedProblem{h, d, perm_src, s->k, offsets, s->N, rows_all, rows_max, w_gate,
+                            w_up, (int64_t)dff * d, d, dff, d, act, dff, 0, (uint32_t)(esz * T * d),
                             part, part_cnt, part_floats};
     TRY(hip_check(run(p, true), "gate/up GEMM"));
     if (dfs) {
@@ -294,8 +314,8 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
       TRY(hip_check(run(p, true), "shared gate/up GEMM"));
     }
   } else {
-    p = moe::GroupedProblem{act, dff, nullptr, 1, offsets, s->N, R, T, w_down, nullptr,
-                            (int64_t)d * dff, dff, d, dff, out_rows, d, 0, (uint32_t)(esz * R * dff),
+    p = moe::GroupedProblem{act, dff, nullptr, 1, offsets, s->N, rows_all, rows_max, w_down,
+                            nullptr, (int64_t)d * dff, dff, d, dff, out_rows, d, 0, (uint32_t)(esz * R * dff),
                             part, part_cnt, part_floats};
     TRY(hip_check(run(p, false), "down GEMM"));
     if (dfs) {
@@ -325,8 +345,8 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
                       const void* w_up, const void* w_down, const void* sh_gate,
                       const void* sh_up, const void* sh_down, void* y, int32_t* topk_ids,
                       float* topk_gates, int32_t* counts, float* f_out, float* p_out,
-                      float* l_aux, float* z_loss, float* entropy, void* ws, size_t ws_bytes,
-                      void* stream, void* const* events) {
+                      float* l_aux, float* z_loss, float* entropy, float* cap_stats, void* ws,
+                      size_t ws_bytes, void* stream, void* const* events) {
   TRY(check_shape(s));
   TRY(need16(h, "h"));
   TRY(need16(w_router, "w_router"));
@@ -344,6 +364,7 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   TRY(opt4(l_aux, "l_aux"));
   TRY(opt4(z_loss, "z_loss"));
   TRY(opt4(entropy, "entropy"));
+  TRY(opt4(cap_stats, "cap_stats"));
   if (events)
     for (int i = 0; i < 6; ++i)
       if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[] holds a NULL event");
@@ -366,7 +387,7 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   TRY(route_impl(s, h, w_router, b_router, b_select, ids, gates, p_mean, z_loss, entropy, L.r,
                  ws, st));
   TRY(mark(events, 1, st));
-  TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, st));
+  TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, cap_stats, st));
   TRY(mark(events, 2, st));
   TRY(ffn_stage(s, true, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
                 ws, L.x, st));
@@ -426,8 +447,8 @@ moe_status moe_route(const moe_shape* s, const void* h, const void* w_router,
 
 moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids, int32_t* counts,
                         int32_t* offsets, int32_t* perm_src, int32_t* row_of,
-                        const float* p_mean, float* f_out, float* l_aux, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        const float* p_mean, float* f_out, float* l_aux, float* cap_stats,
+                        void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
   g_err.clear();
@@ -440,10 +461,11 @@ moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids, int32_t* co
   TRY(opt4(p_mean, "p_mean"));
   TRY(opt4(f_out, "f_out"));
   TRY(opt4(l_aux, "l_aux"));
+  TRY(opt4(cap_stats, "cap_stats"));
   if (l_aux && !p_mean) return fail(MOE_ERR_INVALID_ARG, "l_aux requested without p_mean");
   if (s->T == 0) return MOE_OK;
   return dispatch_impl(s, topk_ids, counts, offsets, perm_src, row_of, p_mean, f_out, l_aux,
-                       static_cast<hipStream_t>(stream));
+                       cap_stats, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_expert_ffn(const moe_shape* s, const void* h, const int32_t* perm_src,
@@ -488,12 +510,12 @@ moe_status moe_layer_fused(const moe_shape* s, const void* h, const void* w_rout
                            const void* w_up, const void* w_down, const void* sh_gate,
                            const void* sh_up, const void* sh_down, void* y, int32_t* topk_ids,
                            float* topk_gates, int32_t* counts, float* f_out, float* p_out,
-                           float* l_aux, float* z_loss, float* entropy, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           float* l_aux, float* z_loss, float* entropy, float* cap_stats,
+                           void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                     sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss,
-                    entropy, ws, ws_bytes, stream, nullptr);
+                    entropy, cap_stats, ws, ws_bytes, stream, nullptr);
 }
 
 moe_status moe_layer_fused_marked(const moe_shape* s, const void* h, const void* w_router,
@@ -502,13 +524,13 @@ moe_status moe_layer_fused_marked(const moe_shape* s, const void* h, const void*
                                   const void* sh_gate, const void* sh_up, const void* sh_down,
                                   void* y, int32_t* topk_ids, float* topk_gates,
                                   int32_t* counts, float* f_out, float* p_out, float* l_aux,
-                                  float* z_loss, float* entropy, void* ws, size_t ws_bytes,
-                                  void* stream, void* const* events) {
+                                  float* z_loss, float* entropy, float* cap_stats, void* ws,
+                                  size_t ws_bytes, void* stream, void* const* events) {
   g_err.clear();
   if (!events) return fail(MOE_ERR_INVALID_ARG, "events is NULL");
   return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                     sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss,
-                    entropy, ws, ws_bytes, stream, events);
+                    entropy, cap_stats, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

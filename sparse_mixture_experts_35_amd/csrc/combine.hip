@@ -4,6 +4,9 @@
 // "MoE：router 怎样选 expert" (cooking-agi), section on how outputs come
 // back; page "【大模型】MoE（专家混合模型）简介" (horizon.auto), §3 ④ Gather].
 //
+// A slot dropped by the expert capacity (row_of = -1) adds nothing [page
+// "MOE 专家选择与路由机制" (wuhy-notes), §六 Expert Capacity].
+//
 // One block per token; each thread owns 16-byte column chunks and reads the
 // k rows (and the shared row) at those columns, so every load is coalesced;
 // fp32 accumulation in slot order; no atomics.
@@ -32,6 +35,7 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     }
     for (int j = 0; j < k; ++j) {
       const int64_t r = row_of[(int64_t)t * k + j];
+      if (r < 0) continue;
       const float g = gates[(int64_t)t * k + j];
       float v[8];
       unpack_bf16x8(*reinterpret_cast<const u32x4*>(rows + r * d + c), v);
@@ -55,6 +59,7 @@ __global__ __launch_bounds__(kThreads) void combine_f32_kernel(
     float acc = has_shared ? rows[(R + t) * d + c] : 0.0f;
     for (int j = 0; j < k; ++j) {
       const int64_t r = row_of[(int64_t)t * k + j];
+      if (r < 0) continue;
       acc = fmaf(gates[(int64_t)t * k + j], rows[r * d + c], acc);
     }
     y[(int64_t)t * d + c] = acc;

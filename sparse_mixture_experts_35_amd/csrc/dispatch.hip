@@ -15,9 +15,15 @@
 // of expert e's slots at its stable rank. No atomic decides any position and
 // no float is summed by an atomic.
 //
+// Expert capacity [wuhy-notes §六 Expert Capacity]: with a capacity C, expert
+// e keeps its first kept_e = min(counts_e, C) slots in that order; offsets
+// are the prefix of the kept counts and a later slot gets row_of = -1.
+//
 // Statistics [page "拆解 MoE：单个 Token 如何经过专家层" (feinterview),
-// load-balance section]: f_e = counts_e / (T·k); block 0 also forms
-// L_aux = α·N·Σ_e f_e p_e with a fixed-order reduction.
+// load-balance section]: f_e = counts_e / (T·k) (the routing, before any
+// drop); block 0 also forms L_aux = α·N·Σ_e f_e p_e with a fixed-order
+// reduction, and the capacity usage and dropped fraction from the exact
+// integer total of kept slots [wuhy-notes, monitoring list].
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -50,12 +56,14 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const int32_t* __restrict__ ids, int T, int k, int N, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ row_of,
     const float* __restrict__ p_mean, float* __restrict__ f_out, float* __restrict__ l_aux,
-    float alpha) {
+    float alpha, int cap_in, float* __restrict__ cap_stats) {
   __shared__ int s_hist[512];
   __shared__ int s_wave[4];
   __shared__ float s_red[kThreads];
   const int e = blockIdx.x, tid = threadIdx.x;
   const int R = T * k;
+  const bool limited = cap_in > 0;
+  const int cap = limited ? cap_in : 0x7fffffff;
 
   for (int i = tid; i < N; i += kThreads) s_hist[i] = 0;
   __syncthreads();
@@ -65,18 +73,32 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
   }
   __syncthreads();
 
-  // offsets[e] = sum of the counts of experts below e
+  // offsets[e] = sum of the kept counts of experts below e
   int part = 0;
-  for (int i = tid; i < e; i += kThreads) part += s_hist[i];
+  for (int i = tid; i < e; i += kThreads) part += min(s_hist[i], cap);
   int total;
   block_excl_scan(part, s_wave, total);
   const int off_e = total;
   const int cnt_e = s_hist[e];
+  const int kept_e = min(cnt_e, cap);
   if (tid == 0) {
     counts[e] = cnt_e;
     offsets[e] = off_e;
-    if (e == N - 1) offsets[N] = off_e + cnt_e;
+    if (e == N - 1) offsets[N] = off_e + kept_e;
     if (f_out) f_out[e] = (float)cnt_e / (float)R;
+  }
+
+  if (e == 0 && cap_stats) {
+    // usage = sum kept / (N C), dropped = (T k - sum kept) / (T k); the
+    // integer total is exact, each ratio one double division rounded once
+    int kp = 0;
+    for (int i = tid; i < N; i += kThreads) kp += min(s_hist[i], cap);
+    int kept_all;
+    block_excl_scan(kp, s_wave, kept_all);
+    if (tid == 0) {
+      cap_stats[0] = limited ? (float)((double)kept_all / ((double)N * (double)cap)) : 0.0f;
+      cap_stats[1] = limited ? (float)((double)(R - kept_all) / (double)R) : 0.0f;
+    }
   }
 
   if (e == 0 && l_aux) {
@@ -92,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     if (tid == 0) l_aux[0] = alpha * (float)N * s_red[0];
   }
 
-  // stable placement of expert e's slots
+  // stable placement of expert e's slots; ranks from kept_e on are dropped
   int placed = 0;
   for (int base = 0; base < R && placed < cnt_e; base += kChunk) {
     const int f0 = base + tid * kPerThread;
@@ -109,8 +131,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i)
       if (match[i]) {
-        perm_src[pos] = f0 + i;
-        row_of[f0 + i] = pos;
+        if (pos < off_e + kept_e) {
+          perm_src[pos] = f0 + i;
+          row_of[f0 + i] = pos;
+        } else {
+          row_of[f0 + i] = -1;
+        }
         ++pos;
       }
     placed += chunk_total;
@@ -122,9 +148,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N, int32_t* counts,
                            int32_t* offsets, int32_t* perm_src, int32_t* row_of,
                            const float* p_mean, float* f_out, float* l_aux, float alpha,
-                           hipStream_t st) {
+                           int cap, float* cap_stats, hipStream_t st) {
   hipLaunchKernelGGL(dispatch_kernel, dim3(N), dim3(kThreads), 0, st, ids, T, k, N, counts,
-                     offsets, perm_src, row_of, p_mean, f_out, l_aux, alpha);
+                     offsets, perm_src, row_of, p_mean, f_out, l_aux, alpha, cap, cap_stats);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ __global__ void gateup_f32_kernel(GroupedProblem p) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)p.M * p.Ncols) return;
   const int r = (int)(idx / p.Ncols), n = (int)(idx % p.Ncols);
+  if (p.offsets && r >= p.offsets[p.groups]) return;   // rows past the last group
   const int g = group_of(p.offsets, p.groups, r);
   const int src = p.perm ? p.perm[r] / p.kdiv : r;
   const float* a = static_cast<const float*>(p.A) + (int64_t)src * p.lda;
@@ -41,6 +42,7 @@ __global__ void down_f32_kernel(GroupedProblem p) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)p.M * p.Ncols) return;
   const int r = (int)(idx / p.Ncols), n = (int)(idx % p.Ncols);
+  if (p.offsets && r >= p.offsets[p.groups]) return;   // rows past the last group
   const int g = group_of(p.offsets, p.groups, r);
   const int src = p.perm ? p.perm[r] / p.kdiv : r;
   const float* a = static_cast<const float*>(p.A) + (int64_t)src * p.lda;

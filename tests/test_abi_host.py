@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(M.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -63,7 +63,7 @@ def fused(s, **over):
     st = lib.moe_layer_fused(ctypes.byref(s), args["h"], args["w_router"], args["b_router"],
                              args["b_select"], args["w_gate"], args["w_up"], args["w_down"],
                              args["sh_gate"], args["sh_up"], args["sh_down"], args["y"],
-                             None, None, None, None, None, None, None, None, args["ws"],
+                             None, None, None, None, None, None, None, None, None, args["ws"],
                              args["ws_bytes"], None)
     return st, lib.moe_last_error().decode()
 
@@ -91,6 +91,10 @@ def fused(s, **over):
     (dict(n_groups=8, topk_groups=1, group_topm=1), M.ERR_INVALID_ARG, "fewer than k"),
     (dict(N=256, n_groups=128, topk_groups=8, group_topm=1), M.ERR_UNSUPPORTED, "n_groups > 64"),
     (dict(N=256, n_groups=8, topk_groups=4, group_topm=9), M.ERR_UNSUPPORTED, "group_topm > 8"),
+    (dict(capacity_factor=-0.5), M.ERR_INVALID_ARG, "capacity_factor"),
+    (dict(capacity_factor=float("inf")), M.ERR_INVALID_ARG, "capacity_factor"),
+    (dict(capacity_factor=float("nan")), M.ERR_INVALID_ARG, "capacity_factor"),
+    (dict(N=8, capacity_factor=8.5), M.ERR_INVALID_ARG, "capacity_factor"),
 ])
 def test_bad_shapes(kw, want, msg):
     st, err = fused(shape(**kw))
@@ -121,6 +125,18 @@ def test_zero_tokens_is_a_noop():
     s = shape(T=0)
     st, err = fused(s, ws_bytes=M.workspace_bytes(s))
     assert st == M.OK, err
+    s = shape(T=0, capacity_factor=1.25)
+    st, err = fused(s, ws_bytes=M.workspace_bytes(s))
+    assert st == M.OK, err
+
+
+def test_capacity_factor_limits_accepted():
+    """0 (dropless) and every factor up to N validate (checked with T = 0 so
+    that nothing launches)."""
+    for cf in (0.0, 1e-6, 1.0, 1.25, 8.0):
+        s = shape(T=0, capacity_factor=cf)
+        st, err = fused(s, ws_bytes=M.workspace_bytes(s))
+        assert st == M.OK, (cf, err)
 
 
 def test_other_entry_points_validate():
@@ -136,14 +152,16 @@ def test_other_entry_points_validate():
     assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE + 2,
                          None, FAKE, 1 << 40, None) == M.ERR_INVALID_ARG   # misaligned z_loss
     assert lib.moe_dispatch(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
-                            None, 0, None) == M.ERR_INVALID_ARG     # l_aux without p_mean
+                            None, None, 0, None) == M.ERR_INVALID_ARG     # l_aux without p_mean
     assert lib.moe_dispatch(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, None, None, None,
-                            None, 0, None) == M.ERR_INVALID_ARG
+                            None, None, 0, None) == M.ERR_INVALID_ARG
+    assert lib.moe_dispatch(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                            FAKE + 2, None, 0, None) == M.ERR_INVALID_ARG  # misaligned cap_stats
     assert lib.moe_expert_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                               None, FAKE, FAKE, 8, None) == M.ERR_WORKSPACE
     assert lib.moe_combine(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE + 4, None) == M.ERR_INVALID_ARG
     assert lib.moe_layer_fused_marked(ctypes.byref(s), *([FAKE] * 3), None, *([FAKE] * 3),
-                                      None, None, None, FAKE, *([None] * 8), FAKE, 1 << 40, None,
+                                      None, None, None, FAKE, *([None] * 9), FAKE, 1 << 40, None,
                                       None) == M.ERR_INVALID_ARG
 
 

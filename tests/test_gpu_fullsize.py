@@ -26,7 +26,8 @@ pytestmark = pytest.mark.gpu
 
 import sparse_mixture_experts_35_amd as M  # noqa: E402
 
-FULL = [W.MIXTRAL_PREFILL, W.MIXTRAL_PREFILL_R1, W.MIXTRAL_DECODE, W.QWEN3_30B, W.DEEPSEEK_V3]
+FULL = [W.MIXTRAL_PREFILL, W.MIXTRAL_PREFILL_R1, W.MIXTRAL_DECODE, W.QWEN3_30B, W.QWEN3_30B_CAP,
+        W.DEEPSEEK_V3, W.DEEPSEEK_V3_GROUPED]
 # sampled tokens for the end-to-end y check, and experts whose rows are
 # sampled (None: all experts)
 Y_TOKENS = {2: 24, 3: 16, 4: 16, 5: 4}
@@ -63,7 +64,9 @@ def _sample_rows(offsets, experts, rng):
 def test_full_size_layer(w):
     t = torch()
     inp = W.device_inputs(w)
-    s = M.Shape(w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.mode, w.aux_alpha)
+    g = w.groups or (0, 0, 0)
+    s = M.Shape(w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.mode, w.aux_alpha, *g,
+                capacity_factor=w.capacity_factor)
     args = dict(b_router=inp["b_router"], b_select=inp["b_select"], sh_gate=inp["sh_gate"],
                 sh_up=inp["sh_up"], sh_down=inp["sh_down"])
     print(f"\n[{w.name}] fused layer", flush=True)
@@ -79,7 +82,8 @@ def test_full_size_layer(w):
     ids, gates, p = i32(R), f32(R), f32(N)
     M.route(s, inp["h"], inp["w_router"], inp["b_router"], inp["b_select"], ids, gates, p, ws, nws)
     counts, offsets, perm, row_of, fo, la = i32(N), i32(N + 1), i32(R), i32(R), f32(N), f32(1)
-    M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la)
+    cs = f32(2)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la, cap_stats=cs)
     rows_n = R + (T if w.d_ff_shared else 0)
     out_rows = t.empty((rows_n, w.d), dtype=inp["h"].dtype, device="cuda")
     M.expert_ffn(s, inp["h"], perm, offsets, inp["w_gate"], inp["w_up"], inp["w_down"],
@@ -91,21 +95,26 @@ def test_full_size_layer(w):
     assert t.equal(ids.view(T, k), res["topk_ids"])
     assert t.equal(gates.view(T, k), res["topk_gates"])
     assert t.equal(counts, res["counts"]) and t.equal(p, res["p"]) and t.equal(la, res["l_aux"])
+    assert t.equal(cs, res["cap_stats"])
 
     # ---- routing, dispatch and statistics on every token
     h = _np32(inp["h"])
     wr = _np32(inp["w_router"])
     br, bs = _np32(inp["b_router"]), _np32(inp["b_select"])
-    r = O.route(h, wr, k, w.mode, br, bs)
+    r = O.route(h, wr, k, w.mode, br, bs, w.groups)
     g_ids = host(ids).reshape(T, k)
-    near = check_ids(g_ids, r, k)
+    near = check_ids(g_ids, r, k, grouped=w.groups is not None)
     ok = ~near
     check_gates(host(gates).reshape(T, k), r.gates, 1e-4, ok)
-    d = O.dispatch(g_ids, N)
+    cap = O.expert_capacity(w.capacity_factor, T, k, N) if w.capacity_factor else None
+    d = O.dispatch(g_ids, N, cap)
+    kept = int(d.offsets[-1])
     assert np.array_equal(host(counts), d.counts)
     assert np.array_equal(host(offsets), d.offsets)
-    assert np.array_equal(host(perm), d.perm_src)
+    assert np.array_equal(host(perm)[:kept], d.perm_src)
     assert np.array_equal(host(row_of), d.row_of)
+    want = O.capacity_stats(d, cap) if cap else (0.0, 0.0)
+    assert np.array_equal(host(cs), np.float32(want).astype(np.float64)), (host(cs), want)
     f_ref, p_ref, l_ref = O.load_stats(d.counts, r.stat_prob, k, w.aux_alpha)
     assert np.allclose(host(fo), f_ref, rtol=1e-6, atol=0)
     assert np.allclose(host(p), p_ref, rtol=1e-4, atol=1e-7)
@@ -115,15 +124,16 @@ def test_full_size_layer(w):
     assert abs(zl - zl_ref) <= 1e-4 * abs(zl_ref) + 1e-6, (zl, zl_ref)
     assert abs(ent - ent_ref) <= 1e-4 * abs(ent_ref) + 1e-6, (ent, ent_ref)
     print(f"[{w.name}] routing/dispatch/stats exact; near-tie tokens {int(near.sum())} of {T}; "
-          f"rows per expert min/max {d.counts.min()}/{d.counts.max()}", flush=True)
+          f"rows per expert min/max {d.counts.min()}/{d.counts.max()}; "
+          f"kept {kept} of {R} (C = {cap})", flush=True)
 
     # ---- expert rows on sampled rows (one expert's weights at a time)
     rng = np.random.default_rng(w.cfg_id)
-    nz = np.nonzero(d.counts)[0]
+    nz = np.nonzero(d.kept)[0]
     if ROW_EXPERTS[w.cfg_id] is None:
         experts = nz
     else:
-        order = nz[np.argsort(d.counts[nz], kind="stable")]
+        order = nz[np.argsort(d.kept[nz], kind="stable")]
         m = ROW_EXPERTS[w.cfg_id]
         experts = np.unique(np.concatenate([order[:m // 3], order[-(m // 3):],
                                             rng.choice(order, m - 2 * (m // 3), replace=False)]))
@@ -162,14 +172,16 @@ def test_full_size_layer(w):
     for t0 in range(0, T, chunk):
         tt = np.arange(t0, min(T, t0 + chunk))
         idx = d.row_of.reshape(T, k)[tt]
-        need = np.unique(np.concatenate([idx.reshape(-1), (R + tt) if w.d_ff_shared else []]).astype(np.int64))
+        used = idx[idx >= 0]
+        need = np.unique(np.concatenate([used, (R + tt) if w.d_ff_shared else []]).astype(np.int64))
         part = out_rows.index_select(0, t.from_numpy(need).cuda()).float().cpu().numpy()
         pos = {int(v): i for i, v in enumerate(need)}
         yc = np.zeros((tt.size, w.d))
         if w.d_ff_shared:
             yc += part[[pos[R + int(x)] for x in tt]]
         for j in range(k):
-            yc += g_gates[tt, j:j + 1] * part[[pos[int(x)] for x in idx[:, j]]]
+            keep = idx[:, j] >= 0            # slots the capacity dropped add nothing
+            yc[keep] += g_gates[tt[keep], j:j + 1] * part[[pos[int(x)] for x in idx[keep, j]]]
         check_close_rows(g_y[tt], yc, TOL[w.dtype], what=f"combine tokens {t0}..")
 
     # ---- y end to end on sampled tokens (oracle routing and experts)
@@ -177,6 +189,8 @@ def test_full_size_layer(w):
     n_y = min(Y_TOKENS[w.cfg_id], cand.size)
     toks = np.sort(rng.choice(cand, n_y, replace=False)) if n_y < cand.size else cand
     cache.clear()
-    y_ref = O.layer_tokens(h, r, toks, weights_of, shared)
+    # drops follow the dispatch of the GPU's ids (bit-exact above): a near-tie
+    # choice elsewhere can move which later slots overflow
+    y_ref = O.layer_tokens(h, r, toks, weights_of, shared, row_of=d.row_of if cap else None)
     worst = check_close_rows(g_y[toks], y_ref, TOL[w.dtype], what="y (sampled tokens)")
     print(f"[{w.name}] y on {toks.size} sampled tokens: max row rel err {worst:.3e}", flush=True)

@@ -39,9 +39,14 @@ def f32(n):
 
 
 def shape_of(T, d, N, k, d_ff, d_ff_shared=0, dtype=W.DTYPE_BF16, mode=0, alpha=0.01,
-             groups=None):
+             groups=None, cf=0.0):
     g = groups or (0, 0, 0)
-    return M.Shape(T, d, N, k, d_ff, d_ff_shared, dtype, mode, alpha, *g)
+    return M.Shape(T, d, N, k, d_ff, d_ff_shared, dtype, mode, alpha, *g, cf)
+
+
+def capacity_of(s):
+    """The oracle's capacity C for the shape (None when dropless)."""
+    return O.expert_capacity(s.capacity_factor, s.T, s.k, s.N) if s.capacity_factor else None
 
 
 def groups_of(s):
@@ -69,8 +74,8 @@ def run_steps(s, inp):
     zl, ent = f32(1), f32(1)
     M.route(s, h, wr, br, bs, ids, gates, p, ws, nws, z_loss=zl, entropy=ent)
     counts, offsets, perm, row_of = i32(N), i32(N + 1), i32(T * k), i32(T * k)
-    fo, la = f32(N), f32(1)
-    M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la)
+    fo, la, cs = f32(N), f32(1), f32(2)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la, cap_stats=cs)
     wg, wu, wd = dev(inp["w_gate"], dt), dev(inp["w_up"], dt), dev(inp["w_down"], dt)
     sg, su, sd = dev(inp["sh_gate"], dt), dev(inp["sh_up"], dt), dev(inp["sh_down"], dt)
     rows_n = T * k + (T if s.d_ff_shared else 0)
@@ -82,17 +87,18 @@ def run_steps(s, inp):
     res = dict(ids=host(ids).reshape(T, k), gates=host(gates).reshape(T, k), p=host(p),
                counts=host(counts), offsets=host(offsets), perm=host(perm), row_of=host(row_of),
                f=host(fo), l_aux=float(host(la)[0]), out_rows=host(out_rows), y=host(y),
-               z_loss=float(host(zl)[0]), entropy=float(host(ent)[0]))
+               z_loss=float(host(zl)[0]), entropy=float(host(ent)[0]), cap_stats=host(cs))
     # the fused call on the same inputs must agree bit for bit
     y2 = t.empty_like(y)
     ids2, g2, c2, f2, p2, l2 = i32(T * k), f32(T * k), i32(N), f32(N), f32(N), f32(1)
-    zl2, ent2 = f32(1), f32(1)
+    zl2, ent2, cs2 = f32(1), f32(1), f32(2)
     M.layer_fused(s, h, wr, br, bs, wg, wu, wd, sg, su, sd, y2, ids2, g2, c2, f2, p2, l2, ws, nws,
-                  z_loss=zl2, entropy=ent2)
+                  z_loss=zl2, entropy=ent2, cap_stats=cs2)
     t.cuda.synchronize()
     res["fused"] = dict(y=host(y2), ids=host(ids2).reshape(T, k), gates=host(g2).reshape(T, k),
                         counts=host(c2), f=host(f2), p=host(p2), l_aux=float(host(l2)[0]),
-                        z_loss=float(host(zl2)[0]), entropy=float(host(ent2)[0]))
+                        z_loss=float(host(zl2)[0]), entropy=float(host(ent2)[0]),
+                        cap_stats=host(cs2))
     return res
 
 
@@ -104,11 +110,17 @@ def check_all(s, inp, res, alpha=0.01):
     ok = ~near
     check_gates(res["gates"], r.gates, 1e-4, ok)
     # dispatch: bit-exact against the oracle's dispatch of the GPU's own ids
-    d = O.dispatch(res["ids"], s.N)
+    cap = capacity_of(s)
+    d = O.dispatch(res["ids"], s.N, cap)
+    kept = int(d.offsets[-1])
     assert np.array_equal(res["counts"], d.counts)
     assert np.array_equal(res["offsets"], d.offsets)
-    assert np.array_equal(res["perm"], d.perm_src)
+    assert np.array_equal(res["perm"][:kept], d.perm_src)
     assert np.array_equal(res["row_of"], d.row_of)
+    # capacity usage and dropped fraction: the fp32 rounding of the exact ratios
+    want = O.capacity_stats(d, cap) if cap else (0.0, 0.0)
+    assert np.array_equal(res["cap_stats"], np.float32(want).astype(np.float64)), \
+        (res["cap_stats"], want)
     # stats
     f, p, l_aux = O.load_stats(d.counts, r.stat_prob, s.k, alpha)
     assert np.allclose(res["f"], f, rtol=1e-6, atol=0)
@@ -118,16 +130,27 @@ def check_all(s, inp, res, alpha=0.01):
     zl_ref, ent_ref = O.router_z_loss(r.z), O.routing_entropy(r.stat_prob)
     assert abs(res["z_loss"] - zl_ref) <= 1e-4 * abs(zl_ref) + 1e-6, (res["z_loss"], zl_ref)
     assert abs(res["entropy"] - ent_ref) <= 1e-4 * abs(ent_ref) + 1e-6, (res["entropy"], ent_ref)
-    # expert rows: oracle experts on the GPU's dispatch
+    # expert rows: oracle experts on the GPU's dispatch (rows past the kept
+    # total are not written when the capacity drops slots)
     rows_ref = O.expert_rows(inp["h"], d, s.k, oracle_weights(inp), oracle_shared(inp))
-    check_close_rows(res["out_rows"], rows_ref, tol, what="out_rows")
+    written = np.ones(rows_ref.shape[0], dtype=bool)
+    written[kept:s.T * s.k] = False
+    check_close_rows(res["out_rows"], rows_ref, tol, written, what="out_rows")
     # combine of the GPU's rows and gates
-    y_comb = O.combine(res["out_rows"], res["row_of"], res["gates"], s.d_ff_shared > 0)
+    y_comb = O.combine(np.where(written[:, None], res["out_rows"], 0.0), res["row_of"],
+                       res["gates"], s.d_ff_shared > 0)
     check_close_rows(res["y"], y_comb, tol, what="combine")
-    # end to end against the oracle's own routing (non-near-tie tokens)
+    # end to end against the oracle's own routing (non-near-tie tokens). With
+    # a capacity a near-tie choice can move later tokens' drops, so then the
+    # reference keeps the oracle's gates and experts but the GPU's selection.
     ref = O.layer(inp["h"], inp["w_router"], s.k, s.mode, oracle_weights(inp), inp["b_router"],
-                  inp["b_select"], oracle_shared(inp), alpha, groups_of(s))
-    worst = check_close_rows(res["y"], ref.y, tol, ok, what="y")
+                  inp["b_select"], oracle_shared(inp), alpha, groups_of(s),
+                  capacity_factor=s.capacity_factor or None)
+    y_ref = ref.y
+    if cap and near.any():
+        y_ref = O.combine(rows_ref, d.row_of, np.where(ok[:, None], r.gates, res["gates"]),
+                          s.d_ff_shared > 0)
+    worst = check_close_rows(res["y"], y_ref, tol, ok, what="y")
     # the fused call is the same kernels: identical bits
     fz = res["fused"]
     assert np.array_equal(fz["y"], res["y"])
@@ -136,6 +159,7 @@ def check_all(s, inp, res, alpha=0.01):
     assert np.array_equal(fz["counts"], res["counts"])
     assert np.array_equal(fz["p"], res["p"]) and fz["l_aux"] == res["l_aux"]
     assert fz["z_loss"] == res["z_loss"] and fz["entropy"] == res["entropy"]
+    assert np.array_equal(fz["cap_stats"], res["cap_stats"])
     return worst, int(near.sum())
 
 
@@ -193,6 +217,59 @@ def test_layer_parity_grouped(case):
     res = run_steps(s, inp)
     worst, near = check_all(s, inp, res)
     print(f"{name}: worst row rel err {worst:.2e}, near-ties {near}")
+
+
+CAPACITY_CASES = [
+    # name, T, d, N, k, d_ff, d_ff_shared, dtype, mode, groups, capacity_factor
+    ("f32_cap_sigmoid_shared", 37, 48, 9, 3, 40, 24, W.DTYPE_F32, 2, None, 0.75),
+    ("f32_cap_switch", 64, 32, 4, 1, 64, 0, W.DTYPE_F32, 1, None, 1.0),
+    ("bf16_cap_prefill_bm128", 300, 128, 5, 2, 192, 0, W.DTYPE_BF16, 0, None, 1.0),
+    # C = 33 rows per expert at most: the weight-streaming kernels
+    ("bf16_cap_skinny", 520, 128, 64, 8, 128, 0, W.DTYPE_BF16, 0, None, 0.5),
+    ("bf16_cap_bm256", 2304, 128, 2, 1, 320, 0, W.DTYPE_BF16, 1, None, 1.0),
+    ("bf16_cap_grouped_shared", 300, 128, 64, 8, 128, 128, W.DTYPE_BF16, 2, (8, 4, 2), 1.25),
+    # split-K tail with dropped rows
+    ("bf16_cap_split_k4096", 256, 4096, 2, 1, 256, 0, W.DTYPE_BF16, 0, None, 0.6),
+    # C = T k: nothing dropped, usage 1/N
+    ("bf16_cap_keeps_all", 257, 192, 12, 3, 128, 0, W.DTYPE_BF16, 0, None, 12.0),
+]
+
+
+@pytest.mark.parametrize("case", CAPACITY_CASES, ids=[c[0] for c in CAPACITY_CASES])
+def test_layer_parity_capacity(case):
+    """Expert capacity through every call and the fused layer: bit-exact
+    dispatch with dropped slots (row_of = -1), exact usage and drop
+    fraction, rows and y to tolerance."""
+    name, T, d, N, k, dff, dfs, dt, mode, groups, cf = case
+    inp = W.random_small(T, d, N, k, dff, dfs, dt, mode, seed=len(name), router_bias=(T % 2 == 0))
+    s = shape_of(T, d, N, k, dff, dfs, dt, mode, groups=groups, cf=cf)
+    print(f"case {name}", flush=True)
+    res = run_steps(s, inp)
+    worst, near = check_all(s, inp, res)
+    dropped = int((res["row_of"] < 0).sum())
+    if cf < N / k:
+        assert dropped > 0, "the case is meant to drop slots"
+    else:
+        assert dropped == 0
+    print(f"{name}: worst row rel err {worst:.2e}, near-ties {near}, dropped {dropped}")
+
+
+def test_dispatch_capacity_worked_example_on_gpu():
+    """The four-token grouping example with capacity factor 1 (C = 2): E2's
+    third slot (token 3) is dropped, the rest keep their order."""
+    import pins
+    g = pins.golden("dispatch_grouping_example.json")
+    s = shape_of(4, 64, 4, 2, 64, 0, W.DTYPE_BF16, 0, cf=1.0)
+    t = torch()
+    ids = t.tensor(np.array(g["ids"]).reshape(-1), dtype=t.int32, device="cuda")
+    counts, offsets, perm, row_of, cs = i32(4), i32(5), i32(8), i32(8), f32(2)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, cap_stats=cs)
+    t.cuda.synchronize()
+    assert host(counts).tolist() == [2, 2, 3, 1]
+    assert host(offsets).tolist() == [0, 2, 4, 6, 7]
+    assert host(perm)[:7].tolist() == [0, 4, 2, 7, 1, 3, 5]
+    assert host(row_of).tolist() == [0, 4, 2, 5, 1, 6, -1, 3]
+    assert host(cs).tolist() == [7 / 8, 1 / 8]
 
 
 def test_route_group_limited_worked_example_on_gpu():
@@ -306,26 +383,33 @@ def test_dispatch_grouping_example_on_gpu():
         assert (host(perm)[lo:hi] // 2).tolist() == toks
 
 
-@pytest.mark.parametrize("T,N,k", [(1, 1, 1), (5, 7, 3), (3000, 8, 2), (2500, 128, 8),
-                                   (700, 512, 16), (4097, 33, 5)])
-def test_dispatch_random(T, N, k):
+@pytest.mark.parametrize("T,N,k,cf", [(1, 1, 1, 0.0), (5, 7, 3, 0.0), (3000, 8, 2, 0.0),
+                                      (2500, 128, 8, 0.0), (700, 512, 16, 0.0), (4097, 33, 5, 0.0),
+                                      (1, 1, 1, 1.0), (5, 7, 3, 0.5), (3000, 8, 2, 1.0),
+                                      (2500, 128, 8, 1.25), (700, 512, 16, 2.0),
+                                      (4097, 33, 5, 0.1)])
+def test_dispatch_random(T, N, k, cf):
     rng = np.random.default_rng(T * 31 + N)
     # skewed: low expert ids are more popular
     pr = 1.0 / np.arange(1, N + 1) ** 1.1
     pr /= pr.sum()
     ids = np.stack([rng.choice(N, size=k, replace=False, p=pr) for _ in range(T)]).astype(np.int32)
-    s = shape_of(T, 64, N, k, 64, 0, W.DTYPE_BF16, 0)
+    s = shape_of(T, 64, N, k, 64, 0, W.DTYPE_BF16, 0, cf=cf)
     t = torch()
     counts, offsets, perm, row_of = i32(N), i32(N + 1), i32(T * k), i32(T * k)
     pm = dev_f32(np.full(N, 1.0 / N))
-    fo, la = f32(N), f32(1)
-    M.dispatch(s, t.from_numpy(ids.reshape(-1)).cuda(), counts, offsets, perm, row_of, pm, fo, la)
+    fo, la, cs = f32(N), f32(1), f32(2)
+    M.dispatch(s, t.from_numpy(ids.reshape(-1)).cuda(), counts, offsets, perm, row_of, pm, fo, la,
+               cap_stats=cs)
     t.cuda.synchronize()
-    d = O.dispatch(ids, N)
+    cap = capacity_of(s)
+    d = O.dispatch(ids, N, cap)
     assert np.array_equal(host(counts), d.counts)
     assert np.array_equal(host(offsets), d.offsets)
-    assert np.array_equal(host(perm), d.perm_src)
+    assert np.array_equal(host(perm)[:d.perm_src.size], d.perm_src)
     assert np.array_equal(host(row_of), d.row_of)
+    want = O.capacity_stats(d, cap) if cap else (0.0, 0.0)
+    assert np.array_equal(host(cs), np.float32(want).astype(np.float64))
     assert np.allclose(host(fo), d.counts / (T * k), rtol=1e-6, atol=0)
     assert abs(float(host(la)[0]) - 0.01 * N * np.sum(d.counts / (T * k) / N)) < 1e-6
 

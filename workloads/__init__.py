@@ -62,6 +62,8 @@ class Workload:
     router_bias: str = "none"        # "none" | "zipf"
     zipf_s: float = 1.1
     select_bias: float = 0.0         # b_sel ~ U(-a, a) when mode C
+    capacity_factor: float = 0.0     # 0: dropless; else C = ceil(cf * T * k / N)
+    groups: Optional[tuple] = None   # (n_groups, topk_groups, group_topm) or None
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -97,9 +99,19 @@ DEEPSEEK_V3 = Workload("deepseek_v3_T4096_shared", 5, T=4096, d=7168, N=256,
                        mode=MODE_SIGMOID_BIAS_RENORM, router_std=1.0,
                        select_bias=0.1)
 
+# the skewed fine-grained layer with an expert capacity: the popular experts
+# overflow and drop their latest tokens (same inputs as the dropless one)
+QWEN3_30B_CAP = QWEN3_30B.replace(name="qwen3_30b_a3b_T8192_zipf_cap1.25",
+                                  capacity_factor=1.25)
+
+# the DeepSeek-V3-shaped layer with group-limited selection: 8 groups of 32
+# experts, the 4 best by the sum of their top-2 scores stay candidates
+DEEPSEEK_V3_GROUPED = DEEPSEEK_V3.replace(name="deepseek_v3_T4096_shared_groups8_keep4",
+                                          groups=(8, 4, 2))
+
 ALL = {w.name: w for w in (TINY, TINY_SWITCH, MIXTRAL_PREFILL,
                            MIXTRAL_PREFILL_R1, MIXTRAL_DECODE, QWEN3_30B,
-                           DEEPSEEK_V3)}
+                           QWEN3_30B_CAP, DEEPSEEK_V3, DEEPSEEK_V3_GROUPED)}
 
 
 # --------------------------------------------------------------- host draws
