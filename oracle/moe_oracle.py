@@ -46,6 +46,11 @@ notation, with numpy as the only primitive (matrix products, exp, a sort):
      routing entropy [wuhy-notes §五 and its monitoring list]
   9. dense brute force: every expert on every token, unselected gates zero
      [cooking-agi "怎么知道实现没把梯度弄丢？"]
+ 10. backward: gradients of <dy, y> (+ weighted L_aux and z-loss) for the
+     forward pass's fixed selection; the router learns through the selected
+     gate values (and the full-softmax denominator in mode B)
+     [cooking-agi "top-k 不可导，router 怎么学"; wuhy-notes "Top-k 不可导，
+      为什么 Router 还能学" and the total-loss paragraph]
 
 Readings where the pages are silent or garbled (each is listed in the design
 notes): ties in top-k go to the lower expert index; f_i = count_i / (T k);
@@ -436,6 +441,156 @@ def dense_layer(h, w_router, k, mode, weights_of: WeightsOf, b_router=None,
     if shared is not None:
         y += expert_ffn(h, *shared)
     return y
+
+
+# ------------------------------------------------------------- 10. backward
+# Gradients of the layer for an upstream gradient dy of y (and optional
+# weights d_laux, d_zloss of the two auxiliary losses added to the training
+# objective [wuhy-notes, total-loss paragraph]). The discrete selection and
+# the dispatch are held fixed; gradients reach the router only through the
+# continuous gate values of the selected experts, and through every logit in
+# a normalisation that involves them (the full softmax of mode B)
+# [cooking-agi, "top-k 不可导，router 怎么学"; wuhy-notes "Top-k 不可导，为什么
+# Router 还能学"]. Written from the chain rule of steps 1-8.
+
+def silu_grad(x):
+    """d/dx [x sigmoid(x)] = sigmoid(x) (1 + x (1 - sigmoid(x)))."""
+    s = sigmoid(x)
+    return s * (1.0 + _f64(x) * (1.0 - s))
+
+
+def expert_ffn_backward(x, w_gate, w_up, w_down, dout):
+    """Backward of E(x) = W_down (SiLU(W_gate x) * W_up x) on rows x [n, d]
+    with output gradients dout [n, d]: returns dx [n, d], dW_gate [d_ff, d],
+    dW_up [d_ff, d], dW_down [d, d_ff] (each summed over the rows)."""
+    x, dout = _f64(x), _f64(dout)
+    wg, wu, wd = _f64(w_gate), _f64(w_up), _f64(w_down)
+    gp = x @ wg.T                     # gate pre-activation
+    up = x @ wu.T                     # up projection
+    act = silu(gp) * up
+    dw_down = dout.T @ act
+    dact = dout @ wd
+    du = dact * silu(gp)
+    dgp = dact * up * silu_grad(gp)
+    dw_gate = dgp.T @ x
+    dw_up = du.T @ x
+    dx = dgp @ wg + du @ wu
+    return dx, dw_gate, dw_up, dw_down
+
+
+def gate_backward(routing: Routing, dg, mode):
+    """Router-logit gradient [T, N] of the gate values, given dL/dg [T, k]
+    (zero for slots that contributed nothing). Mode A: g is the softmax of
+    the selected logits; mode B: g is the full-softmax probability, whose
+    denominator holds every logit; mode C: g = s_i / sum of the selected s,
+    s = sigmoid(z) (the selection bias is not differentiated: it only
+    chooses)."""
+    dg = _f64(dg)
+    z = routing.z
+    T, N = z.shape
+    ids = routing.ids
+    dz = np.zeros((T, N))
+    g = routing.gates
+    if mode == MODE_SOFTMAX_RENORM:
+        inner = (g * dg).sum(axis=-1, keepdims=True)
+        np.put_along_axis(dz, ids, g * (dg - inner), axis=-1)
+    elif mode == MODE_SOFTMAX_FULL:
+        P = softmax(z)
+        a = np.zeros((T, N))
+        np.put_along_axis(a, ids, dg, axis=-1)
+        dz = P * (a - (P * a).sum(axis=-1, keepdims=True))
+    elif mode == MODE_SIGMOID_BIAS_RENORM:
+        s_sel = np.take_along_axis(sigmoid(z), ids, axis=-1)
+        S = s_sel.sum(axis=-1, keepdims=True)
+        ds = (dg - (g * dg).sum(axis=-1, keepdims=True)) / S
+        np.put_along_axis(dz, ids, ds * s_sel * (1.0 - s_sel), axis=-1)
+    else:
+        raise ValueError(f"unknown gate mode {mode}")
+    return dz
+
+
+def stats_backward(routing: Routing, counts, k, mode, alpha, d_laux=0.0, d_zloss=0.0):
+    """Router-logit gradient [T, N] of d_laux * L_aux + d_zloss * L_z. In
+    L_aux = alpha N sum_i f_i p_i the fractions f_i are counts (piecewise
+    constant: no gradient) and p_i = (1/T) sum_t P_ti; L_z is the mean squared
+    log-sum-exp of the logits."""
+    z = routing.z
+    T, N = z.shape
+    dz = np.zeros((T, N))
+    if T == 0:
+        return dz
+    if d_laux:
+        f = np.asarray(counts, dtype=F64) / (T * k)
+        a = np.broadcast_to(d_laux * alpha * N * f / T, (T, N))   # dL/dP_ti
+        if mode in (MODE_SOFTMAX_RENORM, MODE_SOFTMAX_FULL):
+            P = softmax(z)
+            dz += P * (a - (P * a).sum(axis=-1, keepdims=True))
+        else:
+            s = sigmoid(z)
+            S = s.sum(axis=-1, keepdims=True)
+            P = s / S
+            ds = (a - (P * a).sum(axis=-1, keepdims=True)) / S
+            dz += ds * s * (1.0 - s)
+    if d_zloss:
+        m = z.max(axis=-1, keepdims=True)
+        lse = m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True))
+        dz += d_zloss * (2.0 / T) * lse * softmax(z)
+    return dz
+
+
+@dataclasses.dataclass
+class LayerGrads:
+    dh: np.ndarray         # [T, d]
+    dw_router: np.ndarray  # [N, d]
+    db_router: np.ndarray  # [N]
+    dw_gate: np.ndarray    # [N, d_ff, d]
+    dw_up: np.ndarray      # [N, d_ff, d]
+    dw_down: np.ndarray    # [N, d, d_ff]
+    dsh: Optional[tuple]   # (d sh_gate, d sh_up, d sh_down) or None
+    dg: np.ndarray         # [T, k] gradient of the gate values
+    dz: np.ndarray         # [T, N] gradient of the router logits
+
+
+def layer_backward(h, w_router, k, mode, weights_of: WeightsOf, dy, b_router=None,
+                   b_select=None, shared=None, alpha=0.01, groups=None,
+                   capacity_factor=None, d_laux=0.0, d_zloss=0.0) -> LayerGrads:
+    """Gradients of <dy, y> + d_laux L_aux + d_zloss L_z with respect to h,
+    W_r, b_r, every expert's weights and the shared expert's weights, for
+    the selection and dispatch of the forward pass. Each kept slot (t, j) of
+    expert e contributes dg[t, j] = <dy_t, E_e(h_t)> and back-propagates
+    g[t, j] dy_t through E_e; a dropped slot contributes nothing."""
+    h, dy = _f64(h), _f64(dy)
+    T, d = h.shape
+    wr = _f64(w_router)
+    N = wr.shape[0]
+    r = route(h, wr, k, mode, b_router, b_select, groups)
+    cap = expert_capacity(capacity_factor, T, k, N) if capacity_factor else None
+    disp = dispatch(r.ids, N, cap)
+    dh = np.zeros((T, d))
+    dg = np.zeros((T, k))
+    dwg, dwu, dwd = [], [], []
+    for e in range(N):
+        wg, wu, wd = weights_of(e)
+        flats = disp.perm_src[disp.offsets[e]:disp.offsets[e + 1]]
+        t, j = flats // k, flats % k
+        x = h[t]
+        dg[t, j] = np.sum(dy[t] * expert_ffn(x, wg, wu, wd), axis=-1)
+        dout = r.gates[t, j][:, None] * dy[t]
+        dx, g_g, g_u, g_d = expert_ffn_backward(x, wg, wu, wd, dout)
+        np.add.at(dh, t, dx)
+        dwg.append(g_g)
+        dwu.append(g_u)
+        dwd.append(g_d)
+    dsh = None
+    if shared is not None:
+        dx, *dsh = expert_ffn_backward(h, *shared, dy)
+        dh += dx
+        dsh = tuple(dsh)
+    dz = gate_backward(r, dg, mode) + stats_backward(r, disp.counts, k, mode, alpha, d_laux,
+                                                     d_zloss)
+    dh += dz @ wr
+    return LayerGrads(dh, dz.T @ h, dz.sum(axis=0), np.stack(dwg), np.stack(dwu), np.stack(dwd),
+                      dsh, dg, dz)
 
 
 # ------------------------------------------------------ comparison helpers

@@ -11,7 +11,9 @@ from oracle import moe_oracle as O
 
 _orig = {n: getattr(O, n) for n in ("router_logits", "softmax", "sigmoid", "topk", "group_limit",
                                      "dispatch", "expert_capacity", "silu", "expert_ffn", "combine",
-                                     "load_stats", "route", "router_z_loss", "routing_entropy")}
+                                     "load_stats", "route", "router_z_loss", "routing_entropy",
+                                     "silu_grad", "expert_ffn_backward", "gate_backward",
+                                     "stats_backward", "layer_backward")}
 
 
 def _route_no_renorm(h, w, k, mode, b_router=None, b_select=None):
@@ -116,6 +118,65 @@ def _combine_negative_row(out_rows, row_of, gates, has_shared=False):
     return y
 
 
+def _ffn_bwd_gate_up_swapped(x, wg, wu, wd, dout):
+    dx, dwg, dwu, dwd = _orig["expert_ffn_backward"](x, wg, wu, wd, dout)
+    return dx, dwu, dwg, dwd
+
+
+def _ffn_bwd_no_dx_up(x, wg, wu, wd, dout):
+    x, dout = np.asarray(x, float), np.asarray(dout, float)
+    gp = x @ np.asarray(wg, float).T
+    up = x @ np.asarray(wu, float).T
+    dact = dout @ np.asarray(wd, float)
+    du = dact * O.silu(gp)
+    dgp = dact * up * O.silu_grad(gp)
+    dx, dwg, dwu, dwd = _orig["expert_ffn_backward"](x, wg, wu, wd, dout)
+    return dgp @ np.asarray(wg, float), dwg, dwu, dwd
+
+
+def _gate_bwd_mode_b_selected_only(routing, dg, mode):
+    dz = _orig["gate_backward"](routing, dg, mode)
+    if mode == O.MODE_SOFTMAX_FULL:
+        mask = np.zeros_like(dz)
+        np.put_along_axis(mask, routing.ids, 1.0, axis=-1)
+        dz = dz * mask
+    return dz
+
+
+def _gate_bwd_mode_a_no_inner(routing, dg, mode):
+    if mode != O.MODE_SOFTMAX_RENORM:
+        return _orig["gate_backward"](routing, dg, mode)
+    dz = np.zeros(routing.z.shape)
+    np.put_along_axis(dz, routing.ids, routing.gates * np.asarray(dg, float), axis=-1)
+    return dz
+
+
+def _gate_bwd_mode_c_biased(routing, dg, mode):
+    if mode != O.MODE_SIGMOID_BIAS_RENORM:
+        return _orig["gate_backward"](routing, dg, mode)
+    s = np.take_along_axis(routing.sel, routing.ids, axis=-1)     # biased scores
+    g = routing.gates
+    ds = (dg - (g * dg).sum(axis=-1, keepdims=True)) / s.sum(axis=-1, keepdims=True)
+    dz = np.zeros(routing.z.shape)
+    np.put_along_axis(dz, routing.ids, ds * s * (1 - s), axis=-1)
+    return dz
+
+
+def _layer_bwd_ignores_capacity(*a, **kw):
+    if len(a) > 11:
+        a = a[:11] + (None,) + a[12:]
+    else:
+        kw["capacity_factor"] = None
+    return _orig["layer_backward"](*a, **kw)
+
+
+def _layer_bwd_no_shared(*a, **kw):
+    g = _orig["layer_backward"](*a, **kw)
+    if g.dsh is not None:
+        g.dsh = tuple(np.zeros_like(v) for v in g.dsh)
+    return g
+
+
 MUTATIONS = {
     "logits_drop_bias": ("router_logits", lambda h, w, b=None: _orig["router_logits"](h, w, None)),
     "logits_expert_index_reversed": ("router_logits", _logits_reversed),
@@ -142,6 +203,20 @@ MUTATIONS = {
     "capacity_drops_earliest": ("dispatch", _dispatch_drop_earliest),
     "capacity_floor": ("expert_capacity", lambda cf, T, k, N: int(math.floor(float(np.float32(cf)) * (T * k) / N))),
     "combine_dropped_slot_wraps": ("combine", _combine_negative_row),
+    "silu_grad_sigmoid_only": ("silu_grad", lambda x: O.sigmoid(x)),
+    "ffn_bwd_gate_up_swapped": ("expert_ffn_backward", _ffn_bwd_gate_up_swapped),
+    "ffn_bwd_dx_misses_up": ("expert_ffn_backward", _ffn_bwd_no_dx_up),
+    "gate_bwd_mode_b_selected_only": ("gate_backward", _gate_bwd_mode_b_selected_only),
+    "gate_bwd_mode_a_no_inner": ("gate_backward", _gate_bwd_mode_a_no_inner),
+    "gate_bwd_mode_c_biased": ("gate_backward", _gate_bwd_mode_c_biased),
+    "stats_bwd_zloss_no_factor_2": ("stats_backward",
+                                    lambda r, c, k, m, a, dl=0.0, dz=0.0:
+                                    _orig["stats_backward"](r, c, k, m, a, dl, dz / 2)),
+    "stats_bwd_laux_sign": ("stats_backward",
+                            lambda r, c, k, m, a, dl=0.0, dz=0.0:
+                            _orig["stats_backward"](r, c, k, m, a, -dl, dz)),
+    "layer_bwd_ignores_capacity": ("layer_backward", _layer_bwd_ignores_capacity),
+    "layer_bwd_no_shared": ("layer_backward", _layer_bwd_no_shared),
     "stats_f_over_T": ("load_stats", lambda c, sp, k, a: _orig["load_stats"](c, sp, 1, a)),
     "stats_no_N_factor": ("load_stats", lambda c, sp, k, a: (lambda f, p, l: (f, p, l / np.asarray(sp).shape[1]))(*_orig["load_stats"](c, sp, k, a))),
 }
