@@ -183,15 +183,24 @@ def _select(sel, k, groups):
     return ids, np.minimum(gap, ggap)
 
 
-def route(h, w_router, k, mode, b_router=None, b_select=None, groups=None) -> Routing:
+def route(h, w_router, k, mode, b_router=None, b_select=None, groups=None,
+          ids=None) -> Routing:
     """Router logits, scores, top-k selection and gate values (steps 1-4).
     ``groups`` = (n_groups, topk_groups, topm) limits the candidates to the
-    best groups first (group_limit); None selects over all experts."""
+    best groups first (group_limit); None selects over all experts. ``ids``
+    [T, k], when given, replaces the selection (gates and statistics are then
+    those of that selection; gap is +inf): the backward pass of another
+    implementation's forward is checked for the selection it made."""
     z = router_logits(h, w_router, b_router)
+    fixed = ids is not None
+    if fixed:
+        ids = np.asarray(ids, dtype=np.int64)
+        gap = np.full(ids.shape[0], np.inf)
     if mode in (MODE_SOFTMAX_RENORM, MODE_SOFTMAX_FULL):
         p = softmax(z)
         sel = p                       # TopK(p_t, k)
-        ids, gap = _select(sel, k, groups)
+        if not fixed:
+            ids, gap = _select(sel, k, groups)
         p_sel = np.take_along_axis(p, ids, axis=-1)
         if mode == MODE_SOFTMAX_RENORM:
             gates = p_sel / p_sel.sum(axis=-1, keepdims=True)
@@ -203,7 +212,8 @@ def route(h, w_router, k, mode, b_router=None, b_select=None, groups=None) -> Ro
             raise ValueError("mode C needs the selection bias")
         s = sigmoid(z)
         sel = s + _f64(b_select)[None, :]
-        ids, gap = _select(sel, k, groups)
+        if not fixed:
+            ids, gap = _select(sel, k, groups)
         s_sel = np.take_along_axis(s, ids, axis=-1)   # unbiased scores
         gates = s_sel / s_sel.sum(axis=-1, keepdims=True)
         stat_prob = s / s.sum(axis=-1, keepdims=True)
@@ -553,17 +563,18 @@ class LayerGrads:
 
 def layer_backward(h, w_router, k, mode, weights_of: WeightsOf, dy, b_router=None,
                    b_select=None, shared=None, alpha=0.01, groups=None,
-                   capacity_factor=None, d_laux=0.0, d_zloss=0.0) -> LayerGrads:
+                   capacity_factor=None, d_laux=0.0, d_zloss=0.0, ids=None) -> LayerGrads:
     """Gradients of <dy, y> + d_laux L_aux + d_zloss L_z with respect to h,
     W_r, b_r, every expert's weights and the shared expert's weights, for
     the selection and dispatch of the forward pass. Each kept slot (t, j) of
     expert e contributes dg[t, j] = <dy_t, E_e(h_t)> and back-propagates
-    g[t, j] dy_t through E_e; a dropped slot contributes nothing."""
+    g[t, j] dy_t through E_e; a dropped slot contributes nothing. ``ids``
+    fixes the selection (see route)."""
     h, dy = _f64(h), _f64(dy)
     T, d = h.shape
     wr = _f64(w_router)
     N = wr.shape[0]
-    r = route(h, wr, k, mode, b_router, b_select, groups)
+    r = route(h, wr, k, mode, b_router, b_select, groups, ids)
     cap = expert_capacity(capacity_factor, T, k, N) if capacity_factor else None
     disp = dispatch(r.ids, N, cap)
     dh = np.zeros((T, d))

@@ -644,4 +644,31 @@ def pin_backward_zero_structure():
     assert not np.any(gr.dz) and not np.any(gr.dw_router) and not np.any(gr.db_router)
 
 
+def pin_route_given_selection():
+    """Routing with a given selection reproduces the oracle's own gates and
+    statistics when that selection is its own; for another selection the
+    gates follow the mode's formula on those experts (mode A: softmax of
+    their logits; B: their full-softmax probabilities; C: their renormalised
+    sigmoids)."""
+    rng = np.random.default_rng(24)
+    h, wr, *_ = _rand_inputs(rng, 9, 6, 7, 4)
+    for mode in (O.MODE_SOFTMAX_RENORM, O.MODE_SOFTMAX_FULL, O.MODE_SIGMOID_BIAS_RENORM):
+        bs = rng.uniform(-0.1, 0.1, 7) if mode == O.MODE_SIGMOID_BIAS_RENORM else None
+        r = O.route(h, wr, 3, mode, b_select=bs)
+        r2 = O.route(h, wr, 3, mode, b_select=bs, ids=r.ids)
+        assert np.array_equal(r2.gates, r.gates) and np.array_equal(r2.stat_prob, r.stat_prob)
+        other = np.tile(np.array([[6, 0, 3]]), (9, 1))
+        g = O.route(h, wr, 3, mode, b_select=bs, ids=other).gates
+        z = h @ wr.T
+        zs = np.take_along_axis(z, other, axis=-1)
+        if mode == O.MODE_SOFTMAX_RENORM:
+            want = scipy.special.softmax(zs, axis=-1)
+        elif mode == O.MODE_SOFTMAX_FULL:
+            want = np.take_along_axis(scipy.special.softmax(z, axis=-1), other, axis=-1)
+        else:
+            sg = scipy.special.expit(zs)
+            want = sg / sg.sum(axis=-1, keepdims=True)
+        assert np.allclose(g, want, rtol=1e-13, atol=0)
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]
