@@ -276,6 +276,59 @@ moe_status moe_layer_fused_marked(const moe_shape* s, const void* h,
                                   float* cap_stats, void* ws, size_t ws_bytes,
                                   void* stream, void* const* events);
 
+/* Host, pure: workspace bytes for moe_layer_backward with this shape (0 for
+ * an invalid shape). It holds the recomputed router logits and gate/up
+ * pre-activations, transposed copies of the expert, shared-expert and
+ * router weights, the intermediate row gradients, zero-padded transposed
+ * activations for the weight gradients and the GEMMs' split-K partials: of
+ * the order of 3x the expert weights plus 10 (T·k + 32·N) max(d, 2 d_ff)
+ * elements. No initialisation needed; one call at a time per workspace. */
+size_t moe_backward_workspace_bytes(const moe_shape* s);
+
+/* Backward pass of the layer for the selection and dispatch of a forward
+ * call: the gradients of  <dy, y> + d_laux·L_aux + d_zloss·L_z  with the
+ * discrete selection held fixed [cooking-agi, "top-k 不可导，router 怎么学" and
+ * "怎么知道实现没把梯度弄丢？"; wuhy-notes, "Top-k 不可导，为什么 Router 还能学"
+ * and the total-loss paragraph].
+ * The router receives gradient only through the gate values of the selected
+ * experts (mode A: the softmax of the selected logits; mode B: the full
+ * softmax, so every logit; mode C: the renormalised sigmoids of the
+ * selected; b_select is not differentiated), plus the L_aux term (f_i are
+ * counts and carry no gradient; p_i = mean_t P_ti does) and the z-loss
+ * term. A slot dropped by the capacity contributes nothing. Experts get
+ * gradient only from their kept rows.
+ * Inputs: the forward's inputs (b_select is not needed) and its outputs
+ *   topk_ids, topk_gates [T, k], counts [N] (routed, before capacity),
+ *   offsets [N+1], perm_src [T·k], row_of [T·k] exactly as moe_route /
+ *   moe_dispatch wrote them for this shape; dy [T, d] dtype; d_laux and
+ *   d_zloss are host scalars (the weights of L_aux and L_z in the loss;
+ *   0 leaves them out).
+ * Outputs (overwritten, not accumulated):
+ *   dh [T, d] dtype; dw_gate, dw_up [N, d_ff, d], dw_down [N, d, d_ff]
+ *   dtype (zero for experts without kept rows); dsh_gate, dsh_up [d_ff_shared,
+ *   d], dsh_down [d, d_ff_shared] dtype, required iff d_ff_shared > 0;
+ *   dw_router [N, d] fp32; db_router [N] fp32, nullable; dgates [T, k]
+ *   fp32, nullable: dL/dg per slot (0 for dropped slots).
+ * Arithmetic: fp32 accumulation; on the bf16 path the recomputed
+ * pre-activations, the row gradients and the router-logit gradient fed to
+ * the weight-gradient GEMMs are rounded to bf16. Deterministic (no float
+ * atomics). Errors as for the other calls (MOE_ERR_UNSUPPORTED also when a
+ * padded transposed activation exceeds 2^31 bytes). */
+moe_status moe_layer_backward(const moe_shape* s, const void* h,
+                              const void* w_router, const float* b_router,
+                              const void* w_gate, const void* w_up,
+                              const void* w_down, const void* sh_gate,
+                              const void* sh_up, const void* sh_down,
+                              const int32_t* topk_ids, const float* topk_gates,
+                              const int32_t* counts, const int32_t* offsets,
+                              const int32_t* perm_src, const int32_t* row_of,
+                              const void* dy, float d_laux, float d_zloss,
+                              void* dh, float* dw_router, float* db_router,
+                              void* dw_gate, void* dw_up, void* dw_down,
+                              void* dsh_gate, void* dsh_up, void* dsh_down,
+                              float* dgates, void* ws, size_t ws_bytes,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

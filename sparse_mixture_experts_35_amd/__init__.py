@@ -22,7 +22,7 @@ MAX_EXPERTS, MAX_TOPK, MAX_GROUPS, MAX_GROUP_TOPM = 512, 16, 64, 8
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_fused",
-           "moe_layer_fused_marked")
+           "moe_layer_fused_marked", "moe_backward_workspace_bytes", "moe_layer_backward")
 
 
 class MoEError(RuntimeError):
@@ -63,6 +63,10 @@ _SIG = {
     "moe_layer_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 20 + [_P, ctypes.c_size_t, _P]),
     "moe_layer_fused_marked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 20
                                + [_P, ctypes.c_size_t, _P, _P]),
+    "moe_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "moe_layer_backward": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 16
+                           + [ctypes.c_float, ctypes.c_float] + [_P] * 10
+                           + [_P, ctypes.c_size_t, _P]),
 }
 
 
@@ -157,6 +161,23 @@ def layer_fused(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh
         arr = (ctypes.c_void_p * 6)(*events)
         _check(lib().moe_layer_fused_marked(*args, ctypes.cast(arr, ctypes.c_void_p)),
                "moe_layer_fused_marked")
+
+
+def backward_workspace_bytes(shape: Shape) -> int:
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(shape)))
+
+
+def layer_backward(shape, h, w_router, b_router, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
+                   topk_ids, topk_gates, counts, offsets, perm_src, row_of, dy, dh, dw_router,
+                   db_router, dw_gate, dw_up, dw_down, dsh_gate=None, dsh_up=None, dsh_down=None,
+                   dgates=None, d_laux=0.0, d_zloss=0.0, ws=None, ws_bytes=0, stream=None):
+    _check(lib().moe_layer_backward(
+        ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down), _ptr(topk_ids),
+        _ptr(topk_gates), _ptr(counts), _ptr(offsets), _ptr(perm_src), _ptr(row_of), _ptr(dy),
+        float(d_laux), float(d_zloss), _ptr(dh), _ptr(dw_router), _ptr(db_router), _ptr(dw_gate),
+        _ptr(dw_up), _ptr(dw_down), _ptr(dsh_gate), _ptr(dsh_up), _ptr(dsh_down), _ptr(dgates),
+        _ptr(ws), ws_bytes, _stream(stream)), "moe_layer_backward")
 
 
 class MoELayer:

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_hip.so")
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "gemm_bf16.hip", "gemm_f32.hip",
-           "combine.hip"]
+           "combine.hip", "backward.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Wno-unused-function", "-Wno-unused-variable",

@@ -400,6 +400,287 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   return MOE_OK;
 }
 
+// ------------------------------------------------------------- backward
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Workspace of the backward pass (offsets in bytes; sizes in elements of the
+// layer dtype unless noted).
+struct BwdWs {
+  RouteWs r;                 // router logits (split-K slices)
+  int64_t Rp, Tp, Np;        // padded K spaces: routed rows, tokens, experts
+  int64_t ta_rows, tb_rows;  // rows of the transposed-activation buffers
+  size_t kofs, kofs_t, dg, dz, dzb;
+  size_t gu, v, dgu, act, gus, vs, dgus, acts;
+  size_t wdT, wguT, sdT, sguT, wrT;
+  size_t dhr, dhs, dhrt;
+  size_t ta, tb, part, cnt, end;
+  int64_t part_floats;
+};
+BwdWs bwd_ws(const moe_shape* s) {
+  BwdWs w;
+  const int64_t T = s->T, N = s->N, k = s->k, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
+  const int64_t R = T * k;
+  const size_t es = esize(s);
+  w.Rp = round_up(R + 32 * N, 64);
+  w.Tp = round_up(T, 64);
+  w.Np = round_up(N, 64);
+  w.ta_rows = std::max(std::max(d, 2 * dff), std::max(2 * dfs, w.Np));
+  w.tb_rows = std::max(std::max(d, dff), dfs);
+  w.r = route_ws(s, 0);
+  size_t o = w.r.end;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o = align_up(o + bytes);
+    return at_;
+  };
+  w.kofs = take(4 * (N + 1));
+  w.kofs_t = take(4 * 2);
+  w.dg = take(4 * R);
+  w.dz = take(4 * T * N);
+  w.dzb = take(es * T * w.Np);
+  w.gu = take(4 * R * 2 * dff);      // fp32 pre-activations and v
+  w.v = take(4 * R * dff);
+  w.dgu = take(es * R * 2 * dff);
+  w.act = take(es * R * dff);
+  w.gus = take(4 * T * 2 * dfs);
+  w.vs = take(4 * T * dfs);
+  w.dgus = take(es * T * 2 * dfs);
+  w.acts = take(es * T * dfs);
+  w.wdT = take(es * N * dff * d);
+  w.wguT = take(es * N * d * 2 * dff);
+  w.sdT = take(es * dfs * d);
+  w.sguT = take(es * d * 2 * dfs);
+  w.wrT = take(es * d * w.Np);
+  w.dhr = take(es * R * d);
+  w.dhs = take(es * T * d);
+  w.dhrt = take(es * T * d);
+  w.ta = take(es * w.ta_rows * w.Rp);
+  w.tb = take(es * w.tb_rows * w.Rp);
+  w.part_floats = 0;
+  if (s->dtype == MOE_BF16) {
+    int64_t f = std::max(moe::split_part_floats(R, s->N, s->d_ff, true),
+                         moe::split_part_floats(R, s->N, s->d, false));
+    f = std::max(f, moe::split_part_floats(R, s->N, s->d_ff, false));
+    f = std::max(f, moe::split_part_floats(T, 1, s->d, false));
+    if (dfs)
+      f = std::max(f, std::max(moe::split_part_floats(T, 1, s->d_ff_shared, true),
+                               moe::split_part_floats(T, 1, s->d_ff_shared, false)));
+    w.part_floats = f;
+  }
+  w.part = take(sizeof(float) * (size_t)w.part_floats);
+  w.cnt = take(w.part_floats ? sizeof(int32_t) * moe::kSplitCounters : 0);
+  w.end = o;
+  return w;
+}
+
+moe_status check_bwd_limits(const moe_shape* s) {
+  const BwdWs w = bwd_ws(s);
+  const int64_t es = (int64_t)esize(s);
+  const int64_t lim2g = 2147483647LL;
+  if (w.ta_rows * w.Rp * es > lim2g || w.tb_rows * w.Rp * es > lim2g ||
+      (int64_t)s->T * s->k * 2 * s->d_ff * es > lim2g ||
+      (int64_t)s->d * 2 * std::max(s->d_ff, s->d_ff_shared) * es > lim2g)
+    return fail(MOE_ERR_UNSUPPORTED, "a backward operand exceeds 2^31 bytes");
+  return MOE_OK;
+}
+
+moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router,
+                         const float* b_router, const void* w_gate, const void* w_up,
+                         const void* w_down, const void* sh_gate, const void* sh_up,
+                         const void* sh_down, const int32_t* ids, const float* gates,
+                         const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                         const int32_t* row_of, const void* dy, float d_laux, float d_zloss,
+                         void* dh, float* dw_router, float* db_router, void* dw_gate,
+                         void* dw_up, void* dw_down, void* dsh_gate, void* dsh_up,
+                         void* dsh_down, float* dgates, void* ws, const BwdWs& W,
+                         hipStream_t st) {
+  const int T = s->T, N = s->N, k = s->k, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
+  const int R = T * k;
+  const bool bf16 = s->dtype == MOE_BF16;
+  const int b = bf16 ? 1 : 0;
+  const size_t es = esize(s);
+  const int ncu = bf16 ? num_cu() : 0;
+  const int C = expert_capacity(s);
+  const int rows_all = C ? (int)std::min<int64_t>(R, (int64_t)N * C) : R;
+  const int rows_max = C ? std::min(T, C) : T;
+  const int Rp = (int)W.Rp, Tp = (int)W.Tp, Np = (int)W.Np;
+  float* part = W.part_floats ? at<float>(ws, W.part) : nullptr;
+  int32_t* cnt = W.part_floats ? at<int32_t>(ws, W.cnt) : nullptr;
+  float* gu = at<float>(ws, W.gu);
+  float* v = at<float>(ws, W.v);
+  char* dgu = at<char>(ws, W.dgu);
+  char* act = at<char>(ws, W.act);
+  float* gus = at<float>(ws, W.gus);
+  float* vs = at<float>(ws, W.vs);
+  char* dgus = at<char>(ws, W.dgus);
+  char* acts = at<char>(ws, W.acts);
+  char* wdT = at<char>(ws, W.wdT);
+  char* wguT = at<char>(ws, W.wguT);
+  char* sdT = at<char>(ws, W.sdT);
+  char* sguT = at<char>(ws, W.sguT);
+  char* wrT = at<char>(ws, W.wrT);
+  char* dhr = at<char>(ws, W.dhr);
+  char* dhs = at<char>(ws, W.dhs);
+  char* dhrt = at<char>(ws, W.dhrt);
+  char* ta = at<char>(ws, W.ta);
+  char* tb = at<char>(ws, W.tb);
+  int32_t* kofs = at<int32_t>(ws, W.kofs);
+  int32_t* kofs_t = at<int32_t>(ws, W.kofs_t);
+  float* dg = at<float>(ws, W.dg);
+  float* dz = at<float>(ws, W.dz);
+  char* dzb = at<char>(ws, W.dzb);
+  // kind 0: gate/up pre-activations (fp32 out); 1: plain product, fp32 out;
+  // 2: plain product in the layer dtype
+  auto grouped = [&](const moe::GroupedProblem& p, int kind, const char* what) -> moe_status {
+    hipError_t e;
+    if (bf16)
+      e = kind == 0 ? moe::launch_gateup_preact_bf16(p, ncu, st)
+          : kind == 1 ? moe::launch_down_f32out_bf16(p, ncu, st)
+                      : moe::launch_down_bf16(p, ncu, st);
+    else
+      e = kind == 0 ? moe::launch_gateup_preact_f32(p, st) : moe::launch_down_f32(p, st);
+    return hip_check(e, what);
+  };
+  auto kgroup = [&](const void* A, int lda, int64_t a_rows, const void* B, int ldb,
+                    int64_t b_rows, const int32_t* ko, int G, int M, int Ncols, void* Cout,
+                    int64_t gstride, int ldc, bool f32out, const char* what) -> moe_status {
+    if (bf16)
+      return hip_check(moe::launch_kgroup_bf16(A, lda, a_rows, B, ldb, b_rows, ko, G, M, Ncols,
+                                               Cout, gstride, ldc, f32out, st), what);
+    return hip_check(moe::launch_kgroup_f32(static_cast<const float*>(A), lda,
+                                            static_cast<const float*>(B), ldb, ko, G, M, Ncols,
+                                            static_cast<float*>(Cout), gstride, ldc, st), what);
+  };
+  auto pack = [&](const void* src, int ld_src, int ncols, const int32_t* pm, int kdiv,
+                  const float* scale, const int32_t* offs, const int32_t* ko, int G,
+                  int n_single, int64_t p_limit, void* dst, int64_t ld_dst, int batch,
+                  int64_t sb, int64_t db, const char* what) -> moe_status {
+    return hip_check(moe::launch_pack_t(src, ld_src, ncols, pm, kdiv, scale, offs, ko, G,
+                                        n_single, p_limit, dst, ld_dst, b, st, batch, sb, db),
+                     what);
+  };
+
+  // 1. router logits again (split-K slices, as in the forward)
+  float* z_part = at<float>(ws, W.r.z);
+  int splits = 1;
+  if (bf16) {
+    splits = moe::router_splits(T, d, N);
+    TRY(hip_check(moe::launch_router_gemm_bf16(h, w_router, z_part, T, d, N, splits, st),
+                  "router GEMM"));
+  } else {
+    TRY(hip_check(moe::launch_router_logits_f32(static_cast<const float*>(h),
+                                                static_cast<const float*>(w_router), z_part, T,
+                                                d, N, st),
+                  "router logits"));
+  }
+  // 2. gate/up pre-activations of the kept rows (and the shared expert)
+  TRY(grouped(moe::GroupedProblem{h, d, perm, k, offsets, N, rows_all, rows_max, w_gate, w_up,
+                                  (int64_t)dff * d, d, dff, d, gu, 2 * dff, 0,
+                                  (uint32_t)(es * T * d), part, cnt, W.part_floats},
+              0, "gate/up recompute"));
+  if (dfs)
+    TRY(grouped(moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d,
+                                    dfs, d, gus, 2 * dfs, 0, (uint32_t)(es * T * d), part, cnt,
+                                    W.part_floats},
+                0, "shared gate/up recompute"));
+  // 3. v = W_down^T dy per kept row: W_down transposed to [d_ff, d] per expert
+  TRY(pack(w_down, dff, dff, nullptr, 1, nullptr, nullptr, nullptr, 0, d, d, wdT, d, N,
+           (int64_t)d * dff, (int64_t)dff * d, "W_down transpose"));
+  TRY(grouped(moe::GroupedProblem{dy, d, perm, k, offsets, N, rows_all, rows_max, wdT, nullptr,
+                                  (int64_t)dff * d, d, dff, d, v, dff, 0, (uint32_t)(es * T * d),
+                                  part, cnt, W.part_floats},
+              1, "v GEMM"));
+  if (dfs) {
+    TRY(pack(sh_down, dfs, dfs, nullptr, 1, nullptr, nullptr, nullptr, 0, d, d, sdT, d, 1, 0, 0,
+             "shared W_down transpose"));
+    TRY(grouped(moe::GroupedProblem{dy, d, nullptr, 1, nullptr, 1, T, T, sdT, nullptr, 0, d, dfs,
+                                    d, vs, dfs, 0, (uint32_t)(es * T * d), part, cnt,
+                                    W.part_floats},
+                1, "shared v GEMM"));
+  }
+  // 4. SwiGLU backward: act, [dgp | du] in place, dg per slot
+  TRY(hip_check(moe::launch_swiglu_bwd(gu, v, act, dgu, perm, gates, dg, offsets, N, rows_all,
+                                       dff, b, st), "SwiGLU backward"));
+  if (dfs)
+    TRY(hip_check(moe::launch_swiglu_bwd(gus, vs, acts, dgus, nullptr, nullptr, nullptr, nullptr,
+                                         0, T, dfs, b, st), "shared SwiGLU backward"));
+  // 5. router-logit gradient, b_r gradient
+  TRY(hip_check(moe::launch_route_bwd(z_part, splits, b_router, ids, gates, dg, row_of, counts, T,
+                                      N, k, s->mode, s->aux_alpha, d_laux, d_zloss, dz, dzb, Np,
+                                      b, dgates, st), "router backward"));
+  if (db_router) TRY(hip_check(moe::launch_colsum(dz, T, N, db_router, st), "b_r gradient"));
+  // 6. row gradients of h: [W_gate; W_up]^T [dgp | du] per kept row, the
+  //    shared expert's, and the router's dz W_r
+  TRY(pack(w_gate, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dff, dff, wguT, 2 * dff, N,
+           (int64_t)dff * d, (int64_t)d * 2 * dff, "W_gate transpose"));
+  TRY(pack(w_up, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dff, dff, wguT + es * dff,
+           2 * dff, N, (int64_t)dff * d, (int64_t)d * 2 * dff, "W_up transpose"));
+  TRY(grouped(moe::GroupedProblem{dgu, 2 * dff, nullptr, 1, offsets, N, rows_all, rows_max, wguT,
+                                  nullptr, (int64_t)d * 2 * dff, 2 * dff, d, 2 * dff, dhr, d, 0,
+                                  (uint32_t)(es * R * 2 * dff), part, cnt, W.part_floats},
+              2, "dh rows GEMM"));
+  if (dfs) {
+    TRY(pack(sh_gate, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dfs, dfs, sguT, 2 * dfs, 1,
+             0, 0, "shared W_gate transpose"));
+    TRY(pack(sh_up, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dfs, dfs, sguT + es * dfs,
+             2 * dfs, 1, 0, 0, "shared W_up transpose"));
+    TRY(grouped(moe::GroupedProblem{dgus, 2 * dfs, nullptr, 1, nullptr, 1, T, T, sguT, nullptr, 0,
+                                    2 * dfs, d, 2 * dfs, dhs, d, 0, (uint32_t)(es * T * 2 * dfs),
+                                    part, cnt, W.part_floats},
+                2, "shared dh GEMM"));
+  }
+  TRY(pack(w_router, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, N, Np, wrT, Np, 1, 0, 0,
+           "W_r transpose"));
+  TRY(grouped(moe::GroupedProblem{dzb, Np, nullptr, 1, nullptr, 1, T, T, wrT, nullptr, 0, Np, d,
+                                  Np, dhrt, d, 0, (uint32_t)(es * T * Np), part, cnt,
+                                  W.part_floats},
+              2, "router dh GEMM"));
+  TRY(hip_check(moe::launch_dh_combine(dhr, row_of, dfs ? dhs : nullptr, dhrt, dh, T, k, d, b,
+                                       st), "dh combine"));
+  // 7. expert weight gradients over each expert's kept rows (padded K ranges)
+  TRY(hip_check(moe::launch_kofs(offsets, N, 0, kofs, st), "K ranges"));
+  TRY(pack(dy, d, d, perm, k, gates, offsets, kofs, N, 0, Rp, ta, Rp, 1, 0, 0, "dOut transpose"));
+  TRY(pack(act, dff, dff, nullptr, 1, nullptr, offsets, kofs, N, 0, Rp, tb, Rp, 1, 0, 0,
+           "act transpose"));
+  TRY(kgroup(ta, Rp, d, tb, Rp, dff, kofs, N, d, dff, dw_down, (int64_t)d * dff, dff, false,
+             "W_down gradient"));
+  TRY(pack(dgu, 2 * dff, 2 * dff, nullptr, 1, nullptr, offsets, kofs, N, 0, Rp, ta, Rp, 1, 0, 0,
+           "dgu transpose"));
+  TRY(pack(h, d, d, perm, k, nullptr, offsets, kofs, N, 0, Rp, tb, Rp, 1, 0, 0, "h transpose"));
+  TRY(kgroup(ta, Rp, 2 * dff, tb, Rp, d, kofs, N, dff, d, dw_gate, (int64_t)dff * d, d, false,
+             "W_gate gradient"));
+  TRY(kgroup(ta + es * (size_t)dff * Rp, Rp, dff, tb, Rp, d, kofs, N, dff, d, dw_up,
+             (int64_t)dff * d, d, false, "W_up gradient"));
+  // 8. shared-expert and router weight gradients over all tokens
+  TRY(hip_check(moe::launch_kofs(nullptr, 1, T, kofs_t, st), "token K range"));
+  if (dfs) {
+    TRY(pack(dy, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, T, Tp, ta, Tp, 1, 0, 0,
+             "shared dOut transpose"));
+    TRY(pack(acts, dfs, dfs, nullptr, 1, nullptr, nullptr, nullptr, 0, T, Tp, tb, Tp, 1, 0, 0,
+             "shared act transpose"));
+    TRY(kgroup(ta, Tp, d, tb, Tp, dfs, kofs_t, 1, d, dfs, dsh_down, 0, dfs, false,
+               "shared W_down gradient"));
+    TRY(pack(dgus, 2 * dfs, 2 * dfs, nullptr, 1, nullptr, nullptr, nullptr, 0, T, Tp, ta, Tp, 1,
+             0, 0, "shared dgu transpose"));
+  }
+  TRY(pack(h, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, T, Tp, tb, Tp, 1, 0, 0,
+           "h transpose (all tokens)"));
+  if (dfs) {
+    TRY(kgroup(ta, Tp, 2 * dfs, tb, Tp, d, kofs_t, 1, dfs, d, dsh_gate, 0, d, false,
+               "shared W_gate gradient"));
+    TRY(kgroup(ta + es * (size_t)dfs * Tp, Tp, dfs, tb, Tp, d, kofs_t, 1, dfs, d, dsh_up, 0, d,
+               false, "shared W_up gradient"));
+  }
+  TRY(pack(dzb, Np, N, nullptr, 1, nullptr, nullptr, nullptr, 0, T, Tp, ta, Tp, 1, 0, 0,
+           "dz transpose"));
+  if (bf16) {
+    TRY(kgroup(ta, Tp, N, tb, Tp, d, kofs_t, 1, N, d, dw_router, 0, d, true, "W_r gradient"));
+  } else {
+    TRY(kgroup(ta, Tp, N, tb, Tp, d, kofs_t, 1, N, d, dw_router, 0, d, true, "W_r gradient"));
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -503,6 +784,64 @@ moe_status moe_combine(const moe_shape* s, const void* out_rows, const int32_t* 
   TRY(need16(y, "y"));
   if (s->T == 0) return MOE_OK;
   return combine_impl(s, out_rows, row_of, topk_gates, y, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_backward_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return bwd_ws(s).end;
+}
+
+moe_status moe_layer_backward(const moe_shape* s, const void* h, const void* w_router,
+                              const float* b_router, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* sh_gate, const void* sh_up,
+                              const void* sh_down, const int32_t* topk_ids,
+                              const float* topk_gates, const int32_t* counts,
+                              const int32_t* offsets, const int32_t* perm_src,
+                              const int32_t* row_of, const void* dy, float d_laux,
+                              float d_zloss, void* dh, float* dw_router, float* db_router,
+                              void* dw_gate, void* dw_up, void* dw_down, void* dsh_gate,
+                              void* dsh_up, void* dsh_down, float* dgates, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_err.clear();
+  TRY(check_shape(s));
+  TRY(need16(h, "h"));
+  TRY(need16(w_router, "w_router"));
+  TRY(opt4(b_router, "b_router"));
+  TRY(need16(w_gate, "w_gate"));
+  TRY(need16(w_up, "w_up"));
+  TRY(need16(w_down, "w_down"));
+  TRY(check_shared(s, sh_gate, sh_up, sh_down));
+  TRY(need4(topk_ids, "topk_ids"));
+  TRY(need4(topk_gates, "topk_gates"));
+  TRY(need4(counts, "counts"));
+  TRY(need4(offsets, "offsets"));
+  TRY(need4(perm_src, "perm_src"));
+  TRY(need4(row_of, "row_of"));
+  TRY(need16(dy, "dy"));
+  TRY(need16(dh, "dh"));
+  TRY(need4(dw_router, "dw_router"));
+  TRY(opt4(db_router, "db_router"));
+  TRY(need16(dw_gate, "dw_gate"));
+  TRY(need16(dw_up, "dw_up"));
+  TRY(need16(dw_down, "dw_down"));
+  if (s->d_ff_shared) {
+    TRY(need16(dsh_gate, "dsh_gate"));
+    TRY(need16(dsh_up, "dsh_up"));
+    TRY(need16(dsh_down, "dsh_down"));
+  } else if (dsh_gate || dsh_up || dsh_down) {
+    return fail(MOE_ERR_INVALID_ARG, "shared-expert gradients given but d_ff_shared = 0");
+  }
+  TRY(opt4(dgates, "dgates"));
+  if (!std::isfinite(d_laux) || !std::isfinite(d_zloss))
+    return fail(MOE_ERR_INVALID_ARG, "d_laux and d_zloss must be finite");
+  TRY(check_bwd_limits(s));
+  const BwdWs W = bwd_ws(s);
+  TRY(check_ws(ws, ws_bytes, W.end));
+  if (s->T == 0) return MOE_OK;
+  return backward_impl(s, h, w_router, b_router, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
+                       topk_ids, topk_gates, counts, offsets, perm_src, row_of, dy, d_laux,
+                       d_zloss, dh, dw_router, db_router, dw_gate, dw_up, dw_down, dsh_gate,
+                       dsh_up, dsh_down, dgates, ws, W, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_layer_fused(const moe_shape* s, const void* h, const void* w_router,

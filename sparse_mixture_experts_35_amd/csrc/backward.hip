@@ -1,0 +1,496 @@
+// Backward pass of the layer: the kernels around the GEMMs.
+//
+// For the forward pass's selection and dispatch, the gradient of
+// <dy, y> + d_laux L_aux + d_zloss L_z follows the chain rule of the forward
+// steps. The router learns only through the gate values of the selected
+// experts, and through every logit that a normalisation involves (the full
+// softmax of mode B) [page "MoE：router 怎样选 expert" (cooking-agi), section
+// "top-k 不可导，router 怎么学"; page "MOE 专家选择与路由机制" (wuhy-notes),
+// "Top-k 不可导，为什么 Router 还能学" and the total-loss paragraph].
+//
+// Per kept bucket row r (token t, slot j, expert e, gate g):
+//   v_r     = W_down^(e)^T dy_t                       (GEMM, elsewhere; fp32)
+//   dg_tj   = <v_r, act_r> = <dy_t, E_e(h_t)>          (swiglu_bwd_kernel)
+//   dact_r  = g v_r; du = dact SiLU(gp); dgp = dact up SiLU'(gp)
+//   dh rows = W_gate^T dgp + W_up^T du                 (GEMM)
+// and per token the router-logit gradient dz_t (route_bwd_kernel). Weight
+// gradients are GEMMs over each expert's rows, taken as K ranges of
+// transposed, zero-padded copies of the row-major activations (pack_t).
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+template <typename TE>
+__device__ __forceinline__ float ld(const TE* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld<bf16_t>(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <typename TE>
+__device__ __forceinline__ void st(TE* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void st<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void st<bf16_t>(bf16_t* p, int64_t i, float v) {
+  p[i] = (bf16_t)f32_to_bf16(v);
+}
+
+constexpr int kT = 256;
+
+// kofs[e] = sum over e' < e of the kept rows of e' rounded up to 32 (the
+// padded K range of expert e in the transposed copies); with no offsets one
+// range of n_single rows.
+__global__ __launch_bounds__(kT) void kofs_kernel(const int32_t* __restrict__ offsets, int G,
+                                                  int n_single, int32_t* __restrict__ kofs) {
+  __shared__ int s_wave[kT / 64];
+  if (!offsets) {
+    if (threadIdx.x == 0) {
+      kofs[0] = 0;
+      kofs[1] = (n_single + 31) & ~31;
+    }
+    return;
+  }
+  // G <= 512: two entries per thread, in order
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int c[2], sum = 0;
+  for (int i = 0; i < 2; ++i) {
+    const int e = 2 * tid + i;
+    c[i] = e < G ? ((offsets[e + 1] - offsets[e] + 31) & ~31) : 0;
+    sum += c[i];
+  }
+  int incl = sum;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wave[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += s_wave[i];
+  int run = base + incl - sum;
+  for (int i = 0; i < 2; ++i) {
+    const int e = 2 * tid + i;
+    if (e < G) kofs[e] = run;
+    run += c[i];
+    if (e == G - 1) kofs[G] = run;
+  }
+}
+
+// Transposed, padded copy: dst[c][kofs[e] + i] = scale * src[row][c] for the
+// i-th kept row of expert e (bucket row r = offsets[e] + i; source row
+// perm[r] / kdiv, or r without perm; scale = scale[perm[r]] (or [r]), or 1),
+// zero in the padding of each range and up to p_limit. 64 x 64 tiles through
+// LDS; grid (p_limit / 64, ncols / 64, batch): batch b reads src + b *
+// src_bstride and writes dst + b * dst_bstride (per-expert weight copies).
+template <typename TE>
+__global__ __launch_bounds__(kT) void pack_t_kernel(
+    const TE* __restrict__ src, int ld_src, int ncols, const int32_t* __restrict__ perm,
+    int kdiv, const float* __restrict__ scale, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ kofs, int G, int n_single, int64_t p_limit, TE* __restrict__ dst,
+    int64_t ld_dst, int64_t src_bstride, int64_t dst_bstride) {
+  __shared__ float tile[64][65];
+  const int tid = threadIdx.x;
+  src += blockIdx.z * src_bstride;
+  dst += blockIdx.z * dst_bstride;
+  const int64_t p0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  {
+    const int row = tid >> 2, cs = (tid & 3) * 16;
+    const int64_t p = p0 + row;
+    int64_t srow = -1;
+    float sc = 1.0f;
+    if (offsets) {
+      if (p < kofs[G]) {
+        int lo = 0, hi = G;              // kofs[lo] <= p < kofs[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (kofs[mid] <= p) lo = mid; else hi = mid;
+        }
+        const int64_t local = p - kofs[lo];
+        if (local < offsets[lo + 1] - offsets[lo]) {
+          const int64_t r = offsets[lo] + local;
+          srow = perm ? perm[r] / kdiv : r;
+          if (scale) sc = scale[perm ? perm[r] : r];
+        }
+      }
+    } else if (p < n_single) {
+      srow = p;
+      if (scale) sc = scale[p];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = c0 + cs + i;
+      tile[row][cs + i] = (srow >= 0 && c < ncols) ? sc * ld(src, srow * ld_src + c) : 0.0f;
+    }
+  }
+  __syncthreads();
+  {
+    const int crow = tid >> 2, ps = (tid & 3) * 16;
+    const int c = c0 + crow;
+    if (c < ncols) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t p = p0 + ps + i;
+        if (p < p_limit) st(dst, (int64_t)c * ld_dst + p, tile[ps + i][crow]);
+      }
+    }
+  }
+}
+
+// One block per bucket row r < rows (rows = offsets[G], or the grid):
+// gu[r] = [gp | up] and v[r] in fp32; act[r] = SiLU(gp) up and
+// dgu[r] = [dgp | du] out in the layer dtype; dg_slot[perm[r]] = <v_r, act_r>
+// in fp32 from the fp32 inputs (fixed-order block reduction). The
+// pre-activations and v stay fp32 because dg is a dot product that can
+// cancel.
+template <typename TO>
+__global__ __launch_bounds__(kT) void swiglu_bwd_kernel(
+    const float* __restrict__ gu, const float* __restrict__ v, TO* __restrict__ act,
+    TO* __restrict__ dgu, const int32_t* __restrict__ perm, const float* __restrict__ gates,
+    float* __restrict__ dg_slot, const int32_t* __restrict__ offsets, int G, int d_ff) {
+  __shared__ float s_red[kT];
+  const int64_t r = blockIdx.x;
+  if (offsets && r >= offsets[G]) return;
+  const int tid = threadIdx.x;
+  const float g = gates ? gates[perm[r]] : 1.0f;
+  const float* gr = gu + r * 2 * d_ff;
+  const float* vr = v + r * d_ff;
+  TO* ar = act + r * d_ff;
+  TO* dr = dgu + r * 2 * d_ff;
+  float dot = 0.0f;
+  for (int j = tid; j < d_ff; j += kT) {
+    const float gp = gr[j], up = gr[d_ff + j], vv = vr[j];
+    const float s = 1.0f / (1.0f + expf(-gp));
+    const float si = gp * s;
+    const float a = si * up;
+    dot = fmaf(vv, a, dot);
+    const float dact = g * vv;
+    st(ar, j, a);
+    st(dr, j, dact * up * s * (1.0f + gp * (1.0f - s)));
+    st(dr, d_ff + j, dact * si);
+  }
+  if (!dg_slot) return;
+  s_red[tid] = dot;
+  __syncthreads();
+  for (int o = kT / 2; o > 0; o >>= 1) {
+    if (tid < o) s_red[tid] += s_red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) dg_slot[perm[r]] = s_red[0];
+}
+
+// One wave per token: router-logit gradient dz_t [N] (fp32 and a bf16 copy
+// zero-padded to ldzb columns). z_t is re-formed from the split-K slices in
+// the forward's order. Task part through the selected gates (dg of a
+// dropped slot is 0); L_aux part (f_i = counts_i / (T k) constant, p_i the
+// mean routing probability); z-loss part (2 / T) LSE_t softmax(z_t).
+constexpr int kMaxPerLane = 8;   // N <= 512
+template <typename TZ>
+__global__ __launch_bounds__(64) void route_bwd_kernel(
+    const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
+    const int32_t* __restrict__ ids, const float* __restrict__ gates,
+    const float* __restrict__ dg_slot, const int32_t* __restrict__ row_of,
+    const int32_t* __restrict__ counts, int T, int N, int k, int mode, float alpha,
+    float d_laux, float d_zloss, float* __restrict__ dz, TZ* __restrict__ dzb, int ldzb,
+    float* __restrict__ dg_out) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const int64_t TN = (int64_t)T * N;
+  float z[kMaxPerLane], dzl[kMaxPerLane];
+  float m = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kMaxPerLane; ++q) {
+    const int i = lane + 64 * q;
+    float v = -INFINITY;
+    if (i < N) {
+      const float* zp = z_part + (int64_t)t * N + i;
+      v = 0.0f;
+      for (int s = 0; s < splits; ++s) v += zp[s * TN];
+      if (b_router) v += b_router[i];
+    }
+    z[q] = v;
+    dzl[q] = 0.0f;
+    m = fmaxf(m, v);
+  }
+  m = wave_max(m);
+  float se = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kMaxPerLane; ++q) se += (lane + 64 * q < N) ? expf(z[q] - m) : 0.0f;
+  se = wave_sum(se);
+  const float lse = m + logf(se);
+  auto P = [&](int q) { return expf(z[q] - m) / se; };   // softmax probability
+  auto sig = [&](float x) { return 1.0f / (1.0f + expf(-x)); };
+
+  // ---- task gradient through the selected gates
+  const int64_t f0 = (int64_t)t * k;
+  float inner = 0.0f, inner_p = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const float dgj = row_of[f0 + j] >= 0 ? dg_slot[f0 + j] : 0.0f;
+    inner += gates[f0 + j] * dgj;
+    if (dg_out && lane == 0) dg_out[f0 + j] = dgj;
+  }
+  // per-slot values are uniform across the wave: read them in the loop
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[f0 + j];
+    const float dgj = row_of[f0 + j] >= 0 ? dg_slot[f0 + j] : 0.0f;
+    const float gj = gates[f0 + j];
+    const int q = e >> 6;
+    if (mode == 0) {
+      if ((e & 63) == lane) {
+#pragma unroll
+        for (int qq = 0; qq < kMaxPerLane; ++qq)
+          if (qq == q) dzl[qq] += gj * (dgj - inner);
+      }
+    } else if (mode == 1) {
+      // a_i = dg at the selected experts; dz_i = P_i (a_i - sum_l P_l a_l)
+      if ((e & 63) == lane) {
+#pragma unroll
+        for (int qq = 0; qq < kMaxPerLane; ++qq)
+          if (qq == q) dzl[qq] += P(qq) * dgj;
+      }
+    }
+  }
+  if (mode == 1) {
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[f0 + j];
+      const float dgj = row_of[f0 + j] >= 0 ? dg_slot[f0 + j] : 0.0f;
+      float pe = 0.0f;
+      if ((e & 63) == lane) {
+#pragma unroll
+        for (int qq = 0; qq < kMaxPerLane; ++qq)
+          if (qq == (e >> 6)) pe = P(qq);
+      }
+      inner_p += wave_sum(pe) * dgj;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; ++q)
+      if (lane + 64 * q < N) dzl[q] -= P(q) * inner_p;
+  }
+  if (mode == 2) {
+    // s_sel = sigmoid of the selected logits, S = their sum
+    float S = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[f0 + j];
+      float ze = 0.0f;
+      if ((e & 63) == lane) {
+#pragma unroll
+        for (int qq = 0; qq < kMaxPerLane; ++qq)
+          if (qq == (e >> 6)) ze = z[qq];
+      }
+      S += sig(wave_sum(ze));
+    }
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[f0 + j];
+      const float dgj = row_of[f0 + j] >= 0 ? dg_slot[f0 + j] : 0.0f;
+      if ((e & 63) == lane) {
+#pragma unroll
+        for (int qq = 0; qq < kMaxPerLane; ++qq)
+          if (qq == (e >> 6)) {
+            const float s = sig(z[qq]);
+            dzl[qq] += (dgj - inner) / S * s * (1.0f - s);
+          }
+      }
+    }
+  }
+
+  // ---- L_aux: dL/dP_ti = d_laux alpha N f_i / T
+  if (d_laux != 0.0f) {
+    const float cst = d_laux * alpha * (float)N / ((float)T * (float)T * (float)k);
+    float a[kMaxPerLane];
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; ++q) {
+      const int i = lane + 64 * q;
+      a[q] = i < N ? cst * (float)counts[i] : 0.0f;
+    }
+    if (mode == 2) {
+      float S = 0.0f, pa = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kMaxPerLane; ++q)
+        if (lane + 64 * q < N) S += sig(z[q]);
+      S = wave_sum(S);
+#pragma unroll
+      for (int q = 0; q < kMaxPerLane; ++q)
+        if (lane + 64 * q < N) pa += sig(z[q]) / S * a[q];
+      pa = wave_sum(pa);
+#pragma unroll
+      for (int q = 0; q < kMaxPerLane; ++q)
+        if (lane + 64 * q < N) {
+          const float s = sig(z[q]);
+          dzl[q] += (a[q] - pa) / S * s * (1.0f - s);
+        }
+    } else {
+      float pa = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kMaxPerLane; ++q)
+        if (lane + 64 * q < N) pa += P(q) * a[q];
+      pa = wave_sum(pa);
+#pragma unroll
+      for (int q = 0; q < kMaxPerLane; ++q)
+        if (lane + 64 * q < N) dzl[q] += P(q) * (a[q] - pa);
+    }
+  }
+  // ---- z-loss
+  if (d_zloss != 0.0f) {
+    const float c = d_zloss * 2.0f / (float)T * lse;
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; ++q)
+      if (lane + 64 * q < N) dzl[q] += c * P(q);
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxPerLane; ++q) {
+    const int i = lane + 64 * q;
+    if (i < N) dz[(int64_t)t * N + i] = dzl[q];
+    if (i < ldzb) st(dzb, (int64_t)t * ldzb + i, i < N ? dzl[q] : 0.0f);
+  }
+}
+
+// db[i] = sum_t dz[t][i] in a fixed order: four partial sums over quarters
+// of the tokens, added in order.
+__global__ __launch_bounds__(kT) void colsum_kernel(const float* __restrict__ dz, int T, int N,
+                                                    float* __restrict__ db) {
+  __shared__ float s_part[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
+  const int t0 = (int)((int64_t)T * w / 4), t1 = (int)((int64_t)T * (w + 1) / 4);
+  float s = 0.0f;
+  if (i < N)
+    for (int t = t0; t < t1; ++t) s += dz[(int64_t)t * N + i];
+  s_part[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && i < N) db[i] = ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
+}
+
+// dh[t] = sum_j rows[row_of[t k + j]] (kept slots, slot order) + shared[t]
+// + router[t], accumulated in fp32.
+template <typename TE>
+__global__ __launch_bounds__(kT) void dh_combine_kernel(
+    const TE* __restrict__ rows, const int32_t* __restrict__ row_of,
+    const TE* __restrict__ shared, const TE* __restrict__ router, TE* __restrict__ dh, int k,
+    int d) {
+  const int64_t t = blockIdx.x;
+  for (int c = threadIdx.x; c < d; c += kT) {
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = row_of[t * k + j];
+      if (r >= 0) acc += ld(rows, r * d + c);
+    }
+    if (shared) acc += ld(shared, t * d + c);
+    acc += ld(router, t * d + c);
+    st(dh, t * d + c, acc);
+  }
+}
+
+// fp32 weight gradients: C_g[m][n] = sum over k in [kofs[g], kofs[g+1]) of
+// A[m][k] B[n][k]; one thread per output element.
+__global__ void kgroup_f32_kernel(const float* __restrict__ A, int lda,
+                                  const float* __restrict__ B, int ldb,
+                                  const int32_t* __restrict__ kofs, int M, int Ncols,
+                                  float* __restrict__ C, int64_t c_gstride, int ldc) {
+  const int g = blockIdx.y;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * Ncols) return;
+  const int m = (int)(idx / Ncols), n = (int)(idx % Ncols);
+  const int k0 = kofs[g], k1 = kofs[g + 1];
+  const float* a = A + (int64_t)m * lda;
+  const float* b = B + (int64_t)n * ldb;
+  float s = 0.0f;
+  for (int kk = k0; kk < k1; ++kk) s = fmaf(a[kk], b[kk], s);
+  C[(int64_t)g * c_gstride + (int64_t)m * ldc + n] = s;
+}
+
+}  // namespace
+
+hipError_t launch_kofs(const int32_t* offsets, int G, int n_single, int32_t* kofs,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(kofs_kernel, dim3(1), dim3(kT), 0, st, offsets, G, n_single, kofs);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_t(const void* src, int ld_src, int ncols, const int32_t* perm, int kdiv,
+                         const float* scale, const int32_t* offsets, const int32_t* kofs, int G,
+                         int n_single, int64_t p_limit, void* dst, int64_t ld_dst, int bf16,
+                         hipStream_t st, int batch, int64_t src_bstride, int64_t dst_bstride) {
+  if (p_limit == 0 || ncols == 0 || batch == 0) return hipSuccess;
+  dim3 grid((unsigned)((p_limit + 63) / 64), (unsigned)((ncols + 63) / 64), (unsigned)batch);
+  if (bf16)
+    hipLaunchKernelGGL(pack_t_kernel<bf16_t>, grid, dim3(kT), 0, st,
+                       static_cast<const bf16_t*>(src), ld_src, ncols, perm, kdiv, scale, offsets,
+                       kofs, G, n_single, p_limit, static_cast<bf16_t*>(dst), ld_dst, src_bstride,
+                       dst_bstride);
+  else
+    hipLaunchKernelGGL(pack_t_kernel<float>, grid, dim3(kT), 0, st,
+                       static_cast<const float*>(src), ld_src, ncols, perm, kdiv, scale, offsets,
+                       kofs, G, n_single, p_limit, static_cast<float*>(dst), ld_dst, src_bstride,
+                       dst_bstride);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const float* gu, const float* v, void* act, void* dgu,
+                             const int32_t* perm, const float* gates, float* dg_slot,
+                             const int32_t* offsets, int G, int rows_bound, int d_ff, int bf16,
+                             hipStream_t st) {
+  if (rows_bound == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(swiglu_bwd_kernel<bf16_t>, dim3(rows_bound), dim3(kT), 0, st, gu, v,
+                       static_cast<bf16_t*>(act), static_cast<bf16_t*>(dgu), perm, gates, dg_slot,
+                       offsets, G, d_ff);
+  else
+    hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(rows_bound), dim3(kT), 0, st, gu, v,
+                       static_cast<float*>(act), static_cast<float*>(dgu), perm, gates, dg_slot,
+                       offsets, G, d_ff);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const float* z_part, int splits, const float* b_router,
+                            const int32_t* ids, const float* gates, const float* dg_slot,
+                            const int32_t* row_of, const int32_t* counts, int T, int N, int k,
+                            int mode, float alpha, float d_laux, float d_zloss, float* dz,
+                            void* dzb, int ldzb, int bf16, float* dg_out, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(route_bwd_kernel<bf16_t>, dim3(T), dim3(64), 0, st, z_part, splits,
+                       b_router, ids, gates, dg_slot, row_of, counts, T, N, k, mode, alpha,
+                       d_laux, d_zloss, dz, static_cast<bf16_t*>(dzb), ldzb, dg_out);
+  else
+    hipLaunchKernelGGL(route_bwd_kernel<float>, dim3(T), dim3(64), 0, st, z_part, splits,
+                       b_router, ids, gates, dg_slot, row_of, counts, T, N, k, mode, alpha,
+                       d_laux, d_zloss, dz, static_cast<float*>(dzb), ldzb, dg_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const float* dz, int T, int N, float* db, hipStream_t st) {
+  hipLaunchKernelGGL(colsum_kernel, dim3((N + 63) / 64), dim3(kT), 0, st, dz, T, N, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_combine(const void* rows, const int32_t* row_of, const void* shared,
+                             const void* router, void* dh, int T, int k, int d, int bf16,
+                             hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(dh_combine_kernel<bf16_t>, dim3(T), dim3(kT), 0, st,
+                       static_cast<const bf16_t*>(rows), row_of,
+                       static_cast<const bf16_t*>(shared), static_cast<const bf16_t*>(router),
+                       static_cast<bf16_t*>(dh), k, d);
+  else
+    hipLaunchKernelGGL(dh_combine_kernel<float>, dim3(T), dim3(kT), 0, st,
+                       static_cast<const float*>(rows), row_of, static_cast<const float*>(shared),
+                       static_cast<const float*>(router), static_cast<float*>(dh), k, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_kgroup_f32(const float* A, int lda, const float* B, int ldb,
+                             const int32_t* kofs, int groups, int M, int Ncols, float* C,
+                             int64_t c_gstride, int ldc, hipStream_t st) {
+  const int64_t n = (int64_t)M * Ncols;
+  if (n == 0 || groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(kgroup_f32_kernel, dim3((unsigned)((n + 255) / 256), groups), dim3(256), 0,
+                     st, A, lda, B, ldb, kofs, M, Ncols, C, c_gstride, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace moe

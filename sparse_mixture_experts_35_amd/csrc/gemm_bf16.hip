@@ -272,7 +272,14 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[C::NB][C::FM][C::FN]) {
         for (int i = 0; i < 16; ++i) acc[nb][fm][fn][i] = 0.0f;
 }
 
-enum Epi { EPI_SWIGLU = 0, EPI_STORE_BF16 = 1 };
+// SWIGLU: SiLU(gate)·up; STORE_BF16: the accumulator; STORE_DUAL: the gate
+// and up accumulators side by side, gate in columns [0, Ncols) and up in
+// [Ncols, 2 Ncols) of each output row (the backward pass's recompute of the
+// pre-activations).
+// STORE_F32 / STORE_DUAL_F32: the same as fp32 (the backward pass's
+// intermediates that feed a reduction).
+enum Epi { EPI_SWIGLU = 0, EPI_STORE_BF16 = 1, EPI_STORE_DUAL = 2, EPI_STORE_F32 = 3,
+           EPI_STORE_DUAL_F32 = 4 };
 
 // Output column of MFMA block fn, lane column lr, in a wave's TN-wide strip:
 // B rows are staged so that blocks 2j and 2j+1 hold the even and odd columns
@@ -290,10 +297,13 @@ __device__ __forceinline__ int strip_col(int fn, int lr) {
 // out-of-range offset, so there are no branches.
 template <class C, int EPI>
 __device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][C::FN],
-                                              bf16_t* __restrict__ Cout, int64_t ldc,
+                                              void* __restrict__ Cout, int64_t ldc,
                                               int64_t row0_out, int rows_valid, int n0,
                                               int Ncols) {
   static_assert(C::FN % 2 == 0, "column pairs need an even number of MFMA blocks");
+  constexpr bool F32 = EPI == EPI_STORE_F32 || EPI == EPI_STORE_DUAL_F32;
+  constexpr bool TWO = EPI == EPI_STORE_DUAL || EPI == EPI_STORE_DUAL_F32;
+  constexpr int ES = F32 ? 4 : 2;      // output element bytes
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave index, tile origin and extent are uniform: keep them scalar (they
@@ -309,9 +319,10 @@ __device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][
   row0_out = (int64_t)(((uint64_t)r0hi << 32) | r0lo);
   // Row stride in bytes, made opaque so the compiler recomputes the row
   // offsets per tile instead of hoisting (and spilling) all of them.
-  int ldc2 = (int)ldc * 2;
+  int ldc2 = (int)ldc * ES;
   asm volatile("" : "+s"(ldc2));
-  const Rsrc out = make_rsrc(Cout + row0_out * ldc, (uint32_t)rows_valid * (uint32_t)ldc2);
+  const Rsrc out = make_rsrc(static_cast<char*>(Cout) + row0_out * ldc * ES,
+                             (uint32_t)rows_valid * (uint32_t)ldc2);
   const uint32_t lane_row = (uint32_t)(4 * lh) * (uint32_t)ldc2;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
@@ -320,10 +331,34 @@ __device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][
 #pragma unroll
     for (int fe = 0; fe < C::FN; fe += 2) {
       const int col = n0 + wn * C::TN + strip_col(fe, lr);
-      const uint32_t voff = col < Ncols ? lane_row + (uint32_t)col * 2u : 0xC0000000u;
+      const uint32_t voff = col < Ncols ? lane_row + (uint32_t)col * ES : 0xC0000000u;
+      const uint32_t voff_up = col < Ncols ? voff + (uint32_t)Ncols * ES : 0xC0000000u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int rrow = rb + 8 * (i >> 2) + (i & 3);   // + 4*lh (in voff)
+        static_assert(!TWO || C::DUAL, "storing gate and up needs both");
+        if constexpr (F32) {
+          // two 4-byte stores per column pair (a 2-vector 8-byte store built
+          // here was compiled to store one row's data to every row)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0][fm][fe + h2][i]), out,
+                                                  voff + 4 * h2, rrow * ldc2, 0);
+            if constexpr (TWO)
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __float_as_uint(acc[C::NB - 1][fm][fe + h2][i]), out, voff_up + 4 * h2,
+                  rrow * ldc2, 0);
+          }
+          continue;
+        }
+        if constexpr (TWO) {
+          __builtin_amdgcn_raw_buffer_store_b32(
+              pack_bf16x2_hw(acc[0][fm][fe][i], acc[0][fm][fe + 1][i]), out, voff, rrow * ldc2, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              pack_bf16x2_hw(acc[C::NB - 1][fm][fe][i], acc[C::NB - 1][fm][fe + 1][i]), out,
+              voff_up, rrow * ldc2, 0);
+          continue;
+        }
         float v0, v1;
         if (EPI == EPI_SWIGLU) {
           v0 = silu_fast(acc[0][fm][fe][i]) * acc[C::NB - 1][fm][fe][i];
@@ -676,7 +711,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
       }
     }
     if (write)
-      epilogue_bf16<C, EPI>(acc, static_cast<bf16_t*>(p.C), p.ldc, p.c_row0 + ti.m0,
+      epilogue_bf16<C, EPI>(acc, p.C, p.ldc, p.c_row0 + ti.m0,
                             ti.m_end - ti.m0, ti.n0, p.Ncols);
     if (dynamic) {
       __syncthreads();                 // every thread has read s_item / s_last
@@ -689,6 +724,58 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
 
 __global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// Weight gradients: C_g = A[:, K_g] · B[:, K_g]^T for every group g, with
+// K_g = [kofs[g], kofs[g+1]) (multiples of 32, possibly empty) a column
+// range of the K-contiguous operands A [M rows, lda] and B [Ncols rows, ldb]
+// (the backward pass's transposed activations, one padded K range per
+// expert). C_g is [M, Ncols] at C + g * c_gstride, row-major with ldc,
+// written as bf16 or fp32. Grid: (m-tiles x n-tiles, groups).
+template <class C, bool F32OUT>
+__global__ __launch_bounds__(kThreads, C::OCC) void kgroup_gemm_kernel(
+    const bf16_t* __restrict__ A, int lda, uint32_t a_bytes, const bf16_t* __restrict__ B,
+    int ldb, uint32_t b_bytes, const int32_t* __restrict__ kofs, int M, int Ncols,
+    void* __restrict__ Cout, int64_t c_gstride, int ldc) {
+  __shared__ __attribute__((aligned(1024))) char S0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S3[C::STAGES == 4 ? C::STAGE : 1024];
+  const int g = blockIdx.y;
+  const int nt_n = (Ncols + C::BN - 1) / C::BN;
+  const int m0 = (int)(blockIdx.x / nt_n) * C::BM, n0 = (int)(blockIdx.x % nt_n) * C::BN;
+  const int k_begin = __builtin_amdgcn_readfirstlane(kofs[g]);
+  const int k_len = __builtin_amdgcn_readfirstlane(kofs[g + 1]) - k_begin;
+  f32x16 acc[C::NB][C::FM][C::FN];
+  zero_acc<C>(acc);
+  if (k_len > 0) {
+    uint32_t aoff[C::NAW], boff[C::NBW];
+    dma_offsets<C>(aoff, boff, nullptr, 1, lda, m0, M, ldb, n0, Ncols);
+    const Rsrc rA = make_rsrc(A, a_bytes), rB = make_rsrc(B, b_bytes);
+    const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / C::WN;
+    const int v = min(max((M - m0 - wm * C::TM + 31) / 32, 0), C::FM);
+    mainloop_rows<C, C::FM>(v, S0, S1, S2, S3, rA, aoff, rB, rB, boff, k_begin, k_len, acc);
+  }
+  if constexpr (F32OUT) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int lr = lane & 31, lh = lane >> 5;
+    float* out = static_cast<float*>(Cout) + (int64_t)g * c_gstride;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int col = n0 + wn * C::TN + strip_col(fn, lr);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = m0 + wm * C::TM + fm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+          if (r < M && col < Ncols) out[(int64_t)r * ldc + col] = acc[0][fm][fn][i];
+        }
+      }
+  } else {
+    epilogue_bf16<C, EPI_STORE_BF16>(acc, static_cast<bf16_t*>(Cout) + (int64_t)g * c_gstride,
+                                     ldc, m0, min(C::BM, M - m0), n0, Ncols);
+  }
 }
 
 // Router logits as a split-K GEMM: z_part[s][T][N] = h[:, Ks] · W_r[:, Ks]^T.
@@ -931,6 +1018,43 @@ hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu, hipStream_t st)
   if (tall_tiles(p, Down256::BN, num_cu))
     return launch_grouped<Down256, EPI_STORE_BF16>(p, num_cu, st);
   return launch_grouped<Down128, EPI_STORE_BF16>(p, num_cu, st);
+}
+
+// Gate and up pre-activations of the routed rows as fp32, side by side in C
+// (ldc = 2 Ncols): the same tiles and schedule as the SwiGLU launch, any row
+// count.
+hipError_t launch_gateup_preact_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
+  if (tall_tiles(p, GateUp256::BN, num_cu))
+    return launch_grouped<GateUp256, EPI_STORE_DUAL_F32>(p, num_cu, st);
+  return launch_grouped<GateUp128, EPI_STORE_DUAL_F32>(p, num_cu, st);
+}
+
+// C = A·B0^T stored as fp32, any row count (the grouped tiles only).
+hipError_t launch_down_f32out_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
+  if (tall_tiles(p, Down256::BN, num_cu))
+    return launch_grouped<Down256, EPI_STORE_F32>(p, num_cu, st);
+  return launch_grouped<Down128, EPI_STORE_F32>(p, num_cu, st);
+}
+
+hipError_t launch_kgroup_bf16(const void* A_, int lda, int64_t a_rows, const void* B_, int ldb,
+                              int64_t b_rows, const int32_t* kofs, int groups, int M, int Ncols,
+                              void* C, int64_t c_gstride, int ldc, bool f32out, hipStream_t st) {
+  if (groups == 0 || M == 0 || Ncols == 0) return hipSuccess;
+  const bf16_t* A = static_cast<const bf16_t*>(A_);
+  const bf16_t* B = static_cast<const bf16_t*>(B_);
+  const uint32_t ab = (uint32_t)(a_rows * lda * 2), bb = (uint32_t)(b_rows * ldb * 2);
+  if (f32out) {
+    using K = Router;
+    dim3 grid((unsigned)(((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN)), groups);
+    hipLaunchKernelGGL((kgroup_gemm_kernel<K, true>), grid, dim3(kThreads), 0, st, A, lda, ab, B,
+                       ldb, bb, kofs, M, Ncols, C, c_gstride, ldc);
+  } else {
+    using K = Down128;
+    dim3 grid((unsigned)(((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN)), groups);
+    hipLaunchKernelGGL((kgroup_gemm_kernel<K, false>), grid, dim3(kThreads), 0, st, A, lda, ab, B,
+                       ldb, bb, kofs, M, Ncols, C, c_gstride, ldc);
+  }
+  return hipGetLastError();
 }
 
 int64_t split_part_floats(int64_t M, int G, int Ncols, bool dual) {

@@ -38,6 +38,28 @@ __global__ void gateup_f32_kernel(GroupedProblem p) {
   static_cast<float*>(p.C)[(p.c_row0 + r) * p.ldc + n] = silu_precise(sg) * su;
 }
 
+// Gate and up pre-activations side by side (ldc = 2 Ncols): the backward
+// pass's recompute.
+__global__ void gateup_preact_f32_kernel(GroupedProblem p) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)p.M * p.Ncols) return;
+  const int r = (int)(idx / p.Ncols), n = (int)(idx % p.Ncols);
+  if (p.offsets && r >= p.offsets[p.groups]) return;
+  const int g = group_of(p.offsets, p.groups, r);
+  const int src = p.perm ? p.perm[r] / p.kdiv : r;
+  const float* a = static_cast<const float*>(p.A) + (int64_t)src * p.lda;
+  const float* wg = static_cast<const float*>(p.B0) + g * p.b_gstride + (int64_t)n * p.ldb;
+  const float* wu = static_cast<const float*>(p.B1) + g * p.b_gstride + (int64_t)n * p.ldb;
+  float sg = 0.0f, su = 0.0f;
+  for (int c = 0; c < p.K; ++c) {
+    sg = fmaf(a[c], wg[c], sg);
+    su = fmaf(a[c], wu[c], su);
+  }
+  float* out = static_cast<float*>(p.C) + (p.c_row0 + r) * p.ldc;
+  out[n] = sg;
+  out[p.Ncols + n] = su;
+}
+
 __global__ void down_f32_kernel(GroupedProblem p) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)p.M * p.Ncols) return;
@@ -58,6 +80,14 @@ hipError_t launch_gateup_f32(const GroupedProblem& p, hipStream_t st) {
   const int64_t n = (int64_t)p.M * p.Ncols;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(gateup_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_preact_f32(const GroupedProblem& p, hipStream_t st) {
+  const int64_t n = (int64_t)p.M * p.Ncols;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gateup_preact_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     st, p);
   return hipGetLastError();
 }
 

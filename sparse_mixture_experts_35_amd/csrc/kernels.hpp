@@ -92,9 +92,65 @@ hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu,
 // C = A·B0^T                        (bf16 in/out, fp32 accumulate)
 hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu,
                             hipStream_t st);
+// gate and up pre-activations side by side as fp32: C [rows, 2 Ncols] float,
+// ldc = 2 Ncols
+hipError_t launch_gateup_preact_bf16(const GroupedProblem& p, int num_cu,
+                                     hipStream_t st);
+// C = A·B0^T (bf16 in, fp32 out)
+hipError_t launch_down_f32out_bf16(const GroupedProblem& p, int num_cu,
+                                   hipStream_t st);
+// C_g = A[:, kofs[g]:kofs[g+1]] · B[:, kofs[g]:kofs[g+1]]^T for g < groups
+// (A [a_rows, lda] and B [b_rows, ldb] bf16, K ranges multiples of 32);
+// C_g [M, Ncols] at C + g * c_gstride elements, bf16 or fp32 (f32out)
+hipError_t launch_kgroup_bf16(const void* A, int lda, int64_t a_rows,
+                              const void* B, int ldb, int64_t b_rows,
+                              const int32_t* kofs, int groups, int M, int Ncols,
+                              void* C, int64_t c_gstride, int ldc, bool f32out,
+                              hipStream_t st);
 // fp32 versions (plain FMA kernels)
 hipError_t launch_gateup_f32(const GroupedProblem& p, hipStream_t st);
 hipError_t launch_down_f32(const GroupedProblem& p, hipStream_t st);
+
+hipError_t launch_gateup_preact_f32(const GroupedProblem& p, hipStream_t st);
+
+// ---------------------------------------------------------------- backward
+// Padded K ranges: kofs[e] = sum over e' < e of round32(kept rows of e'),
+// kofs[G] the total; offsets NULL: kofs = {0, round32(n_single)}.
+hipError_t launch_kofs(const int32_t* offsets, int G, int n_single,
+                       int32_t* kofs, hipStream_t st);
+// dst[c][kofs[e] + i] = scale * src[row][c] for the i-th kept row of expert
+// e (row = perm[r] / kdiv or r; scale from scale[perm[r]] or scale[r]);
+// zeros in the padding, for padded indices below p_limit
+hipError_t launch_pack_t(const void* src, int ld_src, int ncols,
+                         const int32_t* perm, int kdiv, const float* scale,
+                         const int32_t* offsets, const int32_t* kofs, int G,
+                         int n_single, int64_t p_limit, void* dst,
+                         int64_t ld_dst, int bf16, hipStream_t st,
+                         int batch = 1, int64_t src_bstride = 0,
+                         int64_t dst_bstride = 0);
+// gu [rows, 2 d_ff] = [gp | up] and v [rows, d_ff] fp32 in; act [rows, d_ff]
+// and dgu [rows, 2 d_ff] = [dgp | du] out (bf16 or fp32); dg_slot[perm[r]]
+// = <v_r, act_r> (nullable; gates NULL: gate 1)
+hipError_t launch_swiglu_bwd(const float* gu, const float* v, void* act,
+                             void* dgu, const int32_t* perm, const float* gates,
+                             float* dg_slot, const int32_t* offsets, int G,
+                             int rows_bound, int d_ff, int bf16, hipStream_t st);
+hipError_t launch_route_bwd(const float* z_part, int splits,
+                            const float* b_router, const int32_t* ids,
+                            const float* gates, const float* dg_slot,
+                            const int32_t* row_of, const int32_t* counts, int T,
+                            int N, int k, int mode, float alpha, float d_laux,
+                            float d_zloss, float* dz, void* dzb, int ldzb,
+                            int bf16, float* dg_out, hipStream_t st);
+hipError_t launch_colsum(const float* dz, int T, int N, float* db,
+                         hipStream_t st);
+hipError_t launch_dh_combine(const void* rows, const int32_t* row_of,
+                             const void* shared, const void* router, void* dh,
+                             int T, int k, int d, int bf16, hipStream_t st);
+hipError_t launch_kgroup_f32(const float* A, int lda, const float* B, int ldb,
+                             const int32_t* kofs, int groups, int M, int Ncols,
+                             float* C, int64_t c_gstride, int ldc,
+                             hipStream_t st);
 
 // ---------------------------------------------------------------- combine
 hipError_t launch_combine(const void* out_rows, const int32_t* row_of,

@@ -184,3 +184,42 @@ def test_header_compiles(lang, compiler, tmp_path):
     r = subprocess.run([compiler, "-fsyntax-only", "-Wall", "-Werror", "-I", os.path.dirname(HDR),
                         str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def backward(s, **over):
+    names = ["h", "w_router", "b_router", "w_gate", "w_up", "w_down", "sh_gate", "sh_up",
+             "sh_down", "topk_ids", "topk_gates", "counts", "offsets", "perm_src", "row_of", "dy"]
+    outs = ["dh", "dw_router", "db_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up",
+            "dsh_down", "dgates"]
+    args = {n: FAKE for n in names + outs}
+    for n in ("b_router", "sh_gate", "sh_up", "sh_down", "db_router", "dsh_gate", "dsh_up",
+              "dsh_down", "dgates"):
+        args[n] = None
+    args.update(d_laux=0.0, d_zloss=0.0, ws=FAKE, ws_bytes=1 << 40)
+    args.update(over)
+    lib = M.lib()
+    st = lib.moe_layer_backward(ctypes.byref(s), *[args[n] for n in names], args["d_laux"],
+                                args["d_zloss"], *[args[n] for n in outs], args["ws"],
+                                args["ws_bytes"], None)
+    return st, lib.moe_last_error().decode()
+
+
+def test_backward_validates():
+    s = shape()
+    assert M.backward_workspace_bytes(s) > M.workspace_bytes(s) > 0
+    assert M.backward_workspace_bytes(shape(k=9)) == 0
+    assert backward(shape(T=0), ws_bytes=M.backward_workspace_bytes(shape(T=0)))[0] == M.OK
+    st, err = backward(s, dy=None)
+    assert st == M.ERR_INVALID_ARG and "dy" in err
+    st, err = backward(s, dw_router=FAKE + 2)
+    assert st == M.ERR_INVALID_ARG and "dw_router" in err
+    st, err = backward(s, dsh_gate=FAKE)
+    assert st == M.ERR_INVALID_ARG and "d_ff_shared" in err
+    st, err = backward(shape(d_ff_shared=128), sh_gate=FAKE, sh_up=FAKE, sh_down=FAKE)
+    assert st == M.ERR_INVALID_ARG and "dsh_gate" in err
+    st, err = backward(s, d_laux=float("nan"))
+    assert st == M.ERR_INVALID_ARG and "finite" in err
+    st, err = backward(s, ws_bytes=M.backward_workspace_bytes(s) - 1)
+    assert st == M.ERR_WORKSPACE
+    st, err = backward(shape(T=1 << 20, d=4096, d_ff=14336, N=8, k=2))
+    assert st == M.ERR_UNSUPPORTED and "2^31" in err
