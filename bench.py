@@ -20,6 +20,9 @@ inputs are already resident in HBM. Prints ONE JSON line.
             while the kernel sources match the ones that were counted
   decode    the same layer at a decode batch (16 tokens) on the same
             weights: tokens/s and HBM GB/s of the touched experts' weights
+  backward  moe_layer_backward on the same workload (the forward's selection
+            made once beforehand): ms per call and the algorithmic TFLOP/s of
+            the gradients (2x the forward's expert flops plus the router's)
   variants  the fine-grained skewed layer (128 experts, top-8) dropless and
             with expert capacity 1.25 (capacity usage, dropped fraction),
             and the DeepSeek-V3-shaped layer without and with group-limited
@@ -217,6 +220,75 @@ def run_variant(M, torch, w, steps, warmup):
     torch.cuda.empty_cache()
     return out
 
+
+def run_backward(M, torch, w, inp, steps, warmup):
+    """moe_layer_backward on the workload: the forward's selection and
+    dispatch are made once (moe_route, moe_dispatch) before the clock
+    starts; each timed step is one backward call (recomputing the router
+    logits and gate/up pre-activations) with a fixed upstream gradient and
+    both auxiliary-loss weights set. Timed with events on the stream the
+    library launches on."""
+    g = w.groups or (0, 0, 0)
+    s = M.Shape(w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.mode, w.aux_alpha, *g,
+                capacity_factor=w.capacity_factor)
+    T, d, N, k, dff, dfs = w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared
+    dev = inp["h"].device
+    E = lambda shp, dt=inp["h"].dtype: torch.empty(shp, dtype=dt, device=dev)
+    nws = M.workspace_bytes(s)
+    ws = E(nws, torch.uint8)
+    ids, gates = E(T * k, torch.int32), E(T * k, torch.float32)
+    M.route(s, inp["h"], inp["w_router"], inp["b_router"], inp["b_select"], ids, gates, None, ws,
+            nws)
+    counts, offsets = E(N, torch.int32), E(N + 1, torch.int32)
+    perm, row_of = E(T * k, torch.int32), E(T * k, torch.int32)
+    M.dispatch(s, ids, counts, offsets, perm, row_of)
+    del ws
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12345)
+    dy = torch.randn((T, d), generator=gen, device=dev).to(inp["h"].dtype)
+    out = dict(dh=E((T, d)), dw_router=E((N, d), torch.float32), db_router=E(N, torch.float32),
+               dw_gate=E((N, dff, d)), dw_up=E((N, dff, d)), dw_down=E((N, d, dff)),
+               dgates=E(T * k, torch.float32))
+    if dfs:
+        out.update(dsh_gate=E((dfs, d)), dsh_up=E((dfs, d)), dsh_down=E((d, dfs)))
+    nb = M.backward_workspace_bytes(s)
+    bws = E(nb, torch.uint8)
+
+    def step():
+        M.layer_backward(s, inp["h"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                         inp["w_up"], inp["w_down"], inp["sh_gate"], inp["sh_up"], inp["sh_down"],
+                         ids, gates, counts, offsets, perm, row_of, dy, out["dh"],
+                         out["dw_router"], out["db_router"], out["dw_gate"], out["dw_up"],
+                         out["dw_down"], out.get("dsh_gate"), out.get("dsh_up"),
+                         out.get("dsh_down"), out["dgates"], 1.0, 1e-3, bws, nb)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_ev = a.elapsed_time(b) / steps
+    c = counts.cpu().numpy()
+    rows = int(np.minimum(c, kept_counts(w, c)).sum())
+    # algorithmic flops: dh rows (4 d d_ff) + v (2 d d_ff) + dW_gate/up (4 d d_ff) + dW_down
+    # (2 d d_ff) per kept row, the same for the shared expert per token, and the router's
+    # dz W_r and dz^T h (4 d N per token); the recompute of the pre-activations is not counted
+    flops = 12.0 * d * dff * rows + 12.0 * d * dfs * T + 4.0 * d * N * T
+    tf = flops / (ms_ev * 1e-3) / 1e12
+    res = {"workload": w.name, "ms_per_step": wall / steps * 1e3, "events_ms": ms_ev,
+           "tokens_per_s": T * steps / wall, "algorithmic_tflop": flops / 1e12,
+           "tflops": tf, "frac_mfma_peak": tf / PEAK_BF16_TFLOPS,
+           "workspace_gb": nb / 1e9}
+    del bws, out
+    torch.cuda.empty_cache()
+    return res
+
 def cpu_baseline(w, inp, sample_tokens, min_seconds=10.0, max_reps=5):
     """The float64 oracle on the first `sample_tokens` tokens (routing,
     their experts, combine, statistics), timed on the host and repeated
@@ -269,6 +341,8 @@ def main():
                     help="tokens of the workload the CPU baseline runs (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the capacity / group-limited / fine-grained variant workloads")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -345,6 +419,8 @@ def main():
                          "hbm_gbs_layer": dbytes / (dms * 1e-3) / 1e9,
                          "frac_hbm_peak_layer": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "stages_ms": dstage}
+    if not a.no_backward:
+        out["backward"] = run_backward(M, torch, w, inp, a.steps, a.warmup)
     if not a.no_variants:
         del inp
         torch.cuda.empty_cache()
