@@ -409,7 +409,7 @@ struct BwdWs {
   RouteWs r;                 // router logits (split-K slices)
   int64_t Rp, Tp, Np;        // padded K spaces: routed rows, tokens, experts
   int64_t ta_rows, tb_rows;  // rows of the transposed-activation buffers
-  size_t kofs, kofs_t, dg, dz, dzb;
+  size_t kofs, kofs_t, dg, dz, dzb, colpart;
   size_t gu, v, dgu, act, gus, vs, dgus, acts;
   size_t wdT, wguT, sdT, sguT, wrT;
   size_t dhr, dhs, dhrt;
@@ -437,6 +437,7 @@ BwdWs bwd_ws(const moe_shape* s) {
   w.kofs_t = take(4 * 2);
   w.dg = take(4 * R);
   w.dz = take(4 * T * N);
+  w.colpart = take(4 * (size_t)moe::colsum_chunks((int)T) * N);
   w.dzb = take(es * T * w.Np);
   w.gu = take(4 * R * 2 * dff);      // fp32 pre-activations and v
   w.v = take(4 * R * dff);
@@ -608,7 +609,9 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   TRY(hip_check(moe::launch_route_bwd(z_part, splits, b_router, ids, gates, dg, row_of, counts, T,
                                       N, k, s->mode, s->aux_alpha, d_laux, d_zloss, dz, dzb, Np,
                                       b, dgates, st), "router backward"));
-  if (db_router) TRY(hip_check(moe::launch_colsum(dz, T, N, db_router, st), "b_r gradient"));
+  if (db_router)
+    TRY(hip_check(moe::launch_colsum(dz, T, N, at<float>(ws, W.colpart), db_router, st),
+                  "b_r gradient"));
   // 6. row gradients of h: [W_gate; W_up]^T [dgp | du] per kept row, the
   //    shared expert's, and the router's dz W_r
   TRY(pack(w_gate, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dff, dff, wguT, 2 * dff, N,

@@ -40,6 +40,13 @@ __device__ __forceinline__ void st<bf16_t>(bf16_t* p, int64_t i, float v) {
   p[i] = (bf16_t)f32_to_bf16(v);
 }
 
+template <typename TE>
+__device__ __forceinline__ TE from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return (bf16_t)f32_to_bf16(v); }
+
 constexpr int kT = 256;
 
 // kofs[e] = sum over e' < e of the kept rows of e' rounded up to 32 (the
@@ -84,24 +91,32 @@ __global__ __launch_bounds__(kT) void kofs_kernel(const int32_t* __restrict__ of
 // Transposed, padded copy: dst[c][kofs[e] + i] = scale * src[row][c] for the
 // i-th kept row of expert e (bucket row r = offsets[e] + i; source row
 // perm[r] / kdiv, or r without perm; scale = scale[perm[r]] (or [r]), or 1),
-// zero in the padding of each range and up to p_limit. 64 x 64 tiles through
-// LDS; grid (p_limit / 64, ncols / 64, batch): batch b reads src + b *
-// src_bstride and writes dst + b * dst_bstride (per-expert weight copies).
-template <typename TE>
+// zero in the padding of each range and up to p_limit. A block moves a tile
+// of 64 padded rows p x 64 columns c: the 64 rows' sources are resolved once
+// into LDS, each row segment is read with 16-byte loads, the tile is staged
+// in LDS (row pitch padded against bank conflicts) and written out along p
+// with 16-byte stores. Grid (p_limit / 64, ncols / 64, batch): batch b reads
+// src + b * src_bstride and writes dst + b * dst_bstride (per-expert weight
+// copies). VEC: rows and strides allow 16-byte accesses (the launcher
+// checks); otherwise element by element.
+template <typename TE, bool VEC>
 __global__ __launch_bounds__(kT) void pack_t_kernel(
     const TE* __restrict__ src, int ld_src, int ncols, const int32_t* __restrict__ perm,
     int kdiv, const float* __restrict__ scale, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ kofs, int G, int n_single, int64_t p_limit, TE* __restrict__ dst,
     int64_t ld_dst, int64_t src_bstride, int64_t dst_bstride) {
-  __shared__ float tile[64][65];
+  constexpr int V = VEC ? 16 / sizeof(TE) : 1;   // elements per access
+  constexpr int PITCH = 66;                   // LDS row pitch (elements): no bank conflicts
+  __shared__ TE tile[64][PITCH];
+  __shared__ int64_t s_row[64];
+  __shared__ float s_scale[64];
   const int tid = threadIdx.x;
   src += blockIdx.z * src_bstride;
   dst += blockIdx.z * dst_bstride;
   const int64_t p0 = (int64_t)blockIdx.x * 64;
   const int c0 = blockIdx.y * 64;
-  {
-    const int row = tid >> 2, cs = (tid & 3) * 16;
-    const int64_t p = p0 + row;
+  if (tid < 64) {
+    const int64_t p = p0 + tid;
     int64_t srow = -1;
     float sc = 1.0f;
     if (offsets) {
@@ -122,22 +137,51 @@ __global__ __launch_bounds__(kT) void pack_t_kernel(
       srow = p;
       if (scale) sc = scale[p];
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = c0 + cs + i;
-      tile[row][cs + i] = (srow >= 0 && c < ncols) ? sc * ld(src, srow * ld_src + c) : 0.0f;
-    }
+    s_row[tid] = srow;
+    s_scale[tid] = sc;
   }
   __syncthreads();
-  {
-    const int crow = tid >> 2, ps = (tid & 3) * 16;
-    const int c = c0 + crow;
-    if (c < ncols) {
+  // load: 64 rows x 64 columns = 64 x (64 / V) vectors
+  constexpr int VPR = 64 / V;                 // vectors per row
+  for (int q = tid; q < 64 * VPR; q += kT) {
+    const int row = q / VPR, cv = (q % VPR) * V;
+    const int64_t srow = s_row[row];
+    const int c = c0 + cv;
+    TE vals[V];
+    if (srow >= 0 && c < ncols) {
+      const float sc = s_scale[row];
+      if constexpr (VEC) {
+        // may read past ncols, never past the row (ld_src is a multiple of V)
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(src + srow * ld_src + c);
+        const TE* e = reinterpret_cast<const TE*>(&raw);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t p = p0 + ps + i;
-        if (p < p_limit) st(dst, (int64_t)c * ld_dst + p, tile[ps + i][crow]);
+        for (int i = 0; i < V; ++i) vals[i] = sc == 1.0f ? e[i] : from_f32<TE>(sc * ld(e, i));
+      } else {
+        const TE e = src[srow * ld_src + c];
+        vals[0] = sc == 1.0f ? e : from_f32<TE>(sc * ld(&e, 0));
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) vals[i] = from_f32<TE>(0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) tile[row][cv + i] = vals[i];
+  }
+  __syncthreads();
+  // store: 64 columns x 64 rows = 64 x (64 / V) vectors along p
+  for (int q = tid; q < 64 * VPR; q += kT) {
+    const int col = q / VPR, pv = (q % VPR) * V;
+    const int c = c0 + col;
+    const int64_t p = p0 + pv;
+    if (c >= ncols || p >= p_limit) continue;
+    if constexpr (VEC) {
+      TE vals[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) vals[i] = tile[pv + i][col];
+      *reinterpret_cast<u32x4*>(dst + (int64_t)c * ld_dst + p) =
+          *reinterpret_cast<const u32x4*>(vals);
+    } else {
+      dst[(int64_t)c * ld_dst + p] = tile[pv][col];
     }
   }
 }
@@ -348,20 +392,35 @@ __global__ __launch_bounds__(64) void route_bwd_kernel(
   }
 }
 
-// db[i] = sum_t dz[t][i] in a fixed order: four partial sums over quarters
-// of the tokens, added in order.
-__global__ __launch_bounds__(kT) void colsum_kernel(const float* __restrict__ dz, int T, int N,
-                                                    float* __restrict__ db) {
+// db[i] = sum_t dz[t][i] in a fixed order, in two passes: partial sums over
+// chunks of kColChunk tokens (grid: columns / 64 x chunks; four waves each
+// take a quarter of the chunk, added in order), then the chunk partials in
+// chunk order.
+constexpr int kColChunk = 128;
+__global__ __launch_bounds__(kT) void colsum_part_kernel(const float* __restrict__ dz, int T, int N,
+                                                         float* __restrict__ part) {
   __shared__ float s_part[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = blockIdx.x * 64 + lane;
-  const int t0 = (int)((int64_t)T * w / 4), t1 = (int)((int64_t)T * (w + 1) / 4);
+  const int t0 = blockIdx.y * kColChunk + w * (kColChunk / 4);
+  const int t1 = min(t0 + kColChunk / 4, T);
   float s = 0.0f;
   if (i < N)
     for (int t = t0; t < t1; ++t) s += dz[(int64_t)t * N + i];
   s_part[w][lane] = s;
   __syncthreads();
-  if (w == 0 && i < N) db[i] = ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
+  if (w == 0 && i < N)
+    part[(int64_t)blockIdx.y * N + i] =
+        ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
+}
+__global__ __launch_bounds__(kT) void colsum_final_kernel(const float* __restrict__ part,
+                                                          int chunks, int N,
+                                                          float* __restrict__ db) {
+  const int i = blockIdx.x * kT + threadIdx.x;
+  if (i >= N) return;
+  float s = 0.0f;
+  for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * N + i];
+  db[i] = s;
 }
 
 // dh[t] = sum_j rows[row_of[t k + j]] (kept slots, slot order) + shared[t]
@@ -416,16 +475,22 @@ hipError_t launch_pack_t(const void* src, int ld_src, int ncols, const int32_t* 
                          hipStream_t st, int batch, int64_t src_bstride, int64_t dst_bstride) {
   if (p_limit == 0 || ncols == 0 || batch == 0) return hipSuccess;
   dim3 grid((unsigned)((p_limit + 63) / 64), (unsigned)((ncols + 63) / 64), (unsigned)batch);
-  if (bf16)
-    hipLaunchKernelGGL(pack_t_kernel<bf16_t>, grid, dim3(kT), 0, st,
-                       static_cast<const bf16_t*>(src), ld_src, ncols, perm, kdiv, scale, offsets,
-                       kofs, G, n_single, p_limit, static_cast<bf16_t*>(dst), ld_dst, src_bstride,
-                       dst_bstride);
-  else
-    hipLaunchKernelGGL(pack_t_kernel<float>, grid, dim3(kT), 0, st,
-                       static_cast<const float*>(src), ld_src, ncols, perm, kdiv, scale, offsets,
-                       kofs, G, n_single, p_limit, static_cast<float*>(dst), ld_dst, src_bstride,
-                       dst_bstride);
+  const int V = bf16 ? 8 : 4;
+  const bool vec = ld_src % V == 0 && ld_dst % V == 0 && p_limit % V == 0 &&
+                   src_bstride % V == 0 && dst_bstride % V == 0 &&
+                   (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+#define MOE_PACK(TE, VEC)                                                                      \
+  hipLaunchKernelGGL((pack_t_kernel<TE, VEC>), grid, dim3(kT), 0, st,                          \
+                     static_cast<const TE*>(src), ld_src, ncols, perm, kdiv, scale, offsets,   \
+                     kofs, G, n_single, p_limit, static_cast<TE*>(dst), ld_dst, src_bstride,   \
+                     dst_bstride)
+  if (bf16) {
+    if (vec) MOE_PACK(bf16_t, true); else MOE_PACK(bf16_t, false);
+  } else {
+    if (vec) MOE_PACK(float, true); else MOE_PACK(float, false);
+  }
+#undef MOE_PACK
   return hipGetLastError();
 }
 
@@ -462,8 +527,15 @@ hipError_t launch_route_bwd(const float* z_part, int splits, const float* b_rout
   return hipGetLastError();
 }
 
-hipError_t launch_colsum(const float* dz, int T, int N, float* db, hipStream_t st) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((N + 63) / 64), dim3(kT), 0, st, dz, T, N, db);
+int colsum_chunks(int T) { return (T + kColChunk - 1) / kColChunk; }
+
+hipError_t launch_colsum(const float* dz, int T, int N, float* part, float* db, hipStream_t st) {
+  const int chunks = colsum_chunks(T);
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_part_kernel, dim3((N + 63) / 64, chunks), dim3(kT), 0, st, dz, T, N,
+                     part);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + kT - 1) / kT), dim3(kT), 0, st, part, chunks,
+                     N, db);
   return hipGetLastError();
 }
 

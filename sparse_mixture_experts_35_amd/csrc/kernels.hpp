@@ -142,7 +142,9 @@ hipError_t launch_route_bwd(const float* z_part, int splits,
                             int N, int k, int mode, float alpha, float d_laux,
                             float d_zloss, float* dz, void* dzb, int ldzb,
                             int bf16, float* dg_out, hipStream_t st);
-hipError_t launch_colsum(const float* dz, int T, int N, float* db,
+// db[i] = sum_t dz[t][i] (fixed order); part holds colsum_chunks(T) x N floats
+int colsum_chunks(int T);
+hipError_t launch_colsum(const float* dz, int T, int N, float* part, float* db,
                          hipStream_t st);
 hipError_t launch_dh_combine(const void* rows, const int32_t* row_of,
                              const void* shared, const void* router, void* dh,
