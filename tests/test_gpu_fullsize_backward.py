@@ -1,0 +1,137 @@
+"""GPU parity of moe_layer_backward at the full Mixtral-8x7B prefill size
+(T = 4096, d = 4096, d_ff = 14336, 8 experts, top-2, bf16), in the launch
+configuration the benchmark times (inputs drawn on the device, the same
+seeded upstream gradient, d_laux = 1, d_zloss = 1e-3), against the float64
+oracle on sampled outputs it can compute one at a time:
+  * dL/dg and dh on sampled tokens: each token's experts forward and
+    backward on its own row (the oracle's expert_ffn / expert_ffn_backward),
+    its router-logit gradient from the oracle's gate_backward and
+    stats_backward rows (row-wise in the tokens, the L_aux term from the
+    counts of every token);
+  * sampled rows of dW_gate and dW_up of two experts: the oracle's expert
+    backward restricted to those hidden units is exact for them;
+  * sampled rows of dW_down of the smallest expert (the full expert
+    backward on its rows).
+The router's weight gradients need every token's dL/dg and are checked at
+the smaller sizes only (tests/test_gpu_backward.py)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import moe_oracle as O
+from helpers import TOL, check_close_rows, host, torch
+
+pytestmark = pytest.mark.gpu
+
+import sparse_mixture_experts_35_amd as M  # noqa: E402
+
+D_LAUX, D_ZLOSS = 1.0, 1e-3      # as in the benchmark's backward leg
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    M.lib()
+
+
+def _np(x):
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def test_full_size_backward_mixtral_prefill():
+    t = torch()
+    w = W.MIXTRAL_PREFILL
+    T, d, N, k, dff = w.T, w.d, w.N, w.k, w.d_ff
+    inp = W.device_inputs(w)
+    s = M.Shape(T, d, N, k, dff, 0, w.dtype, w.mode, w.aux_alpha)
+    E = lambda shp, dt=t.bfloat16: t.empty(shp, dtype=dt, device="cuda")
+    nws = M.workspace_bytes(s)
+    ws = E(nws, t.uint8)
+    ids, gates = E(T * k, t.int32), E(T * k, t.float32)
+    M.route(s, inp["h"], inp["w_router"], inp["b_router"], None, ids, gates, None, ws, nws)
+    counts, offsets = E(N, t.int32), E(N + 1, t.int32)
+    perm, row_of = E(T * k, t.int32), E(T * k, t.int32)
+    M.dispatch(s, ids, counts, offsets, perm, row_of)
+    del ws
+    gen = t.Generator(device="cuda")
+    gen.manual_seed(12345)
+    dy = t.randn((T, d), generator=gen, device="cuda").to(t.bfloat16)
+    g = dict(dh=E((T, d)), dw_router=E((N, d), t.float32), db_router=E(N, t.float32),
+             dw_gate=E((N, dff, d)), dw_up=E((N, dff, d)), dw_down=E((N, d, dff)),
+             dgates=E(T * k, t.float32))
+    nb = M.backward_workspace_bytes(s)
+    bws = E(nb, t.uint8)
+    print(f"\n[{w.name}] backward, workspace {nb / 1e9:.2f} GB", flush=True)
+    M.layer_backward(s, inp["h"], inp["w_router"], inp["b_router"], inp["w_gate"], inp["w_up"],
+                     inp["w_down"], None, None, None, ids, gates, counts, offsets, perm, row_of,
+                     dy, g["dh"], g["dw_router"], g["db_router"], g["dw_gate"], g["dw_up"],
+                     g["dw_down"], None, None, None, g["dgates"], D_LAUX, D_ZLOSS, bws, nb)
+    t.cuda.synchronize()
+    del bws
+
+    h, wr, dyh = _np(inp["h"]), _np(inp["w_router"]), _np(dy)
+    g_ids = host(ids).reshape(T, k)
+    g_cnt = host(counts)
+    assert np.array_equal(g_cnt, np.bincount(g_ids.reshape(-1), minlength=N))
+    r = O.route(h, wr, k, w.mode, ids=g_ids)
+    offs, pm = host(offsets), host(perm)
+    rng = np.random.default_rng(99)
+    tol = TOL[w.dtype]
+    cache = {}
+
+    def weights_of(e):
+        if e not in cache:
+            cache.clear()
+            cache[e] = tuple(_np(inp[key][e]) for key in ("w_gate", "w_up", "w_down"))
+        return cache[e]
+
+    # ---- dL/dg and dh on sampled tokens
+    toks = np.unique(np.concatenate([[0, 1, T - 1], rng.integers(0, T, 13)]))
+    dg = np.zeros((T, k))
+    dx = np.zeros((toks.size, d))
+    for e in range(N):
+        for n, tt in enumerate(toks):
+            for j in range(k):
+                if g_ids[tt, j] != e:
+                    continue
+                wg, wu, wd = weights_of(e)
+                x = h[tt:tt + 1]
+                dg[tt, j] = float(np.sum(dyh[tt] * O.expert_ffn(x, wg, wu, wd)[0]))
+                dx[n] += O.expert_ffn_backward(x, wg, wu, wd, r.gates[tt, j] * dyh[tt:tt + 1])[0][0]
+    dz = O.gate_backward(r, dg, w.mode) + O.stats_backward(r, g_cnt, k, w.mode, w.aux_alpha,
+                                                           D_LAUX, D_ZLOSS)
+    dh_ref = dx + dz[toks] @ wr
+    check_close_rows(host(g["dgates"]).reshape(T, k)[toks], dg[toks], tol, what="dgates (sampled)")
+    worst = check_close_rows(host(g["dh"][t.from_numpy(toks).cuda()]), dh_ref, tol,
+                             what="dh (sampled tokens)")
+    print(f"[{w.name}] dh on {toks.size} tokens: max row rel err {worst:.2e}", flush=True)
+
+    # ---- sampled rows of dW_gate / dW_up (hidden units js of two experts)
+    def expert_rows(e):
+        flats = pm[offs[e]:offs[e + 1]]
+        tk, sl = flats // k, flats % k
+        return h[tk], r.gates[tk, sl][:, None] * dyh[tk]
+
+    small = int(np.argmin(g_cnt))
+    for e in sorted({small, int(rng.integers(0, N))}):
+        wg, wu, wd = weights_of(e)
+        x, dout = expert_rows(e)
+        js = np.unique(np.concatenate([[0, dff - 1], rng.integers(0, dff, 4)]))
+        _, dwg, dwu, _ = O.expert_ffn_backward(x, wg[js], wu[js], wd[:, js], dout)
+        gg = _np(g["dw_gate"][e][t.from_numpy(js).cuda()])
+        gu_ = _np(g["dw_up"][e][t.from_numpy(js).cuda()])
+        check_close_rows(gg, dwg, tol, what=f"dW_gate[{e}] rows")
+        worst = check_close_rows(gu_, dwu, tol, what=f"dW_up[{e}] rows")
+        print(f"[{w.name}] dW_gate/dW_up rows of expert {e} ({x.shape[0]} rows): "
+              f"max row rel err {worst:.2e}", flush=True)
+
+    # ---- sampled rows of dW_down of the smallest expert (full expert backward)
+    wg, wu, wd = weights_of(small)
+    x, dout = expert_rows(small)
+    cs = np.unique(np.concatenate([[0, d - 1], rng.integers(0, d, 6)]))
+    _, _, _, dwd = O.expert_ffn_backward(x, wg, wu, wd[cs], dout[:, cs])
+    worst = check_close_rows(_np(g["dw_down"][small][t.from_numpy(cs).cuda()]), dwd, tol,
+                             what=f"dW_down[{small}] rows")
+    print(f"[{w.name}] dW_down rows of expert {small}: max row rel err {worst:.2e}", flush=True)
