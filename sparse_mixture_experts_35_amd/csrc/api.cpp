@@ -235,6 +235,26 @@ T* at(void* ws, size_t off) {
 }
 
 // ------------------------------------------------------------ stage impls
+// Router logits as split-K slices z_part[splits][T][N] (bf16: a GEMV for a
+// few tokens, else the split-K GEMM; fp32: one slice).
+moe_status router_logits(const moe_shape* s, const void* h, const void* w_router, float* z_part,
+                         int& splits, hipStream_t st) {
+  splits = 1;
+  if (s->dtype == MOE_BF16) {
+    if (moe::router_use_gemv(s->T, s->N))
+      return hip_check(moe::launch_router_gemv_bf16(h, w_router, z_part, s->T, s->d, s->N, st),
+                       "router GEMV");
+    splits = moe::router_splits(s->T, s->d, s->N);
+    return hip_check(moe::launch_router_gemm_bf16(h, w_router, z_part, s->T, s->d, s->N, splits,
+                                                  st),
+                     "router GEMM");
+  }
+  return hip_check(moe::launch_router_logits_f32(static_cast<const float*>(h),
+                                                 static_cast<const float*>(w_router), z_part,
+                                                 s->T, s->d, s->N, st),
+                   "router logits");
+}
+
 moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
                       const float* b_router, const float* b_select, int32_t* ids,
                       float* gates, float* p_mean, float* z_loss, float* entropy,
@@ -243,24 +263,18 @@ moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
   float* p_part = at<float>(ws, W.p_part);
   float* zl_part = (z_loss || entropy) ? at<float>(ws, W.zl_part) : nullptr;
   int splits = 1;
-  if (s->dtype == MOE_BF16) {
-    splits = moe::router_splits(s->T, s->d, s->N);
-    TRY(hip_check(moe::launch_router_gemm_bf16(h, w_router, z_part, s->T, s->d, s->N, splits, st),
-                  "router GEMM"));
-  } else {
-    TRY(hip_check(moe::launch_router_logits_f32(static_cast<const float*>(h),
-                                                static_cast<const float*>(w_router), z_part,
-                                                s->T, s->d, s->N, st),
-                  "router logits"));
-  }
+  TRY(router_logits(s, h, w_router, z_part, splits, st));
   // a group limit that keeps every group changes nothing
   const bool grouped = s->n_groups > 1 && s->topk_groups < s->n_groups;
   const moe::GroupLimit gl{grouped ? s->n_groups : 0, s->topk_groups, s->group_topm};
+  // a single selection block writes the final statistics itself
+  const bool single = moe::route_select_blocks(s->T, s->N) == 1;
+  const moe::RouteFinal fin{p_mean, z_loss, entropy, single ? 1 : 0};
   TRY(hip_check(moe::launch_route_select(z_part, splits, b_router, b_select, ids, gates,
                                          p_mean ? p_part : nullptr, zl_part, s->T, s->N, s->k,
-                                         s->mode, gl, st),
+                                         s->mode, gl, fin, st),
                 "route select"));
-  if (p_mean || zl_part)
+  if (!single && (p_mean || zl_part))
     TRY(hip_check(moe::launch_p_reduce(p_part, p_mean, zl_part, z_loss, entropy,
                                        moe::route_select_blocks(s->T, s->N), s->T, s->N, st),
                   "p reduce"));
@@ -564,16 +578,7 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   // 1. router logits again (split-K slices, as in the forward)
   float* z_part = at<float>(ws, W.r.z);
   int splits = 1;
-  if (bf16) {
-    splits = moe::router_splits(T, d, N);
-    TRY(hip_check(moe::launch_router_gemm_bf16(h, w_router, z_part, T, d, N, splits, st),
-                  "router GEMM"));
-  } else {
-    TRY(hip_check(moe::launch_router_logits_f32(static_cast<const float*>(h),
-                                                static_cast<const float*>(w_router), z_part, T,
-                                                d, N, st),
-                  "router logits"));
-  }
+  TRY(router_logits(s, h, w_router, z_part, splits, st));
   // 2. gate/up pre-activations of the kept rows (and the shared expert)
   TRY(grouped(moe::GroupedProblem{h, d, perm, k, offsets, N, rows_all, rows_max, w_gate, w_up,
                                   (int64_t)dff * d, d, dff, d, gu, 2 * dff, 0,

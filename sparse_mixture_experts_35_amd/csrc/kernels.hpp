@@ -27,11 +27,24 @@ struct GroupLimit {
 int route_select_blocks(int T, int N);
 // (zl_part, when given: per-block sums of the squared log-sum-exp of the
 // logits and of the routing entropy, 2 floats per block)
+// Final statistics written by the selection kernel itself when it runs as
+// a single block (on = request; the launcher clears it otherwise): sum / T,
+// which equals the reduction kernel's result bit for bit.
+struct RouteFinal {
+  float* p_mean;
+  float* z_loss;
+  float* entropy;
+  int on;
+};
 hipError_t launch_route_select(const float* z_part, int splits,
                                const float* b_router, const float* b_select,
                                int32_t* ids, float* gates, float* p_part,
                                float* zl_part, int T, int N, int k, int mode,
-                               GroupLimit gl, hipStream_t st);
+                               GroupLimit gl, RouteFinal fin, hipStream_t st);
+// small T·N: router logits by a GEMV kernel (one slice, splits = 1)
+bool router_use_gemv(int T, int N);
+hipError_t launch_router_gemv_bf16(const void* h, const void* w, float* z,
+                                   int T, int d, int N, hipStream_t st);
 // p_mean (nullable) from p_part; z_loss / entropy (nullable) from zl_part
 hipError_t launch_p_reduce(const float* p_part, float* p_mean,
                            const float* zl_part, float* z_loss, float* entropy,

@@ -33,6 +33,32 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxK = 16;
 
+// Router logits for a few tokens (bf16): one wave per (token, expert) dot
+// product, 16-byte loads of both rows, fp32 products summed per lane in
+// order and then across the wave by a fixed butterfly. For T·N small, where
+// a tiled GEMM would compute mostly padding.
+__global__ __launch_bounds__(256) void router_gemv_bf16_kernel(const bf16_t* __restrict__ h,
+                                                               const bf16_t* __restrict__ w,
+                                                               float* __restrict__ z, int T,
+                                                               int d, int N) {
+  const int64_t wv = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wv >= (int64_t)T * N) return;
+  const int t = (int)(wv / N), e = (int)(wv % N);
+  const bf16_t* a = h + (int64_t)t * d;
+  const bf16_t* b = w + (int64_t)e * d;
+  float s = 0.0f;
+  for (int c = lane * 8; c < d; c += 512) {
+    float x[8], y[8];
+    unpack_bf16x8(*reinterpret_cast<const u32x4*>(a + c), x);
+    unpack_bf16x8(*reinterpret_cast<const u32x4*>(b + c), y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf(x[i], y[i], s);
+  }
+  s = wave_sum(s);
+  if (lane == 0) z[wv] = s;
+}
+
 __global__ void router_logits_f32_kernel(const float* __restrict__ h,
                                          const float* __restrict__ w, float* __restrict__ z,
                                          int T, int d, int N) {
@@ -58,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
     const float* __restrict__ b_select, int32_t* __restrict__ ids,
     float* __restrict__ gates, float* __restrict__ p_part, float* __restrict__ zl_part, int T,
-    int N, int k, GroupLimit gl) {
+    int N, int k, GroupLimit gl, RouteFinal fin) {
   constexpr int TPW = 64 / LPT;               // tokens per wave per iteration
   constexpr int TPB = 4 * TPW * ITER;         // tokens per block
   constexpr int GPL = 64 / LPT;               // groups per lane at most (64 groups)
@@ -347,6 +373,8 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
 #pragma unroll
         for (int g = 0; g < TPW; ++g) sum += s_zl[ww][g * LPT][tid];
       zl_part[(int64_t)blockIdx.x * 2 + tid] = sum;
+      float* out = tid == 0 ? fin.z_loss : fin.entropy;
+      if (fin.on && out) *out = sum / (float)T;
     }
   }
   if (p_part) {
@@ -361,6 +389,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
 #pragma unroll
         for (int g = 0; g < TPW; ++g) sum += s_p[ww][g * LPT + e % LPT][e / LPT];
       p_part[(int64_t)blockIdx.x * N + e] = sum;
+      if (fin.on && fin.p_mean) fin.p_mean[e] = sum / (float)T;
     }
   }
 }
@@ -427,19 +456,19 @@ template <int LPT, int VPL, int ITER>
 hipError_t launch_select_t(const float* z_part, int splits, const float* b_router,
                            const float* b_select, int32_t* ids, float* gates, float* p_part,
                            float* zl_part, int T, int N, int k, int mode, GroupLimit gl,
-                           int blocks, hipStream_t st) {
+                           int blocks, RouteFinal fin, hipStream_t st) {
   switch (mode) {
     case 0:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 0, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl, fin);
       break;
     case 1:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 1, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl, fin);
       break;
     default:
       hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 2, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl);
+                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl, fin);
       break;
   }
   return hipGetLastError();
@@ -456,6 +485,18 @@ hipError_t launch_router_logits_f32(const float* h, const float* w, float* z, in
   return hipGetLastError();
 }
 
+bool router_use_gemv(int T, int N) { return T <= 64 && (int64_t)T * N <= 2048; }
+
+hipError_t launch_router_gemv_bf16(const void* h, const void* w, float* z, int T, int d, int N,
+                                   hipStream_t st) {
+  const int64_t waves = (int64_t)T * N;
+  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_gemv_bf16_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     st, static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(w), z, T, d,
+                     N);
+  return hipGetLastError();
+}
+
 int route_select_blocks(int T, int N) {
   const SelectCfg c = select_cfg(N);
   return (T + c.tpb - 1) / c.tpb;
@@ -464,14 +505,15 @@ int route_select_blocks(int T, int N) {
 hipError_t launch_route_select(const float* z_part, int splits, const float* b_router,
                                const float* b_select, int32_t* ids, float* gates,
                                float* p_part, float* zl_part, int T, int N, int k, int mode,
-                               GroupLimit gl, hipStream_t st) {
+                               GroupLimit gl, RouteFinal fin, hipStream_t st) {
   const SelectCfg c = select_cfg(N);
   const int blocks = (T + c.tpb - 1) / c.tpb;
   if (blocks == 0) return hipSuccess;
+  fin.on = fin.on && blocks == 1;
 #define MOE_SEL(L, V, I)                                                                    \
   if (c.lpt == L && c.vpl == V)                                                             \
     return launch_select_t<L, V, I>(z_part, splits, b_router, b_select, ids, gates, p_part, \
-                                    zl_part, T, N, k, mode, gl, blocks, st);
+                                    zl_part, T, N, k, mode, gl, blocks, fin, st);
   MOE_SEL(8, 1, 1)
   MOE_SEL(16, 1, 1)
   MOE_SEL(32, 1, 2)
