@@ -37,6 +37,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -51,7 +52,7 @@ METRIC = "MoE-layer tokens/sec at 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-GEMM_SOURCES = ("gemm_bf16.hip", "common.hpp", "kernels.hpp")
+GEMM_SOURCES = ("gemm_bf16.hip", "common.hpp")
 VARIANTS = (W.QWEN3_30B, W.QWEN3_30B_CAP, W.DEEPSEEK_V3, W.DEEPSEEK_V3_GROUPED)
 
 
@@ -405,7 +406,7 @@ def main():
                   "experts_touched": touched, "max_rows": int(counts.max())},
     }
     if not a.no_decode and w.T > a.decode_tokens:
-        wd = w.replace(name=w.name.split("_T")[0] + f"_decode_T{a.decode_tokens}",
+        wd = w.replace(name=re.sub(r"prefill_T\d+", f"decode_T{a.decode_tokens}", w.name),
                        T=a.decode_tokens)
         dinp = dict(inp)
         dinp["h"] = inp["h"][:a.decode_tokens].contiguous()
@@ -419,6 +420,16 @@ def main():
                          "hbm_gbs_layer": dbytes / (dms * 1e-3) / 1e9,
                          "frac_hbm_peak_layer": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "stages_ms": dstage}
+        # weight-streaming kernels: algorithmic bytes (touched experts' weights,
+        # rows in and out) against the counted HBM bytes per launch
+        gb = {"gate_up": gateup_work(wd, dcounts)[1],
+              "down": dtouched * w.d * w.d_ff * 2 + int(dcounts.sum()) * (w.d + w.d_ff) * 2}
+        out["decode"]["kernels"] = {
+            n: {"ms": dstage[n], "algorithmic_bytes": gb[n],
+                "gbs": gb[n] / (dstage[n] * 1e-3) / 1e9,
+                "frac_hbm_peak": gb[n] / (dstage[n] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "traffic": measured_traffic(wd.name, f"skinny_gemm_{n.replace('_', '')}")}
+            for n in ("gate_up", "down")}
     if not a.no_backward:
         out["backward"] = run_backward(M, torch, w, inp, a.steps, a.warmup)
     if not a.no_variants:
