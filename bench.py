@@ -242,7 +242,7 @@ def run_backward(M, torch, w, inp, steps, warmup):
             nws)
     counts, offsets = E(N, torch.int32), E(N + 1, torch.int32)
     perm, row_of = E(T * k, torch.int32), E(T * k, torch.int32)
-    M.dispatch(s, ids, counts, offsets, perm, row_of)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, ws=ws, ws_bytes=nws)
     del ws
     gen = torch.Generator(device=dev)
     gen.manual_seed(12345)

@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_GROUPS 64
@@ -151,7 +151,8 @@ const char* moe_last_error(void);
 
 /* Host, pure: workspace bytes that suffice for EVERY call below with this
  * shape (the fused layer needs the most). 0 for an invalid shape.
- * moe_dispatch and moe_combine use no workspace. moe_route keeps the
+ * moe_combine uses no workspace; moe_dispatch keeps per-chunk expert counts
+ * (ceil(T·k / 1024)·N int32) at the start of its workspace. moe_route keeps the
  * router's partial logits and per-block probability sums there;
  * moe_expert_ffn keeps the SwiGLU activations (T·k·d_ff + T·d_ff_shared
  * elements) and, on the bf16 path, up to 64 MiB of fp32 split-K partial
@@ -203,6 +204,8 @@ moe_status moe_route(const moe_shape* s, const void* h, const void* w_router,
  *            the dropped fraction (T·k − Σ_e kept_e) / (T·k), each the fp32
  *            rounding of the exact ratio; both 0 without a capacity
  *            [wuhy-notes, monitoring list: capacity usage, dropped tokens]
+ *   ws       workspace of at least moe_workspace_bytes(s) bytes (it uses the
+ *            per-chunk counts described there)
  * Deterministic: no atomic decides any order or any float sum.
  * [wuhy-notes §三 Token Dispatch, §六 Expert Capacity; horizon.auto §3 ②;
  *  feinterview load-balance section] */

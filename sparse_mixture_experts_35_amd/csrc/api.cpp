@@ -175,10 +175,15 @@ FfnWs ffn_ws(const moe_shape* s, size_t base) {
   w.end = f ? align_up(w.cnt + sizeof(int32_t) * moe::kSplitCounters) : w.cnt;
   return w;
 }
+// dispatch scratch: per-chunk expert counts
+size_t dispatch_ws_bytes(const moe_shape* s) {
+  return align_up(sizeof(int32_t) * (size_t)moe::dispatch_chunks(s->T, s->k) * s->N);
+}
+
 struct FusedWs {
   RouteWs r;
   FfnWs x;
-  size_t p_mean, ids, gates, counts, offsets, perm, row_of, f, rows, end;
+  size_t p_mean, ids, gates, counts, offsets, perm, row_of, f, dhist, rows, end;
 };
 FusedWs fused_ws(const moe_shape* s) {
   FusedWs w;
@@ -192,7 +197,8 @@ FusedWs fused_ws(const moe_shape* s) {
   w.perm = align_up(w.offsets + 4 * (N + 1));
   w.row_of = align_up(w.perm + 4 * R);
   w.f = align_up(w.row_of + 4 * R);
-  w.x = ffn_ws(s, align_up(w.f + 4 * N + 4));
+  w.dhist = align_up(w.f + 4 * N + 4);
+  w.x = ffn_ws(s, w.dhist + dispatch_ws_bytes(s));
   w.rows = w.x.end;
   w.end = align_up(w.rows + esize(s) * (R + (s->d_ff_shared ? T : 0)) * s->d);
   return w;
@@ -284,10 +290,10 @@ moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
 moe_status dispatch_impl(const moe_shape* s, const int32_t* ids, int32_t* counts,
                          int32_t* offsets, int32_t* perm_src, int32_t* row_of,
                          const float* p_mean, float* f_out, float* l_aux, float* cap_stats,
-                         hipStream_t st) {
+                         int32_t* hist, hipStream_t st) {
   return hip_check(moe::launch_dispatch(ids, s->T, s->k, s->N, counts, offsets, perm_src, row_of,
                                         p_mean, f_out, l_aux, s->aux_alpha, expert_capacity(s),
-                                        cap_stats, st),
+                                        cap_stats, hist, st),
                    "dispatch");
 }
 
@@ -401,7 +407,8 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   TRY(route_impl(s, h, w_router, b_router, b_select, ids, gates, p_mean, z_loss, entropy, L.r,
                  ws, st));
   TRY(mark(events, 1, st));
-  TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, cap_stats, st));
+  TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, cap_stats,
+                    at<int32_t>(ws, L.dhist), st));
   TRY(mark(events, 2, st));
   TRY(ffn_stage(s, true, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
                 ws, L.x, st));
@@ -738,8 +745,6 @@ moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids, int32_t* co
                         int32_t* offsets, int32_t* perm_src, int32_t* row_of,
                         const float* p_mean, float* f_out, float* l_aux, float* cap_stats,
                         void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   g_err.clear();
   TRY(check_shape(s));
   TRY(need4(topk_ids, "topk_ids"));
@@ -752,9 +757,10 @@ moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_ids, int32_t* co
   TRY(opt4(l_aux, "l_aux"));
   TRY(opt4(cap_stats, "cap_stats"));
   if (l_aux && !p_mean) return fail(MOE_ERR_INVALID_ARG, "l_aux requested without p_mean");
+  TRY(check_ws(ws, ws_bytes, dispatch_ws_bytes(s)));
   if (s->T == 0) return MOE_OK;
   return dispatch_impl(s, topk_ids, counts, offsets, perm_src, row_of, p_mean, f_out, l_aux,
-                       cap_stats, static_cast<hipStream_t>(stream));
+                       cap_stats, static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_expert_ffn(const moe_shape* s, const void* h, const int32_t* perm_src,

@@ -51,13 +51,15 @@ hipError_t launch_p_reduce(const float* p_part, float* p_mean,
                            int blocks, int T, int N, hipStream_t st);
 
 // --------------------------------------------------------------- dispatch
-// cap: expert capacity C >= 1, or 0 for none; cap_stats nullable
+// cap: expert capacity C >= 1, or 0 for none; cap_stats nullable; hist:
+// dispatch_chunks(T, k) x N int32 of scratch (per-chunk expert counts)
+int dispatch_chunks(int T, int k);
 hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N,
                            int32_t* counts, int32_t* offsets,
                            int32_t* perm_src, int32_t* row_of,
                            const float* p_mean, float* f_out, float* l_aux,
                            float alpha, int cap, float* cap_stats,
-                           hipStream_t st);
+                           int32_t* hist, hipStream_t st);
 
 // ---------------------------------------------------------------- experts
 // One grouped problem: rows of A gathered through perm (token = perm[r] /

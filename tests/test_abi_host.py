@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(M.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_status_strings():

@@ -45,7 +45,7 @@ def run_backward(s, inp, dy, d_laux, d_zloss):
     M.route(s, h, wr, br, bs, ids, gates, p, ws, nws)
     counts, offsets = _empty(N, t.int32), _empty(N + 1, t.int32)
     perm, row_of = _empty(T * k, t.int32), _empty(T * k, t.int32)
-    M.dispatch(s, ids, counts, offsets, perm, row_of)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, ws=ws, ws_bytes=nws)
     td = tdtype(dt)
     dyd = dev(dy, dt)
     g = dict(dh=_empty((T, d), td), dw_router=_empty((N, d), t.float32),

@@ -83,7 +83,7 @@ def test_full_size_layer(w):
     M.route(s, inp["h"], inp["w_router"], inp["b_router"], inp["b_select"], ids, gates, p, ws, nws)
     counts, offsets, perm, row_of, fo, la = i32(N), i32(N + 1), i32(R), i32(R), f32(N), f32(1)
     cs = f32(2)
-    M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la, cap_stats=cs)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la, ws=ws, ws_bytes=nws, cap_stats=cs)
     rows_n = R + (T if w.d_ff_shared else 0)
     out_rows = t.empty((rows_n, w.d), dtype=inp["h"].dtype, device="cuda")
     M.expert_ffn(s, inp["h"], perm, offsets, inp["w_gate"], inp["w_up"], inp["w_down"],

@@ -53,7 +53,7 @@ def test_full_size_backward_mixtral_prefill():
     M.route(s, inp["h"], inp["w_router"], inp["b_router"], None, ids, gates, None, ws, nws)
     counts, offsets = E(N, t.int32), E(N + 1, t.int32)
     perm, row_of = E(T * k, t.int32), E(T * k, t.int32)
-    M.dispatch(s, ids, counts, offsets, perm, row_of)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, ws=ws, ws_bytes=nws)
     del ws
     gen = t.Generator(device="cuda")
     gen.manual_seed(12345)

@@ -75,7 +75,7 @@ def run_steps(s, inp):
     M.route(s, h, wr, br, bs, ids, gates, p, ws, nws, z_loss=zl, entropy=ent)
     counts, offsets, perm, row_of = i32(N), i32(N + 1), i32(T * k), i32(T * k)
     fo, la, cs = f32(N), f32(1), f32(2)
-    M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la, cap_stats=cs)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, p, fo, la, ws=ws, ws_bytes=nws, cap_stats=cs)
     wg, wu, wd = dev(inp["w_gate"], dt), dev(inp["w_up"], dt), dev(inp["w_down"], dt)
     sg, su, sd = dev(inp["sh_gate"], dt), dev(inp["sh_up"], dt), dev(inp["sh_down"], dt)
     rows_n = T * k + (T if s.d_ff_shared else 0)
@@ -263,7 +263,8 @@ def test_dispatch_capacity_worked_example_on_gpu():
     t = torch()
     ids = t.tensor(np.array(g["ids"]).reshape(-1), dtype=t.int32, device="cuda")
     counts, offsets, perm, row_of, cs = i32(4), i32(5), i32(8), i32(8), f32(2)
-    M.dispatch(s, ids, counts, offsets, perm, row_of, cap_stats=cs)
+    ws, nws = workspace(s)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, ws=ws, ws_bytes=nws, cap_stats=cs)
     t.cuda.synchronize()
     assert host(counts).tolist() == [2, 2, 3, 1]
     assert host(offsets).tolist() == [0, 2, 4, 6, 7]
@@ -374,7 +375,8 @@ def test_dispatch_grouping_example_on_gpu():
     t = torch()
     ids = t.tensor(np.array(g["ids"]).reshape(-1), dtype=t.int32, device="cuda")
     counts, offsets, perm, row_of = i32(4), i32(5), i32(8), i32(8)
-    M.dispatch(s, ids, counts, offsets, perm, row_of)
+    ws, nws = workspace(s)
+    M.dispatch(s, ids, counts, offsets, perm, row_of, ws=ws, ws_bytes=nws)
     t.cuda.synchronize()
     assert host(counts).tolist() == [2, 2, 3, 1]
     assert host(perm).tolist() == [0, 4, 2, 7, 1, 3, 6, 5]
@@ -399,8 +401,9 @@ def test_dispatch_random(T, N, k, cf):
     counts, offsets, perm, row_of = i32(N), i32(N + 1), i32(T * k), i32(T * k)
     pm = dev_f32(np.full(N, 1.0 / N))
     fo, la, cs = f32(N), f32(1), f32(2)
+    ws, nws = workspace(s)
     M.dispatch(s, t.from_numpy(ids.reshape(-1)).cuda(), counts, offsets, perm, row_of, pm, fo, la,
-               cap_stats=cs)
+               ws=ws, ws_bytes=nws, cap_stats=cs)
     t.cuda.synchronize()
     cap = capacity_of(s)
     d = O.dispatch(ids, N, cap)
