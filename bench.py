@@ -85,6 +85,33 @@ def measured_traffic(workload, kernel):
         return None
 
 
+def library_gemm(torch, w, steps=10, warmup=3):
+    """Context only: the vendor library (hipBLASLt through torch.bmm) on the
+    uniform-batch equivalent of the gate/up GEMM of the workload, N
+    experts x [T k / N rows, d] x [d, 2 d_ff], bf16. Prints one JSON line."""
+    rows = w.T * w.k // w.N
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    a = torch.randn(w.N, rows, w.d, generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn(w.N, w.d, 2 * w.d_ff, generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.empty(w.N, rows, 2 * w.d_ff, device="cuda", dtype=torch.bfloat16)
+    for _ in range(warmup):
+        torch.bmm(a, b, out=c)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        torch.bmm(a, b, out=c)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    fl = 2.0 * w.N * rows * w.d * 2 * w.d_ff
+    tf = fl / (ms * 1e-3) / 1e12
+    print(json.dumps({"library_gemm": "torch.bmm (hipBLASLt)", "workload": w.name,
+                      "shape": [w.N, rows, w.d, 2 * w.d_ff], "ms": ms, "tflops": tf,
+                      "frac_mfma_peak": tf / PEAK_BF16_TFLOPS}), flush=True)
+
+
 def copy_calibration(torch, gib=1, reps=5):
     """A plain device copy of a known size: its FETCH_SIZE / WRITE_SIZE
     readings per dispatch give the bytes-per-count scale of the counters."""
@@ -348,6 +375,9 @@ def main():
                     help="skip the capacity / group-limited / fine-grained variant workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the vendor library on the uniform-batch equivalent of the "
+                         "workload's gate/up GEMM (context) and exit")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this "
@@ -362,6 +392,9 @@ def main():
         sys.exit(1)
     if a.copy_calibration:
         copy_calibration(torch)
+        return
+    if a.library_gemm:
+        library_gemm(torch, W.ALL[a.workload], a.steps, a.warmup)
         return
     M.lib()   # fail loudly if the HIP library is missing
 
