@@ -1048,6 +1048,12 @@ hipError_t launch_kgroup_bf16(const void* A_, int lda, int64_t a_rows, const voi
     dim3 grid((unsigned)(((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN)), groups);
     hipLaunchKernelGGL((kgroup_gemm_kernel<K, true>), grid, dim3(kThreads), 0, st, A, lda, ab, B,
                        ldb, bb, kofs, M, Ncols, C, c_gstride, ldc);
+  } else if (M >= 512) {
+    // 256 x 256 tiles: half the operand traffic per flop of 128 x 256
+    using K = Down256;
+    dim3 grid((unsigned)(((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN)), groups);
+    hipLaunchKernelGGL((kgroup_gemm_kernel<K, false>), grid, dim3(kThreads), 0, st, A, lda, ab, B,
+                       ldb, bb, kofs, M, Ncols, C, c_gstride, ldc);
   } else {
     using K = Down128;
     dim3 grid((unsigned)(((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN)), groups);
