@@ -22,7 +22,9 @@ inputs are already resident in HBM. Prints ONE JSON line.
             weights: tokens/s and HBM GB/s of the touched experts' weights
   backward  moe_layer_backward on the same workload (the forward's selection
             made once beforehand): ms per call and the algorithmic TFLOP/s of
-            the gradients (2x the forward's expert flops plus the router's)
+            the gradients (2x the forward's expert flops plus the router's);
+            train_step: moe_layer_forward_train (keeping the pre-activations)
+            then the backward that uses them, per step
   variants  the fine-grained skewed layer (128 experts, top-8) dropless and
             with expert capacity 1.25 (capacity usage, dropped fraction),
             and the DeepSeek-V3-shaped layer without and with group-limited
@@ -302,6 +304,45 @@ def run_backward(M, torch, w, inp, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_ev = a.elapsed_time(b) / steps
+    # training step: the training forward keeps the dispatch and the gate/up
+    # pre-activations, the backward uses them (no recompute)
+    pre = E(M.preact_floats(s), torch.float32)
+    nws = M.workspace_bytes(s)
+    fws = E(nws, torch.uint8)
+    y = E((T, d))
+    ids_t, gates_t, counts_t = E(T * k, torch.int32), E(T * k, torch.float32), E(N, torch.int32)
+    off_t, perm_t, row_t = E(N + 1, torch.int32), E(T * k, torch.int32), E(T * k, torch.int32)
+
+    def train_step(evs=None):
+        if evs:
+            evs[0].record()
+        M.layer_forward_train(s, inp["h"], inp["w_router"], inp["b_router"], inp["b_select"],
+                              inp["w_gate"], inp["w_up"], inp["w_down"], inp["sh_gate"],
+                              inp["sh_up"], inp["sh_down"], y, ids_t, gates_t, counts_t, off_t,
+                              perm_t, row_t, preact=pre, ws=fws, ws_bytes=nws)
+        if evs:
+            evs[1].record()
+        M.layer_backward(s, inp["h"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                         inp["w_up"], inp["w_down"], inp["sh_gate"], inp["sh_up"],
+                         inp["sh_down"], ids_t, gates_t, counts_t, off_t, perm_t, row_t, dy,
+                         out["dh"], out["dw_router"], out["db_router"], out["dw_gate"],
+                         out["dw_up"], out["dw_down"], out.get("dsh_gate"), out.get("dsh_up"),
+                         out.get("dsh_down"), out["dgates"], 1.0, 1e-3, bws, nb, preact=pre)
+        if evs:
+            evs[2].record()
+
+    for _ in range(warmup):
+        train_step()
+    torch.cuda.synchronize()
+    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t1 = time.perf_counter()
+    for i in range(steps):
+        train_step(tev[i])
+    torch.cuda.synchronize()
+    twall = time.perf_counter() - t1
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in tev) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in tev) / steps
+    del fws, pre
     c = counts.cpu().numpy()
     rows = int(np.minimum(c, kept_counts(w, c)).sum())
     # algorithmic flops: dh rows (4 d d_ff) + v (2 d d_ff) + dW_gate/up (4 d d_ff) + dW_down
@@ -312,7 +353,11 @@ def run_backward(M, torch, w, inp, steps, warmup):
     res = {"workload": w.name, "ms_per_step": wall / steps * 1e3, "events_ms": ms_ev,
            "tokens_per_s": T * steps / wall, "algorithmic_tflop": flops / 1e12,
            "tflops": tf, "frac_mfma_peak": tf / PEAK_BF16_TFLOPS,
-           "workspace_gb": nb / 1e9}
+           "workspace_gb": nb / 1e9,
+           "train_step": {"ms_per_step": twall / steps * 1e3,
+                          "tokens_per_s": T * steps / twall,
+                          "forward_train_ms": fwd_ms, "backward_with_preact_ms": bwd_ms,
+                          "backward_tflops": flops / (bwd_ms * 1e-3) / 1e12}}
     del bws, out
     torch.cuda.empty_cache()
     return res

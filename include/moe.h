@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_GROUPS 64
@@ -279,6 +279,33 @@ moe_status moe_layer_fused_marked(const moe_shape* s, const void* h,
                                   float* cap_stats, void* ws, size_t ws_bytes,
                                   void* stream, void* const* events);
 
+/* The forward pass for training: moe_layer_fused that also returns what
+ * moe_layer_backward takes, so that the backward neither re-routes nor (with
+ * preact) recomputes the gate/up GEMM.
+ *   topk_ids, topk_gates [T, k], counts [N], offsets [N+1], perm_src [T·k],
+ *   row_of [T·k]: required outputs, as moe_route / moe_dispatch define them;
+ *   preact fp32 out, nullable: the gate and up pre-activations of every kept
+ *     row, [T·k, 2·d_ff] in bucket order (row r of expert e = the bucket row
+ *     of moe_dispatch; gate in columns [0, d_ff), up in [d_ff, 2·d_ff); rows
+ *     from offsets[N] on are not written), then, with a shared expert,
+ *     [T, 2·d_ff_shared] for the shared expert; 4-byte aligned. With preact
+ *     the gate/up GEMM runs on its grouped tiles at every row count.
+ *   p_out, l_aux, z_loss, entropy: nullable, as in moe_layer_fused.
+ * y and every output equal moe_layer_fused's on the same inputs (at decode
+ * sizes with preact, within rounding: another tile shape). */
+moe_status moe_layer_forward_train(const moe_shape* s, const void* h,
+                                   const void* w_router, const float* b_router,
+                                   const float* b_select, const void* w_gate,
+                                   const void* w_up, const void* w_down,
+                                   const void* sh_gate, const void* sh_up,
+                                   const void* sh_down, void* y,
+                                   int32_t* topk_ids, float* topk_gates,
+                                   int32_t* counts, int32_t* offsets,
+                                   int32_t* perm_src, int32_t* row_of,
+                                   float* preact, float* p_out, float* l_aux,
+                                   float* z_loss, float* entropy, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* Host, pure: workspace bytes for moe_layer_backward with this shape (0 for
  * an invalid shape). It holds the recomputed router logits and gate/up
  * pre-activations, transposed copies of the expert, shared-expert and
@@ -303,7 +330,10 @@ size_t moe_backward_workspace_bytes(const moe_shape* s);
  * Inputs: the forward's inputs (b_select is not needed) and its outputs
  *   topk_ids, topk_gates [T, k], counts [N] (routed, before capacity),
  *   offsets [N+1], perm_src [T·k], row_of [T·k] exactly as moe_route /
- *   moe_dispatch wrote them for this shape; dy [T, d] dtype; d_laux and
+ *   moe_dispatch (or moe_layer_forward_train) wrote them for this shape;
+ *   preact fp32, nullable: moe_layer_forward_train's pre-activations (the
+ *   backward then skips their recompute; the gradients are the same bits);
+ *   dy [T, d] dtype; d_laux and
  *   d_zloss are host scalars (the weights of L_aux and L_z in the loss;
  *   0 leaves them out).
  * Outputs (overwritten, not accumulated):
@@ -325,7 +355,8 @@ moe_status moe_layer_backward(const moe_shape* s, const void* h,
                               const int32_t* topk_ids, const float* topk_gates,
                               const int32_t* counts, const int32_t* offsets,
                               const int32_t* perm_src, const int32_t* row_of,
-                              const void* dy, float d_laux, float d_zloss,
+                              const float* preact, const void* dy, float d_laux,
+                              float d_zloss,
                               void* dh, float* dw_router, float* db_router,
                               void* dw_gate, void* dw_up, void* dw_down,
                               void* dsh_gate, void* dsh_up, void* dsh_down,

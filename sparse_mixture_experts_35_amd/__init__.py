@@ -22,7 +22,8 @@ MAX_EXPERTS, MAX_TOPK, MAX_GROUPS, MAX_GROUP_TOPM = 512, 16, 64, 8
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_fused",
-           "moe_layer_fused_marked", "moe_backward_workspace_bytes", "moe_layer_backward")
+           "moe_layer_fused_marked", "moe_layer_forward_train", "moe_backward_workspace_bytes",
+           "moe_layer_backward")
 
 
 class MoEError(RuntimeError):
@@ -64,7 +65,9 @@ _SIG = {
     "moe_layer_fused_marked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 20
                                + [_P, ctypes.c_size_t, _P, _P]),
     "moe_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
-    "moe_layer_backward": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 16
+    "moe_layer_forward_train": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 22
+                                + [_P, ctypes.c_size_t, _P]),
+    "moe_layer_backward": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 17
                            + [ctypes.c_float, ctypes.c_float] + [_P] * 10
                            + [_P, ctypes.c_size_t, _P]),
 }
@@ -163,6 +166,24 @@ def layer_fused(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh
                "moe_layer_fused_marked")
 
 
+def layer_forward_train(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate,
+                        sh_up, sh_down, y, topk_ids, topk_gates, counts, offsets, perm_src,
+                        row_of, preact=None, p_out=None, l_aux=None, z_loss=None, entropy=None,
+                        ws=None, ws_bytes=0, stream=None):
+    _check(lib().moe_layer_forward_train(
+        ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(b_select),
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),
+        _ptr(y), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _ptr(offsets), _ptr(perm_src),
+        _ptr(row_of), _ptr(preact), _ptr(p_out), _ptr(l_aux), _ptr(z_loss), _ptr(entropy),
+        _ptr(ws), ws_bytes, _stream(stream)), "moe_layer_forward_train")
+
+
+def preact_floats(shape: Shape) -> int:
+    """fp32 elements of moe_layer_forward_train's pre-activation output."""
+    return (shape.T * shape.k * 2 * shape.d_ff
+            + (shape.T * 2 * shape.d_ff_shared if shape.d_ff_shared else 0))
+
+
 def backward_workspace_bytes(shape: Shape) -> int:
     return int(lib().moe_backward_workspace_bytes(ctypes.byref(shape)))
 
@@ -170,11 +191,13 @@ def backward_workspace_bytes(shape: Shape) -> int:
 def layer_backward(shape, h, w_router, b_router, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
                    topk_ids, topk_gates, counts, offsets, perm_src, row_of, dy, dh, dw_router,
                    db_router, dw_gate, dw_up, dw_down, dsh_gate=None, dsh_up=None, dsh_down=None,
-                   dgates=None, d_laux=0.0, d_zloss=0.0, ws=None, ws_bytes=0, stream=None):
+                   dgates=None, d_laux=0.0, d_zloss=0.0, ws=None, ws_bytes=0, stream=None,
+                   preact=None):
     _check(lib().moe_layer_backward(
         ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down), _ptr(topk_ids),
-        _ptr(topk_gates), _ptr(counts), _ptr(offsets), _ptr(perm_src), _ptr(row_of), _ptr(dy),
+        _ptr(topk_gates), _ptr(counts), _ptr(offsets), _ptr(perm_src), _ptr(row_of),
+        _ptr(preact), _ptr(dy),
         float(d_laux), float(d_zloss), _ptr(dh), _ptr(dw_router), _ptr(db_router), _ptr(dw_gate),
         _ptr(dw_up), _ptr(dw_down), _ptr(dsh_gate), _ptr(dsh_up), _ptr(dsh_down), _ptr(dgates),
         _ptr(ws), ws_bytes, _stream(stream)), "moe_layer_backward")

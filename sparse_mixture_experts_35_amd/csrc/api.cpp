@@ -301,7 +301,7 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
                      const int32_t* offsets, const void* w_gate, const void* w_up,
                      const void* w_down, const void* sh_gate, const void* sh_up,
                      const void* sh_down, void* out_rows, void* ws, const FfnWs& W,
-                     hipStream_t st) {
+                     hipStream_t st, float* preact = nullptr) {
   const int T = s->T, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
   void* act = at<char>(ws, W.act);
   float* part = W.cnt > W.part ? at<float>(ws, W.part) : nullptr;
@@ -325,12 +325,13 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
   if (gateup) {
     p = moe::GroupedProblem{h, d, perm_src, s->k, offsets, s->N, rows_all, rows_max, w_gate,
                             w_up, (int64_t)dff * d, d, dff, d, act, dff, 0, (uint32_t)(esz * T * d),
-                            part, part_cnt, part_floats};
+                            part, part_cnt, part_floats, preact, 2 * (int64_t)dff};
     TRY(hip_check(run(p, true), "gate/up GEMM"));
     if (dfs) {
       p = moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d, dfs, d,
                               act_sh, dfs, 0, (uint32_t)(esz * T * d),
-                              part, part_cnt, part_floats};
+                              part, part_cnt, part_floats,
+                              preact ? preact + (int64_t)R * 2 * dff : nullptr, 2 * (int64_t)dfs};
       TRY(hip_check(run(p, true), "shared gate/up GEMM"));
     }
   } else {
@@ -360,13 +361,22 @@ moe_status mark(void* const* events, int i, hipStream_t st) {
   return hip_check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st), "event record");
 }
 
+// What the training forward returns besides the fused call's outputs.
+struct TrainOut {
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* row_of;
+  float* preact;
+};
+
 moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
                       const float* b_router, const float* b_select, const void* w_gate,
                       const void* w_up, const void* w_down, const void* sh_gate,
                       const void* sh_up, const void* sh_down, void* y, int32_t* topk_ids,
                       float* topk_gates, int32_t* counts, float* f_out, float* p_out,
                       float* l_aux, float* z_loss, float* entropy, float* cap_stats, void* ws,
-                      size_t ws_bytes, void* stream, void* const* events) {
+                      size_t ws_bytes, void* stream, void* const* events,
+                      const TrainOut& train = TrainOut{nullptr, nullptr, nullptr, nullptr}) {
   TRY(check_shape(s));
   TRY(need16(h, "h"));
   TRY(need16(w_router, "w_router"));
@@ -385,6 +395,10 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   TRY(opt4(z_loss, "z_loss"));
   TRY(opt4(entropy, "entropy"));
   TRY(opt4(cap_stats, "cap_stats"));
+  TRY(opt4(train.offsets, "offsets"));
+  TRY(opt4(train.perm, "perm_src"));
+  TRY(opt4(train.row_of, "row_of"));
+  TRY(opt4(train.preact, "preact"));
   if (events)
     for (int i = 0; i < 6; ++i)
       if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[] holds a NULL event");
@@ -398,9 +412,9 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   int32_t* cnt = counts ? counts : at<int32_t>(ws, L.counts);
   const bool want_p = p_out || l_aux;
   float* p_mean = want_p ? (p_out ? p_out : at<float>(ws, L.p_mean)) : nullptr;
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* perm = at<int32_t>(ws, L.perm);
-  int32_t* row_of = at<int32_t>(ws, L.row_of);
+  int32_t* offsets = train.offsets ? train.offsets : at<int32_t>(ws, L.offsets);
+  int32_t* perm = train.perm ? train.perm : at<int32_t>(ws, L.perm);
+  int32_t* row_of = train.row_of ? train.row_of : at<int32_t>(ws, L.row_of);
   void* rows = at<char>(ws, L.rows);
 
   TRY(mark(events, 0, st));
@@ -411,7 +425,7 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
                     at<int32_t>(ws, L.dhist), st));
   TRY(mark(events, 2, st));
   TRY(ffn_stage(s, true, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
-                ws, L.x, st));
+                ws, L.x, st, train.preact));
   TRY(mark(events, 3, st));
   TRY(ffn_stage(s, false, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
                 ws, L.x, st));
@@ -511,11 +525,11 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
                          const void* w_down, const void* sh_gate, const void* sh_up,
                          const void* sh_down, const int32_t* ids, const float* gates,
                          const int32_t* counts, const int32_t* offsets, const int32_t* perm,
-                         const int32_t* row_of, const void* dy, float d_laux, float d_zloss,
-                         void* dh, float* dw_router, float* db_router, void* dw_gate,
-                         void* dw_up, void* dw_down, void* dsh_gate, void* dsh_up,
-                         void* dsh_down, float* dgates, void* ws, const BwdWs& W,
-                         hipStream_t st) {
+                         const int32_t* row_of, const float* preact, const void* dy,
+                         float d_laux, float d_zloss, void* dh, float* dw_router,
+                         float* db_router, void* dw_gate, void* dw_up, void* dw_down,
+                         void* dsh_gate, void* dsh_up, void* dsh_down, float* dgates, void* ws,
+                         const BwdWs& W, hipStream_t st) {
   const int T = s->T, N = s->N, k = s->k, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
   const int R = T * k;
   const bool bf16 = s->dtype == MOE_BF16;
@@ -528,11 +542,12 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   const int Rp = (int)W.Rp, Tp = (int)W.Tp, Np = (int)W.Np;
   float* part = W.part_floats ? at<float>(ws, W.part) : nullptr;
   int32_t* cnt = W.part_floats ? at<int32_t>(ws, W.cnt) : nullptr;
-  float* gu = at<float>(ws, W.gu);
+  // the forward's pre-activations when it kept them, else recomputed here
+  float* gu = preact ? const_cast<float*>(preact) : at<float>(ws, W.gu);
   float* v = at<float>(ws, W.v);
   char* dgu = at<char>(ws, W.dgu);
   char* act = at<char>(ws, W.act);
-  float* gus = at<float>(ws, W.gus);
+  float* gus = preact ? const_cast<float*>(preact) + (int64_t)R * 2 * dff : at<float>(ws, W.gus);
   float* vs = at<float>(ws, W.vs);
   char* dgus = at<char>(ws, W.dgus);
   char* acts = at<char>(ws, W.acts);
@@ -586,16 +601,19 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   float* z_part = at<float>(ws, W.r.z);
   int splits = 1;
   TRY(router_logits(s, h, w_router, z_part, splits, st));
-  // 2. gate/up pre-activations of the kept rows (and the shared expert)
-  TRY(grouped(moe::GroupedProblem{h, d, perm, k, offsets, N, rows_all, rows_max, w_gate, w_up,
-                                  (int64_t)dff * d, d, dff, d, gu, 2 * dff, 0,
-                                  (uint32_t)(es * T * d), part, cnt, W.part_floats},
-              0, "gate/up recompute"));
-  if (dfs)
-    TRY(grouped(moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d,
-                                    dfs, d, gus, 2 * dfs, 0, (uint32_t)(es * T * d), part, cnt,
-                                    W.part_floats},
-                0, "shared gate/up recompute"));
+  // 2. gate/up pre-activations of the kept rows (and the shared expert),
+  //    unless the forward kept them
+  if (!preact) {
+    TRY(grouped(moe::GroupedProblem{h, d, perm, k, offsets, N, rows_all, rows_max, w_gate, w_up,
+                                    (int64_t)dff * d, d, dff, d, gu, 2 * dff, 0,
+                                    (uint32_t)(es * T * d), part, cnt, W.part_floats},
+                0, "gate/up recompute"));
+    if (dfs)
+      TRY(grouped(moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d,
+                                      dfs, d, gus, 2 * dfs, 0, (uint32_t)(es * T * d), part,
+                                      cnt, W.part_floats},
+                  0, "shared gate/up recompute"));
+  }
   // 3. v = W_down^T dy per kept row: W_down transposed to [d_ff, d] per expert
   TRY(pack(w_down, dff, dff, nullptr, 1, nullptr, nullptr, nullptr, 0, d, d, wdT, d, N,
            (int64_t)d * dff, (int64_t)dff * d, "W_down transpose"));
@@ -811,8 +829,9 @@ moe_status moe_layer_backward(const moe_shape* s, const void* h, const void* w_r
                               const void* sh_down, const int32_t* topk_ids,
                               const float* topk_gates, const int32_t* counts,
                               const int32_t* offsets, const int32_t* perm_src,
-                              const int32_t* row_of, const void* dy, float d_laux,
-                              float d_zloss, void* dh, float* dw_router, float* db_router,
+                              const int32_t* row_of, const float* preact, const void* dy,
+                              float d_laux, float d_zloss, void* dh, float* dw_router,
+                              float* db_router,
                               void* dw_gate, void* dw_up, void* dw_down, void* dsh_gate,
                               void* dsh_up, void* dsh_down, float* dgates, void* ws,
                               size_t ws_bytes, void* stream) {
@@ -831,6 +850,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* h, const void* w_r
   TRY(need4(offsets, "offsets"));
   TRY(need4(perm_src, "perm_src"));
   TRY(need4(row_of, "row_of"));
+  TRY(opt4(preact, "preact"));
   TRY(need16(dy, "dy"));
   TRY(need16(dh, "dh"));
   TRY(need4(dw_router, "dw_router"));
@@ -853,7 +873,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* h, const void* w_r
   TRY(check_ws(ws, ws_bytes, W.end));
   if (s->T == 0) return MOE_OK;
   return backward_impl(s, h, w_router, b_router, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
-                       topk_ids, topk_gates, counts, offsets, perm_src, row_of, dy, d_laux,
+                       topk_ids, topk_gates, counts, offsets, perm_src, row_of, preact, dy, d_laux,
                        d_zloss, dh, dw_router, db_router, dw_gate, dw_up, dw_down, dsh_gate,
                        dsh_up, dsh_down, dgates, ws, W, static_cast<hipStream_t>(stream));
 }
@@ -869,6 +889,28 @@ moe_status moe_layer_fused(const moe_shape* s, const void* h, const void* w_rout
   return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                     sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss,
                     entropy, cap_stats, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_forward_train(const moe_shape* s, const void* h, const void* w_router,
+                                   const float* b_router, const float* b_select,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   const void* sh_gate, const void* sh_up, const void* sh_down,
+                                   void* y, int32_t* topk_ids, float* topk_gates,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                                   int32_t* row_of, float* preact, float* p_out, float* l_aux,
+                                   float* z_loss, float* entropy, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  g_err.clear();
+  TRY(need4(topk_ids, "topk_ids"));
+  TRY(need4(topk_gates, "topk_gates"));
+  TRY(need4(counts, "counts"));
+  TRY(need4(offsets, "offsets"));
+  TRY(need4(perm_src, "perm_src"));
+  TRY(need4(row_of, "row_of"));
+  return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
+                    sh_down, y, topk_ids, topk_gates, counts, nullptr, p_out, l_aux, z_loss,
+                    entropy, nullptr, ws, ws_bytes, stream, nullptr,
+                    TrainOut{offsets, perm_src, row_of, preact});
 }
 
 moe_status moe_layer_fused_marked(const moe_shape* s, const void* h, const void* w_router,

@@ -278,8 +278,10 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[C::NB][C::FM][C::FN]) {
 // pre-activations).
 // STORE_F32 / STORE_DUAL_F32: the same as fp32 (the backward pass's
 // intermediates that feed a reduction).
+// SWIGLU_SAVE: SWIGLU, and the fp32 gate and up accumulators side by side
+// in a second output (the training forward keeps them for the backward).
 enum Epi { EPI_SWIGLU = 0, EPI_STORE_BF16 = 1, EPI_STORE_DUAL = 2, EPI_STORE_F32 = 3,
-           EPI_STORE_DUAL_F32 = 4 };
+           EPI_STORE_DUAL_F32 = 4, EPI_SWIGLU_SAVE = 5 };
 
 // Output column of MFMA block fn, lane column lr, in a wave's TN-wide strip:
 // B rows are staged so that blocks 2j and 2j+1 hold the even and odd columns
@@ -299,7 +301,8 @@ template <class C, int EPI>
 __device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][C::FN],
                                               void* __restrict__ Cout, int64_t ldc,
                                               int64_t row0_out, int rows_valid, int n0,
-                                              int Ncols) {
+                                              int Ncols, float* __restrict__ C2 = nullptr,
+                                              int64_t ldc2_el = 0) {
   static_assert(C::FN % 2 == 0, "column pairs need an even number of MFMA blocks");
   constexpr bool F32 = EPI == EPI_STORE_F32 || EPI == EPI_STORE_DUAL_F32;
   constexpr bool TWO = EPI == EPI_STORE_DUAL || EPI == EPI_STORE_DUAL_F32;
@@ -324,6 +327,15 @@ __device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][
   const Rsrc out = make_rsrc(static_cast<char*>(Cout) + row0_out * ldc * ES,
                              (uint32_t)rows_valid * (uint32_t)ldc2);
   const uint32_t lane_row = (uint32_t)(4 * lh) * (uint32_t)ldc2;
+  // second output (SWIGLU_SAVE): fp32 rows of 2 Ncols
+  int ldcs = (int)ldc2_el * 4;
+  asm volatile("" : "+s"(ldcs));
+  Rsrc out2 = out;
+  uint32_t lane_row2 = 0;
+  if constexpr (EPI == EPI_SWIGLU_SAVE) {
+    out2 = make_rsrc(C2 + row0_out * ldc2_el, (uint32_t)rows_valid * (uint32_t)ldcs);
+    lane_row2 = (uint32_t)(4 * lh) * (uint32_t)ldcs;
+  }
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
     const int rb = wm * C::TM + fm * 32;
@@ -359,8 +371,20 @@ __device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][
               voff_up, rrow * ldc2, 0);
           continue;
         }
+        if constexpr (EPI == EPI_SWIGLU_SAVE) {
+          const uint32_t v2 = col < Ncols ? lane_row2 + (uint32_t)col * 4u : 0xC0000000u;
+          const uint32_t v2u = col < Ncols ? v2 + (uint32_t)Ncols * 4u : 0xC0000000u;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0][fm][fe + h2][i]), out2,
+                                                  v2 + 4 * h2, rrow * ldcs, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(acc[C::NB - 1][fm][fe + h2][i]), out2, v2u + 4 * h2,
+                rrow * ldcs, 0);
+          }
+        }
         float v0, v1;
-        if (EPI == EPI_SWIGLU) {
+        if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) {
           v0 = silu_fast(acc[0][fm][fe][i]) * acc[C::NB - 1][fm][fe][i];
           v1 = silu_fast(acc[0][fm][fe + 1][i]) * acc[C::NB - 1][fm][fe + 1][i];
         } else {
@@ -712,7 +736,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
     }
     if (write)
       epilogue_bf16<C, EPI>(acc, p.C, p.ldc, p.c_row0 + ti.m0,
-                            ti.m_end - ti.m0, ti.n0, p.Ncols);
+                            ti.m_end - ti.m0, ti.n0, p.Ncols, p.C2, p.ldc2);
     if (dynamic) {
       __syncthreads();                 // every thread has read s_item / s_last
       if (tid == 0) s_item = nxt;
@@ -1007,6 +1031,13 @@ static bool tall_tiles(const GroupedProblem& p, int bn, int num_cu) {
 }
 
 hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
+  if (p.C2) {
+    // keeping the pre-activations: the grouped tiles at any row count, the
+    // same tiles and schedule as the backward's recompute
+    if (tall_tiles(p, GateUp256::BN, num_cu))
+      return launch_grouped<GateUp256, EPI_SWIGLU_SAVE>(p, num_cu, st);
+    return launch_grouped<GateUp128, EPI_SWIGLU_SAVE>(p, num_cu, st);
+  }
   if (p.max_rows <= 64) return launch_skinny_any<true>(p, st);
   if (tall_tiles(p, GateUp256::BN, num_cu))
     return launch_grouped<GateUp256, EPI_SWIGLU>(p, num_cu, st);

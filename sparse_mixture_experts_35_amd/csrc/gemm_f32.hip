@@ -36,6 +36,10 @@ __global__ void gateup_f32_kernel(GroupedProblem p) {
     su = fmaf(a[c], wu[c], su);
   }
   static_cast<float*>(p.C)[(p.c_row0 + r) * p.ldc + n] = silu_precise(sg) * su;
+  if (p.C2) {
+    p.C2[(p.c_row0 + r) * p.ldc2 + n] = sg;
+    p.C2[(p.c_row0 + r) * p.ldc2 + p.Ncols + n] = su;
+  }
 }
 
 // Gate and up pre-activations side by side (ldc = 2 Ncols): the backward

@@ -91,6 +91,11 @@ struct GroupedProblem {
   float* part;
   int32_t* part_cnt;
   int64_t part_floats;
+  // gate/up GEMM only, nullable: also store the fp32 gate and up
+  // pre-activations of each row at C2 + (c_row0 + r) * ldc2, gate in columns
+  // [0, Ncols), up in [Ncols, 2 Ncols) (kept for the backward pass)
+  float* C2;
+  int64_t ldc2;
 };
 
 constexpr int kSplitCounters = 1024;

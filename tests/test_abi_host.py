@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(M.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def test_status_strings():
@@ -188,12 +188,13 @@ def test_header_compiles(lang, compiler, tmp_path):
 
 def backward(s, **over):
     names = ["h", "w_router", "b_router", "w_gate", "w_up", "w_down", "sh_gate", "sh_up",
-             "sh_down", "topk_ids", "topk_gates", "counts", "offsets", "perm_src", "row_of", "dy"]
+             "sh_down", "topk_ids", "topk_gates", "counts", "offsets", "perm_src", "row_of",
+             "preact", "dy"]
     outs = ["dh", "dw_router", "db_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up",
             "dsh_down", "dgates"]
     args = {n: FAKE for n in names + outs}
-    for n in ("b_router", "sh_gate", "sh_up", "sh_down", "db_router", "dsh_gate", "dsh_up",
-              "dsh_down", "dgates"):
+    for n in ("b_router", "sh_gate", "sh_up", "sh_down", "preact", "db_router", "dsh_gate",
+              "dsh_up", "dsh_down", "dgates"):
         args[n] = None
     args.update(d_laux=0.0, d_zloss=0.0, ws=FAKE, ws_bytes=1 << 40)
     args.update(over)
@@ -223,3 +224,22 @@ def test_backward_validates():
     assert st == M.ERR_WORKSPACE
     st, err = backward(shape(T=1 << 20, d=4096, d_ff=14336, N=8, k=2))
     assert st == M.ERR_UNSUPPORTED and "2^31" in err
+
+
+def test_forward_train_validates():
+    lib = M.lib()
+    s = shape()
+    def call(**over):
+        a = dict(h=FAKE, w_router=FAKE, b_router=None, b_select=None, w_gate=FAKE, w_up=FAKE,
+                 w_down=FAKE, sh_gate=None, sh_up=None, sh_down=None, y=FAKE, topk_ids=FAKE,
+                 topk_gates=FAKE, counts=FAKE, offsets=FAKE, perm_src=FAKE, row_of=FAKE,
+                 preact=None, p_out=None, l_aux=None, z_loss=None, entropy=None)
+        a.update(over)
+        st = lib.moe_layer_forward_train(ctypes.byref(s), *a.values(), FAKE, 1 << 40, None)
+        return st, lib.moe_last_error().decode()
+    st, err = call(offsets=None)
+    assert st == M.ERR_INVALID_ARG and "offsets" in err
+    st, err = call(preact=FAKE + 2)
+    assert st == M.ERR_INVALID_ARG and "preact" in err
+    st, err = call(h=None)
+    assert st == M.ERR_INVALID_ARG and "h" in err

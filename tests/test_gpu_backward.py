@@ -155,3 +155,99 @@ def test_backward_zero_structure_on_gpu():
     assert np.abs(res["dw_router"]).max() <= 1e-6 and np.abs(res["db_router"]).max() <= 1e-6
     assert not np.any(res["dw_gate"][3]) and not np.any(res["dw_down"][3])
     check_backward(s, inp, dy, res, 0.0, 0.0)
+
+
+TRAIN_CASES = [
+    # name, T, d, N, k, d_ff, d_ff_shared, dtype, mode, groups, capacity
+    ("f32_C_shared_cap", 37, 48, 9, 3, 40, 24, W.DTYPE_F32, 2, None, 0.75),
+    ("bf16_A_prefill", 300, 128, 5, 2, 192, 0, W.DTYPE_BF16, 0, None, 0.0),
+    ("bf16_C_grouped_cap_shared", 300, 128, 64, 8, 128, 128, W.DTYPE_BF16, 2, (8, 4, 2), 1.25),
+    # at most 64 rows per expert: the training forward takes the grouped tiles
+    ("bf16_B_skinny_shared", 40, 128, 16, 4, 192, 128, W.DTYPE_BF16, 1, None, 0.0),
+    ("bf16_A_split_k4096", 256, 4096, 2, 1, 256, 0, W.DTYPE_BF16, 0, None, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", TRAIN_CASES, ids=[c[0] for c in TRAIN_CASES])
+def test_forward_train_and_backward_with_preact(case):
+    """moe_layer_forward_train gives moe_layer_fused's y (bit for bit unless
+    the fused call streams weights for <= 64 rows per expert, then within
+    tolerance) and moe_route / moe_dispatch's outputs bit for bit; its kept
+    pre-activations equal h W_gate^T and h W_up^T per kept row; the backward
+    fed with them gives the recomputing backward's gradients bit for bit."""
+    t = torch()
+    name, T, d, N, k, dff, dfs, dt, mode, groups, cf = case
+    inp = W.random_small(T, d, N, k, dff, dfs, dt, mode, seed=len(name) + 11,
+                         router_bias=(T % 2 == 0))
+    g = groups or (0, 0, 0)
+    s = M.Shape(T, d, N, k, dff, dfs, dt, mode, 0.01, *g, capacity_factor=cf)
+    print(f"case {name}", flush=True)
+    td = tdtype(dt)
+    h, wr = dev(inp["h"], dt), dev(inp["w_router"], dt)
+    br, bs = dev_f32(inp["b_router"]), dev_f32(inp["b_select"])
+    wg, wu, wd = dev(inp["w_gate"], dt), dev(inp["w_up"], dt), dev(inp["w_down"], dt)
+    sg, su, sd = dev(inp["sh_gate"], dt), dev(inp["sh_up"], dt), dev(inp["sh_down"], dt)
+    R = T * k
+    nws = M.workspace_bytes(s)
+    ws = _empty(max(nws, 1), t.uint8)
+    y = _empty((T, d), td)
+    ids, gates, counts = _empty(R, t.int32), _empty(R, t.float32), _empty(N, t.int32)
+    offsets, perm, row_of = _empty(N + 1, t.int32), _empty(R, t.int32), _empty(R, t.int32)
+    pre = _empty(M.preact_floats(s), t.float32)
+    M.layer_forward_train(s, h, wr, br, bs, wg, wu, wd, sg, su, sd, y, ids, gates, counts,
+                          offsets, perm, row_of, preact=pre, ws=ws, ws_bytes=nws)
+    # the fused call and the step-by-step routing on the same inputs
+    y2 = _empty((T, d), td)
+    M.layer_fused(s, h, wr, br, bs, wg, wu, wd, sg, su, sd, y2, ws=ws, ws_bytes=nws)
+    ids2, gates2, counts2 = _empty(R, t.int32), _empty(R, t.float32), _empty(N, t.int32)
+    off2, perm2, row2 = _empty(N + 1, t.int32), _empty(R, t.int32), _empty(R, t.int32)
+    M.route(s, h, wr, br, bs, ids2, gates2, None, ws, nws)
+    M.dispatch(s, ids2, counts2, off2, perm2, row2, ws=ws, ws_bytes=nws)
+    t.cuda.synchronize()
+    assert t.equal(ids, ids2) and t.equal(gates, gates2) and t.equal(counts, counts2)
+    kept = int(host(off2)[-1])
+    assert t.equal(offsets, off2) and t.equal(perm[:kept], perm2[:kept]) and t.equal(row_of, row2)
+    rows_max = int(np.diff(host(off2)).max())
+    if dt == W.DTYPE_BF16 and rows_max <= 64:
+        check_close_rows(host(y), host(y2), TOL[dt], what="y (forward_train vs fused)")
+    else:
+        assert t.equal(y, y2), "forward_train y differs from the fused call"
+    # kept pre-activations against numpy on the kept rows
+    offs, pm = host(off2), host(perm2)
+    P = host(pre)
+    for e in range(N):
+        for r in range(offs[e], offs[e + 1], max(1, (offs[e + 1] - offs[e]) // 3)):
+            x = inp["h"][pm[r] // k].astype(np.float64)
+            want = np.concatenate([inp["w_gate"][e] @ x, inp["w_up"][e] @ x])
+            got = P[r * 2 * dff:(r + 1) * 2 * dff]
+            assert np.abs(got - want).max() <= 1e-3 * max(1.0, np.abs(want).max()), (e, r)
+    # backward with and without the kept pre-activations
+    rng = np.random.default_rng(len(name))
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    if dt == W.DTYPE_BF16:
+        dy = W.round_to_bf16(dy)
+    dyd = dev(dy, dt)
+    outs = []
+    for use in (None, pre):
+        gg = dict(dh=_empty((T, d), td), dw_router=_empty((N, d), t.float32),
+                  db_router=_empty(N, t.float32), dw_gate=_empty((N, dff, d), td),
+                  dw_up=_empty((N, dff, d), td), dw_down=_empty((N, d, dff), td),
+                  dgates=_empty(R, t.float32))
+        if dfs:
+            gg.update(dsh_gate=_empty((dfs, d), td), dsh_up=_empty((dfs, d), td),
+                      dsh_down=_empty((d, dfs), td))
+        nb = M.backward_workspace_bytes(s)
+        bws = _empty(max(nb, 1), t.uint8)
+        M.layer_backward(s, h, wr, br, wg, wu, wd, sg, su, sd, ids, gates, counts, offsets, perm,
+                         row_of, dyd, gg["dh"], gg["dw_router"], gg["db_router"], gg["dw_gate"],
+                         gg["dw_up"], gg["dw_down"], gg.get("dsh_gate"), gg.get("dsh_up"),
+                         gg.get("dsh_down"), gg["dgates"], 0.4, 0.2, bws, nb, preact=use)
+        t.cuda.synchronize()
+        outs.append(gg)
+    for key in outs[0]:
+        assert t.equal(outs[0][key], outs[1][key]), f"{key}: kept vs recomputed pre-activations"
+    res = {key: host(v) for key, v in outs[1].items()}
+    res["ids"] = host(ids).reshape(T, k)
+    res["row_of"] = host(row_of)
+    worst = check_backward(s, inp, dy, res, 0.4, 0.2)
+    print(f"{name}: " + ", ".join(f"{k_} {v:.1e}" for k_, v in worst.items()))
