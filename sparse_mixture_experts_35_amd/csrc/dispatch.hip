@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_place_kernel(
 
 }  // namespace
 
-int dispatch_chunks(int T, int k) { return (T * k + kChunk - 1) / kChunk; }
+int dispatch_chunks(int T, int k) { return (int)(((int64_t)T * k + kChunk - 1) / kChunk); }
 
 hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N, int32_t* counts,
                            int32_t* offsets, int32_t* perm_src, int32_t* row_of,
