@@ -12,8 +12,11 @@ oracle on sampled outputs it can compute one at a time:
     backward restricted to those hidden units is exact for them;
   * sampled rows of dW_down of the smallest expert (the full expert
     backward on its rows).
-The router's weight gradients need every token's dL/dg and are checked at
-the smaller sizes only (tests/test_gpu_backward.py)."""
+The benchmark's training step (moe_layer_forward_train keeping the
+pre-activations, then the backward using them) must give the fused call's y
+and the checked gradients bit for bit. The router's weight gradients need
+every token's dL/dg and are checked at the smaller sizes only
+(tests/test_gpu_backward.py)."""
 import numpy as np
 import pytest
 
@@ -69,7 +72,38 @@ def test_full_size_backward_mixtral_prefill():
                      dy, g["dh"], g["dw_router"], g["db_router"], g["dw_gate"], g["dw_up"],
                      g["dw_down"], None, None, None, g["dgates"], D_LAUX, D_ZLOSS, bws, nb)
     t.cuda.synchronize()
-    del bws
+
+    # the benchmark's training step: the training forward keeps the dispatch
+    # and the pre-activations, the backward uses them; same bits as above
+    nws = M.workspace_bytes(s)
+    ws = E(nws, t.uint8)
+    pre = E(M.preact_floats(s), t.float32)
+    y_t, y_f = E((T, d)), E((T, d))
+    ids_t, gates_t, counts_t = E(T * k, t.int32), E(T * k, t.float32), E(N, t.int32)
+    off_t, perm_t, row_t = E(N + 1, t.int32), E(T * k, t.int32), E(T * k, t.int32)
+    M.layer_forward_train(s, inp["h"], inp["w_router"], inp["b_router"], None, inp["w_gate"],
+                          inp["w_up"], inp["w_down"], None, None, None, y_t, ids_t, gates_t,
+                          counts_t, off_t, perm_t, row_t, preact=pre, ws=ws, ws_bytes=nws)
+    M.layer_fused(s, inp["h"], inp["w_router"], inp["b_router"], None, inp["w_gate"], inp["w_up"],
+                  inp["w_down"], None, None, None, y_f, ws=ws, ws_bytes=nws)
+    t.cuda.synchronize()
+    del ws
+    kept = int(host(offsets)[-1])
+    assert t.equal(y_t, y_f), "training forward y differs from the fused call"
+    assert t.equal(ids_t, ids) and t.equal(gates_t, gates) and t.equal(counts_t, counts)
+    assert t.equal(off_t, offsets) and t.equal(perm_t[:kept], perm[:kept]) and t.equal(row_t, row_of)
+    g2 = {key: t.empty_like(v) for key, v in g.items()}
+    M.layer_backward(s, inp["h"], inp["w_router"], inp["b_router"], inp["w_gate"], inp["w_up"],
+                     inp["w_down"], None, None, None, ids_t, gates_t, counts_t, off_t, perm_t,
+                     row_t, dy, g2["dh"], g2["dw_router"], g2["db_router"], g2["dw_gate"],
+                     g2["dw_up"], g2["dw_down"], None, None, None, g2["dgates"], D_LAUX, D_ZLOSS,
+                     bws, nb, preact=pre)
+    t.cuda.synchronize()
+    for key in g:
+        assert t.equal(g[key], g2[key]), f"{key}: kept vs recomputed pre-activations"
+    print(f"[{w.name}] training forward and backward with kept pre-activations: same bits",
+          flush=True)
+    del bws, pre, g2
 
     h, wr, dyh = _np(inp["h"]), _np(inp["w_router"]), _np(dy)
     g_ids = host(ids).reshape(T, k)
