@@ -266,7 +266,12 @@ moe_status moe_layer_fused(const moe_shape* s, const void* h,
  * `stream` at the stage boundaries, for timing: events[0] before routing,
  * [1] after routing, [2] after dispatch, [3] after the gate/up GEMM
  * (SwiGLU), [4] after the down GEMM, [5] after combine. `events` is a host
- * array of 6 hipEvent_t (as void*), all non-NULL. */
+ * array of 6 hipEvent_t (as void*); a NULL entry records nothing at that
+ * boundary. Where one kernel does two stages, the boundary between them is
+ * recorded back to back: [1] and [2] when a batch that fits one selection
+ * block and one dispatch chunk is selected and dispatched by one kernel, [4]
+ * and [5] when the combine runs inside the down GEMM (bf16, at most 64 rows
+ * per expert). */
 moe_status moe_layer_fused_marked(const moe_shape* s, const void* h,
                                   const void* w_router, const float* b_router,
                                   const float* b_select, const void* w_gate,

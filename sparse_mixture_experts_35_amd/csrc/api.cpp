@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <mutex>
+#include <optional>
 #include <string>
 
 #include "../../include/moe.h"
@@ -183,7 +184,7 @@ size_t dispatch_ws_bytes(const moe_shape* s) {
 struct FusedWs {
   RouteWs r;
   FfnWs x;
-  size_t p_mean, ids, gates, counts, offsets, perm, row_of, f, dhist, rows, end;
+  size_t p_mean, ids, gates, counts, offsets, perm, row_of, f, dhist, cmb, rows, end;
 };
 FusedWs fused_ws(const moe_shape* s) {
   FusedWs w;
@@ -198,7 +199,8 @@ FusedWs fused_ws(const moe_shape* s) {
   w.row_of = align_up(w.perm + 4 * R);
   w.f = align_up(w.row_of + 4 * R);
   w.dhist = align_up(w.f + 4 * N + 4);
-  w.x = ffn_ws(s, w.dhist + dispatch_ws_bytes(s));
+  w.cmb = w.dhist + dispatch_ws_bytes(s);
+  w.x = ffn_ws(s, align_up(w.cmb + 4 * (size_t)moe::combine_counters(s->d)));
   w.rows = w.x.end;
   w.end = align_up(w.rows + esize(s) * (R + (s->d_ff_shared ? T : 0)) * s->d);
   return w;
@@ -261,10 +263,17 @@ moe_status router_logits(const moe_shape* s, const void* h, const void* w_router
                    "router logits");
 }
 
+// A batch that fits one selection block and one dispatch chunk.
+bool route_dispatch_fits(const moe_shape* s) {
+  return moe::route_select_blocks(s->T, s->N) == 1 && moe::dispatch_chunks(s->T, s->k) == 1;
+}
+
+// dq (only when route_dispatch_fits): the selection kernel also dispatches.
 moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
                       const float* b_router, const float* b_select, int32_t* ids,
                       float* gates, float* p_mean, float* z_loss, float* entropy,
-                      const RouteWs& W, void* ws, hipStream_t st) {
+                      const RouteWs& W, void* ws, hipStream_t st,
+                      const std::optional<moe::DispatchOut>& dq = std::nullopt) {
   float* z_part = at<float>(ws, W.z);
   float* p_part = at<float>(ws, W.p_part);
   float* zl_part = (z_loss || entropy) ? at<float>(ws, W.zl_part) : nullptr;
@@ -278,8 +287,8 @@ moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
   const moe::RouteFinal fin{p_mean, z_loss, entropy, single ? 1 : 0};
   TRY(hip_check(moe::launch_route_select(z_part, splits, b_router, b_select, ids, gates,
                                          p_mean ? p_part : nullptr, zl_part, s->T, s->N, s->k,
-                                         s->mode, gl, fin, st),
-                "route select"));
+                                         s->mode, gl, fin, st, dq ? &*dq : nullptr),
+                dq ? "route select + dispatch" : "route select"));
   if (!single && (p_mean || zl_part))
     TRY(hip_check(moe::launch_p_reduce(p_part, p_mean, zl_part, z_loss, entropy,
                                        moe::route_select_blocks(s->T, s->N), s->T, s->N, st),
@@ -290,10 +299,11 @@ moe_status route_impl(const moe_shape* s, const void* h, const void* w_router,
 moe_status dispatch_impl(const moe_shape* s, const int32_t* ids, int32_t* counts,
                          int32_t* offsets, int32_t* perm_src, int32_t* row_of,
                          const float* p_mean, float* f_out, float* l_aux, float* cap_stats,
-                         int32_t* hist, hipStream_t st) {
+                         int32_t* hist, hipStream_t st, int32_t* zero = nullptr,
+                         int zero_n = 0) {
   return hip_check(moe::launch_dispatch(ids, s->T, s->k, s->N, counts, offsets, perm_src, row_of,
                                         p_mean, f_out, l_aux, s->aux_alpha, expert_capacity(s),
-                                        cap_stats, hist, st),
+                                        cap_stats, hist, st, zero, zero_n),
                    "dispatch");
 }
 
@@ -301,7 +311,8 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
                      const int32_t* offsets, const void* w_gate, const void* w_up,
                      const void* w_down, const void* sh_gate, const void* sh_up,
                      const void* sh_down, void* out_rows, void* ws, const FfnWs& W,
-                     hipStream_t st, float* preact = nullptr) {
+                     hipStream_t st, float* preact = nullptr,
+                     const moe::CombineFuse* fuse = nullptr, bool* combined = nullptr) {
   const int T = s->T, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
   void* act = at<char>(ws, W.act);
   float* part = W.cnt > W.part ? at<float>(ws, W.part) : nullptr;
@@ -335,16 +346,22 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
       TRY(hip_check(run(p, true), "shared gate/up GEMM"));
     }
   } else {
-    p = moe::GroupedProblem{act, dff, nullptr, 1, offsets, s->N, rows_all, rows_max, w_down,
-                            nullptr, (int64_t)d * dff, dff, d, dff, out_rows, d, 0, (uint32_t)(esz * R * dff),
-                            part, part_cnt, part_floats};
-    TRY(hip_check(run(p, false), "down GEMM"));
-    if (dfs) {
-      p = moe::GroupedProblem{act_sh, dfs, nullptr, 1, nullptr, 1, T, T, sh_down, nullptr, 0,
-                              dfs, d, dfs, out_rows, d, (int64_t)R, (uint32_t)(esz * T * dfs),
-                              part, part_cnt, part_floats};
-      TRY(hip_check(run(p, false), "shared down GEMM"));
+    const moe::GroupedProblem pr{act, dff, nullptr, 1, offsets, s->N, rows_all, rows_max, w_down,
+                                 nullptr, (int64_t)d * dff, dff, d, dff, out_rows, d, 0,
+                                 (uint32_t)(esz * R * dff), part, part_cnt, part_floats};
+    const moe::GroupedProblem ps{act_sh, dfs, nullptr, 1, nullptr, 1, T, T, sh_down, nullptr, 0,
+                                 dfs, d, dfs, out_rows, d, (int64_t)R, (uint32_t)(esz * T * dfs),
+                                 part, part_cnt, part_floats};
+    // the combine fused into the weight-streaming down GEMM: the shared
+    // expert's rows first, then the routed rows and the combine
+    const bool fused = fuse && bf16 && moe::down_combine_ok(pr, *fuse);
+    if (combined) *combined = fused;
+    if (fused) {
+      if (dfs) TRY(hip_check(run(ps, false), "shared down GEMM"));
+      return hip_check(moe::launch_down_combine_bf16(pr, *fuse, st), "down GEMM + combine");
     }
+    TRY(hip_check(run(pr, false), "down GEMM"));
+    if (dfs) TRY(hip_check(run(ps, false), "shared down GEMM"));
   }
   return MOE_OK;
 }
@@ -357,7 +374,7 @@ moe_status combine_impl(const moe_shape* s, const void* out_rows, const int32_t*
 }
 
 moe_status mark(void* const* events, int i, hipStream_t st) {
-  if (!events) return MOE_OK;
+  if (!events || !events[i]) return MOE_OK;
   return hip_check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st), "event record");
 }
 
@@ -399,9 +416,6 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   TRY(opt4(train.perm, "perm_src"));
   TRY(opt4(train.row_of, "row_of"));
   TRY(opt4(train.preact, "preact"));
-  if (events)
-    for (int i = 0; i < 6; ++i)
-      if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[] holds a NULL event");
   const FusedWs L = fused_ws(s);
   TRY(check_ws(ws, ws_bytes, L.end));
   if (s->T == 0) return MOE_OK;
@@ -417,20 +431,35 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   int32_t* row_of = train.row_of ? train.row_of : at<int32_t>(ws, L.row_of);
   void* rows = at<char>(ws, L.rows);
 
+  int32_t* cmb_cnt = at<int32_t>(ws, L.cmb);
+  const int cmb_n = moe::combine_counters(s->d);
+
   TRY(mark(events, 0, st));
-  TRY(route_impl(s, h, w_router, b_router, b_select, ids, gates, p_mean, z_loss, entropy, L.r,
-                 ws, st));
-  TRY(mark(events, 1, st));
-  TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, cap_stats,
-                    at<int32_t>(ws, L.dhist), st));
+  if (route_dispatch_fits(s)) {
+    // one selection block and one dispatch chunk: a single kernel selects
+    // and dispatches (same bits as the separate kernels)
+    TRY(route_impl(s, h, w_router, b_router, b_select, ids, gates, p_mean, z_loss, entropy, L.r,
+                   ws, st,
+                   moe::DispatchOut{cnt, offsets, perm, row_of, f_out, l_aux, s->aux_alpha,
+                                    expert_capacity(s), cap_stats, cmb_cnt, cmb_n}));
+    TRY(mark(events, 1, st));
+  } else {
+    TRY(route_impl(s, h, w_router, b_router, b_select, ids, gates, p_mean, z_loss, entropy, L.r,
+                   ws, st));
+    TRY(mark(events, 1, st));
+    TRY(dispatch_impl(s, ids, cnt, offsets, perm, row_of, p_mean, f_out, l_aux, cap_stats,
+                      at<int32_t>(ws, L.dhist), st, cmb_cnt, cmb_n));
+  }
   TRY(mark(events, 2, st));
   TRY(ffn_stage(s, true, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
                 ws, L.x, st, train.preact));
   TRY(mark(events, 3, st));
+  const moe::CombineFuse fuse{row_of, gates, y, s->T, s->k, s->d_ff_shared ? 1 : 0, cmb_cnt};
+  bool combined = false;
   TRY(ffn_stage(s, false, h, perm, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down, rows,
-                ws, L.x, st));
+                ws, L.x, st, nullptr, &fuse, &combined));
   TRY(mark(events, 4, st));
-  TRY(combine_impl(s, rows, row_of, gates, y, st));
+  if (!combined) TRY(combine_impl(s, rows, row_of, gates, y, st));
   TRY(mark(events, 5, st));
   return MOE_OK;
 }

@@ -850,22 +850,11 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(
 // loads 32 contiguous bytes of weight row i at k = 64c + 16q, so each group
 // of four lanes reads one full 128-byte line; the A fragments use the same
 // k mapping.
-template <int MT, int CT, bool DUAL>
-__global__ __launch_bounds__(kThreads) void skinny_gemm_kernel(GroupedProblem p) {
+template <int MT, int CT, bool DUAL, bool CMB>
+__device__ __forceinline__ void skinny_tile(const GroupedProblem& p, int r0, int cnt,
+                                            f32x4 (&red)[4][(DUAL ? 2 : 1) * MT * CT][64]) {
   constexpr int NB = DUAL ? 2 : 1;
-  constexpr int NACC = NB * MT * CT;
-  __shared__ f32x4 red[4][NACC][64];
   const int g = blockIdx.x;
-  int r0, cnt;
-  if (p.offsets) {
-    r0 = p.offsets[g];
-    cnt = p.offsets[g + 1] - r0;
-  } else {
-    r0 = g * 16 * MT;
-    cnt = min(p.M - r0, 16 * MT);
-  }
-  if (cnt <= 0) return;
-  cnt = min(cnt, 16 * MT);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
   const int n0 = blockIdx.y * 16 * CT;
@@ -949,6 +938,7 @@ __global__ __launch_bounds__(kThreads) void skinny_gemm_kernel(GroupedProblem p)
   __syncthreads();
 
   bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
+  __shared__ __attribute__((aligned(16))) bf16_t s_out[CMB ? 16 * MT : 1][16 * CT];
   for (int q = w; q < MT * CT; q += 4) {
     const int mt = q / CT, ct = q % CT;
     const f32x4 a0 = red[0][q][lane] + red[1][q][lane] + red[2][q][lane] + red[3][q][lane];
@@ -963,27 +953,117 @@ __global__ __launch_bounds__(kThreads) void skinny_gemm_kernel(GroupedProblem p)
       const int m = mt * 16 + lq * 4 + i;
       if (m < cnt && col < p.Ncols) {
         const float v = DUAL ? silu_fast(a0[i]) * a1[i] : a0[i];
-        Cout[(p.c_row0 + r0 + m) * (int64_t)p.ldc + col] = (bf16_t)f32_to_bf16(v);
+        if constexpr (CMB)
+          s_out[m][ct * 16 + li] = (bf16_t)f32_to_bf16(v);
+        else
+          Cout[(p.c_row0 + r0 + m) * (int64_t)p.ldc + col] = (bf16_t)f32_to_bf16(v);
+      }
+    }
+  }
+  if constexpr (CMB) {
+    // 16-byte agent-coherent stores of the tile's rows (byte offsets below
+    // 2^31: checked by the launcher)
+    __syncthreads();
+    constexpr int CPR = 2 * CT;                  // 8-column chunks per row
+    const Rsrc rc = make_rsrc(Cout, 0x7fffffffu);
+    for (int i = tid; i < cnt * CPR; i += kThreads) {
+      const int m = i / CPR, ch = i % CPR;
+      const int col = n0 + ch * 8;
+      if (col < p.Ncols) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&s_out[m][ch * 8]);
+        const int64_t off = ((p.c_row0 + r0 + m) * (int64_t)p.ldc + col) * 2;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, (uint32_t)off, 0, kSc1);
       }
     }
   }
 }
 
-template <int MT, bool DUAL>
-hipError_t launch_skinny(const GroupedProblem& p, hipStream_t st) {
+// The combine of one column range [n0, n0 + 16 CT) by the last block of the
+// range to arrive; rows are read with agent-coherent loads.
+template <int CT>
+__device__ __forceinline__ void skinny_combine(const GroupedProblem& p, const CombineFuse& cf) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  wait_vmcnt<0>();                    // this wave's row stores are complete
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(cf.cnt + blockIdx.y, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(s_last)) return;
+  constexpr int CPR = 2 * CT;
+  const int n0 = blockIdx.y * 16 * CT;
+  const int64_t R = (int64_t)cf.T * cf.k;
+  const Rsrc rc = make_rsrc(p.C, 0x7fffffffu);
+  bf16_t* __restrict__ y = static_cast<bf16_t*>(cf.y);
+  for (int i = tid; i < cf.T * CPR; i += kThreads) {
+    const int t = i / CPR, col = n0 + (i % CPR) * 8;
+    if (col >= p.Ncols) continue;
+    float acc[8];
+    if (cf.has_shared) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+          rc, (uint32_t)(((R + t) * p.ldc + col) * 2), 0, kSc1);
+      unpack_bf16x8(v, acc);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    }
+    for (int j = 0; j < cf.k; ++j) {
+      const int64_t r = cf.row_of[(int64_t)t * cf.k + j];
+      if (r < 0) continue;
+      const float gt = cf.gates[(int64_t)t * cf.k + j];
+      float v[8];
+      unpack_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)((r * p.ldc + col) * 2),
+                                                          0, kSc1),
+                    v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(gt, v[e], acc[e]);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(y + (int64_t)t * p.Ncols + col) = o;
+  }
+}
+
+// CMB (down GEMM with the combine fused): rows are written with
+// agent-coherent stores, then every block of a column range bumps that
+// range's arrival counter (the blocks of experts without rows too); the
+// last to arrive sums each token's rows over those columns into y, with the
+// separate combine kernel's arithmetic and order (same bits).
+template <int MT, int CT, bool DUAL, bool CMB>
+__global__ __launch_bounds__(kThreads) void skinny_gemm_kernel(GroupedProblem p, CombineFuse cf) {
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int NACC = NB * MT * CT;
+  __shared__ f32x4 red[4][NACC][64];
+  const int g = blockIdx.x;
+  int r0, cnt;
+  if (p.offsets) {
+    r0 = p.offsets[g];
+    cnt = p.offsets[g + 1] - r0;
+  } else {
+    r0 = g * 16 * MT;
+    cnt = min(p.M - r0, 16 * MT);
+  }
+  if (cnt > 0) skinny_tile<MT, CT, DUAL, CMB>(p, r0, min(cnt, 16 * MT), red);
+  if constexpr (CMB) skinny_combine<CT>(p, cf);
+}
+
+template <int MT, bool DUAL, bool CMB = false>
+hipError_t launch_skinny(const GroupedProblem& p, hipStream_t st,
+                         const CombineFuse& cf = CombineFuse{}) {
   constexpr int CT = (MT == 1) ? 4 : (MT == 2 ? 2 : 1);
   const int G = p.offsets ? p.groups : (p.M + 16 * MT - 1) / (16 * MT);
   dim3 grid(G, (p.Ncols + 16 * CT - 1) / (16 * CT));
   if (G == 0) return hipSuccess;
-  hipLaunchKernelGGL((skinny_gemm_kernel<MT, CT, DUAL>), grid, dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((skinny_gemm_kernel<MT, CT, DUAL, CMB>), grid, dim3(kThreads), 0, st, p, cf);
   return hipGetLastError();
 }
 
-template <bool DUAL>
-hipError_t launch_skinny_any(const GroupedProblem& p, hipStream_t st) {
-  if (p.max_rows <= 16) return launch_skinny<1, DUAL>(p, st);
-  if (p.max_rows <= 32) return launch_skinny<2, DUAL>(p, st);
-  return launch_skinny<4, DUAL>(p, st);
+template <bool DUAL, bool CMB = false>
+hipError_t launch_skinny_any(const GroupedProblem& p, hipStream_t st,
+                             const CombineFuse& cf = CombineFuse{}) {
+  if (p.max_rows <= 16) return launch_skinny<1, DUAL, CMB>(p, st, cf);
+  if (p.max_rows <= 32) return launch_skinny<2, DUAL, CMB>(p, st, cf);
+  return launch_skinny<4, DUAL, CMB>(p, st, cf);
 }
 
 template <class C, int EPI>
@@ -1042,6 +1122,20 @@ hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu, hipStream_t s
   if (tall_tiles(p, GateUp256::BN, num_cu))
     return launch_grouped<GateUp256, EPI_SWIGLU>(p, num_cu, st);
   return launch_grouped<GateUp128, EPI_SWIGLU>(p, num_cu, st);
+}
+
+int combine_counters(int d) { return (d + 15) / 16; }
+
+bool down_combine_ok(const GroupedProblem& p, const CombineFuse& cf) {
+  const int64_t rows = (int64_t)cf.T * cf.k + (cf.has_shared ? cf.T : 0);
+  return p.max_rows <= 64 && p.offsets && p.c_row0 == 0 && p.ldc == p.Ncols &&
+         p.Ncols % 8 == 0 && rows * p.ldc * 2 <= 0x7fffffffLL;
+}
+
+hipError_t launch_down_combine_bf16(const GroupedProblem& p, const CombineFuse& cf,
+                                    hipStream_t st) {
+  if (!down_combine_ok(p, cf)) return hipErrorNotSupported;
+  return launch_skinny_any<false, true>(p, st, cf);
 }
 
 hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {

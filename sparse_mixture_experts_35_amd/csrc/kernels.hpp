@@ -36,11 +36,29 @@ struct RouteFinal {
   float* entropy;
   int on;
 };
+// Outputs of the dispatch when the selection kernel also dispatches (see
+// launch_dispatch; p_mean is fin.p_mean)
+struct DispatchOut {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_src;
+  int32_t* row_of;
+  float* f_out;
+  float* l_aux;
+  float alpha;
+  int cap;
+  float* cap_stats;
+  int32_t* zero;
+  int zero_n;
+};
+// dq != NULL: one block selects and then dispatches (T fits one selection
+// block and T·k one dispatch chunk, else hipErrorInvalidValue)
 hipError_t launch_route_select(const float* z_part, int splits,
                                const float* b_router, const float* b_select,
                                int32_t* ids, float* gates, float* p_part,
                                float* zl_part, int T, int N, int k, int mode,
-                               GroupLimit gl, RouteFinal fin, hipStream_t st);
+                               GroupLimit gl, RouteFinal fin, hipStream_t st,
+                               const DispatchOut* dq = nullptr);
 // small T·N: router logits by a GEMV kernel (one slice, splits = 1)
 bool router_use_gemv(int T, int N);
 hipError_t launch_router_gemv_bf16(const void* h, const void* w, float* z,
@@ -52,14 +70,16 @@ hipError_t launch_p_reduce(const float* p_part, float* p_mean,
 
 // --------------------------------------------------------------- dispatch
 // cap: expert capacity C >= 1, or 0 for none; cap_stats nullable; hist:
-// dispatch_chunks(T, k) x N int32 of scratch (per-chunk expert counts)
+// dispatch_chunks(T, k) x N int32 of scratch (per-chunk expert counts);
+// zero_n int32 at zero are cleared (counters of a later kernel)
 int dispatch_chunks(int T, int k);
 hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N,
                            int32_t* counts, int32_t* offsets,
                            int32_t* perm_src, int32_t* row_of,
                            const float* p_mean, float* f_out, float* l_aux,
                            float alpha, int cap, float* cap_stats,
-                           int32_t* hist, hipStream_t st);
+                           int32_t* hist, hipStream_t st,
+                           int32_t* zero = nullptr, int zero_n = 0);
 
 // ---------------------------------------------------------------- experts
 // One grouped problem: rows of A gathered through perm (token = perm[r] /
@@ -112,6 +132,24 @@ hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu,
 // C = A·B0^T                        (bf16 in/out, fp32 accumulate)
 hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu,
                             hipStream_t st);
+// Combine fused into the weight-streaming down GEMM (at most 64 rows per
+// expert): y[t] = (shared row) + sum_j gates[t k + j] rows[row_of[t k + j]],
+// rows being the GEMM's own output C (c_row0 0, ldc = Ncols = d; the shared
+// expert's rows [T k, T k + T) written before the launch). cnt:
+// combine_counters(d) int32, zero at launch.
+struct CombineFuse {
+  const int32_t* row_of;
+  const float* gates;
+  void* y;
+  int T, k;
+  int has_shared;
+  int32_t* cnt;
+};
+int combine_counters(int d);
+bool down_combine_ok(const GroupedProblem& p, const CombineFuse& cf);
+// hipErrorNotSupported unless down_combine_ok
+hipError_t launch_down_combine_bf16(const GroupedProblem& p, const CombineFuse& cf,
+                                    hipStream_t st);
 // gate and up pre-activations side by side as fp32: C [rows, 2 Ncols] float,
 // ldc = 2 Ncols
 hipError_t launch_gateup_preact_bf16(const GroupedProblem& p, int num_cu,

@@ -25,6 +25,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "dispatch_place.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -79,9 +80,10 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
 // A group of LPT lanes routes one token (LPT = 8/16/32 for N up to that
 // many experts, else 64); lane li of the group holds experts li, li+LPT, ...
 // (VPL values). All reductions stay inside the group (xor offsets < LPT).
+// Block blk of the selection (tokens [blk·TPB, (blk+1)·TPB)).
 template <int LPT, int VPL, int MODE, int ITER>
-__global__ __launch_bounds__(kThreads) void route_select_kernel(
-    const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
+__device__ __forceinline__ void route_select_block(
+    int blk, const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
     const float* __restrict__ b_select, int32_t* __restrict__ ids,
     float* __restrict__ gates, float* __restrict__ p_part, float* __restrict__ zl_part, int T,
     int N, int k, GroupLimit gl, RouteFinal fin) {
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   float zl_acc = 0.0f, ent_acc = 0.0f;        // this lane's tokens (lane li == 0)
 
   for (int it = 0; it < ITER; ++it) {
-    const int t = blockIdx.x * TPB + (it * 4 + w) * TPW + grp;
+    const int t = blk * TPB + (it * 4 + w) * TPW + grp;
     const bool tok = t < T;
     // ---- logits: split-K slices summed in order, then the router bias
     float zv[VPL], sel[VPL], aux[VPL];
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
       for (int ww = 0; ww < 4; ++ww)
 #pragma unroll
         for (int g = 0; g < TPW; ++g) sum += s_zl[ww][g * LPT][tid];
-      zl_part[(int64_t)blockIdx.x * 2 + tid] = sum;
+      zl_part[(int64_t)blk * 2 + tid] = sum;
       float* out = tid == 0 ? fin.z_loss : fin.entropy;
       if (fin.on && out) *out = sum / (float)T;
     }
@@ -388,10 +390,39 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
       for (int ww = 0; ww < 4; ++ww)
 #pragma unroll
         for (int g = 0; g < TPW; ++g) sum += s_p[ww][g * LPT + e % LPT][e / LPT];
-      p_part[(int64_t)blockIdx.x * N + e] = sum;
+      p_part[(int64_t)blk * N + e] = sum;
       if (fin.on && fin.p_mean) fin.p_mean[e] = sum / (float)T;
     }
   }
+}
+
+template <int LPT, int VPL, int MODE, int ITER>
+__global__ __launch_bounds__(kThreads) void route_select_kernel(
+    const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
+    const float* __restrict__ b_select, int32_t* __restrict__ ids,
+    float* __restrict__ gates, float* __restrict__ p_part, float* __restrict__ zl_part, int T,
+    int N, int k, GroupLimit gl, RouteFinal fin) {
+  route_select_block<LPT, VPL, MODE, ITER>(blockIdx.x, z_part, splits, b_router, b_select, ids,
+                                           gates, p_part, zl_part, T, N, k, gl, fin);
+}
+
+// Selection and dispatch of a batch that fits one selection block and one
+// dispatch chunk, in one block: the selection writes ids, gates and the
+// final statistics, then (after a block barrier, which makes those global
+// writes visible to the whole block) the same block places the slots. The
+// results are those of the two separate kernels, bit for bit.
+template <int LPT, int VPL, int MODE, int ITER>
+__global__ __launch_bounds__(kThreads) void route_dispatch_kernel(
+    const float* __restrict__ z_part, int splits, const float* __restrict__ b_router,
+    const float* __restrict__ b_select, int32_t* __restrict__ ids,
+    float* __restrict__ gates, float* __restrict__ p_part, float* __restrict__ zl_part, int T,
+    int N, int k, GroupLimit gl, RouteFinal fin, DispatchOut dq) {
+  route_select_block<LPT, VPL, MODE, ITER>(0, z_part, splits, b_router, b_select, ids, gates,
+                                           p_part, zl_part, T, N, k, gl, fin);
+  __syncthreads();
+  dsp::place_chunk(0, ids, T, k, N, nullptr, 1, dq.counts, dq.offsets, dq.perm_src, dq.row_of,
+                   fin.p_mean, dq.f_out, dq.l_aux, dq.alpha, dq.cap, dq.cap_stats, dq.zero,
+                   dq.zero_n);
 }
 
 // p_mean[e] = (sum over blocks of p_part[b][e]) / T: one block per expert,
@@ -452,23 +483,40 @@ SelectCfg select_cfg(int N) {
   return c;
 }
 
+// dq == NULL: the selection kernel (blocks of it); else the single-block
+// selection + dispatch kernel
+template <int LPT, int VPL, int MODE, int ITER>
+void launch_select_m(const float* z_part, int splits, const float* b_router,
+                     const float* b_select, int32_t* ids, float* gates, float* p_part,
+                     float* zl_part, int T, int N, int k, GroupLimit gl, int blocks,
+                     RouteFinal fin, const DispatchOut* dq, hipStream_t st) {
+  if (dq)
+    hipLaunchKernelGGL((route_dispatch_kernel<LPT, VPL, MODE, ITER>), dim3(1), dim3(kThreads), 0,
+                       st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N,
+                       k, gl, fin, *dq);
+  else
+    hipLaunchKernelGGL((route_select_kernel<LPT, VPL, MODE, ITER>), dim3(blocks), dim3(kThreads),
+                       0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T,
+                       N, k, gl, fin);
+}
+
 template <int LPT, int VPL, int ITER>
 hipError_t launch_select_t(const float* z_part, int splits, const float* b_router,
                            const float* b_select, int32_t* ids, float* gates, float* p_part,
                            float* zl_part, int T, int N, int k, int mode, GroupLimit gl,
-                           int blocks, RouteFinal fin, hipStream_t st) {
+                           int blocks, RouteFinal fin, const DispatchOut* dq, hipStream_t st) {
   switch (mode) {
     case 0:
-      hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 0, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl, fin);
+      launch_select_m<LPT, VPL, 0, ITER>(z_part, splits, b_router, b_select, ids, gates, p_part,
+                                         zl_part, T, N, k, gl, blocks, fin, dq, st);
       break;
     case 1:
-      hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 1, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl, fin);
+      launch_select_m<LPT, VPL, 1, ITER>(z_part, splits, b_router, b_select, ids, gates, p_part,
+                                         zl_part, T, N, k, gl, blocks, fin, dq, st);
       break;
     default:
-      hipLaunchKernelGGL((route_select_kernel<LPT, VPL, 2, ITER>), dim3(blocks), dim3(kThreads),
-                         0, st, z_part, splits, b_router, b_select, ids, gates, p_part, zl_part, T, N, k, gl, fin);
+      launch_select_m<LPT, VPL, 2, ITER>(z_part, splits, b_router, b_select, ids, gates, p_part,
+                                         zl_part, T, N, k, gl, blocks, fin, dq, st);
       break;
   }
   return hipGetLastError();
@@ -505,15 +553,21 @@ int route_select_blocks(int T, int N) {
 hipError_t launch_route_select(const float* z_part, int splits, const float* b_router,
                                const float* b_select, int32_t* ids, float* gates,
                                float* p_part, float* zl_part, int T, int N, int k, int mode,
-                               GroupLimit gl, RouteFinal fin, hipStream_t st) {
+                               GroupLimit gl, RouteFinal fin, hipStream_t st,
+                               const DispatchOut* dq) {
   const SelectCfg c = select_cfg(N);
   const int blocks = (T + c.tpb - 1) / c.tpb;
   if (blocks == 0) return hipSuccess;
   fin.on = fin.on && blocks == 1;
+  if (dq) {
+    // the fused kernel is one block; its dispatch reads the p_mean it wrote
+    if (blocks != 1 || dispatch_chunks(T, k) != 1) return hipErrorInvalidValue;
+    fin.on = 1;
+  }
 #define MOE_SEL(L, V, I)                                                                    \
   if (c.lpt == L && c.vpl == V)                                                             \
     return launch_select_t<L, V, I>(z_part, splits, b_router, b_select, ids, gates, p_part, \
-                                    zl_part, T, N, k, mode, gl, blocks, fin, st);
+                                    zl_part, T, N, k, mode, gl, blocks, fin, dq, st);
   MOE_SEL(8, 1, 1)
   MOE_SEL(16, 1, 1)
   MOE_SEL(32, 1, 2)

@@ -182,6 +182,14 @@ CASES = [
     ("bf16_split_k4096", 256, 4096, 2, 1, 256, 0, W.DTYPE_BF16, 0),
     ("bf16_split_down_k8192", 256, 256, 2, 1, 8192, 0, W.DTYPE_BF16, 1),
     ("bf16_split_shared_k4096", 128, 4096, 4, 1, 128, 4096, W.DTYPE_BF16, 2),
+    # one selection block and one dispatch chunk: selection and dispatch in
+    # one kernel; at most 64 rows per expert: the combine inside the
+    # weight-streaming down GEMM (bf16)
+    ("bf16_decode_T1", 1, 128, 8, 2, 128, 0, W.DTYPE_BF16, 0),
+    ("bf16_decode_T32_shared", 32, 256, 8, 2, 384, 128, W.DTYPE_BF16, 0),
+    ("bf16_decode_T16_N64_sigmoid", 16, 128, 64, 6, 128, 0, W.DTYPE_BF16, 2),
+    ("bf16_decode_T5_N512_k16_shared", 5, 64, 512, 16, 64, 64, W.DTYPE_BF16, 1),
+    ("f32_decode_T16_switch", 16, 32, 4, 1, 64, 0, W.DTYPE_F32, 1),
 ]
 
 
@@ -204,6 +212,7 @@ GROUPED_CASES = [
     ("f32_grouped_C_shared", 64, 32, 12, 3, 40, 24, W.DTYPE_F32, 2, (3, 2, 2)),
     ("bf16_grouped_N256_64groups", 150, 64, 256, 8, 64, 0, W.DTYPE_BF16, 0, (64, 8, 4)),
     ("bf16_grouped_N512_16groups", 100, 64, 512, 16, 64, 0, W.DTYPE_BF16, 2, (16, 3, 8)),
+    ("bf16_grouped_decode_T12", 12, 128, 32, 4, 128, 0, W.DTYPE_BF16, 2, (8, 2, 2)),
 ]
 
 
@@ -232,6 +241,8 @@ CAPACITY_CASES = [
     ("bf16_cap_split_k4096", 256, 4096, 2, 1, 256, 0, W.DTYPE_BF16, 0, None, 0.6),
     # C = T k: nothing dropped, usage 1/N
     ("bf16_cap_keeps_all", 257, 192, 12, 3, 128, 0, W.DTYPE_BF16, 0, None, 12.0),
+    # selection, dispatch with drops and the fused combine of a decode batch
+    ("bf16_cap_decode_T16_shared", 16, 128, 8, 2, 192, 64, W.DTYPE_BF16, 0, None, 0.5),
 ]
 
 
