@@ -9,8 +9,8 @@
 //   S_t = TopK(score_t, k) + gates   [wuhy-notes §二 第三步; cooking-agi first
 //                                     section; pwwt.cn §2.1 route()]
 //
-// A group of lanes per token (8 lanes when N <= 8, up to a whole wavefront
-// for N > 32; each lane holds up to eight experts in registers, N <= 512).
+// A group of lanes per token (8 lanes when N <= 8, up to a whole wavefront;
+// a lane holds one expert, or eight when N > 64, in registers; N <= 512).
 // Top-k is k rounds of a group-wide argmax (butterfly over __shfl_xor) on
 // (score, index) with the lower index winning ties. In the softmax modes the
 // selection runs on z, which orders the experts exactly as the softmax does.
@@ -472,11 +472,18 @@ __global__ __launch_bounds__(kThreads) void p_reduce_kernel(const float* __restr
 struct SelectCfg {
   int lpt, vpl, iter, tpb;
 };
+// Up to 64 experts: one expert per lane (8, 16, 32 or 64 lanes per token).
+// More: eight per lane (16, 32 or 64 lanes), so that a token's reductions
+// take fewer shuffle steps and a wave routes several tokens at once.
 SelectCfg select_cfg(int N) {
   SelectCfg c;
-  c.lpt = N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : 64;
-  c.vpl = (N + c.lpt - 1) / c.lpt;
-  if (c.vpl > 1) c.vpl = c.vpl <= 2 ? 2 : c.vpl <= 4 ? 4 : 8;
+  if (N <= 64) {
+    c.lpt = N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : 64;
+    c.vpl = 1;
+  } else {
+    c.lpt = N <= 128 ? 16 : N <= 256 ? 32 : 64;
+    c.vpl = 8;
+  }
   const int tpw = 64 / c.lpt;
   c.iter = (4 * tpw >= 16) ? 1 : 16 / (4 * tpw);
   c.tpb = 4 * tpw * c.iter;
@@ -572,8 +579,8 @@ hipError_t launch_route_select(const float* z_part, int splits, const float* b_r
   MOE_SEL(16, 1, 1)
   MOE_SEL(32, 1, 2)
   MOE_SEL(64, 1, 4)
-  MOE_SEL(64, 2, 4)
-  MOE_SEL(64, 4, 4)
+  MOE_SEL(16, 8, 1)
+  MOE_SEL(32, 8, 2)
   MOE_SEL(64, 8, 4)
 #undef MOE_SEL
   return hipErrorInvalidValue;

@@ -190,6 +190,11 @@ CASES = [
     ("bf16_decode_T16_N64_sigmoid", 16, 128, 64, 6, 128, 0, W.DTYPE_BF16, 2),
     ("bf16_decode_T5_N512_k16_shared", 5, 64, 512, 16, 64, 64, W.DTYPE_BF16, 1),
     ("f32_decode_T16_switch", 16, 32, 4, 1, 64, 0, W.DTYPE_F32, 1),
+    ("bf16_decode_T16_N128_k8", 16, 128, 128, 8, 64, 0, W.DTYPE_BF16, 0),
+    # more than 64 experts: eight experts per lane, 16 / 32 / 64 lanes a token
+    ("bf16_N100_k6_switch", 300, 128, 100, 6, 128, 0, W.DTYPE_BF16, 1),
+    ("bf16_N200_sigmoid_shared", 150, 64, 200, 8, 64, 64, W.DTYPE_BF16, 2),
+    ("f32_N128_k8", 40, 32, 128, 8, 32, 0, W.DTYPE_F32, 0),
 ]
 
 
