@@ -38,7 +38,10 @@ def host(t):
     t = t.detach().cpu()
     if t.dtype in (tt.int32, tt.int64):
         return t.numpy().astype(np.int64)
-    return t.float().numpy().astype(np.float64)
+    # buffers with rows a call does not write (dropped slots) may hold
+    # signalling-NaN bit patterns; their cast is not an error
+    with np.errstate(invalid="ignore"):
+        return t.float().numpy().astype(np.float64)
 
 
 def tdtype(dtype):
