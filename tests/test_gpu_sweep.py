@@ -6,7 +6,7 @@ modes, with and without a shared expert, a group limit and an expert
 capacity — so that the kernel
 variants meet combinations the hand-picked cases do not (selection layouts,
 single-block selection + dispatch, skinny and tiled GEMMs, split-K tails,
-the fused decode combine)."""
+the fused decode combine), and the backward pass on the first 40 of them."""
 import math
 
 import numpy as np
@@ -79,3 +79,26 @@ def test_sweep(case):
     if cap is None:
         assert dropped == 0
     print(f"{name}: worst row rel err {worst:.2e}, near-ties {near}, dropped {dropped}")
+
+
+# The backward pass on the first 40 shapes of the sweep, with the auxiliary
+# loss weights drawn too.
+BWD_CASES = CASES[:40]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_sweep_backward(case):
+    from test_gpu_backward import check_backward, run_backward
+    name, T, d, N, k, dff, dfs, dt, mode, groups, cf = case
+    inp = W.random_small(T, d, N, k, dff, dfs, dt, mode, seed=len(name) + T,
+                         router_bias=(T % 2 == 0))
+    s = shape_of(T, d, N, k, dff, dfs, dt, mode, groups=groups, cf=cf)
+    rng = np.random.default_rng(len(name) + 3)
+    d_laux, d_zloss = (float(x) for x in rng.choice([0.0, 0.3, 1.0], size=2))
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    if dt == W.DTYPE_BF16:
+        dy = W.round_to_bf16(dy)
+    print(f"case {name} d_laux {d_laux} d_zloss {d_zloss}", flush=True)
+    res = run_backward(s, inp, dy, d_laux, d_zloss)
+    worst = check_backward(s, inp, dy, res, d_laux, d_zloss)
+    print(f"{name}: " + ", ".join(f"{k_} {v:.1e}" for k_, v in worst.items()))
