@@ -480,6 +480,18 @@ struct BwdWs {
   size_t ta, tb, part, cnt, end;
   int64_t part_floats;
 };
+// Rows per expert at most (all routed rows of a token set, or the capacity).
+int bwd_rows_max(const moe_shape* s) {
+  const int C = expert_capacity(s);
+  return C ? std::min(s->T, C) : s->T;
+}
+// bf16 with more than 64 rows per expert (per shared-expert call: T): v and
+// the h-row gradients read the weights in their own [K, N] layout (no
+// transposed copies); fewer rows take the weight-streaming kernels, which
+// read K-contiguous (transposed) weights.
+bool bwd_nn(const moe_shape* s) { return s->dtype == MOE_BF16 && bwd_rows_max(s) > 64; }
+bool bwd_nn_shared(const moe_shape* s) { return s->dtype == MOE_BF16 && s->T > 64; }
+
 BwdWs bwd_ws(const moe_shape* s) {
   BwdWs w;
   const int64_t T = s->T, N = s->N, k = s->k, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
@@ -511,10 +523,11 @@ BwdWs bwd_ws(const moe_shape* s) {
   w.vs = take(4 * T * dfs);
   w.dgus = take(es * T * 2 * dfs);
   w.acts = take(es * T * dfs);
-  w.wdT = take(es * N * dff * d);
-  w.wguT = take(es * N * d * 2 * dff);
-  w.sdT = take(es * dfs * d);
-  w.sguT = take(es * d * 2 * dfs);
+  const bool nn = bwd_nn(s), nn_sh = bwd_nn_shared(s);
+  w.wdT = take(nn ? 0 : es * N * dff * d);
+  w.wguT = take(nn ? 0 : es * N * d * 2 * dff);
+  w.sdT = take(nn_sh ? 0 : es * dfs * d);
+  w.sguT = take(nn_sh ? 0 : es * d * 2 * dfs);
   w.wrT = take(es * d * w.Np);
   w.dhr = take(es * R * d);
   w.dhs = take(es * T * d);
@@ -567,7 +580,8 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   const int ncu = bf16 ? num_cu() : 0;
   const int C = expert_capacity(s);
   const int rows_all = C ? (int)std::min<int64_t>(R, (int64_t)N * C) : R;
-  const int rows_max = C ? std::min(T, C) : T;
+  const int rows_max = bwd_rows_max(s);
+  const bool nn = bwd_nn(s), nn_sh = bwd_nn_shared(s);
   const int Rp = (int)W.Rp, Tp = (int)W.Tp, Np = (int)W.Np;
   float* part = W.part_floats ? at<float>(ws, W.part) : nullptr;
   int32_t* cnt = W.part_floats ? at<int32_t>(ws, W.cnt) : nullptr;
@@ -607,6 +621,13 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
       e = kind == 0 ? moe::launch_gateup_preact_f32(p, st) : moe::launch_down_f32(p, st);
     return hip_check(e, what);
   };
+  // B in its own [K, N] layout (bf16, more than 64 rows per group)
+  auto grouped_nn = [&](const moe::GroupedProblem& p, bool f32out,
+                        const char* what) -> moe_status {
+    return hip_check(f32out ? moe::launch_down_nn_f32out_bf16(p, ncu, st)
+                            : moe::launch_down_nn_bf16(p, ncu, st),
+                     what);
+  };
   auto kgroup = [&](const void* A, int lda, int64_t a_rows, const void* B, int ldb,
                     int64_t b_rows, const int32_t* ko, int G, int M, int Ncols, void* Cout,
                     int64_t gstride, int ldc, bool f32out, const char* what) -> moe_status {
@@ -643,14 +664,28 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
                                       cnt, W.part_floats},
                   0, "shared gate/up recompute"));
   }
-  // 3. v = W_down^T dy per kept row: W_down transposed to [d_ff, d] per expert
-  TRY(pack(w_down, dff, dff, nullptr, 1, nullptr, nullptr, nullptr, 0, d, d, wdT, d, N,
-           (int64_t)d * dff, (int64_t)dff * d, "W_down transpose"));
-  TRY(grouped(moe::GroupedProblem{dy, d, perm, k, offsets, N, rows_all, rows_max, wdT, nullptr,
-                                  (int64_t)dff * d, d, dff, d, v, dff, 0, (uint32_t)(es * T * d),
-                                  part, cnt, W.part_floats},
-              1, "v GEMM"));
-  if (dfs) {
+  // 3. v = W_down^T dy per kept row: W_down as it is ([d, d_ff] per expert,
+  //    K = d), or transposed to [d_ff, d] for the weight-streaming kernels
+  if (nn) {
+    TRY(grouped_nn(moe::GroupedProblem{dy, d, perm, k, offsets, N, rows_all, rows_max, w_down,
+                                       nullptr, (int64_t)d * dff, dff, dff, d, v, dff, 0,
+                                       (uint32_t)(es * T * d), part, cnt, W.part_floats, nullptr,
+                                       0, 0},
+                   true, "v GEMM"));
+  } else {
+    TRY(pack(w_down, dff, dff, nullptr, 1, nullptr, nullptr, nullptr, 0, d, d, wdT, d, N,
+             (int64_t)d * dff, (int64_t)dff * d, "W_down transpose"));
+    TRY(grouped(moe::GroupedProblem{dy, d, perm, k, offsets, N, rows_all, rows_max, wdT, nullptr,
+                                    (int64_t)dff * d, d, dff, d, v, dff, 0,
+                                    (uint32_t)(es * T * d), part, cnt, W.part_floats},
+                1, "v GEMM"));
+  }
+  if (dfs && nn_sh) {
+    TRY(grouped_nn(moe::GroupedProblem{dy, d, nullptr, 1, nullptr, 1, T, T, sh_down, nullptr, 0,
+                                       dfs, dfs, d, vs, dfs, 0, (uint32_t)(es * T * d), part, cnt,
+                                       W.part_floats, nullptr, 0, 0},
+                   true, "shared v GEMM"));
+  } else if (dfs) {
     TRY(pack(sh_down, dfs, dfs, nullptr, 1, nullptr, nullptr, nullptr, 0, d, d, sdT, d, 1, 0, 0,
              "shared W_down transpose"));
     TRY(grouped(moe::GroupedProblem{dy, d, nullptr, 1, nullptr, 1, T, T, sdT, nullptr, 0, d, dfs,
@@ -671,17 +706,32 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   if (db_router)
     TRY(hip_check(moe::launch_colsum(dz, T, N, at<float>(ws, W.colpart), db_router, st),
                   "b_r gradient"));
-  // 6. row gradients of h: [W_gate; W_up]^T [dgp | du] per kept row, the
-  //    shared expert's, and the router's dz W_r
-  TRY(pack(w_gate, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dff, dff, wguT, 2 * dff, N,
-           (int64_t)dff * d, (int64_t)d * 2 * dff, "W_gate transpose"));
-  TRY(pack(w_up, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dff, dff, wguT + es * dff,
-           2 * dff, N, (int64_t)dff * d, (int64_t)d * 2 * dff, "W_up transpose"));
-  TRY(grouped(moe::GroupedProblem{dgu, 2 * dff, nullptr, 1, offsets, N, rows_all, rows_max, wguT,
-                                  nullptr, (int64_t)d * 2 * dff, 2 * dff, d, 2 * dff, dhr, d, 0,
-                                  (uint32_t)(es * R * 2 * dff), part, cnt, W.part_floats},
-              2, "dh rows GEMM"));
-  if (dfs) {
+  // 6. row gradients of h: [W_gate; W_up]^T [dgp | du] per kept row (K =
+  //    2 d_ff: W_gate's rows, then W_up's), the shared expert's, and the
+  //    router's dz W_r
+  if (nn) {
+    TRY(grouped_nn(moe::GroupedProblem{dgu, 2 * dff, nullptr, 1, offsets, N, rows_all, rows_max,
+                                       w_gate, w_up, (int64_t)dff * d, d, d, 2 * dff, dhr, d, 0,
+                                       (uint32_t)(es * R * 2 * dff), part, cnt, W.part_floats,
+                                       nullptr, 0, dff},
+                   false, "dh rows GEMM"));
+  } else {
+    TRY(pack(w_gate, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dff, dff, wguT, 2 * dff, N,
+             (int64_t)dff * d, (int64_t)d * 2 * dff, "W_gate transpose"));
+    TRY(pack(w_up, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dff, dff, wguT + es * dff,
+             2 * dff, N, (int64_t)dff * d, (int64_t)d * 2 * dff, "W_up transpose"));
+    TRY(grouped(moe::GroupedProblem{dgu, 2 * dff, nullptr, 1, offsets, N, rows_all, rows_max,
+                                    wguT, nullptr, (int64_t)d * 2 * dff, 2 * dff, d, 2 * dff, dhr,
+                                    d, 0, (uint32_t)(es * R * 2 * dff), part, cnt,
+                                    W.part_floats},
+                2, "dh rows GEMM"));
+  }
+  if (dfs && nn_sh) {
+    TRY(grouped_nn(moe::GroupedProblem{dgus, 2 * dfs, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up,
+                                       0, d, d, 2 * dfs, dhs, d, 0, (uint32_t)(es * T * 2 * dfs),
+                                       part, cnt, W.part_floats, nullptr, 0, dfs},
+                   false, "shared dh GEMM"));
+  } else if (dfs) {
     TRY(pack(sh_gate, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dfs, dfs, sguT, 2 * dfs, 1,
              0, 0, "shared W_gate transpose"));
     TRY(pack(sh_up, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, dfs, dfs, sguT + es * dfs,
@@ -735,11 +785,7 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   }
   TRY(pack(dzb, Np, N, nullptr, 1, nullptr, nullptr, nullptr, 0, T, Tp, ta, Tp, 1, 0, 0,
            "dz transpose"));
-  if (bf16) {
-    TRY(kgroup(ta, Tp, N, tb, Tp, d, kofs_t, 1, N, d, dw_router, 0, d, true, "W_r gradient"));
-  } else {
-    TRY(kgroup(ta, Tp, N, tb, Tp, d, kofs_t, 1, N, d, dw_router, 0, d, true, "W_r gradient"));
-  }
+  TRY(kgroup(ta, Tp, N, tb, Tp, d, kofs_t, 1, N, d, dw_router, 0, d, true, "W_r gradient"));
   return MOE_OK;
 }
 

@@ -36,7 +36,10 @@ constexpr int kXcds = 8;   // MI355X: 8 XCDs; block b runs on XCD b % 8
 // (two blocks: two waves per SIMD, each hides the other's waits).
 // (64-deep slabs, whose loads cover whole cache lines, were measured too:
 // they halve the L1-to-L2 requests but did not make the kernel faster.)
-template <int BM_, int BN_, bool DUAL_, int STAGES_, int OCC_>
+// NN: B is given as [K rows][N columns] (N contiguous, the weights' own
+// layout in the backward pass) and staged as BK rows of BN columns; its
+// MFMA fragments are read with the LDS transpose read (one B, no DUAL).
+template <int BM_, int BN_, bool DUAL_, int STAGES_, int OCC_, bool NN_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 32;
   static constexpr bool DUAL = DUAL_;
@@ -58,7 +61,20 @@ struct TileCfg {
   static_assert(FM >= 1 && FN >= 1, "tile too small");
   static_assert(BM % (4 * RPI) == 0 && BROWS % (4 * RPI) == 0, "tile rows vs load blocks");
   static_assert(STAGES == 3 || STAGES == 4, "pipeline shape");
+  static constexpr bool NN = NN_;
+  static constexpr int BROWB = BN * 2;              // NN: bytes of one staged B row (one k)
+  static_assert(!NN || (!DUAL && BK * BROWB == BROWS * ROWB && BROWB % 256 == 0),
+                "NN: one B, the same stage size, whole 16-chunk groups per row");
 };
+
+// NN: chunk swizzle of staged B row r. A transpose read takes, in each group
+// of 16 lanes, 8 bytes from each of four consecutive rows at the same two
+// logical chunks; XOR-ing the chunk index with 4 (r & 3) puts the four
+// rows' chunk pairs on distinct banks.
+__device__ __forceinline__ int nn_swz(int r) { return 4 * (r & 3); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_t;
 
 // Chunk swizzle of staged row r: logical 16-byte chunk c lives at c ^ swz(r).
 // ds_read_b128 serves 16 consecutive lanes per pass from 64 four-byte banks.
@@ -79,10 +95,14 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // chunk (l % CH) ^ swz(row).
 // PART selects the loads: all of them (-1), or the first (0) or second (1)
 // half of the wave's list (A blocks, then B blocks).
+// NN: B0 is this slab's B source and kbytes_b the byte offset of its first
+// row (A still advances by kbytes).
 template <class C, int PART = -1>
 __device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const uint32_t* aoff,
-                                         Rsrc B0, Rsrc B1, const uint32_t* boff, int kbytes) {
+                                         Rsrc B0, Rsrc B1, const uint32_t* boff, int kbytes,
+                                         int kbytes_b) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS address in SALU
+  const int kb = C::NN ? kbytes_b : kbytes;                          // B's offset along K
 #pragma unroll
   for (int q = 0; q < C::NLW; ++q) {
     if (PART >= 0 && (q < C::NLW / 2) != (PART == 0)) continue;
@@ -94,7 +114,7 @@ __device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const ui
       const bool up = C::DUAL && 4 * j * C::RPI >= C::BN;   // B block w + 4j holds up rows
       __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? B1 : B0,
                                                (lds_ptr_t)(st + C::A_BYTES + (w + 4 * j) * 1024),
-                                               16, boff[j], kbytes, 0, 0);
+                                               16, boff[j], kb, 0, 0);
     }
   }
 }
@@ -120,6 +140,28 @@ __device__ __forceinline__ void read_frags(const char* __restrict__ st, int ks, 
 #pragma unroll
   for (int fm = 0; fm < V; ++fm)
     f.a[fm] = *reinterpret_cast<const u32x4*>(a + fm * 32 * C::ROWB);
+  if constexpr (C::NN) {
+    // lane j of 16-lane group q gets the four k values of column j from the
+    // 8-byte reads of the group's lanes 4c + j/4 (row c, columns 4 (j % 4)..);
+    // groups 0/1 and 2/3 take columns 0-15 / 16-31 of the block, and the two
+    // k halves; two reads give the eight k values of the fragment
+    const int i = lane & 15, g16 = (lane >> 4) & 1;
+    const char* bb = st + C::A_BYTES;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int n = wn * C::TN + fn * 32 + 16 * g16 + 4 * (i & 3);
+      v4i16 hv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * ks + 8 * lh + 4 * h + (i >> 2);
+        const char* q = bb + row * C::BROWB + (((n >> 3) ^ nn_swz(row)) << 4) + ((n & 7) << 1);
+        hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)q);
+      }
+      const u32x2 lo = __builtin_bit_cast(u32x2, hv[0]), hi = __builtin_bit_cast(u32x2, hv[1]);
+      f.b[0][fn] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -191,20 +233,19 @@ __device__ __forceinline__ void weave() {
 //     queueing several loads behind the other waves' between two MFMAs.
 template <class C, int V>
 __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict__ nxt,
-                                       char* __restrict__ dst, int kload_bytes,
-                                       Frags<C>& f0, Frags<C>& f1, Rsrc A,
-                                       const uint32_t* aoff, Rsrc B0, Rsrc B1,
-                                       const uint32_t* boff,
+                                       char* __restrict__ dst, int kload_bytes, int kload_b,
+                                       Rsrc B0, Frags<C>& f0, Frags<C>& f1, Rsrc A,
+                                       const uint32_t* aoff, Rsrc B1, const uint32_t* boff,
                                        f32x16 (&acc)[C::NB][C::FM][C::FN]) {
   read_frags<C, V>(cur, 1, f1);
   mma<C, V>(f0, acc);
-  dma_slab<C, 0>(dst, A, aoff, B0, B1, boff, kload_bytes);
+  dma_slab<C, 0>(dst, A, aoff, B0, B1, boff, kload_bytes, kload_b);
   weave<C, V, C::NLW / 2, true, true>();
   wait_vmcnt_lds<(C::STAGES - 2) * C::NLW - C::NLW / 2>();
   __builtin_amdgcn_s_barrier();
   read_frags<C, V>(nxt, 0, f0);
   mma<C, V>(f1, acc);
-  dma_slab<C, 1>(dst, A, aoff, B0, B1, boff, kload_bytes);
+  dma_slab<C, 1>(dst, A, aoff, B0, B1, boff, kload_bytes, kload_b);
   weave<C, V, C::NLW - C::NLW / 2, true, true>();
 }
 
@@ -213,48 +254,64 @@ __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict_
 // ring of LDS stages; the loop is unrolled by STAGES so that every stage is
 // a distinct LDS object. Loads past the last slab re-load the last slab, so
 // every step issues the same number of loads and the vmcnt accounting holds.
+// NN: B rows (K) are ldb_bytes apart; rows at and past nn_k1 (when > 0) come
+// from B1 at row - nn_k1, the others from B0.
 template <class C, int V = C::FM>
 __device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict__ S1,
                                          char* __restrict__ S2, char* __restrict__ S3,
                                          Rsrc A, const uint32_t* aoff, Rsrc B0, Rsrc B1,
                                          const uint32_t* boff, int k_begin, int k_len,
-                                         f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+                                         f32x16 (&acc)[C::NB][C::FM][C::FN],
+                                         int ldb_bytes = 0, int nn_k1 = 0) {
   constexpr int STEP = C::BK * 2;
   const int KT = k_len / C::BK;
   const int kb = k_begin * 2;
   auto kbyte = [&](int k) { return kb + min(k, KT - 1) * STEP; };
+  // this slab's B source and the byte offset of its first B row
+  auto brow = [&](int k) { return k_begin + min(k, KT - 1) * C::BK; };
+  auto bsrc = [&](int k) {
+    if constexpr (C::NN) return (nn_k1 > 0 && brow(k) >= nn_k1) ? B1 : B0;
+    return B0;
+  };
+  auto kbyte_b = [&](int k) {
+    if constexpr (C::NN) {
+      const int r = brow(k);
+      return (nn_k1 > 0 && r >= nn_k1 ? r - nn_k1 : r) * ldb_bytes;
+    }
+    return kbyte(k);
+  };
   Frags<C> f0, f1;
   if constexpr (C::STAGES == 4) {
-    dma_slab<C>(S0, A, aoff, B0, B1, boff, kbyte(0));
-    dma_slab<C>(S1, A, aoff, B0, B1, boff, kbyte(1));
-    dma_slab<C>(S2, A, aoff, B0, B1, boff, kbyte(2));
+    dma_slab<C>(S0, A, aoff, bsrc(0), B1, boff, kbyte(0), kbyte_b(0));
+    dma_slab<C>(S1, A, aoff, bsrc(1), B1, boff, kbyte(1), kbyte_b(1));
+    dma_slab<C>(S2, A, aoff, bsrc(2), B1, boff, kbyte(2), kbyte_b(2));
     wait_vmcnt<2 * C::NLW>();
     __builtin_amdgcn_s_barrier();
     read_frags<C, V>(S0, 0, f0);
     int k = 0;
     for (; k + 4 <= KT; k += 4) {
-      k_step<C, V>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C, V>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C, V>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C, V>(S3, S0, S2, kbyte(k + 6), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S0, S1, S3, kbyte(k + 3), kbyte_b(k + 3), bsrc(k + 3), f0, f1, A, aoff, B1, boff, acc);
+      k_step<C, V>(S1, S2, S0, kbyte(k + 4), kbyte_b(k + 4), bsrc(k + 4), f0, f1, A, aoff, B1, boff, acc);
+      k_step<C, V>(S2, S3, S1, kbyte(k + 5), kbyte_b(k + 5), bsrc(k + 5), f0, f1, A, aoff, B1, boff, acc);
+      k_step<C, V>(S3, S0, S2, kbyte(k + 6), kbyte_b(k + 6), bsrc(k + 6), f0, f1, A, aoff, B1, boff, acc);
     }
-    if (k < KT) k_step<C, V>(S0, S1, S3, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
-    if (k + 1 < KT) k_step<C, V>(S1, S2, S0, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
-    if (k + 2 < KT) k_step<C, V>(S2, S3, S1, kbyte(k + 5), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k < KT) k_step<C, V>(S0, S1, S3, kbyte(k + 3), kbyte_b(k + 3), bsrc(k + 3), f0, f1, A, aoff, B1, boff, acc);
+    if (k + 1 < KT) k_step<C, V>(S1, S2, S0, kbyte(k + 4), kbyte_b(k + 4), bsrc(k + 4), f0, f1, A, aoff, B1, boff, acc);
+    if (k + 2 < KT) k_step<C, V>(S2, S3, S1, kbyte(k + 5), kbyte_b(k + 5), bsrc(k + 5), f0, f1, A, aoff, B1, boff, acc);
   } else {
-    dma_slab<C>(S0, A, aoff, B0, B1, boff, kbyte(0));
-    dma_slab<C>(S1, A, aoff, B0, B1, boff, kbyte(1));
+    dma_slab<C>(S0, A, aoff, bsrc(0), B1, boff, kbyte(0), kbyte_b(0));
+    dma_slab<C>(S1, A, aoff, bsrc(1), B1, boff, kbyte(1), kbyte_b(1));
     wait_vmcnt<C::NLW>();
     __builtin_amdgcn_s_barrier();
     read_frags<C, V>(S0, 0, f0);
     int k = 0;
     for (; k + 3 <= KT; k += 3) {
-      k_step<C, V>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C, V>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
-      k_step<C, V>(S2, S0, S1, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+      k_step<C, V>(S0, S1, S2, kbyte(k + 2), kbyte_b(k + 2), bsrc(k + 2), f0, f1, A, aoff, B1, boff, acc);
+      k_step<C, V>(S1, S2, S0, kbyte(k + 3), kbyte_b(k + 3), bsrc(k + 3), f0, f1, A, aoff, B1, boff, acc);
+      k_step<C, V>(S2, S0, S1, kbyte(k + 4), kbyte_b(k + 4), bsrc(k + 4), f0, f1, A, aoff, B1, boff, acc);
     }
-    if (k < KT) k_step<C, V>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
-    if (k + 1 < KT) k_step<C, V>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+    if (k < KT) k_step<C, V>(S0, S1, S2, kbyte(k + 2), kbyte_b(k + 2), bsrc(k + 2), f0, f1, A, aoff, B1, boff, acc);
+    if (k + 1 < KT) k_step<C, V>(S1, S2, S0, kbyte(k + 3), kbyte_b(k + 3), bsrc(k + 3), f0, f1, A, aoff, B1, boff, acc);
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -340,6 +397,28 @@ __device__ __forceinline__ void epilogue_bf16(const f32x16 (&acc)[C::NB][C::FM][
   for (int fm = 0; fm < C::FM; ++fm) {
     const int rb = wm * C::TM + fm * 32;
     if (rb >= rows_valid) break;             // the rest of this wave's rows are padding
+    if constexpr (C::NN) {
+      // NN tiles keep plain columns (MFMA block fn, lane column lr -> fn·32 +
+      // lr): one store per element
+      static_assert(EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32, "NN: plain stores only");
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int col = n0 + wn * C::TN + fn * 32 + lr;
+        const uint32_t voff = col < Ncols ? lane_row + (uint32_t)col * ES : 0xC0000000u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rrow = rb + 8 * (i >> 2) + (i & 3);   // + 4*lh (in voff)
+          if constexpr (F32)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0][fm][fn][i]), out, voff,
+                                                  rrow * ldc2, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16(
+                (unsigned short)(pack_bf16x2_hw(acc[0][fm][fn][i], 0.0f) & 0xffffu), out, voff,
+                rrow * ldc2, 0);
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int fe = 0; fe < C::FN; fe += 2) {
       const int col = n0 + wn * C::TN + strip_col(fe, lr);
@@ -430,6 +509,19 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (
       aoff[j] = (uint32_t)(src * lda * 2 + ((ch ^ swz<C>(row)) << 4));
     }
   }
+  if constexpr (C::NN) {
+    // B block w + 4j covers bytes [1 KiB (w + 4j), +1 KiB) of the B part:
+    // staged row (k) r, physical chunk c holds columns n0 + 8 (c ^ nn_swz(r));
+    // columns past Ncols read zeros
+#pragma unroll
+    for (int j = 0; j < C::NBW; ++j) {
+      const int byte = 1024 * (w + 4 * j) + 16 * lane;
+      const int r = byte / C::BROWB, c = (byte % C::BROWB) / 16;
+      const int col = n0 + 8 * (c ^ nn_swz(r));
+      boff[j] = col < Ncols ? (uint32_t)(r * ldb * 2 + col * 2) : 0x80000000u;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < C::NBW; ++j) {
     const int row = C::RPI * (w + 4 * j) + rl;  // B row within the stage's B part
@@ -481,13 +573,15 @@ template <class C, int W>
 __device__ __forceinline__ void mainloop_rows(int v, char* S0, char* S1, char* S2, char* S3,
                                               Rsrc A, const uint32_t* aoff, Rsrc B0, Rsrc B1,
                                               const uint32_t* boff, int k_begin, int k_len,
-                                              f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+                                              f32x16 (&acc)[C::NB][C::FM][C::FN],
+                                              int ldb_bytes = 0, int nn_k1 = 0) {
   if (v == W || W == 0) {
-    mainloop<C, W>(S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+    mainloop<C, W>(S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc, ldb_bytes, nn_k1);
     return;
   }
   if constexpr (W > 0)
-    mainloop_rows<C, W - 1>(v, S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+    mainloop_rows<C, W - 1>(v, S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc,
+                            ldb_bytes, nn_k1);
 }
 
 // acc = A[tile rows] · B[tile columns]^T over k in [k_begin, k_begin + k_len).
@@ -498,15 +592,28 @@ __device__ __forceinline__ void tile_mainloop(const GroupedProblem& p, const Til
                                               f32x16 (&acc)[C::NB][C::FM][C::FN]) {
   uint32_t aoff[C::NAW], boff[C::NBW];
   dma_offsets<C>(aoff, boff, p.perm, p.kdiv, p.lda, ti.m0, ti.m_end, p.ldb, ti.n0, p.Ncols);
-  const uint32_t bbytes = (uint32_t)((int64_t)p.Ncols * p.ldb * 2);
-  const Rsrc rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)ti.g * p.b_gstride, bbytes);
-  const Rsrc rB1 = C::DUAL ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)ti.g * p.b_gstride, bbytes) : rB0;
+  Rsrc rB0, rB1;
+  if constexpr (C::NN) {
+    // B0 holds K rows [0, k1) (all K when k1 = 0), B1 rows [k1, K)
+    const int k1 = p.b_k1 > 0 ? p.b_k1 : p.K;
+    const int64_t rowb = (int64_t)p.ldb * 2;
+    rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)ti.g * p.b_gstride,
+                    (uint32_t)(k1 * rowb));
+    rB1 = p.b_k1 > 0 ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)ti.g * p.b_gstride,
+                                 (uint32_t)((p.K - k1) * rowb))
+                     : rB0;
+  } else {
+    const uint32_t bbytes = (uint32_t)((int64_t)p.Ncols * p.ldb * 2);
+    rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)ti.g * p.b_gstride, bbytes);
+    rB1 = C::DUAL ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)ti.g * p.b_gstride, bbytes) : rB0;
+  }
   zero_acc<C>(acc);
   // row blocks of this wave that hold rows of the group: the MFMAs of the
   // others would only multiply padding (zeros), so they are not issued
   const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / C::WN;
   const int v = min(max((ti.m_end - ti.m0 - wm * C::TM + 31) / 32, 0), C::FM);
-  mainloop_rows<C, C::FM>(v, S0, S1, S2, S3, rA, aoff, rB0, rB1, boff, k_begin, k_len, acc);
+  mainloop_rows<C, C::FM>(v, S0, S1, S2, S3, rA, aoff, rB0, rB1, boff, k_begin, k_len, acc,
+                          p.ldb * 2, p.b_k1);
 }
 
 // A tile's fp32 partial sums in the split-K workspace, element-major
@@ -1095,6 +1202,8 @@ using GateUp128 = TileCfg<128, 128, true, 3, 2>;    // 128 rows, 2 blocks per CU
 using Down128 = TileCfg<128, 256, false, 3, 2>;
 using Down256 = TileCfg<256, 256, false, 4, 1>;
 using Router = TileCfg<128, 128, false, 4, 1>;
+using Down128NN = TileCfg<128, 256, false, 3, 2, true>;
+using Down256NN = TileCfg<256, 256, false, 4, 1, true>;
 
 // Rows per expert at most 64: weight streaming. Otherwise 256-row tiles (one
 // block per CU) when experts average at least 1024 rows or the 256-row tile
@@ -1143,6 +1252,29 @@ hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu, hipStream_t st)
   if (tall_tiles(p, Down256::BN, num_cu))
     return launch_grouped<Down256, EPI_STORE_BF16>(p, num_cu, st);
   return launch_grouped<Down128, EPI_STORE_BF16>(p, num_cu, st);
+}
+
+// NN (B as [K rows][N columns]): the grouped tiles at more than 64 rows per
+// group; at most 64 the weight-streaming kernels need K-contiguous weights
+bool down_nn_ok(const GroupedProblem& p) {
+  const int k1 = p.b_k1 > 0 ? p.b_k1 : p.K;
+  return p.max_rows > 64 && p.Ncols % 8 == 0 && p.ldb % 8 == 0 && p.K % 32 == 0 &&
+         k1 % 32 == 0 && (int64_t)(k1 > p.K - k1 ? k1 : p.K - k1) * p.ldb * 2 <= 0x7fffffffLL;
+}
+
+template <int EPI>
+static hipError_t launch_down_nn(const GroupedProblem& p, int num_cu, hipStream_t st) {
+  if (!down_nn_ok(p)) return hipErrorNotSupported;
+  if (tall_tiles(p, Down256NN::BN, num_cu)) return launch_grouped<Down256NN, EPI>(p, num_cu, st);
+  return launch_grouped<Down128NN, EPI>(p, num_cu, st);
+}
+
+hipError_t launch_down_nn_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
+  return launch_down_nn<EPI_STORE_BF16>(p, num_cu, st);
+}
+
+hipError_t launch_down_nn_f32out_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
+  return launch_down_nn<EPI_STORE_F32>(p, num_cu, st);
 }
 
 // Gate and up pre-activations of the routed rows as fp32, side by side in C

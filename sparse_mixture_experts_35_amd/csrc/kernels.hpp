@@ -116,6 +116,9 @@ struct GroupedProblem {
   // [0, Ncols), up in [Ncols, 2 Ncols) (kept for the backward pass)
   float* C2;
   int64_t ldc2;
+  // B given as [K rows][ldb] (N contiguous; the down-type NN launchers
+  // only): rows [0, b_k1) at B0, rows [b_k1, K) at B1 (b_k1 = 0: all at B0)
+  int b_k1;
 };
 
 constexpr int kSplitCounters = 1024;
@@ -157,6 +160,12 @@ hipError_t launch_gateup_preact_bf16(const GroupedProblem& p, int num_cu,
 // C = A·B0^T (bf16 in, fp32 out)
 hipError_t launch_down_f32out_bf16(const GroupedProblem& p, int num_cu,
                                    hipStream_t st);
+// C = A·B with B given as [K rows][ldb] (the weights' own layout; rows past
+// b_k1 from B1), bf16 or fp32 out; hipErrorNotSupported unless down_nn_ok
+// (more than 64 rows per group, sizes multiples of 8 / 32)
+bool down_nn_ok(const GroupedProblem& p);
+hipError_t launch_down_nn_bf16(const GroupedProblem& p, int num_cu, hipStream_t st);
+hipError_t launch_down_nn_f32out_bf16(const GroupedProblem& p, int num_cu, hipStream_t st);
 // C_g = A[:, kofs[g]:kofs[g+1]] · B[:, kofs[g]:kofs[g+1]]^T for g < groups
 // (A [a_rows, lda] and B [b_rows, ldb] bf16, K ranges multiples of 32);
 // C_g [M, Ncols] at C + g * c_gstride elements, bf16 or fp32 (f32out)
