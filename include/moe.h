@@ -313,11 +313,13 @@ moe_status moe_layer_forward_train(const moe_shape* s, const void* h,
 
 /* Host, pure: workspace bytes for moe_layer_backward with this shape (0 for
  * an invalid shape). It holds the recomputed router logits and gate/up
- * pre-activations, transposed copies of the expert, shared-expert and
- * router weights, the intermediate row gradients, zero-padded transposed
- * activations for the weight gradients and the GEMMs' split-K partials: of
- * the order of 3x the expert weights plus 10 (T·k + 32·N) max(d, 2 d_ff)
- * elements. No initialisation needed; one call at a time per workspace. */
+ * pre-activations, the intermediate row gradients, zero-padded transposed
+ * activations for the weight gradients, the GEMMs' split-K partials, a
+ * transposed copy of the router weights and, only where an expert (or the
+ * shared expert) has at most 64 rows or the dtype is fp32, transposed
+ * copies of its weights: of the order of 10 (T·k + 32·N) max(d, 2 d_ff)
+ * elements (plus 3x the expert weights in those cases). No initialisation
+ * needed; one call at a time per workspace. */
 size_t moe_backward_workspace_bytes(const moe_shape* s);
 
 /* Backward pass of the layer for the selection and dispatch of a forward
