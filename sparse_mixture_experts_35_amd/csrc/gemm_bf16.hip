@@ -206,7 +206,9 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 template <class C, int V, int LOADS, bool READS, bool SPREAD = false>
 __device__ __forceinline__ void weave() {
   constexpr int NMF = C::NB * V * C::FN;          // MFMAs per k-step
-  constexpr int NRD = READS && V > 0 ? V + C::NB * C::FN : 0;
+  // LDS reads of a k-step: one per A fragment, one per B fragment (two with
+  // the NN transpose reads)
+  constexpr int NRD = READS && V > 0 ? V + C::NB * C::FN * (C::NN ? 2 : 1) : 0;
   if constexpr (NMF == 0) return;
   constexpr int FIRST = (!SPREAD && LOADS > 0 && NRD < NMF) ? NRD : 0;   // first slot with loads
 #pragma unroll
