@@ -1,7 +1,8 @@
-"""The fused layer captured in a HIP graph: the library allocates nothing,
-records no memset (counters are cleared by a kernel) and synchronises
-nothing, so a caller can capture it. Each replay, with eager library work in
-between, must give the eager call's bits (the kernels are deterministic)."""
+"""The fused layer, and a whole training step (training forward + backward),
+captured in a HIP graph: the library allocates nothing, records no memset
+(counters are cleared by a kernel) and synchronises nothing, so a caller can
+capture it. Each replay, with eager library work in between, must give the
+eager call's bits (the kernels are deterministic)."""
 import numpy as np
 import pytest
 
@@ -78,3 +79,72 @@ def test_fused_layer_in_a_graph(case):
         call(y_other, h2, ws2)
         t.cuda.synchronize()
         assert not t.equal(y_other, y_eager)
+
+
+TRAIN_CASES = [
+    # name, T, d, N, k, d_ff, d_ff_shared, mode
+    ("bf16_train_prefill_shared", 300, 128, 8, 2, 192, 128, 2),
+    ("bf16_train_skinny", 40, 128, 16, 4, 192, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", TRAIN_CASES, ids=[c[0] for c in TRAIN_CASES])
+def test_training_step_in_a_graph(case):
+    """moe_layer_forward_train (keeping the pre-activations) followed by
+    moe_layer_backward, captured as one graph: each replay gives the eager
+    step's outputs and gradients bit for bit."""
+    t = torch()
+    name, T, d, N, k, dff, dfs, mode = case
+    dt = W.DTYPE_BF16
+    inp = W.random_small(T, d, N, k, dff, dfs, dt, mode, seed=len(name), router_bias=True)
+    s = M.Shape(T, d, N, k, dff, dfs, dt, mode, 0.01)
+    h, wr = dev(inp["h"], dt), dev(inp["w_router"], dt)
+    br, bs = dev_f32(inp["b_router"]), dev_f32(inp["b_select"])
+    wg, wu, wd = dev(inp["w_gate"], dt), dev(inp["w_up"], dt), dev(inp["w_down"], dt)
+    sg, su, sd = dev(inp["sh_gate"], dt), dev(inp["sh_up"], dt), dev(inp["sh_down"], dt)
+    dy = dev(W.round_to_bf16(np.random.default_rng(7).standard_normal((T, d)).astype(np.float32)),
+             dt)
+    E = lambda shp, ty=t.bfloat16: t.empty(shp, dtype=ty, device="cuda")
+    R = T * k
+    nws, nb = M.workspace_bytes(s), M.backward_workspace_bytes(s)
+    ws, bws = E(nws, t.uint8), E(nb, t.uint8)
+    pre = E(M.preact_floats(s), t.float32)
+    y = E((T, d))
+    ids, gates, counts = E(R, t.int32), E(R, t.float32), E(N, t.int32)
+    offs, perm, row_of = E(N + 1, t.int32), E(R, t.int32), E(R, t.int32)
+    g = dict(dh=E((T, d)), dwr=E((N, d), t.float32), dbr=E(N, t.float32), dwg=E((N, dff, d)),
+             dwu=E((N, dff, d)), dwd=E((N, d, dff)), dgates=E(R, t.float32))
+    if dfs:
+        g.update(dsg=E((dfs, d)), dsu=E((dfs, d)), dsd=E((d, dfs)))
+
+    def step():
+        M.layer_forward_train(s, h, wr, br, bs, wg, wu, wd, sg, su, sd, y, ids, gates, counts,
+                              offs, perm, row_of, preact=pre, ws=ws, ws_bytes=nws)
+        M.layer_backward(s, h, wr, br, wg, wu, wd, sg, su, sd, ids, gates, counts, offs, perm,
+                         row_of, dy, g["dh"], g["dwr"], g["dbr"], g["dwg"], g["dwu"], g["dwd"],
+                         g.get("dsg"), g.get("dsu"), g.get("dsd"), g["dgates"], 0.5, 0.1, bws, nb,
+                         preact=pre)
+
+    step()
+    t.cuda.synchronize()
+    want = {key: v.clone() for key, v in g.items()}
+    want["y"] = y.clone()
+    print(f"case {name}", flush=True)
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        step()                          # warm-up on the capture stream
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    graph = t.cuda.CUDAGraph()
+    with t.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for v in list(g.values()) + [y]:
+            v.zero_()
+        graph.replay()
+        t.cuda.synchronize()
+        for key, v in list(g.items()) + [("y", y)]:
+            assert t.equal(v, want[key]), f"replay {rep}: {key} differs from the eager step"
+        step()                          # eager work between replays
+        t.cuda.synchronize()
