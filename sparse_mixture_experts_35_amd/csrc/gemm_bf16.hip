@@ -283,6 +283,8 @@ __device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict
     return kbyte(k);
   };
   Frags<C> f0, f1;
+  // (the k_step calls are spelled out: wrapping them in a lambda changed the
+  // register allocation and doubled the NN tiles' time)
   if constexpr (C::STAGES == 4) {
     dma_slab<C>(S0, A, aoff, bsrc(0), B1, boff, kbyte(0), kbyte_b(0));
     dma_slab<C>(S1, A, aoff, bsrc(1), B1, boff, kbyte(1), kbyte_b(1));
