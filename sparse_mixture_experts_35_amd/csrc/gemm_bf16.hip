@@ -536,18 +536,24 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (
 }
 
 // Tile t of the tile list -> expert g, rows [m0, m_end), first column n0.
-// Tile order: groups of GN = 2 n-tiles, m-tiles (all experts) inside, so the
+// Tile order: groups of GN n-tiles, m-tiles (all experts) inside, so the
 // blocks of one XCD that run at the same time (neighbouring tiles) cover
 // many m-tiles of few experts and share their B columns in L2, and pairs of
-// them share A rows. Narrower groups measured faster than 4, 8 or 16 on the
-// Mixtral, Qwen3-30B and DeepSeek-V3 shapes (fewer weight re-reads).
+// them share A rows. GN = 2: narrower groups measured faster than 4, 8 or 16 on the
+// Mixtral, Qwen3-30B and DeepSeek-V3 shapes (fewer weight re-reads), except
+// where the experts average at most 1.5 m-tiles: then an expert's B columns
+// are read by one tile anyway, and the down-type GEMM is faster with groups
+// of GN = 8 n-tiles sharing the A rows (DeepSeek-V3 shape: 2.05 -> 1.94 ms).
 struct TileInfo {
   int g, m0, m_end, n0;
 };
 template <class C>
+__device__ __forceinline__ int tile_group_width(int total_mt, int G) {
+  return (!C::DUAL && 2 * total_mt <= 3 * G) ? 8 : 2;
+}
+template <class C>
 __device__ __forceinline__ TileInfo tile_info(const GroupedProblem& p, const int* s_pref, int G,
-                                              int total_mt, int nt_n, int64_t t) {
-  constexpr int GN = 2;
+                                              int total_mt, int nt_n, int64_t t, int GN) {
   const int64_t sg = (int64_t)total_mt * GN;
   const int nsup = (int)(t / sg);
   const int within = (int)(t - (int64_t)nsup * sg);
@@ -758,6 +764,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
   __syncthreads();
 
   const int total_mt = __builtin_amdgcn_readfirstlane(s_pref[G]);
+  const int gn = tile_group_width<C>(total_mt, G);
   const int nt_n = (p.Ncols + C::BN - 1) / C::BN;
   const int64_t total = (int64_t)total_mt * nt_n;
   if (total == 0) return;
@@ -823,7 +830,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
     }
     const int k0 = (KT * s / S) * C::BK, k1 = (KT * (s + 1) / S) * C::BK;
 
-    const TileInfo ti = tile_info<C>(p, s_pref, G, total_mt, nt_n, t);
+    const TileInfo ti = tile_info<C>(p, s_pref, G, total_mt, nt_n, t, gn);
     f32x16 acc[C::NB][C::FM][C::FN];
     tile_mainloop<C>(p, ti, rA, S0, S1, S2, S3, k0, k1 - k0, acc);
     int nxt = 0;
