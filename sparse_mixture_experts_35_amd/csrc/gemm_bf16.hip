@@ -16,7 +16,11 @@
 //    epilogue.
 //  * decode (≤ 64 rows per expert): weight-streaming split-K kernels, B read
 //    straight from HBM into registers (no LDS), v_mfma_f32_16x16x32_bf16,
-//    four waves reduce through LDS in a fixed order.
+//    four waves reduce through LDS in a fixed order; the down GEMM can run
+//    the combine in its last blocks.
+// The backward pass adds down-type tiles whose B is given as [K rows][N
+// columns] (the weights as stored; LDS transpose reads for its fragments)
+// and the weight-gradient GEMMs over per-expert K ranges.
 #include "common.hpp"
 #include "kernels.hpp"
 
