@@ -32,7 +32,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxK = 16;
 
 // Router logits for a few tokens (bf16): one wave per (token, expert) dot
 // product, 16-byte loads of both rows, fp32 products summed per lane in
@@ -207,14 +206,10 @@ __device__ __forceinline__ void route_select_block(
       }
       __syncthreads();                       // before the next tokens reuse s_g
     }
-    // ---- top-k: k rounds of a group-wide argmax, lower index wins ties
-    int win_id[kMaxK];
-    float win_aux[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      win_id[j] = 0;
-      win_aux[j] = 0.0f;
-    }
+    // ---- top-k: k rounds of a group-wide argmax, lower index wins ties;
+    //      lane j of the group keeps the j-th winner (k <= LPT)
+    int my_id = 0;
+    float my_aux = 0.0f, aux0 = 0.0f;
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY, ba = 0.0f;
       int bi = 0x7fffffff;
@@ -243,12 +238,11 @@ __device__ __forceinline__ void route_select_block(
         for (int i = 0; i < VPL; ++i)
           if (i == bi / LPT) cand[i] = false;
       }
-#pragma unroll
-      for (int jj = 0; jj < kMaxK; ++jj)
-        if (jj == j) {
-          win_id[jj] = bi;
-          win_aux[jj] = ba;
-        }
+      if (li == j) {
+        my_id = bi;
+        my_aux = ba;
+      }
+      if (j == 0) aux0 = ba;                 // the largest selected
     }
     // ---- full-softmax max and denominator (mode B gates, p statistics,
     //      z-loss)
@@ -305,39 +299,24 @@ __device__ __forceinline__ void route_select_block(
         ent_acc += ent;
       }
     }
-    // ---- gates
-    float gsel[kMaxK];
+    // ---- gates of the selected (lane li < k holds slot li), the sums over
+    //      the k slots by the group's butterfly
+    float my_g;
     if (MODE == 0) {
-      // softmax over the selected logits; win_aux[0] is the largest
-      float sum = 0.0f;
+      // softmax over the selected logits (aux0 is the largest)
+      const float ex = li < k ? expf(my_aux - aux0) : 0.0f;
+      float sum = ex;
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        gsel[j] = (j < k) ? expf(win_aux[j] - win_aux[0]) : 0.0f;
-        sum += gsel[j];
-      }
-      const float inv = 1.0f / sum;
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) gsel[j] *= inv;
+      for (int o = LPT / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      my_g = ex * (1.0f / sum);
     } else if (MODE == 1) {
-      const float inv = 1.0f / denom_all;
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) gsel[j] = (j < k) ? expf(win_aux[j] - zmax) * inv : 0.0f;
+      my_g = expf(my_aux - zmax) * (1.0f / denom_all);
     } else {
-      float sum = 0.0f;
+      float sum = li < k ? my_aux : 0.0f;
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) sum += (j < k) ? win_aux[j] : 0.0f;
-      const float inv = 1.0f / sum;
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) gsel[j] = (j < k) ? win_aux[j] * inv : 0.0f;
+      for (int o = LPT / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      my_g = my_aux * (1.0f / sum);
     }
-    int my_id = 0;
-    float my_g = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j == li) {
-        my_id = win_id[j];
-        my_g = gsel[j];
-      }
     if (tok && li < k) {
       ids[(int64_t)t * k + li] = my_id;
       gates[(int64_t)t * k + li] = my_g;
@@ -565,6 +544,7 @@ hipError_t launch_route_select(const float* z_part, int splits, const float* b_r
   const SelectCfg c = select_cfg(N);
   const int blocks = (T + c.tpb - 1) / c.tpb;
   if (blocks == 0) return hipSuccess;
+  if (k > c.lpt) return hipErrorInvalidValue;   // a lane per selected slot (k <= 16 <= LPT, or k <= N <= LPT)
   fin.on = fin.on && blocks == 1;
   if (dq) {
     // the fused kernel is one block; its dispatch reads the p_mean it wrote
