@@ -152,7 +152,8 @@ const char* moe_last_error(void);
 /* Host, pure: workspace bytes that suffice for EVERY call below with this
  * shape (the fused layer needs the most). 0 for an invalid shape.
  * moe_combine uses no workspace; moe_dispatch keeps per-chunk expert counts
- * (ceil(T·k / 1024)·N int32) at the start of its workspace. moe_route keeps the
+ * at the start of its workspace (none when T·k <= 1024, else N rows of
+ * ceil(T·k / 256) int32 rounded up to a multiple of 4). moe_route keeps the
  * router's partial logits and per-block probability sums there;
  * moe_expert_ffn keeps the SwiGLU activations (T·k·d_ff + T·d_ff_shared
  * elements) and, on the bf16 path, up to 64 MiB of fp32 split-K partial

@@ -178,7 +178,7 @@ FfnWs ffn_ws(const moe_shape* s, size_t base) {
 }
 // dispatch scratch: per-chunk expert counts
 size_t dispatch_ws_bytes(const moe_shape* s) {
-  return align_up(sizeof(int32_t) * (size_t)moe::dispatch_chunks(s->T, s->k) * s->N);
+  return align_up(sizeof(int32_t) * (size_t)moe::dispatch_hist_ints(s->T, s->k, s->N));
 }
 
 struct FusedWs {

@@ -8,10 +8,12 @@
 // Within an expert the copies keep token order, which makes the permutation
 // unique (the pages' grouped listing is in token order).
 //
-// Two kernels over chunks of kChunk consecutive flat slots f = t·k + j (one
-// kernel, counting its own chunk, when there is a single chunk):
+// Two kernels over chunks of consecutive flat slots f = t·k + j (one kernel,
+// counting its own chunk, when all slots fit one chunk of 1024; else chunks
+// of 256):
 //  1. dispatch_hist_kernel: block c counts its chunk's slots per expert (LDS
-//     integer atomics: counts do not depend on their order) into hist[c][e];
+//     integer atomics: counts do not depend on their order) into hist[e][c]
+//     (expert-major, rows padded to a multiple of 4 chunks with zeros);
 //  2. dispatch_place_kernel: block c sums the chunk counts into the expert
 //     totals (and, over the chunks before c, the number of each expert's
 //     slots that precede the chunk), scans the kept totals into offsets, then
@@ -39,19 +41,25 @@ using dsp::kMaxN;
 using dsp::kThreads;
 
 __global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(const int32_t* __restrict__ ids,
-                                                                 int R, int N,
+                                                                 int R, int N, int chunks,
                                                                  int32_t* __restrict__ hist) {
   __shared__ int s_h[kMaxN];
   const int tid = threadIdx.x;
   for (int i = tid; i < N; i += kThreads) s_h[i] = 0;
   __syncthreads();
-  const int f0 = blockIdx.x * kChunk, f1 = min(f0 + kChunk, R);
+  const int chunk = dsp::chunk_slots(R);
+  const int f0 = blockIdx.x * chunk, f1 = min(f0 + chunk, R);
   for (int f = f0 + tid; f < f1; f += kThreads) {
     const int id = ids[f];
     if ((unsigned)id < (unsigned)N) atomicAdd(&s_h[id], 1);
   }
   __syncthreads();
-  for (int i = tid; i < N; i += kThreads) hist[(int64_t)blockIdx.x * N + i] = s_h[i];
+  const int ld = dsp::hist_ld(chunks);
+  for (int i = tid; i < N; i += kThreads) hist[(int64_t)i * ld + blockIdx.x] = s_h[i];
+  if (blockIdx.x == 0) {
+    const int pad = ld - chunks;
+    for (int i = tid; i < N * pad; i += kThreads) hist[(int64_t)(i / pad) * ld + chunks + i % pad] = 0;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_place_kernel(
@@ -67,7 +75,16 @@ __global__ __launch_bounds__(kThreads) void dispatch_place_kernel(
 
 }  // namespace
 
-int dispatch_chunks(int T, int k) { return (int)(((int64_t)T * k + kChunk - 1) / kChunk); }
+int dispatch_chunks(int T, int k) {
+  const int64_t R = (int64_t)T * k;
+  const int chunk = dsp::chunk_slots(R);
+  return (int)((R + chunk - 1) / chunk);
+}
+
+int64_t dispatch_hist_ints(int T, int k, int N) {
+  const int chunks = dispatch_chunks(T, k);
+  return chunks > 1 ? (int64_t)N * dsp::hist_ld(chunks) : 0;
+}
 
 hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N, int32_t* counts,
                            int32_t* offsets, int32_t* perm_src, int32_t* row_of,
@@ -78,7 +95,7 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N, int32_t* cou
   if (chunks == 0) return hipSuccess;
   if (chunks > 1)
     hipLaunchKernelGGL(dispatch_hist_kernel, dim3(chunks), dim3(kThreads), 0, st, ids, T * k, N,
-                       hist);
+                       chunks, hist);
   hipLaunchKernelGGL(dispatch_place_kernel, dim3(chunks), dim3(kThreads), 0, st, ids, T, k, N,
                      chunks > 1 ? hist : nullptr, chunks, counts, offsets, perm_src, row_of,
                      p_mean, f_out, l_aux, alpha, cap, cap_stats, zero, zero_n);

@@ -25,9 +25,21 @@ namespace moe {
 namespace dsp {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 1024;                       // flat slots per block
-constexpr int kRounds = kChunk / kThreads;         // slots per thread
+constexpr int kChunk = 1024;                       // slots of a single-chunk dispatch
+constexpr int kChunkMulti = 256;                   // slots per block otherwise
+constexpr int kRounds = kChunk / kThreads;         // slots per thread at most
 constexpr int kMaxN = 512;
+
+// Flat slots per dispatch block: one block for up to kChunk slots (decode
+// batches: one kernel), else kChunkMulti (more, shorter blocks).
+__host__ __device__ __forceinline__ int chunk_slots(int64_t R) {
+  return R <= kChunk ? kChunk : kChunkMulti;
+}
+
+// Row stride of the per-chunk counts, stored expert-major as hist[e][c]:
+// the chunk count rounded up to 4 (the pad columns hold zeros), so that a
+// row reads as int4.
+__host__ __device__ __forceinline__ int hist_ld(int chunks) { return (chunks + 3) & ~3; }
 
 // exclusive scan over the block of one value per thread; total in `total`
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int& total) {
@@ -63,14 +75,16 @@ __device__ __forceinline__ void place_chunk(
   __shared__ int s_wc[4][kMaxN];   // per-wave counts of the current round
   __shared__ int s_wave[4];
   __shared__ float s_red[kThreads];
+  __shared__ int s_pt[kThreads], s_pb[kThreads];   // partial sums of the chunk counts
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int R = T * k;
   const bool limited = cap_in > 0;
   const int cap = limited ? cap_in : 0x7fffffff;
+  const int chunk = chunk_slots(R);
 
   // this thread's slots of the chunk, loaded up front (slot r0 + tid of
   // round r0 / kThreads)
-  const int f0 = c * kChunk, f1 = min(f0 + kChunk, R);
+  const int f0 = c * chunk, f1 = min(f0 + chunk, R);
   int my_e[kRounds];
 #pragma unroll
   for (int q = 0; q < kRounds; ++q) {
@@ -79,17 +93,45 @@ __device__ __forceinline__ void place_chunk(
     my_e[q] = (unsigned)id < (unsigned)N ? id : -1;
   }
   if (hist) {
-    for (int e = tid; e < N; e += kThreads) {
+    // P threads share an expert's row of chunk counts, each summing a range
+    // of whole int4 groups: the loads of a range are independent, so few
+    // round trips to the memory the counts were written through
+    const int ld = hist_ld(chunks);
+    const int P = N >= kThreads ? 1 : kThreads / N;
+    const int L = ((ld / 4 + P - 1) / P) * 4;       // chunks per thread
+    for (int i = tid; i < N * P; i += kThreads) {
+      const int e = i % N, p = i / N;
+      const int c0 = p * L, c1 = min(c0 + L, ld);
+      const int4* row = reinterpret_cast<const int4*>(hist + (int64_t)e * ld);
       int tot = 0, base = 0;
 #pragma unroll 8
-      for (int cc = 0; cc < chunks; ++cc) {
-        const int v = hist[(int64_t)cc * N + e];
-        base += cc < c ? v : 0;
-        tot += v;
+      for (int cc = c0; cc < c1; cc += 4) {
+        const int4 v = row[cc >> 2];
+        tot += v.x + v.y + v.z + v.w;
+        base += (cc < c ? v.x : 0) + (cc + 1 < c ? v.y : 0) + (cc + 2 < c ? v.z : 0) +
+                (cc + 3 < c ? v.w : 0);
       }
-      s_cnt[e] = tot;
-      s_base[e] = base;
-      s_run[e] = 0;
+      if (P == 1) {
+        s_cnt[e] = tot;
+        s_base[e] = base;
+        s_run[e] = 0;
+      } else {
+        s_pt[i] = tot;
+        s_pb[i] = base;
+      }
+    }
+    if (P > 1) {
+      __syncthreads();
+      for (int e = tid; e < N; e += kThreads) {
+        int tot = 0, base = 0;
+        for (int p = 0; p < P; ++p) {
+          tot += s_pt[p * N + e];
+          base += s_pb[p * N + e];
+        }
+        s_cnt[e] = tot;
+        s_base[e] = base;
+        s_run[e] = 0;
+      }
     }
   } else {
     // a single chunk: count it here

@@ -70,9 +70,11 @@ hipError_t launch_p_reduce(const float* p_part, float* p_mean,
 
 // --------------------------------------------------------------- dispatch
 // cap: expert capacity C >= 1, or 0 for none; cap_stats nullable; hist:
-// dispatch_chunks(T, k) x N int32 of scratch (per-chunk expert counts);
-// zero_n int32 at zero are cleared (counters of a later kernel)
+// dispatch_hist_ints(T, k, N) int32 of scratch, 16-byte aligned (per-chunk
+// expert counts); zero_n int32 at zero are cleared (counters of a later
+// kernel)
 int dispatch_chunks(int T, int k);
+int64_t dispatch_hist_ints(int T, int k, int N);
 hipError_t launch_dispatch(const int32_t* ids, int T, int k, int N,
                            int32_t* counts, int32_t* offsets,
                            int32_t* perm_src, int32_t* row_of,
