@@ -8,8 +8,9 @@
 // "MOE 专家选择与路由机制" (wuhy-notes), §六 Expert Capacity].
 //
 // One block per token; each thread owns 16-byte column chunks and reads the
-// k rows (and the shared row) at those columns, so every load is coalesced;
-// fp32 accumulation in slot order; no atomics.
+// k rows (and the shared row) at those columns, so every load is coalesced,
+// four slots' loads in flight at once; fp32 accumulation in slot order; no
+// atomics.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,14 +34,28 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
     }
-    for (int j = 0; j < k; ++j) {
-      const int64_t r = row_of[(int64_t)t * k + j];
-      if (r < 0) continue;
-      const float g = gates[(int64_t)t * k + j];
-      float v[8];
-      unpack_bf16x8(*reinterpret_cast<const u32x4*>(rows + r * d + c), v);
+    // slots in groups of four: the group's row loads are all issued before
+    // the first of them is used, then added in slot order
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      int64_t r[4];
+      float g[4];
+      u32x4 raw[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q;
+        r[q] = j < k ? row_of[(int64_t)t * k + j] : -1;
+        g[q] = j < k ? gates[(int64_t)t * k + j] : 0.0f;
+        raw[q] = r[q] >= 0 ? *reinterpret_cast<const u32x4*>(rows + r[q] * d + c)
+                           : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (r[q] < 0) continue;
+        float v[8];
+        unpack_bf16x8(raw[q], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[q], v[i], acc[i]);
+      }
     }
     u32x4 o;
 #pragma unroll
