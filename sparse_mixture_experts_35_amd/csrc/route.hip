@@ -452,19 +452,23 @@ struct SelectCfg {
   int lpt, vpl, iter, tpb;
 };
 // Up to 64 experts: one expert per lane (8, 16, 32 or 64 lanes per token).
-// More: eight per lane (16, 32 or 64 lanes), so that a token's reductions
-// take fewer shuffle steps and a wave routes several tokens at once.
-SelectCfg select_cfg(int N) {
+// More: four per lane up to 256 experts (32 or 64 lanes), eight beyond (64
+// lanes), so that a token's reductions take few shuffle steps. A block
+// routes each of its groups' tokens once (ITER 1) for batches of more than
+// 16 tokens, so that there are many short blocks; batches of up to 16
+// tokens loop ITER times so that one block routes them all (the single-block
+// selection + dispatch kernel).
+SelectCfg select_cfg(int T, int N) {
   SelectCfg c;
   if (N <= 64) {
     c.lpt = N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : 64;
     c.vpl = 1;
   } else {
-    c.lpt = N <= 128 ? 16 : N <= 256 ? 32 : 64;
-    c.vpl = 8;
+    c.lpt = N <= 128 ? 32 : 64;
+    c.vpl = N <= 256 ? 4 : 8;
   }
   const int tpw = 64 / c.lpt;
-  c.iter = (4 * tpw >= 16) ? 1 : 16 / (4 * tpw);
+  c.iter = (T > 16 || 4 * tpw >= 16) ? 1 : 16 / (4 * tpw);
   c.tpb = 4 * tpw * c.iter;
   return c;
 }
@@ -532,7 +536,7 @@ hipError_t launch_router_gemv_bf16(const void* h, const void* w, float* z, int T
 }
 
 int route_select_blocks(int T, int N) {
-  const SelectCfg c = select_cfg(N);
+  const SelectCfg c = select_cfg(T, N);
   return (T + c.tpb - 1) / c.tpb;
 }
 
@@ -541,7 +545,7 @@ hipError_t launch_route_select(const float* z_part, int splits, const float* b_r
                                float* p_part, float* zl_part, int T, int N, int k, int mode,
                                GroupLimit gl, RouteFinal fin, hipStream_t st,
                                const DispatchOut* dq) {
-  const SelectCfg c = select_cfg(N);
+  const SelectCfg c = select_cfg(T, N);
   const int blocks = (T + c.tpb - 1) / c.tpb;
   if (blocks == 0) return hipSuccess;
   if (k > c.lpt) return hipErrorInvalidValue;   // a lane per selected slot (k <= 16 <= LPT, or k <= N <= LPT)
@@ -552,15 +556,20 @@ hipError_t launch_route_select(const float* z_part, int splits, const float* b_r
     fin.on = 1;
   }
 #define MOE_SEL(L, V, I)                                                                    \
-  if (c.lpt == L && c.vpl == V)                                                             \
+  if (c.lpt == L && c.vpl == V && c.iter == I)                                             \
     return launch_select_t<L, V, I>(z_part, splits, b_router, b_select, ids, gates, p_part, \
                                     zl_part, T, N, k, mode, gl, blocks, fin, dq, st);
   MOE_SEL(8, 1, 1)
   MOE_SEL(16, 1, 1)
+  MOE_SEL(32, 1, 1)
   MOE_SEL(32, 1, 2)
+  MOE_SEL(64, 1, 1)
   MOE_SEL(64, 1, 4)
-  MOE_SEL(16, 8, 1)
-  MOE_SEL(32, 8, 2)
+  MOE_SEL(32, 4, 1)
+  MOE_SEL(32, 4, 2)
+  MOE_SEL(64, 4, 1)
+  MOE_SEL(64, 4, 4)
+  MOE_SEL(64, 8, 1)
   MOE_SEL(64, 8, 4)
 #undef MOE_SEL
   return hipErrorInvalidValue;

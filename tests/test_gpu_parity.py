@@ -191,7 +191,10 @@ CASES = [
     ("bf16_decode_T5_N512_k16_shared", 5, 64, 512, 16, 64, 64, W.DTYPE_BF16, 1),
     ("f32_decode_T16_switch", 16, 32, 4, 1, 64, 0, W.DTYPE_F32, 1),
     ("bf16_decode_T16_N128_k8", 16, 128, 128, 8, 64, 0, W.DTYPE_BF16, 0),
-    # more than 64 experts: eight experts per lane, 16 / 32 / 64 lanes a token
+    ("bf16_decode_T12_N256_k8_sigmoid_shared", 12, 128, 256, 8, 64, 64, W.DTYPE_BF16, 2),
+    # more than 64 experts: four experts per lane up to 256 (32 or 64 lanes a
+    # token), eight beyond
+    ("bf16_N256_k8_T40", 40, 64, 256, 8, 64, 0, W.DTYPE_BF16, 0),
     ("bf16_N100_k6_switch", 300, 128, 100, 6, 128, 0, W.DTYPE_BF16, 1),
     ("bf16_N200_sigmoid_shared", 150, 64, 200, 8, 64, 64, W.DTYPE_BF16, 2),
     ("f32_N128_k8", 40, 32, 128, 8, 32, 0, W.DTYPE_F32, 0),
@@ -218,6 +221,7 @@ GROUPED_CASES = [
     ("bf16_grouped_N256_64groups", 150, 64, 256, 8, 64, 0, W.DTYPE_BF16, 0, (64, 8, 4)),
     ("bf16_grouped_N512_16groups", 100, 64, 512, 16, 64, 0, W.DTYPE_BF16, 2, (16, 3, 8)),
     ("bf16_grouped_decode_T12", 12, 128, 32, 4, 128, 0, W.DTYPE_BF16, 2, (8, 2, 2)),
+    ("bf16_grouped_decode_T9_N256", 9, 64, 256, 8, 64, 64, W.DTYPE_BF16, 2, (8, 4, 2)),
 ]
 
 
