@@ -1013,6 +1013,7 @@ __device__ __forceinline__ void skinny_tile(const GroupedProblem& p, int r0, int
 
   const int KT = p.K / 64;
   u32x4 bc[NB][CT][2], bn[NB][CT][2];
+  u32x4 ac[MT][2], an[MT][2];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   auto loadB = [&](u32x4 (&dst)[NB][CT][2], int c) {
 #pragma unroll
@@ -1023,16 +1024,26 @@ __device__ __forceinline__ void skinny_tile(const GroupedProblem& p, int r0, int
         for (int s = 0; s < 2; ++s)
           dst[nb][ct][s] = *reinterpret_cast<const u32x4*>(brow[nb][ct] + c * 64 + s * 8);
   };
-  int c = w;
-  if (c < KT) loadB(bc, c);
-  for (; c < KT; c += 4) {
-    if (c + 4 < KT) loadB(bn, c + 4);
-    u32x4 af[MT][2];
+  auto loadA = [&](u32x4 (&dst)[MT][2], int c) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        af[mt][s] = aval[mt] ? *reinterpret_cast<const u32x4*>(arow[mt] + c * 64 + s * 8) : zero4;
+        dst[mt][s] = aval[mt] ? *reinterpret_cast<const u32x4*>(arow[mt] + c * 64 + s * 8) : zero4;
+  };
+  // A and B of chunk c + 4 are loaded together, one chunk ahead of the
+  // MFMAs: loads complete in issue order, so the MFMAs' wait for chunk c
+  // leaves all of chunk c + 4 in flight
+  int c = w;
+  if (c < KT) {
+    loadB(bc, c);
+    loadA(ac, c);
+  }
+  for (; c < KT; c += 4) {
+    if (c + 4 < KT) {
+      loadB(bn, c + 4);
+      loadA(an, c + 4);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -1041,13 +1052,17 @@ __device__ __forceinline__ void skinny_tile(const GroupedProblem& p, int r0, int
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
-            acc[nb][mt][ct] = mfma_16x16x32(af[mt][s], bc[nb][ct][s], acc[nb][mt][ct]);
+            acc[nb][mt][ct] = mfma_16x16x32(ac[mt][s], bc[nb][ct][s], acc[nb][mt][ct]);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int s = 0; s < 2; ++s) bc[nb][ct][s] = bn[nb][ct][s];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) ac[mt][s] = an[mt][s];
   }
 
 #pragma unroll
