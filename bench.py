@@ -19,7 +19,9 @@ inputs are already resident in HBM. Prints ONE JSON line.
             readings (a committed summary under profiles/), reported only
             while the kernel sources match the ones that were counted
   decode    the same layer at a decode batch (16 tokens) on the same
-            weights: tokens/s and HBM GB/s of the touched experts' weights
+            weights: tokens/s and HBM GB/s of the touched experts' weights;
+            other_batches: ms per step and HBM fraction at 1, 4, 32 and 64
+            tokens
   backward  moe_layer_backward on the same workload (the forward's selection
             made once beforehand): ms per call and the algorithmic TFLOP/s of
             the gradients (2x the forward's expert flops plus the router's);
@@ -516,7 +518,6 @@ def main():
         alt = tuple(inp[key].clone() for key in ("w_gate", "w_up", "w_down"))
         dwall, dstage, _, dcounts = run_layer(M, torch, wd, dinp, max(a.steps, 20), a.warmup,
                                               gate_up_events=False, alt_weights=alt)
-        del alt
         dsteps = max(a.steps, 20)
         dms = dwall / dsteps * 1e3
         _, dbytes, dtouched = layer_work(wd, dcounts)
@@ -526,6 +527,23 @@ def main():
                          "hbm_gbs_layer": dbytes / (dms * 1e-3) / 1e9,
                          "frac_hbm_peak_layer": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "stages_ms": dstage, "weight_copies_alternated": 2}
+        # other decode batch sizes, the same way (the first tb tokens)
+        others = []
+        for tb in (1, 4, 32, 64):
+            if tb == a.decode_tokens or tb >= w.T:
+                continue
+            wb = w.replace(name=re.sub(r"prefill_T\d+", f"decode_T{tb}", w.name), T=tb)
+            binp = dict(inp)
+            binp["h"] = inp["h"][:tb].contiguous()
+            bwall, _, _, bcounts = run_layer(M, torch, wb, binp, dsteps, a.warmup,
+                                             gate_up_events=False, alt_weights=alt)
+            bms = bwall / dsteps * 1e3
+            _, bbytes, btouched = layer_work(wb, bcounts)
+            others.append({"T": tb, "ms_per_step": bms, "experts_touched": btouched,
+                           "max_rows": int(bcounts.max()), "weight_bytes": bbytes,
+                           "frac_hbm_peak_layer": bbytes / (bms * 1e-3) / 1e9 / PEAK_HBM_GBS})
+        out["decode"]["other_batches"] = others
+        del alt
         # weight-streaming kernels: algorithmic bytes (touched experts' weights,
         # rows in and out) against the counted HBM bytes per launch
         gb = {"gate_up": gateup_work(wd, dcounts)[1],
