@@ -438,6 +438,8 @@ def main():
                     help="tokens of the workload the CPU baseline runs (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode-batches", action="store_true",
+                    help="skip the decode batches other than --decode-tokens")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement")
     ap.add_argument("--no-variants", action="store_true",
@@ -529,7 +531,7 @@ def main():
                          "stages_ms": dstage, "weight_copies_alternated": 2}
         # other decode batch sizes, the same way (the first tb tokens)
         others = []
-        for tb in (1, 4, 32, 64):
+        for tb in () if a.no_decode_batches else (1, 4, 32, 64):
             if tb == a.decode_tokens or tb >= w.T:
                 continue
             wb = w.replace(name=re.sub(r"prefill_T\d+", f"decode_T{tb}", w.name), T=tb)
