@@ -88,6 +88,25 @@ def check_close_rows(y, y_ref, tol, mask=None, what="y"):
     return worst
 
 
+def check_grad_rows(y, y_ref, tol, what, floor=1e-2):
+    """Per-row relative error of a gradient, each row's scale being the larger
+    of its own max |y_ref| and floor times the tensor's: a row whose exact
+    value is a sum that cancels far below the gradient's scale (a dot
+    product of nearly opposite terms, or a token whose routed slots were all
+    dropped) carries the rounding of its terms, not of its result, so it is
+    compared at the tensor's scale."""
+    y = np.asarray(y, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    if y_ref.size == 0:
+        return 0.0
+    num = np.abs(y - y_ref).max(axis=-1)
+    den = np.maximum(np.abs(y_ref).max(axis=-1), floor * np.abs(y_ref).max())
+    err = num / np.where(den == 0, 1.0, den)
+    worst = float(err.max())
+    assert worst <= tol, f"{what}: max per-row error / row scale {worst:.3e} > {tol:.1e}"
+    return worst
+
+
 def check_gates(g, g_ref, tol, mask):
     err = np.abs(g - g_ref) / np.maximum(np.abs(g_ref), 1e-30)
     worst = float(err[mask].max()) if mask.any() else 0.0
