@@ -300,7 +300,11 @@ __device__ __forceinline__ void route_select_block(
       }
     }
     // ---- gates of the selected (lane li < k holds slot li), the sums over
-    //      the k slots by the group's butterfly
+    //      the k slots by the group's butterfly; correctly rounded divisions,
+    //      so that one selected expert gets a gate of exactly 1 (a product
+    //      with a rounded reciprocal can miss it by an ulp, and the backward's
+    //      renormalisation term, exactly 0 then, would carry that ulp times
+    //      dL/dg into the router gradient)
     float my_g;
     if (MODE == 0) {
       // softmax over the selected logits (aux0 is the largest)
@@ -308,14 +312,14 @@ __device__ __forceinline__ void route_select_block(
       float sum = ex;
 #pragma unroll
       for (int o = LPT / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-      my_g = ex * (1.0f / sum);
+      my_g = ex / sum;
     } else if (MODE == 1) {
-      my_g = expf(my_aux - zmax) * (1.0f / denom_all);
+      my_g = expf(my_aux - zmax) / denom_all;
     } else {
       float sum = li < k ? my_aux : 0.0f;
 #pragma unroll
       for (int o = LPT / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-      my_g = my_aux * (1.0f / sum);
+      my_g = my_aux / sum;
     }
     if (tok && li < k) {
       ids[(int64_t)t * k + li] = my_id;

@@ -134,6 +134,11 @@ BACKWARD_CASES = [
     ("bf16_B_bm256", 2304, 128, 2, 1, 320, 0, W.DTYPE_BF16, 1, None, 0.0, 0.0, 0.2),
     # K = 4096 in the v GEMM: its split-K tail
     ("bf16_A_split_k4096", 256, 4096, 2, 1, 256, 0, W.DTYPE_BF16, 0, None, 0.0, 0.0, 0.0),
+    # one selected expert, renormalised: the gate is exactly 1 and the task
+    # gradient reaches the router through nothing; the router gradient is
+    # the auxiliary loss's alone, far below the scale of dL/dg
+    ("bf16_C_top1_aux_only", 300, 1024, 2, 1, 128, 128, W.DTYPE_BF16, 2, None, 0.0, 1.0, 0.0),
+    ("f32_A_top1_aux_only", 200, 64, 3, 1, 32, 0, W.DTYPE_F32, 0, None, 0.0, 1.0, 0.0),
 ]
 
 
@@ -264,3 +269,20 @@ def test_forward_train_and_backward_with_preact(case):
     res["row_of"] = host(row_of)
     worst = check_backward(s, inp, dy, res, 0.4, 0.2)
     print(f"{name}: " + ", ".join(f"{k_} {v:.1e}" for k_, v in worst.items()))
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_top1_renormalised_gate_is_one(mode):
+    """Top-1 with renormalisation over the selected (modes A and C): every
+    gate is exactly 1."""
+    T, d, N, k = 300, 256, 8, 1
+    inp = W.random_small(T, d, N, k, 64, 0, W.DTYPE_BF16, mode, seed=5, router_bias=True)
+    s = M.Shape(T, d, N, k, 64, 0, W.DTYPE_BF16, mode, 0.01)
+    t = torch()
+    ws = t.empty(M.workspace_bytes(s), dtype=t.uint8, device="cuda")
+    ids = t.empty(T * k, dtype=t.int32, device="cuda")
+    gates = t.empty(T * k, dtype=t.float32, device="cuda")
+    M.route(s, dev(inp["h"], W.DTYPE_BF16), dev(inp["w_router"], W.DTYPE_BF16),
+            dev_f32(inp["b_router"]), dev_f32(inp["b_select"]), ids, gates, None, ws, ws.numel())
+    t.cuda.synchronize()
+    assert np.all(host(gates) == 1.0)
