@@ -105,7 +105,7 @@ def test_full_size_layer(w):
     g_ids = host(ids).reshape(T, k)
     near = check_ids(g_ids, r, k, grouped=w.groups is not None)
     ok = ~near
-    check_gates(host(gates).reshape(T, k), r.gates, 1e-4, ok)
+    check_gates(host(gates).reshape(T, k), r.gates, 1e-4, ok, g_ids, r.ids)
     cap = O.expert_capacity(w.capacity_factor, T, k, N) if w.capacity_factor else None
     d = O.dispatch(g_ids, N, cap)
     kept = int(d.offsets[-1])

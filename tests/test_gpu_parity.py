@@ -108,7 +108,7 @@ def check_all(s, inp, res, alpha=0.01):
                 groups_of(s))
     near = check_ids(res["ids"], r, s.k, grouped=groups_of(s) is not None)
     ok = ~near
-    check_gates(res["gates"], r.gates, 1e-4, ok)
+    check_gates(res["gates"], r.gates, 1e-4, ok, res["ids"], r.ids)
     # dispatch: bit-exact against the oracle's dispatch of the GPU's own ids
     cap = capacity_of(s)
     d = O.dispatch(res["ids"], s.N, cap)
