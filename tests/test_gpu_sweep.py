@@ -6,7 +6,8 @@ modes, with and without a shared expert, a group limit and an expert
 capacity — so that the kernel
 variants meet combinations the hand-picked cases do not (selection layouts,
 single-block selection + dispatch, skinny and tiled GEMMs, split-K tails,
-the fused decode combine), and the backward pass on the first 40 of them."""
+the fused decode combine), and the backward pass on the first 40 of them;
+then 24 larger shapes (800 to 6,000 tokens)."""
 import math
 
 import numpy as np
@@ -102,3 +103,43 @@ def test_sweep_backward(case):
     res = run_backward(s, inp, dy, d_laux, d_zloss)
     worst = check_backward(s, inp, dy, res, d_laux, d_zloss)
     print(f"{name}: " + ", ".join(f"{k_} {v:.1e}" for k_, v in worst.items()))
+
+
+def large_cases(n=24, seed=5):
+    """Deterministic list of larger shapes (800 to 6,000 tokens; up to 512
+    experts): many dispatch chunks, grouped tiles with split-K tails, the
+    selection's one-pass blocks."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        bf16 = rng.random() < 0.85
+        dt = W.DTYPE_BF16 if bf16 else W.DTYPE_F32
+        T = int(rng.integers(800, 6001))
+        N = int(rng.choice([2, 8, 16, 60, 64, 128, 200, 256, 512]))
+        k = int(rng.integers(1, min(N, 8) + 1))
+        d = int(rng.choice([64, 128, 256] if bf16 else [32, 64]))
+        dff = int(rng.choice([64, 128, 256, 384] if bf16 else [32, 48]))
+        dfs = int(rng.choice([0, 0, 128] if bf16 else [0, 32]))
+        mode = int(rng.integers(0, 3))
+        groups = _groups(rng, N, k) if (N >= 4 and rng.random() < 0.25) else None
+        cf = 0.0 if rng.random() < 0.75 else float(rng.choice([0.5, 1.0, 1.25]))
+        name = (f"L{i:02d}_{'bf16' if bf16 else 'f32'}_T{T}_d{d}_N{N}_k{k}_ff{dff}_sh{dfs}_m{mode}"
+                + (f"_g{groups[0]}-{groups[1]}-{groups[2]}" if groups else "")
+                + (f"_cf{cf}" if cf else ""))
+        cases.append((name, T, d, N, k, dff, dfs, dt, mode, groups, cf))
+    return cases
+
+
+LARGE = large_cases()
+
+
+@pytest.mark.parametrize("case", LARGE, ids=[c[0] for c in LARGE])
+def test_sweep_large(case):
+    name, T, d, N, k, dff, dfs, dt, mode, groups, cf = case
+    inp = W.random_small(T, d, N, k, dff, dfs, dt, mode, seed=len(name) + T,
+                         router_bias=(T % 2 == 0))
+    s = shape_of(T, d, N, k, dff, dfs, dt, mode, groups=groups, cf=cf)
+    print(f"case {name}", flush=True)
+    res = run_steps(s, inp)
+    worst, near = check_all(s, inp, res)
+    print(f"{name}: worst row rel err {worst:.2e}, near-ties {near}")
