@@ -216,6 +216,8 @@ __device__ __forceinline__ void place_chunk(
       } else {
         row_of[f] = -1;
       }
+    } else if (f < f1) {
+      row_of[f] = -1;                         // an id outside [0, N): no row
     }
     __syncthreads();
     for (int i = tid; i < N; i += kThreads)

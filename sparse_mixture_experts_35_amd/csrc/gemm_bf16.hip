@@ -1220,7 +1220,12 @@ __global__ __launch_bounds__(kThreads) void skinny_gemm_kernel(GroupedProblem p,
     r0 = g * 16 * MT;
     cnt = min(p.M - r0, 16 * MT);
   }
-  if (cnt > 0) skinny_tile<MT, CT, DUAL, CMB>(p, g, cb, r0, min(cnt, 16 * MT), red);
+  // at most 16·MT rows per pass; more only when a caller's ids name one
+  // expert twice for a token (the row bound of the launch assumes not)
+  for (int base = 0; base < cnt; base += 16 * MT) {
+    if (base > 0) __syncthreads();          // the previous pass's LDS reads are done
+    skinny_tile<MT, CT, DUAL, CMB>(p, g, cb, r0 + base, min(cnt - base, 16 * MT), red);
+  }
   if constexpr (CMB) skinny_combine<CT>(p, cf, cb, ngroups);
 }
 

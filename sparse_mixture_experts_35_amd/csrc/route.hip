@@ -127,6 +127,10 @@ __device__ __forceinline__ void route_select_block(
         aux[i] = v;
         sel[i] = v;
       }
+      // a NaN score (a NaN in h, W_r or the biases) selects as -inf: the
+      // token still gets k distinct experts, lowest indices first among
+      // equals, and its gates come out NaN
+      if (__builtin_isnan(sel[i])) sel[i] = -INFINITY;
     }
     // ---- group limit: keep the gl.keep best expert groups as candidates
     if (gl.n_groups > 0) {
@@ -173,7 +177,7 @@ __device__ __forceinline__ void route_select_block(
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             if (j < gl.topm) sum += top[j];
-          gsc[q] = sum;
+          gsc[q] = __builtin_isnan(sum) ? -INFINITY : sum;
         }
       }
       uint64_t kept = 0;

@@ -671,4 +671,42 @@ def pin_route_given_selection():
         assert np.allclose(g, want, rtol=1e-13, atol=0)
 
 
+
+# ------------------------------------------------------ comparison helpers
+def pin_row_rel_err_hand_cases():
+    """Per-row max |y - y_ref| over max |y_ref|, worked by hand: [1, 2] vs
+    [1, 4] -> 2/4; [-3, 0] vs [-1, 2] -> 2/2 (magnitudes, not signed
+    values); [0.5, -0.25, 7] vs [1, -0.5, 7] -> 0.5/7 (the row's largest
+    reference entry, not the entry where the error is); stacked rows are
+    independent (no tensor-wide scale); a zero reference row gives the
+    absolute difference; no rows, no errors."""
+    a = O.row_rel_err(np.array([[1.0, 2.0]]), np.array([[1.0, 4.0]]))
+    assert a.shape == (1,) and a[0] == 0.5, a
+    b = O.row_rel_err(np.array([[-3.0, 0.0]]), np.array([[-1.0, 2.0]]))
+    assert b[0] == 1.0, b
+    c = O.row_rel_err(np.array([[0.5, -0.25, 7.0]]), np.array([[1.0, -0.5, 7.0]]))
+    assert abs(c[0] - 0.5 / 7.0) < 1e-16, c
+    both = O.row_rel_err(np.array([[1.0, 2.0], [-3.0, 0.0], [10.0, 10.0]]),
+                         np.array([[1.0, 4.0], [-1.0, 2.0], [10.0, 10.0]]))
+    assert both.tolist() == [0.5, 1.0, 0.0], both
+    z = O.row_rel_err(np.array([[0.0, 3e-3], [0.0, 0.0]]), np.zeros((2, 2)))
+    assert z.tolist() == [3e-3, 0.0], z
+    assert O.row_rel_err(np.zeros((0, 4)), np.zeros((0, 4))).shape == (0,)
+
+
+def pin_near_tie_tokens_hand_cases():
+    """A token is near a tie when its gap is strictly below the threshold
+    (1e-4 by default): gaps just below, at and just above it, zero, and
+    +inf (k = N)."""
+    gaps = np.array([0.0, 5e-5, 9.99e-5, 1e-4, 1.0001e-4, 0.3, np.inf])
+    assert O.near_tie_tokens(gaps).tolist() == [True, True, True, False, False, False, False]
+    assert O.near_tie_tokens(np.array([0.5, 1.5]), 1.0).tolist() == [True, False]
+    assert O.near_tie_tokens(np.array([2e-8]), 1e-8).tolist() == [False]
+    # the gap the oracle's own routing reports: a planted tie is near, a
+    # clear winner is not
+    z = np.array([[1.0, 1.0 + 5e-5, -2.0], [3.0, 0.0, -1.0]])
+    r = O.route(z, np.eye(3), 1, O.MODE_SOFTMAX_FULL)
+    assert O.near_tie_tokens(r.gap).tolist() == [True, False], r.gap
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -103,7 +103,7 @@ def test_full_size_layer(w):
     br, bs = _np32(inp["b_router"]), _np32(inp["b_select"])
     r = O.route(h, wr, k, w.mode, br, bs, w.groups)
     g_ids = host(ids).reshape(T, k)
-    near = check_ids(g_ids, r, k, grouped=w.groups is not None)
+    near = check_ids(g_ids, r, k, w.mode, h, wr, br, bs, grouped=w.groups is not None)
     ok = ~near
     check_gates(host(gates).reshape(T, k), r.gates, 1e-4, ok, g_ids, r.ids)
     cap = O.expert_capacity(w.capacity_factor, T, k, N) if w.capacity_factor else None

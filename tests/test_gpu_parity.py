@@ -106,7 +106,8 @@ def check_all(s, inp, res, alpha=0.01):
     tol = TOL[s.dtype]
     r = O.route(inp["h"], inp["w_router"], s.k, s.mode, inp["b_router"], inp["b_select"],
                 groups_of(s))
-    near = check_ids(res["ids"], r, s.k, grouped=groups_of(s) is not None)
+    near = check_ids(res["ids"], r, s.k, s.mode, inp["h"], inp["w_router"], inp["b_router"],
+                     inp["b_select"], grouped=groups_of(s) is not None)
     ok = ~near
     check_gates(res["gates"], r.gates, 1e-4, ok, res["ids"], r.ids)
     # dispatch: bit-exact against the oracle's dispatch of the GPU's own ids
@@ -448,3 +449,103 @@ def test_deterministic_repeat(T, d, N, k, dff, dfs):
     b = run_steps(s, inp)
     for key in ("ids", "gates", "perm", "row_of", "out_rows", "y", "p", "l_aux"):
         assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
+
+
+@pytest.mark.parametrize("T,N,k,mode,dff", [(300, 16, 4, 0, 128), (300, 16, 4, 2, 128),
+                                            (12, 8, 2, 0, 128), (12, 64, 8, 2, 128)])
+def test_nan_token_keeps_valid_routing(T, N, k, mode, dff):
+    """A NaN in one token's hidden state makes all its logits NaN. The token
+    still gets k distinct experts in [0, N) (a NaN selects as -inf, ties to
+    the lower index), only its own y row is non-finite, and every other
+    token's y matches the oracle run without it (tokens do not interact)."""
+    d = 128
+    inp = W.random_small(T, d, N, k, dff, 0, W.DTYPE_BF16, mode, seed=T + N)
+    bad = T // 3
+    h_nan = inp["h"].copy()
+    h_nan[bad, 5] = np.nan
+    s = shape_of(T, d, N, k, dff, 0, W.DTYPE_BF16, mode)
+    dt = W.DTYPE_BF16
+    t = torch()
+    ws, nws = workspace(s)
+    y = t.empty((T, d), dtype=t.bfloat16, device="cuda")
+    ids, gates, counts = i32(T * k), f32(T * k), i32(N)
+    M.layer_fused(s, dev(h_nan, dt), dev(inp["w_router"], dt), dev_f32(inp["b_router"]),
+                  dev_f32(inp["b_select"]), dev(inp["w_gate"], dt), dev(inp["w_up"], dt),
+                  dev(inp["w_down"], dt), None, None, None, y, ids, gates, counts, ws=ws,
+                  ws_bytes=nws)
+    t.cuda.synchronize()
+    g_ids = host(ids).reshape(T, k)
+    assert g_ids.min() >= 0 and g_ids.max() < N
+    assert all(len(set(r.tolist())) == k for r in g_ids)
+    assert g_ids[bad].tolist() == list(range(k)), g_ids[bad]
+    assert host(counts).sum() == T * k
+    yh = host(y)
+    assert not np.isfinite(yh[bad]).any()
+    others = np.arange(T) != bad
+    assert np.isfinite(yh[others]).all()
+    ref = O.layer(np.where(others[:, None], inp["h"], 0.0), inp["w_router"], k, mode,
+                  oracle_weights(inp), inp["b_router"], inp["b_select"])
+    ok = others & ~O.near_tie_tokens(ref.routing.gap)
+    assert np.array_equal(np.sort(g_ids[ok], axis=1), np.sort(ref.routing.ids[ok], axis=1))
+    check_close_rows(yh, ref.y, TOL[dt], ok, what="y (tokens other than the NaN one)")
+
+
+def test_dispatch_ids_out_of_range_get_no_row():
+    """Caller ids outside [0, N) take no bucket row: row_of = -1, and the
+    other slots are placed as if they were absent (stable, by expert)."""
+    T, N, k = 40, 6, 3
+    rng = np.random.default_rng(11)
+    ids = np.stack([rng.choice(N, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[3, 1], ids[17, 0], ids[39, 2] = -1, N, 1 << 20
+    s = shape_of(T, 64, N, k, 64)
+    t = torch()
+    counts, offsets, perm, row_of = i32(N), i32(N + 1), i32(T * k), i32(T * k)
+    row_of.fill_(12345)
+    ws, nws = workspace(s)
+    M.dispatch(s, t.from_numpy(ids.reshape(-1)).cuda(), counts, offsets, perm, row_of, ws=ws,
+               ws_bytes=nws)
+    t.cuda.synchronize()
+    flat = ids.reshape(-1)
+    want_perm = np.concatenate([np.nonzero(flat == e)[0] for e in range(N)])
+    want_counts = np.array([(flat == e).sum() for e in range(N)])
+    want_row = np.full(T * k, -1)
+    want_row[want_perm] = np.arange(want_perm.size)
+    assert np.array_equal(host(counts), want_counts)
+    assert np.array_equal(host(offsets), np.concatenate([[0], np.cumsum(want_counts)]))
+    assert np.array_equal(host(perm)[:want_perm.size], want_perm)
+    assert np.array_equal(host(row_of), want_row)
+
+
+@pytest.mark.parametrize("T,N,k,dff", [(20, 8, 4, 256), (40, 4, 2, 128)])
+def test_repeated_expert_ids_from_the_caller(T, N, k, dff):
+    """Caller ids that name one expert twice for a token: that expert gets
+    more rows than tokens (here more than the weight-streaming kernels take
+    in one pass), every row is still computed, and combine adds both slots."""
+    d = 128
+    inp = W.random_small(T, d, N, k, dff, 0, W.DTYPE_BF16, 0, seed=T)
+    rng = np.random.default_rng(T)
+    ids = np.stack([np.concatenate([[0, 0], rng.choice(np.arange(1, N), size=k - 2,
+                                                        replace=False)]) for _ in range(T)])
+    ids = ids.astype(np.int32)
+    gates = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    s = shape_of(T, d, N, k, dff)
+    dt = W.DTYPE_BF16
+    t = torch()
+    ws, nws = workspace(s)
+    counts, offsets, perm, row_of = i32(N), i32(N + 1), i32(T * k), i32(T * k)
+    M.dispatch(s, t.from_numpy(ids.reshape(-1)).cuda(), counts, offsets, perm, row_of, ws=ws,
+               ws_bytes=nws)
+    out_rows = t.empty((T * k, d), dtype=t.bfloat16, device="cuda")
+    M.expert_ffn(s, dev(inp["h"], dt), perm, offsets, dev(inp["w_gate"], dt),
+                 dev(inp["w_up"], dt), dev(inp["w_down"], dt), None, None, None, out_rows, ws,
+                 nws)
+    y = t.empty((T, d), dtype=t.bfloat16, device="cuda")
+    M.combine(s, out_rows, row_of, dev_f32(gates.reshape(-1)), y)
+    t.cuda.synchronize()
+    assert host(counts)[0] == 2 * T
+    disp = O.dispatch(ids, N)
+    assert np.array_equal(host(perm), disp.perm_src)
+    rows_ref = O.expert_rows(inp["h"], disp, k, oracle_weights(inp))
+    check_close_rows(host(out_rows), rows_ref, TOL[dt], what="out_rows")
+    y_ref = O.combine(rows_ref, disp.row_of, gates.astype(np.float64))
+    check_close_rows(host(y), y_ref, TOL[dt], what="y")

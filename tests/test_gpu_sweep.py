@@ -102,7 +102,7 @@ def test_sweep_backward(case):
     print(f"case {name} d_laux {d_laux} d_zloss {d_zloss}", flush=True)
     res = run_backward(s, inp, dy, d_laux, d_zloss)
     worst = check_backward(s, inp, dy, res, d_laux, d_zloss)
-    print(f"{name}: " + ", ".join(f"{k_} {v:.1e}" for k_, v in worst.items()))
+    print(f"{name}: " + ", ".join(f"{k_} {v[0]:.1e}/{v[1]:.1f}/{v[2]:.2f}" for k_, v in worst.items()))
 
 
 def large_cases(n=24, seed=5):

@@ -13,7 +13,8 @@ _orig = {n: getattr(O, n) for n in ("router_logits", "softmax", "sigmoid", "topk
                                      "dispatch", "expert_capacity", "silu", "expert_ffn", "combine",
                                      "load_stats", "route", "router_z_loss", "routing_entropy",
                                      "silu_grad", "expert_ffn_backward", "gate_backward",
-                                     "stats_backward", "layer_backward")}
+                                     "stats_backward", "layer_backward", "row_rel_err",
+                                     "near_tie_tokens")}
 
 
 def _route_no_renorm(h, w, k, mode, b_router=None, b_select=None):
@@ -217,6 +218,13 @@ MUTATIONS = {
                             _orig["stats_backward"](r, c, k, m, a, -dl, dz)),
     "layer_bwd_ignores_capacity": ("layer_backward", _layer_bwd_ignores_capacity),
     "layer_bwd_no_shared": ("layer_backward", _layer_bwd_no_shared),
+    "row_rel_err_zero": ("row_rel_err", lambda y, r: np.zeros(np.asarray(y).shape[0])),
+    "row_rel_err_tensor_scale": ("row_rel_err", lambda y, r: np.abs(np.asarray(y, float) - np.asarray(r, float)).max(axis=-1) / max(np.abs(np.asarray(r, float)).max(initial=0.0), 1e-300)),
+    "row_rel_err_elementwise": ("row_rel_err", lambda y, r: (np.abs(np.asarray(y, float) - np.asarray(r, float)) / np.maximum(np.abs(np.asarray(r, float)), 1e-300)).max(axis=-1, initial=0.0)),
+    "row_rel_err_mean": ("row_rel_err", lambda y, r: np.abs(np.asarray(y, float) - np.asarray(r, float)).mean(axis=-1) / np.maximum(np.abs(np.asarray(r, float)).max(axis=-1, initial=0.0), 1e-300)),
+    "near_tie_inclusive": ("near_tie_tokens", lambda g, th=1e-4: np.asarray(g) <= th),
+    "near_tie_never": ("near_tie_tokens", lambda g, th=1e-4: np.zeros(np.shape(g), bool)),
+    "near_tie_fixed_threshold": ("near_tie_tokens", lambda g, th=1e-4: np.asarray(g) < 1e-4),
     "stats_f_over_T": ("load_stats", lambda c, sp, k, a: _orig["load_stats"](c, sp, 1, a)),
     "stats_no_N_factor": ("load_stats", lambda c, sp, k, a: (lambda f, p, l: (f, p, l / np.asarray(sp).shape[1]))(*_orig["load_stats"](c, sp, k, a))),
 }
