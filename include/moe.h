@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_GROUPS 64
@@ -262,6 +262,35 @@ moe_status moe_layer_fused(const moe_shape* s, const void* h,
                            float* p_out, float* l_aux, float* z_loss,
                            float* entropy, float* cap_stats, void* ws,
                            size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. moe_layer_fused with no
+ * workspace argument: its scratch is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds
+ * from the first call until the process ends. The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the caller still
+ * passes inputs and outputs, with the arguments, layouts and results of
+ * moe_layer_fused (the same bits). The layout is moe_layer_fused's without
+ * the split-K partial region when no tiled GEMM runs (bf16 with at most 64
+ * rows per expert and a shared expert over at most 64 tokens, or fp32), so
+ * every decode batch of the layer shapes here fits; a shape that needs more
+ * returns MOE_ERR_WORKSPACE before any HIP call.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (each call clears the counters it uses itself): calls that
+ * overlap on one GPU (concurrent streams or threads) race, so serialise
+ * them. Errors: as moe_layer_fused; MOE_ERR_HIP if the scratch's device
+ * address cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_fused_noalloc(const moe_shape* s, const void* h,
+                                   const void* w_router, const float* b_router,
+                                   const float* b_select, const void* w_gate,
+                                   const void* w_up, const void* w_down,
+                                   const void* sh_gate, const void* sh_up,
+                                   const void* sh_down, void* y,
+                                   int32_t* topk_ids, float* topk_gates,
+                                   int32_t* counts, float* f_out, float* p_out,
+                                   float* l_aux, float* z_loss, float* entropy,
+                                   float* cap_stats, void* stream);
 
 /* moe_layer_fused that also records caller-created hipEvent_t handles on
  * `stream` at the stage boundaries, for timing: events[0] before routing,

@@ -23,7 +23,9 @@ MAX_EXPERTS, MAX_TOPK, MAX_GROUPS, MAX_GROUP_TOPM = 512, 16, 64, 8
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_fused",
            "moe_layer_fused_marked", "moe_layer_forward_train", "moe_backward_workspace_bytes",
-           "moe_layer_backward")
+           "moe_layer_backward", "moe_layer_fused_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20     # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoEError(RuntimeError):
@@ -64,6 +66,7 @@ _SIG = {
     "moe_layer_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 20 + [_P, ctypes.c_size_t, _P]),
     "moe_layer_fused_marked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 20
                                + [_P, ctypes.c_size_t, _P, _P]),
+    "moe_layer_fused_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 20 + [_P]),
     "moe_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "moe_layer_forward_train": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_P] * 22
                                 + [_P, ctypes.c_size_t, _P]),
@@ -164,6 +167,20 @@ def layer_fused(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh
         arr = (ctypes.c_void_p * 6)(*events)
         _check(lib().moe_layer_fused_marked(*args, ctypes.cast(arr, ctypes.c_void_p)),
                "moe_layer_fused_marked")
+
+
+def layer_fused_noalloc(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate,
+                        sh_up, sh_down, y, topk_ids=None, topk_gates=None, counts=None,
+                        f_out=None, p_out=None, l_aux=None, stream=None, z_loss=None,
+                        entropy=None, cap_stats=None):
+    """moe_layer_fused_noalloc: the fused layer on the library's static
+    scratch (no workspace argument)."""
+    _check(lib().moe_layer_fused_noalloc(
+        ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(b_select),
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),
+        _ptr(y), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _ptr(f_out), _ptr(p_out),
+        _ptr(l_aux), _ptr(z_loss), _ptr(entropy), _ptr(cap_stats), _stream(stream)),
+        "moe_layer_fused_noalloc")
 
 
 def layer_forward_train(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate,

@@ -167,11 +167,24 @@ int64_t split_floats(const moe_shape* s) {
 struct FfnWs {
   size_t act, part, cnt, end;
 };
-FfnWs ffn_ws(const moe_shape* s, size_t base) {
+// Whether the forward launches a grouped (tiled) GEMM, whose split-K tail
+// uses the partial-sum region: bf16 with more than 64 rows per expert, or a
+// shared expert over more than 64 tokens (at most 64 rows, the weight-
+// streaming kernels run, which need no partials).
+bool grouped_gemm_used(const moe_shape* s) {
+  if (s->dtype != MOE_BF16) return false;
+  const int C = expert_capacity(s);
+  const int rows_max = C ? std::min(s->T, C) : s->T;
+  return rows_max > 64 || (s->d_ff_shared && s->T > 64);
+}
+// trim: no partial-sum region when no grouped GEMM runs (the layout of the
+// allocation-free forward; the caller-workspace calls keep the full one,
+// which the training forward also uses at every row count).
+FfnWs ffn_ws(const moe_shape* s, size_t base, bool trim = false) {
   FfnWs w;
   w.act = base;
   w.part = align_up(w.act + act_bytes(s));
-  const int64_t f = split_floats(s);
+  const int64_t f = (trim && !grouped_gemm_used(s)) ? 0 : split_floats(s);
   w.cnt = align_up(w.part + sizeof(float) * (size_t)f);
   w.end = f ? align_up(w.cnt + sizeof(int32_t) * moe::kSplitCounters) : w.cnt;
   return w;
@@ -186,7 +199,7 @@ struct FusedWs {
   FfnWs x;
   size_t p_mean, ids, gates, counts, offsets, perm, row_of, f, dhist, cmb, rows, end;
 };
-FusedWs fused_ws(const moe_shape* s) {
+FusedWs fused_ws(const moe_shape* s, bool trim = false) {
   FusedWs w;
   w.r = route_ws(s, 0);
   const size_t T = s->T, N = s->N, R = T * s->k;
@@ -200,7 +213,7 @@ FusedWs fused_ws(const moe_shape* s) {
   w.f = align_up(w.row_of + 4 * R);
   w.dhist = align_up(w.f + 4 * N + 4);
   w.cmb = w.dhist + dispatch_ws_bytes(s);
-  w.x = ffn_ws(s, align_up(w.cmb + 4 * (size_t)moe::combine_counters(s->d)));
+  w.x = ffn_ws(s, align_up(w.cmb + 4 * (size_t)moe::combine_counters(s->d)), trim);
   w.rows = w.x.end;
   w.end = align_up(w.rows + esize(s) * (R + (s->d_ff_shared ? T : 0)) * s->d);
   return w;
@@ -234,6 +247,36 @@ int num_cu() {
 moe_status hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// ----------------------------------------------- allocation-free scratch
+// The workspace of moe_layer_fused_noalloc: a file-scope device array, of
+// which every GPU the library runs on holds its own copy until the process
+// ends. In host code the array's name is a host-side stand-in, never a
+// device address: the address of the current device's copy comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept; only that address reaches kernels.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char g_noalloc_scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+
+moe_status noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {nullptr};
+  int dev = -1;
+  TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device index beyond 63 for the static scratch");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(g_noalloc_scratch)),
+                  "hipGetSymbolAddress(scratch)"));
+    if (!p || !aligned16(p)) return fail(MOE_ERR_HIP, "scratch address is not usable");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
   return MOE_OK;
 }
 
@@ -393,7 +436,8 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
                       float* topk_gates, int32_t* counts, float* f_out, float* p_out,
                       float* l_aux, float* z_loss, float* entropy, float* cap_stats, void* ws,
                       size_t ws_bytes, void* stream, void* const* events,
-                      const TrainOut& train = TrainOut{nullptr, nullptr, nullptr, nullptr}) {
+                      const TrainOut& train = TrainOut{nullptr, nullptr, nullptr, nullptr},
+                      bool noalloc = false) {
   TRY(check_shape(s));
   TRY(need16(h, "h"));
   TRY(need16(w_router, "w_router"));
@@ -416,9 +460,20 @@ moe_status layer_impl(const moe_shape* s, const void* h, const void* w_router,
   TRY(opt4(train.perm, "perm_src"));
   TRY(opt4(train.row_of, "row_of"));
   TRY(opt4(train.preact, "preact"));
-  const FusedWs L = fused_ws(s);
-  TRY(check_ws(ws, ws_bytes, L.end));
-  if (s->T == 0) return MOE_OK;
+  const FusedWs L = fused_ws(s, noalloc);
+  if (noalloc) {
+    if (L.end > kNoAllocScratchBytes)
+      return fail(MOE_ERR_WORKSPACE,
+                  "this shape needs " + std::to_string(L.end) + " bytes of scratch, more than "
+                  "the " + std::to_string(kNoAllocScratchBytes) + " the allocation-free call "
+                  "holds; use moe_layer_fused with a workspace");
+    if (s->T == 0) return MOE_OK;
+    TRY(noalloc_scratch(&ws));
+    ws_bytes = L.end;
+  } else {
+    TRY(check_ws(ws, ws_bytes, L.end));
+    if (s->T == 0) return MOE_OK;
+  }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
@@ -964,6 +1019,21 @@ moe_status moe_layer_fused(const moe_shape* s, const void* h, const void* w_rout
   return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                     sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss,
                     entropy, cap_stats, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_fused_noalloc(const moe_shape* s, const void* h, const void* w_router,
+                                   const float* b_router, const float* b_select,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   const void* sh_gate, const void* sh_up, const void* sh_down,
+                                   void* y, int32_t* topk_ids, float* topk_gates,
+                                   int32_t* counts, float* f_out, float* p_out, float* l_aux,
+                                   float* z_loss, float* entropy, float* cap_stats,
+                                   void* stream) {
+  g_err.clear();
+  return layer_impl(s, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
+                    sh_down, y, topk_ids, topk_gates, counts, f_out, p_out, l_aux, z_loss,
+                    entropy, cap_stats, nullptr, 0, stream, nullptr,
+                    TrainOut{nullptr, nullptr, nullptr, nullptr}, true);
 }
 
 moe_status moe_layer_forward_train(const moe_shape* s, const void* h, const void* w_router,

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(M.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def test_status_strings():
@@ -243,3 +243,22 @@ def test_forward_train_validates():
     assert st == M.ERR_INVALID_ARG and "preact" in err
     st, err = call(h=None)
     assert st == M.ERR_INVALID_ARG and "h" in err
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """The allocation-free call checks its arguments and its scratch limit
+    before any HIP call: a shape that needs more than the 64 MiB static
+    scratch (the Mixtral prefill layer: Act alone is 235 MB) is refused with
+    MOE_ERR_WORKSPACE, a bad shape with MOE_ERR_INVALID_ARG."""
+    lib = M.lib()
+    big = M.Shape(4096, 4096, 8, 2, 14336, 0, M.BF16, M.SOFTMAX_RENORM, 0.01)
+    st = lib.moe_layer_fused_noalloc(ctypes.byref(big), *([FAKE] * 3 + [None] * 1 + [FAKE] * 3
+                                                         + [None] * 3 + [FAKE] + [None] * 9),
+                                     None)
+    assert st == M.ERR_WORKSPACE
+    assert "64" in lib.moe_last_error().decode() or "67108864" in lib.moe_last_error().decode()
+    bad = shape(k=9)
+    st = lib.moe_layer_fused_noalloc(ctypes.byref(bad), *([FAKE] * 3 + [None] + [FAKE] * 3
+                                                         + [None] * 3 + [FAKE] + [None] * 9),
+                                     None)
+    assert st == M.ERR_INVALID_ARG
