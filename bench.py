@@ -89,10 +89,11 @@ def measured_traffic(workload, kernel):
         return None
 
 
-def library_gemm(torch, w, steps=10, warmup=3):
+def library_gemm(torch, w, steps=10, warmup=3, seconds=0.0):
     """Context only: the vendor library (hipBLASLt through torch.bmm) on the
     uniform-batch equivalent of the gate/up GEMM of the workload, N
-    experts x [T k / N rows, d] x [d, 2 d_ff], bf16. Prints one JSON line."""
+    experts x [T k / N rows, d] x [d, 2 d_ff], bf16. Prints one JSON line.
+    seconds > 0: back to back for that long instead (power sampling)."""
     rows = w.T * w.k // w.N
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
@@ -101,6 +102,21 @@ def library_gemm(torch, w, steps=10, warmup=3):
     c = torch.empty(w.N, rows, 2 * w.d_ff, device="cuda", dtype=torch.bfloat16)
     for _ in range(warmup):
         torch.bmm(a, b, out=c)
+    if seconds > 0:
+        torch.cuda.synchronize()
+        t0, n = time.time(), 0
+        print(json.dumps({"sustain_start_unix": t0}), flush=True)
+        while time.time() - t0 < seconds:
+            for _ in range(20):
+                torch.bmm(a, b, out=c)
+            torch.cuda.synchronize()
+            n += 20
+        dt = time.time() - t0
+        fl = 2.0 * w.N * rows * w.d * 2 * w.d_ff
+        print(json.dumps({"library_gemm": "torch.bmm (hipBLASLt)", "sustain_s": dt, "steps": n,
+                          "ms": dt / n * 1e3, "tflops": fl / (dt / n) / 1e12,
+                          "sustain_end_unix": time.time()}), flush=True)
+        return
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev[0].record()
@@ -241,6 +257,35 @@ def layer_work(w, counts):
 
 
 
+def stage_work(w, counts):
+    """Algorithmic work of each GEMM stage and of the layer: flops (padding
+    rows never count) and bytes (each touched expert's weights once, the
+    activations each stage reads and writes, the Act and out_rows round
+    trips). counts: the rows each expert computes."""
+    rows = int(counts.sum())
+    touched = int((counts > 0).sum())
+    eb = 2 if w.dtype == W.DTYPE_BF16 else 4
+    d, f, fs, T = w.d, w.d_ff, w.d_ff_shared, w.T
+    gu_fl = 4.0 * d * f * rows + 4.0 * d * fs * T
+    dn_fl = 2.0 * d * f * rows + 2.0 * d * fs * T
+    gu_b = (touched * 2 * f * d + 2 * fs * d + rows * (d + f) + (T * (d + fs) if fs else 0)) * eb
+    dn_b = (touched * f * d + fs * d + rows * (f + d) + (T * (fs + d) if fs else 0)) * eb
+    route_b = (T * d + w.N * d) * eb
+    combine_b = (rows + (T if fs else 0) + T) * d * eb
+    return {"gate_up": (gu_fl, gu_b), "down": (dn_fl, dn_b),
+            "layer": (gu_fl + dn_fl, gu_b + dn_b + route_b + combine_b)}
+
+
+def fractions(flops, nbytes, ms):
+    """Achieved rates of algorithmic work over a duration, as fractions of
+    both MI355X peaks (bf16 dense MFMA and HBM)."""
+    s = ms * 1e-3
+    tf, gbs = flops / s / 1e12, nbytes / s / 1e9
+    return {"ms": ms, "tflops": tf, "frac_mfma_peak": tf / PEAK_BF16_TFLOPS,
+            "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+            "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+
+
 def kept_counts(w, counts):
     """Rows each expert computes: all routed slots, or at most C of them."""
     if not w.capacity_factor:
@@ -259,8 +304,12 @@ def run_variant(M, torch, w, steps, warmup):
     kept = kept_counts(w, counts)
     flops_gu, _, touched = gateup_work(w, kept)
     gu = flops_gu / (run_layer.gate_up_timed * 1e-3) / 1e12
+    sw = stage_work(w, kept)
     out = {"workload": w.name, "tokens_per_s": w.T * steps / wall,
            "ms_per_step": wall / steps * 1e3, "stages_ms": stage,
+           "layer": fractions(*sw["layer"], wall / steps * 1e3),
+           "kernels": {"gate_up": fractions(*sw["gate_up"], run_layer.gate_up_timed),
+                       "down": fractions(*sw["down"], stage["down"])},
            "gate_up_tflops": gu, "gate_up_frac_mfma_peak": gu / PEAK_BF16_TFLOPS,
            "rows_computed": int(kept.sum()), "experts_touched": touched,
            "z_loss": float(extra["z_loss"][0]), "entropy": float(extra["entropy"][0])}
@@ -427,6 +476,116 @@ def cpu_baseline(w, inp, sample_tokens, min_seconds=10.0, max_reps=5):
                       f"experts, combine, stats) in float64 numpy, {reps} pass(es) in {dt:.1f} s"}
 
 
+def run_tiny(M, torch, steps=200, warmup=20):
+    """The tiny fp32 configuration (both of its routing modes) on the GPU:
+    latency per fused step, host-drawn inputs moved to the device first."""
+    res = []
+    for w in (W.TINY, W.TINY_SWITCH):
+        host = W.host_inputs(w)
+        inp = {k_: (None if v is None else torch.from_numpy(v).cuda()) for k_, v in host.items()}
+        torch.cuda.synchronize()
+        wall, stage, _, counts = run_layer(M, torch, w, inp, steps, warmup, gate_up_events=False)
+        ms = wall / steps * 1e3
+        res.append({"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.T * steps / wall,
+                    "layer": fractions(*stage_work(w, counts)["layer"], ms)})
+    return res
+
+
+def host_info():
+    """CPU model, logical CPUs, CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count() or 1, "usable_cpus": usable}
+
+
+def cpu_extras(torch, w, inp, decode_tokens, variants):
+    """The rest of the CPU-baseline leg: the oracle on the tiny fp32
+    configuration with one BLAS thread and with all of them, and the
+    oracle's near-tie count (k-th minus (k+1)-th selection score below 1e-4,
+    the tokens whose expert set may legitimately differ from the GPU's) for
+    every configuration this run measured."""
+    from oracle import moe_oracle as O
+    from threadpoolctl import threadpool_limits
+
+    def oracle_layer_rate(wt, host, seconds=2.0):
+        sh = None if host["sh_gate"] is None else (host["sh_gate"], host["sh_up"], host["sh_down"])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            O.layer(host["h"], host["w_router"], wt.k, wt.mode,
+                    O.weights_getter(host["w_gate"], host["w_up"], host["w_down"]),
+                    host["b_router"], host["b_select"], sh, wt.aux_alpha)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                return wt.T * reps / dt
+
+    tiny = []
+    for wt in (W.TINY, W.TINY_SWITCH):
+        host = W.host_inputs(wt)
+        with threadpool_limits(limits=1):
+            one = oracle_layer_rate(wt, host)
+        tiny.append({"workload": wt.name, "tokens_per_s_1_thread": one,
+                     "tokens_per_s_all_threads": oracle_layer_rate(wt, host)})
+
+    def near(wt, h, wr, br, bs):
+        r = O.route(h, wr, wt.k, wt.mode, br, bs, wt.groups)
+        return {"tokens": int(h.shape[0]), "near_tie": int(O.near_tie_tokens(r.gap).sum())}
+
+    f64 = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
+    ties = {}
+    hw = f64(inp["h"])
+    args = (f64(inp["w_router"]), f64(inp["b_router"]), f64(inp["b_select"]))
+    ties[w.name] = near(w, hw, *args)
+    if decode_tokens and decode_tokens < w.T:
+        ties[f"{w.name} (first {decode_tokens} tokens, decode)"] = near(w, hw[:decode_tokens], *args)
+    for v in variants:
+        vi = W.device_inputs(v, with_weights=False)
+        ties[v.name] = near(v, f64(vi["h"]), f64(vi["w_router"]), f64(vi["b_router"]),
+                            f64(vi["b_select"]))
+        del vi
+    for wt in (W.TINY, W.TINY_SWITCH):
+        host = W.host_inputs(wt, with_weights=False)
+        ties[wt.name] = near(wt, host["h"], host["w_router"], host["b_router"], host["b_select"])
+    return {"tiny_fp32": tiny, "near_tie_tokens": ties}
+
+
+def sustain(M, torch, w, inp, seconds):
+    """The fused step back to back for `seconds` (for sampling board power
+    and clocks from outside, e.g. amd-smi): prints one JSON line."""
+    g = w.groups or (0, 0, 0)
+    s = M.Shape(w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.mode, w.aux_alpha, *g,
+                capacity_factor=w.capacity_factor)
+    layer = M.MoELayer(s)
+    y = torch.empty_like(inp["h"])
+    args = dict(b_router=inp["b_router"], b_select=inp["b_select"], sh_gate=inp["sh_gate"],
+                sh_up=inp["sh_up"], sh_down=inp["sh_down"])
+    for _ in range(3):
+        layer(inp["h"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], out=y, **args)
+    torch.cuda.synchronize()
+    t0, n = time.time(), 0
+    print(json.dumps({"sustain_start_unix": t0}), flush=True)
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            layer(inp["h"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], out=y,
+                  **args)
+        torch.cuda.synchronize()
+        n += 20
+    dt = time.time() - t0
+    print(json.dumps({"workload": w.name, "sustain_s": dt, "steps": n,
+                      "ms_per_step": dt / n * 1e3, "sustain_end_unix": time.time()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +605,11 @@ def main():
                     help="skip the capacity / group-limited / fine-grained variant workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="run the workload's fused step back to back for this many seconds "
+                         "(board power and clock sampling) and exit")
+    ap.add_argument("--no-tiny", action="store_true",
+                    help="skip the tiny fp32 configuration's GPU timing")
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor library on the uniform-batch equivalent of the "
                          "workload's gate/up GEMM (context) and exit")
@@ -465,13 +629,16 @@ def main():
         copy_calibration(torch)
         return
     if a.library_gemm:
-        library_gemm(torch, W.ALL[a.workload], a.steps, a.warmup)
+        library_gemm(torch, W.ALL[a.workload], a.steps, a.warmup, a.sustain)
         return
     M.lib()   # fail loudly if the HIP library is missing
 
     w = W.ALL[a.workload]
     inp = W.device_inputs(w)
     torch.cuda.synchronize()
+    if a.sustain > 0:
+        sustain(M, torch, w, inp, a.sustain)
+        return
     wall, stage, total_ev, counts = run_layer(M, torch, w, inp, a.steps, a.warmup)
     gu_ms = run_layer.gate_up_timed
     ms = wall / a.steps * 1e3
@@ -504,11 +671,12 @@ def main():
                    "d_ff_shared": w.d_ff_shared, "gate_mode": w.mode,
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "layer": {"tflops": lflops / (ms * 1e-3) / 1e12,
-                  "frac_mfma_peak": lflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "layer": {**fractions(*stage_work(w, counts)["layer"], ms),
                   "weight_gbs": lbytes / (ms * 1e-3) / 1e9,
                   "stages_ms": stage, "events_total_ms": total_ev,
                   "experts_touched": touched, "max_rows": int(counts.max())},
+        "kernels": {"gate_up": fractions(*stage_work(w, counts)["gate_up"], gu_ms),
+                    "down": fractions(*stage_work(w, counts)["down"], stage["down"])},
     }
     if not a.no_decode and w.T > a.decode_tokens:
         wd = w.replace(name=re.sub(r"prefill_T\d+", f"decode_T{a.decode_tokens}", w.name),
@@ -525,6 +693,7 @@ def main():
         _, dbytes, dtouched = layer_work(wd, dcounts)
         out["decode"] = {"workload": wd.name, "tokens_per_s": wd.T * dsteps / dwall,
                          "ms_per_step": dms, "experts_touched": dtouched,
+                         "layer": fractions(*stage_work(wd, dcounts)["layer"], dms),
                          "weight_bytes": dbytes,
                          "hbm_gbs_layer": dbytes / (dms * 1e-3) / 1e9,
                          "frac_hbm_peak_layer": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -550,10 +719,9 @@ def main():
         # rows in and out) against the counted HBM bytes per launch
         gb = {"gate_up": gateup_work(wd, dcounts)[1],
               "down": dtouched * w.d * w.d_ff * 2 + int(dcounts.sum()) * (w.d + w.d_ff) * 2}
+        dsw = stage_work(wd, dcounts)
         out["decode"]["kernels"] = {
-            n: {"ms": dstage[n], "algorithmic_bytes": gb[n],
-                "gbs": gb[n] / (dstage[n] * 1e-3) / 1e9,
-                "frac_hbm_peak": gb[n] / (dstage[n] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            n: {**fractions(dsw[n][0], gb[n], dstage[n]),
                 "traffic": measured_traffic(wd.name, f"skinny_gemm_{n.replace('_', '')}")}
             for n in ("gate_up", "down")}
     if not a.no_backward:
@@ -563,8 +731,14 @@ def main():
         torch.cuda.empty_cache()
         out["variants"] = [run_variant(M, torch, v, a.steps, a.warmup) for v in VARIANTS]
         inp = W.device_inputs(w)
+    if not a.no_tiny:
+        out["tiny_fp32"] = run_tiny(M, torch)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_sample)
+        cb = cpu_baseline(w, inp, a.cpu_sample)
+        cb.update(host_info())
+        cb.update(cpu_extras(torch, w, inp, 0 if a.no_decode else a.decode_tokens,
+                             () if a.no_variants else VARIANTS))
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

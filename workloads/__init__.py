@@ -200,10 +200,12 @@ def device_seed(cfg_id: int, tid: int, expert: int = 0) -> int:
     return (cfg_id << 40) | (tid << 20) | expert
 
 
-def device_inputs(w: Workload, device="cuda") -> dict:
+def device_inputs(w: Workload, device="cuda", with_weights: bool = True) -> dict:
     """Inputs of workload ``w`` drawn on the GPU with torch's generator
     (for the full-size workloads). Returns torch tensors in the workload's
-    dtype (biases fp32). The oracle reads them back with ``.cpu()``."""
+    dtype (biases fp32). The oracle reads them back with ``.cpu()``.
+    with_weights=False: the routing inputs only (h, w_router, the biases),
+    the same values; the expert weights are None."""
     import torch
 
     tdt = torch.bfloat16 if w.dtype == DTYPE_BF16 else torch.float32
@@ -231,6 +233,11 @@ def device_inputs(w: Workload, device="cuda") -> dict:
 
     def estd(fan_in):
         return w.expert_std if w.expert_std is not None else 1.0 / math.sqrt(fan_in)
+
+    if not with_weights:
+        for key in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+            out[key] = None
+        return out
 
     def stack(tid, shape, fan_in):
         t = torch.empty((w.N,) + shape, device=device, dtype=tdt)
