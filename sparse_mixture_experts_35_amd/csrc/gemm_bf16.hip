@@ -68,8 +68,8 @@ struct TileCfg {
   static constexpr int NLW = NAW + NBW;             // direct-to-LDS loads per wave per slab
   static_assert(FM >= 1 && FN >= 1, "tile too small");
   static_assert(BM % (4 * RPI) == 0 && BROWS % (4 * RPI) == 0, "tile rows vs load blocks");
-  static_assert((BK == 32 && (STAGES == 3 || STAGES == 4)) || (BK == 64 && STAGES == 2),
-                "pipeline shape");
+  static_assert((BK == 32 && (STAGES == 3 || STAGES == 4)) ||
+                (BK == 64 && (STAGES == 2 || STAGES == 3)), "pipeline shape");
   static constexpr bool NN = NN_;
   static constexpr int BROWB = BN * 2;              // NN: bytes of one staged B row (one k)
   static_assert(!NN || (!DUAL && BK * BROWB == BROWS * ROWB && BROWB % 256 == 0),
@@ -109,11 +109,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // (RPI rows, 1 KiB each); lane l of a block writes bytes [16 l, 16 l + 16)
 // of the block, i.e. row l / CH, physical chunk l % CH, so it loads logical
 // chunk (l % CH) ^ swz(row).
-// PART selects the loads: all of them (-1), or the first (0) or second (1)
-// half of the wave's list (A blocks, then B blocks).
+// PART selects the loads: all of them (-1), the first (0) or second (1)
+// half of the wave's list (A blocks, then B blocks), or the A (2) or B (3)
+// blocks only.
 // NN: B0 is this slab's B source and kbytes_b the byte offset of its first
 // row (A still advances by kbytes).
-template <class C, int PART = -1>
+// 64-deep slabs: wave w fills A blocks NAW w .. NAW w + NAW - 1 instead (the
+// rows BM/4 w .. BM/4 (w + 1) - 1, inside its own row range), and issues only
+// the first NA of them: blocks wholly past the tile's last row would load
+// zeros, which costs the fill path as much as loading data.
+template <class C, int PART = -1, int NA = C::NAW>
 __device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const uint32_t* aoff,
                                          Rsrc B0, Rsrc B1, const uint32_t* boff, int kbytes,
                                          int kbytes_b) {
@@ -121,9 +126,12 @@ __device__ __forceinline__ void dma_slab(char* __restrict__ st, Rsrc A, const ui
   const int kb = C::NN ? kbytes_b : kbytes;                          // B's offset along K
 #pragma unroll
   for (int q = 0; q < C::NLW; ++q) {
-    if (PART >= 0 && (q < C::NLW / 2) != (PART == 0)) continue;
+    if ((PART == 0 || PART == 1) && (q < C::NLW / 2) != (PART == 0)) continue;
+    if ((PART == 2 && q >= C::NAW) || (PART == 3 && q < C::NAW)) continue;
     if (q < C::NAW) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(A, (lds_ptr_t)(st + (w + 4 * q) * 1024), 16,
+      if (q >= NA) continue;
+      const int slot = C::BK == 64 ? C::NAW * w + q : w + 4 * q;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(A, (lds_ptr_t)(st + slot * 1024), 16,
                                                aoff[q], kbytes, 0, 0);
     } else {
       const int j = q - C::NAW;
@@ -275,8 +283,9 @@ __device__ __forceinline__ void k_step(char* __restrict__ cur, char* __restrict_
 // wave's reads of `cur`) and the barrier come after the third k-step, and
 // the last k-step, which reads the next slab's first fragments, issues the
 // first half of the slab after next into `cur`. No branch inside: loads
-// past the last slab re-load it into the free stage.
-template <class C, int V>
+// past the last slab re-load it into the free stage. The first half is the
+// A blocks (NA of them issued), the second the B blocks.
+template <class C, int V, int NA>
 __device__ __forceinline__ void slab_k64(char* __restrict__ cur, char* __restrict__ nxt,
                                          int knext, int knext2, Frags<C>& f0, Frags<C>& f1,
                                          Rsrc A, const uint32_t* aoff, Rsrc B0, Rsrc B1,
@@ -296,32 +305,109 @@ __device__ __forceinline__ void slab_k64(char* __restrict__ cur, char* __restric
   __builtin_amdgcn_s_barrier();
   read_frags<C, V>(nxt, 0, f0);
   mma<C, V>(f1, acc);
-  dma_slab<C, 0>(cur, A, aoff, B0, B1, boff, knext2, knext2);
-  weave<C, V, C::NLW / 2, true, true>();
+  dma_slab<C, 0, NA>(cur, A, aoff, B0, B1, boff, knext2, knext2);
+  weave<C, V, NA, true, true>();
 }
 
-template <class C, int V>
+// A blocks wave (wm, wn) must load for V valid row blocks of its wave row:
+// those that start below row 32 V of the wave row.
+template <class C>
+constexpr int na_k64(int V, int wn) {
+  const int n = (32 * V - wn * C::NAW * C::RPI) / C::RPI;
+  return n < 0 ? 0 : (n > C::NAW ? C::NAW : n);
+}
+
+template <class C, int V, int NA>
 __device__ __forceinline__ void mainloop_k64(char* __restrict__ S0, char* __restrict__ S1, Rsrc A,
                                              const uint32_t* aoff, Rsrc B0, Rsrc B1,
                                              const uint32_t* boff, int k_begin, int k_len,
                                              f32x16 (&acc)[C::NB][C::FM][C::FN]) {
   static_assert(C::BK == 64 && C::STAGES == 2 && !C::NN, "64-deep slabs: two stages");
+  static_assert(C::NAW == C::NBW && C::WN * C::NAW * C::RPI == C::TM,
+                "A blocks are the first half of a wave's loads; a wave row's waves load its rows");
   constexpr int STEP = C::BK * 2;
   const int KT = k_len / C::BK;
   const int kb = k_begin * 2;
   auto kbyte = [&](int k) { return kb + min(k, KT - 1) * STEP; };
   Frags<C> f0, f1;
-  dma_slab<C>(S0, A, aoff, B0, B1, boff, kb, kb);
+  dma_slab<C, -1, NA>(S0, A, aoff, B0, B1, boff, kb, kb);
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   read_frags<C, V>(S0, 0, f0);
-  dma_slab<C, 0>(S1, A, aoff, B0, B1, boff, kbyte(1), kbyte(1));
+  dma_slab<C, 0, NA>(S1, A, aoff, B0, B1, boff, kbyte(1), kbyte(1));
   int k = 0;
   for (; k + 2 <= KT; k += 2) {
-    slab_k64<C, V>(S0, S1, kbyte(k + 1), kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
-    slab_k64<C, V>(S1, S0, kbyte(k + 2), kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+    slab_k64<C, V, NA>(S0, S1, kbyte(k + 1), kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+    slab_k64<C, V, NA>(S1, S0, kbyte(k + 2), kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
   }
-  if (k < KT) slab_k64<C, V>(S0, S1, kbyte(k + 1), kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+  if (k < KT)
+    slab_k64<C, V, NA>(S0, S1, kbyte(k + 1), kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+  wait_vmcnt<0>();
+  __syncthreads();
+}
+
+// ------------------------------------------------- 64-deep slabs, 3 stages
+// Loads run two slabs ahead, so twice the bytes are in flight: for tiles of
+// few rows the weight columns come from HBM at every slab, and one slab in
+// flight per CU leaves HBM latency-bound. Slab k computes from stage k % 3;
+// its first k-step issues the B blocks of slab k + 2, its second the A
+// blocks, into the stage slab k - 1 used (its reads ended before the
+// barrier that closed slab k - 1). After the third k-step a wave waits until
+// at most slab k + 2's loads are outstanding (loads complete in issue
+// order), then the barrier; the fourth k-step reads slab k + 1's first
+// fragments. Loads past the last slab re-load it into the free stage.
+template <class C, int V, int NA>
+__device__ __forceinline__ void slab_k64_3(char* __restrict__ cur, char* __restrict__ nxt,
+                                           char* __restrict__ dst, int kload, Frags<C>& f0,
+                                           Frags<C>& f1, Rsrc A, const uint32_t* aoff, Rsrc B0,
+                                           Rsrc B1, const uint32_t* boff,
+                                           f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  read_frags<C, V>(cur, 1, f1);
+  mma<C, V>(f0, acc);
+  dma_slab<C, 3>(dst, A, aoff, B0, B1, boff, kload, kload);
+  weave<C, V, C::NBW, true, true>();
+  read_frags<C, V>(cur, 2, f0);
+  mma<C, V>(f1, acc);
+  dma_slab<C, 2, NA>(dst, A, aoff, B0, B1, boff, kload, kload);
+  weave<C, V, NA, true, true>();
+  read_frags<C, V>(cur, 3, f1);
+  mma<C, V>(f0, acc);
+  weave<C, V, 0, true, true>();
+  wait_vmcnt_lds<NA + C::NBW>();
+  __builtin_amdgcn_s_barrier();
+  read_frags<C, V>(nxt, 0, f0);
+  mma<C, V>(f1, acc);
+  weave<C, V, 0, true, true>();
+}
+
+template <class C, int V, int NA>
+__device__ __forceinline__ void mainloop_k64_3(char* __restrict__ S0, char* __restrict__ S1,
+                                               char* __restrict__ S2, Rsrc A,
+                                               const uint32_t* aoff, Rsrc B0, Rsrc B1,
+                                               const uint32_t* boff, int k_begin, int k_len,
+                                               f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+  static_assert(C::BK == 64 && C::STAGES == 3 && !C::NN, "64-deep slabs: three stages");
+  static_assert(C::WN * C::NAW * C::RPI == C::TM, "a wave row's waves load its rows");
+  constexpr int STEP = C::BK * 2;
+  const int KT = k_len / C::BK;
+  const int kb = k_begin * 2;
+  auto kbyte = [&](int k) { return kb + min(k, KT - 1) * STEP; };
+  Frags<C> f0, f1;
+  dma_slab<C, -1, NA>(S0, A, aoff, B0, B1, boff, kb, kb);
+  dma_slab<C, -1, NA>(S1, A, aoff, B0, B1, boff, kbyte(1), kbyte(1));
+  wait_vmcnt<NA + C::NBW>();
+  __builtin_amdgcn_s_barrier();
+  read_frags<C, V>(S0, 0, f0);
+  int k = 0;
+  for (; k + 3 <= KT; k += 3) {
+    slab_k64_3<C, V, NA>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+    slab_k64_3<C, V, NA>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
+    slab_k64_3<C, V, NA>(S2, S0, S1, kbyte(k + 4), f0, f1, A, aoff, B0, B1, boff, acc);
+  }
+  if (k < KT)
+    slab_k64_3<C, V, NA>(S0, S1, S2, kbyte(k + 2), f0, f1, A, aoff, B0, B1, boff, acc);
+  if (k + 1 < KT)
+    slab_k64_3<C, V, NA>(S1, S2, S0, kbyte(k + 3), f0, f1, A, aoff, B0, B1, boff, acc);
   wait_vmcnt<0>();
   __syncthreads();
 }
@@ -358,7 +444,20 @@ __device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict
     return kbyte(k);
   };
   if constexpr (C::BK == 64) {
-    mainloop_k64<C, V>(S0, S1, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+    // the wave's A block count depends on its column in the wave grid too
+    constexpr int NA0 = na_k64<C>(V, 0), NA1 = na_k64<C>(V, 1);
+    const bool first = NA0 == NA1 || __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % C::WN == 0;
+    if constexpr (C::STAGES == 3) {
+      if (first)
+        mainloop_k64_3<C, V, NA0>(S0, S1, S2, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+      else
+        mainloop_k64_3<C, V, NA1>(S0, S1, S2, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+    } else {
+      if (first)
+        mainloop_k64<C, V, NA0>(S0, S1, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+      else
+        mainloop_k64<C, V, NA1>(S0, S1, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+    }
     return;
   }
   Frags<C> f0, f1;
@@ -571,7 +670,8 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // Per-lane load offsets of the DMA blocks of wave w: A block w + 4j holds
-// tile rows RPI(w + 4j) .. +RPI-1; lane l loads row RPI(w+4j) + l/CH, logical
+// tile rows RPI(w + 4j) .. +RPI-1 (64-deep slabs: block NAW w + j, rows
+// RPI(NAW w + j) .. +RPI-1); lane l loads the block's row l/CH, logical
 // chunk (l % CH) ^ swz(row). Rows past the group's end load zeros: their
 // MFMAs then work on zero operands, which draws less power than repeating a
 // real row (the GEMMs run at the power limit), and they are never stored.
@@ -583,7 +683,7 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (
   const int rl = lane / C::CH, ch = lane % C::CH;
 #pragma unroll
   for (int j = 0; j < C::NAW; ++j) {
-    const int row = C::RPI * (w + 4 * j) + rl;
+    const int row = C::RPI * (C::BK == 64 ? C::NAW * w + j : w + 4 * j) + rl;
     const int r = m0 + row;
     if (r >= m_end) {
       aoff[j] = 0x80000000u;    // past the descriptor's extent: the load returns zeros
@@ -628,6 +728,10 @@ struct TileInfo {
 };
 template <class C>
 __device__ __forceinline__ int tile_group_width(int total_mt, int G) {
+  // 128-row tiles on 64-deep slabs: at most 2 m-tiles per expert on average
+  // (DeepSeek-V3 shape, down: 2.04 -> 1.93 ms; the Qwen3-30B shape, 4.5
+  // m-tiles per expert, measured no gain)
+  if constexpr (C::BK == 64 && C::STAGES == 3) return (!C::DUAL && total_mt <= 2 * G) ? 8 : 2;
   return (!C::DUAL && 2 * total_mt <= 3 * G) ? 8 : 2;
 }
 template <class C>
@@ -1361,6 +1465,9 @@ using Down256NN = TileCfg<256, 256, false, 4, 1, true>;
 // the 256-row tiles on 64-deep slabs (two 64 KB stages)
 using GateUp256K = TileCfg<256, 128, true, 2, 1, false, 64>;
 using Down256K = TileCfg<256, 256, false, 2, 1, false, 64>;
+// few rows per expert: 128-row tiles, 64-deep slabs, three stages (144 KB)
+using GateUpMid = TileCfg<128, 128, true, 3, 1, false, 64>;
+using DownMid = TileCfg<128, 256, false, 3, 1, false, 64>;
 
 // Rows per expert at most 64: weight streaming. Otherwise 256-row tiles (one
 // block per CU) when experts average at least 1024 rows or the 256-row tile
@@ -1383,16 +1490,29 @@ static bool tall_tiles(const GroupedProblem& p, int bn, int num_cu) {
 // the board's power limit, so fewer requests buy a little clock).
 static bool k64_tiles(const GroupedProblem& p) { return p.K % 64 == 0; }
 
+// Fewer than 768 rows per expert on average: many tiles hold few rows and
+// stream their expert's weight columns from HBM at every slab. 128-row tiles
+// with three 64-deep stages keep two slabs in flight per CU instead of one
+// (DeepSeek-V3 shape, 128 rows per expert: gate/up 3.90 -> 3.40 ms; the
+// Qwen3-30B shape, 512 Zipf-skewed: 3% faster; the Mixtral shape, 1,024:
+// 5% slower, so it keeps the 256-row tiles).
+static bool mid_tiles(const GroupedProblem& p) {
+  const int64_t G = p.offsets ? p.groups : 1;
+  return p.K % 64 == 0 && p.M < 768 * G;
+}
+
 hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
   if (p.C2) {
     // keeping the pre-activations: the grouped tiles at any row count, the
     // same tiles and schedule as the backward's recompute
+    if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_SWIGLU_SAVE>(p, num_cu, st);
     if (tall_tiles(p, GateUp256::BN, num_cu))
       return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_SWIGLU_SAVE>(p, num_cu, st)
                           : launch_grouped<GateUp256, EPI_SWIGLU_SAVE>(p, num_cu, st);
     return launch_grouped<GateUp128, EPI_SWIGLU_SAVE>(p, num_cu, st);
   }
   if (p.max_rows <= 64) return launch_skinny_any<true>(p, st);
+  if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_SWIGLU>(p, num_cu, st);
   if (tall_tiles(p, GateUp256::BN, num_cu))
     return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_SWIGLU>(p, num_cu, st)
                         : launch_grouped<GateUp256, EPI_SWIGLU>(p, num_cu, st);
@@ -1415,6 +1535,7 @@ hipError_t launch_down_combine_bf16(const GroupedProblem& p, const CombineFuse& 
 
 hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
   if (p.max_rows <= 64) return launch_skinny_any<false>(p, st);
+  if (mid_tiles(p)) return launch_grouped<DownMid, EPI_STORE_BF16>(p, num_cu, st);
   if (tall_tiles(p, Down256::BN, num_cu))
     return k64_tiles(p) ? launch_grouped<Down256K, EPI_STORE_BF16>(p, num_cu, st)
                         : launch_grouped<Down256, EPI_STORE_BF16>(p, num_cu, st);
@@ -1448,6 +1569,7 @@ hipError_t launch_down_nn_f32out_bf16(const GroupedProblem& p, int num_cu, hipSt
 // (ldc = 2 Ncols): the same tiles and schedule as the SwiGLU launch, any row
 // count.
 hipError_t launch_gateup_preact_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
+  if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_STORE_DUAL_F32>(p, num_cu, st);
   if (tall_tiles(p, GateUp256::BN, num_cu))
     return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_STORE_DUAL_F32>(p, num_cu, st)
                         : launch_grouped<GateUp256, EPI_STORE_DUAL_F32>(p, num_cu, st);
