@@ -552,7 +552,7 @@ BwdWs bwd_ws(const moe_shape* s) {
   const int64_t T = s->T, N = s->N, k = s->k, d = s->d, dff = s->d_ff, dfs = s->d_ff_shared;
   const int64_t R = T * k;
   const size_t es = esize(s);
-  w.Rp = round_up(R + 32 * N, 64);
+  w.Rp = round_up(R + 64 * N, 64);
   w.Tp = round_up(T, 64);
   w.Np = round_up(N, 64);
   w.ta_rows = std::max(std::max(d, 2 * dff), std::max(2 * dfs, w.Np));

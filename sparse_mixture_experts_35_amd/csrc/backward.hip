@@ -49,16 +49,16 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return (bf16_t)f32
 
 constexpr int kT = 256;
 
-// kofs[e] = sum over e' < e of the kept rows of e' rounded up to 32 (the
-// padded K range of expert e in the transposed copies); with no offsets one
-// range of n_single rows.
+// kofs[e] = sum over e' < e of the kept rows of e' rounded up to 64 (the
+// padded K range of expert e in the transposed copies: whole 64-deep slabs
+// of the weight-gradient GEMMs); with no offsets one range of n_single rows.
 __global__ __launch_bounds__(kT) void kofs_kernel(const int32_t* __restrict__ offsets, int G,
                                                   int n_single, int32_t* __restrict__ kofs) {
   __shared__ int s_wave[kT / 64];
   if (!offsets) {
     if (threadIdx.x == 0) {
       kofs[0] = 0;
-      kofs[1] = (n_single + 31) & ~31;
+      kofs[1] = (n_single + 63) & ~63;
     }
     return;
   }
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kT) void kofs_kernel(const int32_t* __restrict__ of
   int c[2], sum = 0;
   for (int i = 0; i < 2; ++i) {
     const int e = 2 * tid + i;
-    c[i] = e < G ? ((offsets[e + 1] - offsets[e] + 31) & ~31) : 0;
+    c[i] = e < G ? ((offsets[e + 1] - offsets[e] + 63) & ~63) : 0;
     sum += c[i];
   }
   int incl = sum;

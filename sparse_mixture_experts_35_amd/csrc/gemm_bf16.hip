@@ -1052,10 +1052,10 @@ __global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
 }
 
 // Weight gradients: C_g = A[:, K_g] · B[:, K_g]^T for every group g, with
-// K_g = [kofs[g], kofs[g+1]) (multiples of 32, possibly empty) a column
-// range of the K-contiguous operands A [M rows, lda] and B [Ncols rows, ldb]
-// (the backward pass's transposed activations, one padded K range per
-// expert). C_g is [M, Ncols] at C + g * c_gstride, row-major with ldc,
+// K_g = [kofs[g], kofs[g+1]) (whole slabs of the tile configuration,
+// possibly empty) a column range of the K-contiguous operands A [M rows,
+// lda] and B [Ncols rows, ldb] (the backward pass's transposed activations,
+// one padded K range per expert). C_g is [M, Ncols] at C + g * c_gstride, row-major with ldc,
 // written as bf16 or fp32. Grid: (m-tiles x n-tiles, groups).
 template <class C, bool F32OUT>
 __global__ __launch_bounds__(kThreads, C::OCC) void kgroup_gemm_kernel(
@@ -1596,8 +1596,9 @@ hipError_t launch_kgroup_bf16(const void* A_, int lda, int64_t a_rows, const voi
     hipLaunchKernelGGL((kgroup_gemm_kernel<K, true>), grid, dim3(kThreads), 0, st, A, lda, ab, B,
                        ldb, bb, kofs, M, Ncols, C, c_gstride, ldc);
   } else if (M >= 512) {
-    // 256 x 256 tiles: half the operand traffic per flop of 128 x 256
-    using K = Down256;
+    // 256 x 256 tiles: half the operand traffic per flop of 128 x 256; the
+    // K ranges are whole 64-deep slabs
+    using K = Down256K;
     dim3 grid((unsigned)(((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN)), groups);
     hipLaunchKernelGGL((kgroup_gemm_kernel<K, false>), grid, dim3(kThreads), 0, st, A, lda, ab, B,
                        ldb, bb, kofs, M, Ncols, C, c_gstride, ldc);

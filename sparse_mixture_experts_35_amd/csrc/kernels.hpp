@@ -169,7 +169,7 @@ bool down_nn_ok(const GroupedProblem& p);
 hipError_t launch_down_nn_bf16(const GroupedProblem& p, int num_cu, hipStream_t st);
 hipError_t launch_down_nn_f32out_bf16(const GroupedProblem& p, int num_cu, hipStream_t st);
 // C_g = A[:, kofs[g]:kofs[g+1]] · B[:, kofs[g]:kofs[g+1]]^T for g < groups
-// (A [a_rows, lda] and B [b_rows, ldb] bf16, K ranges multiples of 32);
+// (A [a_rows, lda] and B [b_rows, ldb] bf16, K ranges multiples of 64);
 // C_g [M, Ncols] at C + g * c_gstride elements, bf16 or fp32 (f32out)
 hipError_t launch_kgroup_bf16(const void* A, int lda, int64_t a_rows,
                               const void* B, int ldb, int64_t b_rows,
@@ -183,8 +183,8 @@ hipError_t launch_down_f32(const GroupedProblem& p, hipStream_t st);
 hipError_t launch_gateup_preact_f32(const GroupedProblem& p, hipStream_t st);
 
 // ---------------------------------------------------------------- backward
-// Padded K ranges: kofs[e] = sum over e' < e of round32(kept rows of e'),
-// kofs[G] the total; offsets NULL: kofs = {0, round32(n_single)}.
+// Padded K ranges: kofs[e] = sum over e' < e of round64(kept rows of e'),
+// kofs[G] the total; offsets NULL: kofs = {0, round64(n_single)}.
 hipError_t launch_kofs(const int32_t* offsets, int G, int n_single,
                        int32_t* kofs, hipStream_t st);
 // dst[c][kofs[e] + i] = scale * src[row][c] for the i-th kept row of expert
