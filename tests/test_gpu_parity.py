@@ -175,6 +175,10 @@ CASES = [
     ("bf16_prefill_bm128", 300, 128, 5, 2, 192, 0, W.DTYPE_BF16, 0),
     ("bf16_prefill_bm128_shared", 257, 192, 12, 3, 128, 192, W.DTYPE_BF16, 2),
     ("bf16_prefill_bm256", 2304, 128, 2, 1, 320, 0, W.DTYPE_BF16, 1),
+    # at least 768 rows per expert but too few 256-row tiles to fill the
+    # chip: 128-row tiles on 32-deep slabs, two blocks per CU (routed and
+    # shared GEMMs); fewer rows per expert take the three-stage 64-deep tiles
+    ("bf16_prefill_bm128_k32", 900, 128, 2, 2, 192, 128, W.DTYPE_BF16, 0),
     ("bf16_prefill_many_experts", 520, 128, 64, 8, 128, 0, W.DTYPE_BF16, 0),
     ("bf16_k16_N512", 200, 64, 512, 16, 64, 0, W.DTYPE_BF16, 0),
     ("bf16_N1_k1", 100, 64, 1, 1, 64, 64, W.DTYPE_BF16, 0),
