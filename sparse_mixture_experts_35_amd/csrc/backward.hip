@@ -443,24 +443,6 @@ __global__ __launch_bounds__(kT) void dh_combine_kernel(
   }
 }
 
-// fp32 weight gradients: C_g[m][n] = sum over k in [kofs[g], kofs[g+1]) of
-// A[m][k] B[n][k]; one thread per output element.
-__global__ void kgroup_f32_kernel(const float* __restrict__ A, int lda,
-                                  const float* __restrict__ B, int ldb,
-                                  const int32_t* __restrict__ kofs, int M, int Ncols,
-                                  float* __restrict__ C, int64_t c_gstride, int ldc) {
-  const int g = blockIdx.y;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)M * Ncols) return;
-  const int m = (int)(idx / Ncols), n = (int)(idx % Ncols);
-  const int k0 = kofs[g], k1 = kofs[g + 1];
-  const float* a = A + (int64_t)m * lda;
-  const float* b = B + (int64_t)n * ldb;
-  float s = 0.0f;
-  for (int kk = k0; kk < k1; ++kk) s = fmaf(a[kk], b[kk], s);
-  C[(int64_t)g * c_gstride + (int64_t)m * ldc + n] = s;
-}
-
 }  // namespace
 
 hipError_t launch_kofs(const int32_t* offsets, int G, int n_single, int32_t* kofs,
@@ -552,16 +534,6 @@ hipError_t launch_dh_combine(const void* rows, const int32_t* row_of, const void
     hipLaunchKernelGGL(dh_combine_kernel<float>, dim3(T), dim3(kT), 0, st,
                        static_cast<const float*>(rows), row_of, static_cast<const float*>(shared),
                        static_cast<const float*>(router), static_cast<float*>(dh), k, d);
-  return hipGetLastError();
-}
-
-hipError_t launch_kgroup_f32(const float* A, int lda, const float* B, int ldb,
-                             const int32_t* kofs, int groups, int M, int Ncols, float* C,
-                             int64_t c_gstride, int ldc, hipStream_t st) {
-  const int64_t n = (int64_t)M * Ncols;
-  if (n == 0 || groups == 0) return hipSuccess;
-  hipLaunchKernelGGL(kgroup_f32_kernel, dim3((unsigned)((n + 255) / 256), groups), dim3(256), 0,
-                     st, A, lda, B, ldb, kofs, M, Ncols, C, c_gstride, ldc);
   return hipGetLastError();
 }
 

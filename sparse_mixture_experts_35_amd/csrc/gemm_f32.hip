@@ -18,6 +18,55 @@ constexpr int kFM = 64, kFN = 64, kFK = 16;
 constexpr int kFMaxGroups = 512;
 enum F32Mode { F32_SWIGLU = 0, F32_PREACT = 1, F32_DOWN = 2 };
 
+// acc[b] += A[rows] · B_b[columns]^T over k in [kbeg, kend): row i of the
+// staging map (tid / 16 + 16 i) reads arow[i][k] when aval[i] (else 0), and
+// the same for the columns from brow[b][i]; every output's sum runs over k
+// in order.
+template <int NB>
+__device__ __forceinline__ void f32_tile_loop(const float* const (&arow)[4],
+                                              const bool (&aval)[4],
+                                              const float* const (&brow)[NB][4],
+                                              const bool (&bval)[4], int kbeg, int kend,
+                                              float (*sA)[kFM + 4], float (*sB)[kFK][kFN + 4],
+                                              float (&acc)[NB][4][4]) {
+  const int tid = threadIdx.x;
+  const int kk = tid % kFK;
+  const int tx = tid % 16, ty = tid / 16;   // columns 4 tx .. 4 tx + 3, rows 4 ty .. 4 ty + 3
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[b][i][j] = 0.0f;
+  for (int k0 = kbeg; k0 < kend; k0 += kFK) {
+    const int k = k0 + kk;
+    const bool kv = k < kend;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tid / kFK + 16 * i;
+      sA[kk][row] = (aval[i] && kv) ? arow[i][k] : 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sB[b][kk][row] = (bval[i] && kv) ? brow[b][i][k] : 0.0f;
+    }
+    __syncthreads();
+    const int kn = min(kFK, kend - k0);
+    for (int c = 0; c < kn; ++c) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&sA[c][4 * ty]);
+      const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 b4 = *reinterpret_cast<const float4*>(&sB[b][c][4 * tx]);
+        const float w[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[b][i][j] = fmaf(a[i], w[j], acc[b][i][j]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedProblem p, int nt_n) {
   constexpr bool DUAL = MODE != F32_DOWN;
@@ -69,7 +118,6 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedProblem p, int 
 
   // staging: element tid + 256 i of a chunk is row (or column) tid / 16 +
   // 16 i, k = tid % 16 (16 threads read 64 contiguous bytes of a row)
-  const int kk = tid % kFK;
   const float* A = static_cast<const float*>(p.A);
   const float* arow[4];
   const float* brow[NB][4];
@@ -88,42 +136,9 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedProblem p, int 
     if (DUAL) brow[NB - 1][i] = static_cast<const float*>(p.B1) + boff;
   }
 
-  const int tx = tid % 16, ty = tid / 16;   // columns 4 tx .. 4 tx + 3, rows 4 ty .. 4 ty + 3
   float acc[NB][4][4];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[b][i][j] = 0.0f;
-
-  for (int k0 = 0; k0 < p.K; k0 += kFK) {
-    const int k = k0 + kk;
-    const bool kv = k < p.K;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = tid / kFK + 16 * i;
-      sA[kk][row] = (aval[i] && kv) ? arow[i][k] : 0.0f;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) sB[b][kk][row] = (bval[i] && kv) ? brow[b][i][k] : 0.0f;
-    }
-    __syncthreads();
-    const int kn = min(kFK, p.K - k0);
-    for (int c = 0; c < kn; ++c) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&sA[c][4 * ty]);
-      const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float4 b4 = *reinterpret_cast<const float4*>(&sB[b][c][4 * tx]);
-        const float w[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[b][i][j] = fmaf(a[i], w[j], acc[b][i][j]);
-      }
-    }
-    __syncthreads();
-  }
+  f32_tile_loop<NB>(arow, aval, brow, bval, 0, p.K, sA, sB, acc);
+  const int tx = tid % 16, ty = tid / 16;
 
   float* C = static_cast<float*>(p.C);
 #pragma unroll
@@ -148,6 +163,46 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedProblem p, int 
       } else {
         C[orow + n] = acc[0][i][j];
       }
+    }
+  }
+}
+
+// Weight gradients: C_g[m][n] = sum over k in [kofs[g], kofs[g+1]) of
+// A[m][k] B[n][k], a 64 x 64 tile of one group per block.
+__global__ __launch_bounds__(256) void kgroup_f32_kernel(const float* __restrict__ A, int lda,
+                                                         const float* __restrict__ B, int ldb,
+                                                         const int32_t* __restrict__ kofs, int M,
+                                                         int Ncols, float* __restrict__ C,
+                                                         int64_t c_gstride, int ldc, int nt_n) {
+  __shared__ __attribute__((aligned(16))) float sA[kFK][kFM + 4];
+  __shared__ __attribute__((aligned(16))) float sB[1][kFK][kFN + 4];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.y;
+  const int m0 = (int)(blockIdx.x / nt_n) * kFM, n0 = (int)(blockIdx.x % nt_n) * kFN;
+  const float* arow[4];
+  const float* brow[1][4];
+  bool aval[4], bval[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tid / kFK + 16 * i;
+    aval[i] = m0 + row < M;
+    bval[i] = n0 + row < Ncols;
+    arow[i] = A + (int64_t)(aval[i] ? m0 + row : 0) * lda;
+    brow[0][i] = B + (int64_t)(bval[i] ? n0 + row : 0) * ldb;
+  }
+  float acc[1][4][4];
+  f32_tile_loop<1>(arow, aval, brow, bval, kofs[g], kofs[g + 1], sA, sB, acc);
+  const int tx = tid % 16, ty = tid / 16;
+  float* Cg = C + (int64_t)g * c_gstride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 4 * ty + i;
+    if (m >= M) break;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 4 * tx + j;
+      if (n >= Ncols) break;
+      Cg[(int64_t)m * ldc + n] = acc[0][i][j];
     }
   }
 }
@@ -183,6 +238,18 @@ hipError_t launch_gateup_preact_f32(const GroupedProblem& p, hipStream_t st) {
 
 hipError_t launch_down_f32(const GroupedProblem& p, hipStream_t st) {
   return launch_grouped_f32<F32_DOWN>(p, st);
+}
+
+hipError_t launch_kgroup_f32(const float* A, int lda, const float* B, int ldb,
+                             const int32_t* kofs, int groups, int M, int Ncols, float* C,
+                             int64_t c_gstride, int ldc, hipStream_t st) {
+  if ((int64_t)M * Ncols == 0 || groups == 0) return hipSuccess;
+  const int nt_n = (Ncols + kFN - 1) / kFN;
+  const int64_t blocks = (int64_t)((M + kFM - 1) / kFM) * nt_n;
+  if (blocks > 0x7fffffff || groups > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kgroup_f32_kernel, dim3((unsigned)blocks, groups), dim3(256), 0, st, A, lda,
+                     B, ldb, kofs, M, Ncols, C, c_gstride, ldc, nt_n);
+  return hipGetLastError();
 }
 
 }  // namespace moe
