@@ -401,7 +401,7 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
     if (combined) *combined = fused;
     if (fused) {
       if (dfs) TRY(hip_check(run(ps, false), "shared down GEMM"));
-      return hip_check(moe::launch_down_combine_bf16(pr, *fuse, st), "down GEMM + combine");
+      return hip_check(moe::launch_down_combine_bf16(pr, *fuse, ncu, st), "down GEMM + combine");
     }
     TRY(hip_check(run(pr, false), "down GEMM"));
     if (dfs) TRY(hip_check(run(ps, false), "shared down GEMM"));

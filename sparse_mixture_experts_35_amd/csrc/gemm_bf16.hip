@@ -1414,13 +1414,8 @@ __global__ __launch_bounds__(kThreads) void skinny_gemm_kernel(GroupedProblem p,
   if constexpr (CMB) skinny_combine<CT>(p, cf, cb, ngroups);
 }
 
-template <int MT, bool DUAL, bool CMB = false>
-hipError_t launch_skinny(const GroupedProblem& p, hipStream_t st,
-                         const CombineFuse& cf = CombineFuse{}) {
-  // 64 columns per block at every row count: the block's activation rows are
-  // read once per 64 columns (narrower blocks for more rows made those L2
-  // reads outweigh the weights: at T = 64, 0.659 against 0.518 ms per step)
-  constexpr int CT = 4;
+template <int MT, int CT, bool DUAL, bool CMB>
+hipError_t launch_skinny_ct(const GroupedProblem& p, hipStream_t st, const CombineFuse& cf) {
   const int G = p.offsets ? p.groups : (p.M + 16 * MT - 1) / (16 * MT);
   if (G == 0) return hipSuccess;
   const int64_t items = (int64_t)G * ((p.Ncols + 16 * CT - 1) / (16 * CT));
@@ -1429,12 +1424,33 @@ hipError_t launch_skinny(const GroupedProblem& p, hipStream_t st,
   return hipGetLastError();
 }
 
+// 64 columns per block (CT = 4): the block's activation rows are read once
+// per 64 columns (narrower blocks for 33-64 rows made those L2 reads
+// outweigh the weights: at T = 64, 0.659 against 0.518 ms per step). At
+// most 16 rows per expert and fewer work items than two per CU (the
+// experts that can hold rows, at most min(groups, rows), times the column
+// blocks), narrower blocks, 32 or 16 columns, so that every CU streams
+// weights: one token touches two experts, and 64-column blocks gave its
+// down GEMM 128 blocks for 256 CUs.
+template <int MT, bool DUAL, bool CMB = false>
+hipError_t launch_skinny(const GroupedProblem& p, int num_cu, hipStream_t st,
+                         const CombineFuse& cf = CombineFuse{}) {
+  if constexpr (MT == 1) {
+    const int64_t used = p.offsets ? std::min<int64_t>(p.groups, p.M) : (p.M + 15) / 16;
+    auto items = [&](int ct) { return used * ((p.Ncols + 16 * ct - 1) / (16 * ct)); };
+    if (items(4) < 2 * (int64_t)num_cu)
+      return items(2) >= 2 * (int64_t)num_cu ? launch_skinny_ct<1, 2, DUAL, CMB>(p, st, cf)
+                                             : launch_skinny_ct<1, 1, DUAL, CMB>(p, st, cf);
+  }
+  return launch_skinny_ct<MT, 4, DUAL, CMB>(p, st, cf);
+}
+
 template <bool DUAL, bool CMB = false>
-hipError_t launch_skinny_any(const GroupedProblem& p, hipStream_t st,
+hipError_t launch_skinny_any(const GroupedProblem& p, int num_cu, hipStream_t st,
                              const CombineFuse& cf = CombineFuse{}) {
-  if (p.max_rows <= 16) return launch_skinny<1, DUAL, CMB>(p, st, cf);
-  if (p.max_rows <= 32) return launch_skinny<2, DUAL, CMB>(p, st, cf);
-  return launch_skinny<4, DUAL, CMB>(p, st, cf);
+  if (p.max_rows <= 16) return launch_skinny<1, DUAL, CMB>(p, num_cu, st, cf);
+  if (p.max_rows <= 32) return launch_skinny<2, DUAL, CMB>(p, num_cu, st, cf);
+  return launch_skinny<4, DUAL, CMB>(p, num_cu, st, cf);
 }
 
 template <class C, int EPI>
@@ -1517,7 +1533,7 @@ hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu, hipStream_t s
                           : launch_grouped<GateUp256, EPI_SWIGLU_SAVE>(p, num_cu, st);
     return launch_grouped<GateUp128, EPI_SWIGLU_SAVE>(p, num_cu, st);
   }
-  if (p.max_rows <= 64) return launch_skinny_any<true>(p, st);
+  if (p.max_rows <= 64) return launch_skinny_any<true>(p, num_cu, st);
   if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_SWIGLU>(p, num_cu, st);
   if (tall_tiles(p, GateUp256::BN, num_cu))
     return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_SWIGLU>(p, num_cu, st)
@@ -1533,14 +1549,14 @@ bool down_combine_ok(const GroupedProblem& p, const CombineFuse& cf) {
          p.Ncols % 8 == 0 && rows * p.ldc * 2 <= 0x7fffffffLL;
 }
 
-hipError_t launch_down_combine_bf16(const GroupedProblem& p, const CombineFuse& cf,
+hipError_t launch_down_combine_bf16(const GroupedProblem& p, const CombineFuse& cf, int num_cu,
                                     hipStream_t st) {
   if (!down_combine_ok(p, cf)) return hipErrorNotSupported;
-  return launch_skinny_any<false, true>(p, st, cf);
+  return launch_skinny_any<false, true>(p, num_cu, st, cf);
 }
 
 hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
-  if (p.max_rows <= 64) return launch_skinny_any<false>(p, st);
+  if (p.max_rows <= 64) return launch_skinny_any<false>(p, num_cu, st);
   if (mid_tiles(p)) return launch_grouped<DownMid, EPI_STORE_BF16>(p, num_cu, st);
   if (tall_tiles(p, Down256::BN, num_cu))
     return k64_tiles(p) ? launch_grouped<Down256K, EPI_STORE_BF16>(p, num_cu, st)

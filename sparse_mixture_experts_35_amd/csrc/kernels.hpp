@@ -153,7 +153,7 @@ struct CombineFuse {
 int combine_counters(int d);
 bool down_combine_ok(const GroupedProblem& p, const CombineFuse& cf);
 // hipErrorNotSupported unless down_combine_ok
-hipError_t launch_down_combine_bf16(const GroupedProblem& p, const CombineFuse& cf,
+hipError_t launch_down_combine_bf16(const GroupedProblem& p, const CombineFuse& cf, int num_cu,
                                     hipStream_t st);
 // gate and up pre-activations side by side as fp32: C [rows, 2 Ncols] float,
 // ldc = 2 Ncols

@@ -191,6 +191,10 @@ CASES = [
     # one kernel; at most 64 rows per expert: the combine inside the
     # weight-streaming down GEMM (bf16)
     ("bf16_decode_T1", 1, 128, 8, 2, 128, 0, W.DTYPE_BF16, 0),
+    # one token: the weight-streaming kernels narrow their column blocks so
+    # that the two experts' work covers the CUs (32 columns for gate/up
+    # here, 16 for down)
+    ("bf16_decode_T1_wide", 1, 256, 8, 2, 8192, 0, W.DTYPE_BF16, 0),
     ("bf16_decode_T32_shared", 32, 256, 8, 2, 384, 128, W.DTYPE_BF16, 0),
     ("bf16_decode_T16_N64_sigmoid", 16, 128, 64, 6, 128, 0, W.DTYPE_BF16, 2),
     ("bf16_decode_T5_N512_k16_shared", 5, 64, 512, 16, 64, 64, W.DTYPE_BF16, 1),
