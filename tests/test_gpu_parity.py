@@ -447,10 +447,13 @@ def test_dispatch_random(T, N, k, cf):
 
 
 @pytest.mark.parametrize("T,d,N,k,dff,dfs", [(520, 128, 64, 8, 128, 128),
-                                              (256, 256, 2, 1, 8192, 0)])
+                                              (256, 256, 2, 1, 8192, 0),
+                                              (2048, 4096, 2, 1, 256, 0)])
 def test_deterministic_repeat(T, d, N, k, dff, dfs):
     """Same inputs twice: ids, permutation-dependent outputs and y identical
-    (the second shape takes the split-K tail of the grouped GEMMs)."""
+    (the first two shapes run on the three-stage 128-row tiles, the second
+    with the split-K tail of the grouped GEMMs; the third on the 256-row
+    tiles, with a split-K tail in gate/up)."""
     inp = W.random_small(T, d, N, k, dff, dfs, W.DTYPE_BF16, 2, seed=5)
     s = shape_of(T, d, N, k, dff, dfs, W.DTYPE_BF16, 2)
     a = run_steps(s, inp)
