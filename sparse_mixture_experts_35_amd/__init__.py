@@ -83,6 +83,14 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise MoEError(ERR_HIP, "load", f"{LIB_PATH} is missing; build it with "
                            "`python -m sparse_mixture_experts_35_amd.build`")
+        # PyTorch ships its own HIP runtime. With torch loaded first this
+        # library binds to that runtime, so torch's tensors and streams are
+        # valid here; loading this library first and torch afterwards ended
+        # in "no ROCm-capable device is detected" and a crashed process.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         l = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIG.items():
             fn = getattr(l, name)
