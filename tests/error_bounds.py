@@ -36,6 +36,15 @@ with fp32 accumulation noise u_f32 sqrt(n) M for a sum of n terms:
 The checks hold each element's error to a dozen of these standard deviations
 and each tensor's root-mean-square error to a few.
 
+The router logits z are themselves fp32 sums of d products, and the gates
+and the router-logit gradient are nonlinear in them. Their error reaches
+the gradients by first-order propagation (`logit_propagation`): the
+Jacobians of the gates and of dL/dz in each logit column, by central
+differences of the oracle's own gate and statistics backward (the
+selection, dL/dg and the counts held fixed). It matters where a gradient is
+proportional to a logit that cancels: the z-loss term of a token is
+lse(z) P, and a logit near zero carries a large relative error.
+
 `comparison_scores` gives the same kind of bound for the scores the router
 orders its slots by.
 """
@@ -61,13 +70,15 @@ def silu_grad2(x):
     return s * (1.0 - s) * (2.0 + x * (1.0 - 2.0 * s))
 
 
-def expert_scales(x, wg, wu, wd, dout, dy_rows, g=None, u_store=0.0):
+def expert_scales(x, wg, wu, wd, dout, dy_rows, g=None, u_store=0.0, m_gz=None, v_g=None):
     """Magnitudes and noise for one expert's rows x [n, d] with output
     gradients dout (= gate * dy; ``g`` the gates, 1 for the shared expert):
     returns two dicts, M (magnitudes) and S (noise standard deviations), with
     keys dx [n, d], dw_gate, dw_up, dw_down (the weights' shapes) and dg [n]
     (the slot's dL/dg = <dy, E(x)>). ``u_store`` is the unit roundoff of the
-    stored intermediates and outputs (bf16, or fp32)."""
+    stored intermediates and outputs (bf16, or fp32). ``m_gz`` and ``v_g``
+    [n] are the magnitude the gates take from their logits and the gates'
+    error variance (logit_propagation); None for exact gates."""
     x = np.asarray(x, np.float64)
     wg, wu, wd = (np.asarray(w, np.float64) for w in (wg, wu, wd))
     dout = np.asarray(dout, np.float64)
@@ -95,19 +106,26 @@ def expert_scales(x, wg, wu, wd, dout, dy_rows, g=None, u_store=0.0):
     v_vn = acc(m_vn, d)
     m_dg = (_a(dy_rows) * m_out).sum(axis=-1)
     v_dg = (act ** 2 * v_vn + vn ** 2 * v_actf).sum(axis=-1) + acc(m_dg, dff)
-    # SwiGLU backward
+    # SwiGLU backward; the gate's own error enters through g dy and g v
+    m_gz = np.zeros(n) if m_gz is None else np.asarray(m_gz, np.float64)
+    v_g = np.zeros(n) if v_g is None else np.asarray(v_g, np.float64)
     v_ = g[:, None] * vn
-    adout = _a(dout)
+    adout = _a(dout) + m_gz[:, None] * _a(dy_rows)
     m_v = adout @ awd
     v_v = g[:, None] ** 2 * v_vn
     du = v_ * s
     dgp = v_ * up * s1
     m_du = m_v * _a(s) + _a(v_ * s1) * m_gp
     m_dgp = m_v * _a(up * s1) + _a(v_ * s1) * m_up + _a(v_ * up * s2) * m_gp
-    v_du = s ** 2 * v_v + (v_ * s1) ** 2 * v_gp + rnd(du)
-    v_dgp = (up * s1) ** 2 * v_v + (v_ * s1) ** 2 * v_up + (v_ * up * s2) ** 2 * v_gp + rnd(dgp)
+    v_du0 = s ** 2 * v_v + (v_ * s1) ** 2 * v_gp + rnd(du)
+    v_dgp0 = (up * s1) ** 2 * v_v + (v_ * s1) ** 2 * v_up + (v_ * up * s2) ** 2 * v_gp + rnd(dgp)
+    # a gate's error scales its whole row of du and dgp: independent between
+    # rows (the weight gradients), one common factor within a row (dx)
+    du_g, dgp_g = vn * s, vn * up * s1                 # d du / dg, d dgp / dg
+    v_du = v_du0 + du_g ** 2 * v_g[:, None]
+    v_dgp = v_dgp0 + dgp_g ** 2 * v_g[:, None]
     # weight gradients over the rows (dout packed in the stored dtype)
-    v_dout = rnd(dout)
+    v_dout = rnd(dout) + dy_rows ** 2 * v_g[:, None]
     dwd = dout.T @ act
     m_dwd = adout.T @ m_act
     v_dwd = v_dout.T @ act ** 2 + (dout ** 2).T @ v_act + acc(m_dwd, n) + rnd(dwd)
@@ -118,7 +136,8 @@ def expert_scales(x, wg, wu, wd, dout, dy_rows, g=None, u_store=0.0):
     # row gradients of h (each row stored)
     dx = dgp @ wg + du @ wu
     m_dx = m_dgp @ awg + m_du @ awu
-    v_dx = v_dgp @ wg2 + v_du @ wu2 + acc(m_dx, 2 * dff) + rnd(dx)
+    v_dx = (v_dgp0 @ wg2 + v_du0 @ wu2 + (dgp_g @ wg + du_g @ wu) ** 2 * v_g[:, None]
+            + acc(m_dx, 2 * dff) + rnd(dx))
     M = dict(dx=m_dx, dw_gate=m_dwg, dw_up=m_dwu, dw_down=m_dwd, dg=m_dg)
     S = dict(dx=v_dx, dw_gate=v_dwg, dw_up=v_dwu, dw_down=v_dwd, dg=v_dg)
     return M, S
@@ -206,6 +225,79 @@ def router_scales(r, m_dg, counts, k, mode, alpha, d_laux, d_zloss, v_dg=None):
     return m, var
 
 
+def logit_scales(h, w_router, b_router=None):
+    """Magnitude M_z [T, N] of each router logit's terms (|h| |W_r|^T + |b|)
+    and the variance of its fp32 evaluation: d products (exact for bf16
+    operands, fused into the adds for fp32 ones) accumulated in fp32, the
+    bias added, the result rounded once."""
+    h, wr = np.asarray(h, np.float64), np.asarray(w_router, np.float64)
+    nterms = h.shape[1]
+    m_z, z = _a(h) @ _a(wr).T, h @ wr.T
+    if b_router is not None:
+        m_z = m_z + _a(b_router)[None, :]
+        z = z + np.asarray(b_router, np.float64)[None, :]
+        nterms += 1
+    return m_z, (U_F32 * math.sqrt(max(nterms, 1)) * m_z) ** 2 + (U_F32 / SQRT3 * z) ** 2
+
+
+def gates_of(z, ids, mode):
+    """Gate values of the slots ids [T, k] for the logits z [T, N]: the gate
+    step of oracle.route for a fixed selection."""
+    if mode == O.MODE_SIGMOID_BIAS_RENORM:
+        s = np.take_along_axis(O.sigmoid(z), ids, axis=-1)
+        return s / s.sum(axis=-1, keepdims=True)
+    p = np.take_along_axis(O.softmax(z), ids, axis=-1)
+    return p / p.sum(axis=-1, keepdims=True) if mode == O.MODE_SOFTMAX_RENORM else p
+
+
+def logit_propagation(r, dg, counts, k, mode, alpha, d_laux, d_zloss, w_router, m_z, v_z,
+                      step=1e-6):
+    """First-order propagation of the logits' error (magnitude m_z, variance
+    v_z, both [T, N]) into the gates and the router-logit gradient dL/dz =
+    oracle.gate_backward + oracle.stats_backward (dL/dg, the selection and
+    the counts held fixed). Each row of either depends only on its token's
+    logits, so the Jacobian column d / dz[:, i] of every token comes from two
+    evaluations with column i moved by +-step. An entry below the rounding
+    noise of that difference is no dependence and counts as zero. Returns
+    (m_g, v_g) [T, k], (m_dz, v_dz) [T, N] and v_dhr [T, d], the variance of
+    dL/dz W_r with the errors of one token's logits shared by its d entries."""
+    z = np.asarray(r.z, np.float64)
+    T, N = z.shape
+    k_ = r.ids.shape[1]
+    wr = np.asarray(w_router, np.float64)
+    m_g, v_g = np.zeros((T, k_)), np.zeros((T, k_))
+    m_dz, v_dz = np.zeros((T, N)), np.zeros((T, N))
+    v_dhr = np.zeros((T, wr.shape[1]))
+    if T == 0:
+        return m_g, v_g, m_dz, v_dz, v_dhr
+
+    def at(zz):
+        g = gates_of(zz, r.ids, mode)
+        rr = O.Routing(r.ids, g, zz, r.sel, r.gap, r.stat_prob)
+        return g, (O.gate_backward(rr, dg, mode)
+                   + O.stats_backward(rr, counts, k, mode, alpha, d_laux, d_zloss))
+
+    eps = 64.0 * np.finfo(np.float64).eps / (2.0 * step)
+
+    def jac(fp, fm):
+        j = (fp - fm) / (2.0 * step)
+        return np.where(np.abs(j) > eps * (np.abs(fp) + np.abs(fm)), j, 0.0)
+
+    for i in range(N):
+        zp, zm = z.copy(), z.copy()
+        zp[:, i] += step
+        zm[:, i] -= step
+        (gp, dzp), (gm, dzm) = at(zp), at(zm)
+        jg, jd = jac(gp, gm), jac(dzp, dzm)
+        mi, vi = m_z[:, i:i + 1], v_z[:, i:i + 1]
+        m_g += np.abs(jg) * mi
+        v_g += jg ** 2 * vi
+        m_dz += np.abs(jd) * mi
+        v_dz += jd ** 2 * vi
+        v_dhr += (jd @ wr) ** 2 * vi
+    return m_g, v_g, m_dz, v_dz, v_dhr
+
+
 def grad_scales(h, w_router, k, mode, weights_of, dy, b_router=None, b_select=None,
                 shared=None, alpha=0.01, capacity_factor=None, d_laux=0.0, d_zloss=0.0,
                 ids=None, u_store=None, ref=None):
@@ -223,6 +315,15 @@ def grad_scales(h, w_router, k, mode, weights_of, dy, b_router=None, b_select=No
     r = O.route(h, wr, k, mode, b_router, b_select, None, ids)
     cap = O.expert_capacity(capacity_factor, T, k, N) if capacity_factor else None
     disp = O.dispatch(r.ids, N, cap)
+    if ref is None:
+        ref = O.layer_backward(h, wr, k, mode, weights_of, dy, b_router, b_select, shared,
+                               alpha, None, capacity_factor, d_laux, d_zloss, ids=r.ids)
+    # the logits' own fp32 error, through the gates and dL/dz; each gate
+    # also takes a few roundings of its own (exp, sum, quotient)
+    m_z, v_z = logit_scales(h, wr, b_router)
+    m_gz, v_g, m_dzz, v_dzz, v_dhz = logit_propagation(r, ref.dg, disp.counts, k, mode, alpha,
+                                                       d_laux, d_zloss, wr, m_z, v_z)
+    v_g = v_g + 4.0 * (U_F32 / SQRT3 * r.gates) ** 2
     m_dh, v_dh = np.zeros((T, d)), np.zeros((T, d))
     m_dg, v_dg = np.zeros((T, k)), np.zeros((T, k))
     M_w = {key: [] for key in ("dw_gate", "dw_up", "dw_down")}
@@ -232,7 +333,8 @@ def grad_scales(h, w_router, k, mode, weights_of, dy, b_router=None, b_select=No
         flats = disp.perm_src[disp.offsets[e]:disp.offsets[e + 1]]
         t, j = flats // k, flats % k
         gt = r.gates[t, j]
-        Me, Ve = expert_scales(h[t], wg, wu, wd, gt[:, None] * dy[t], dy[t], gt, us)
+        Me, Ve = expert_scales(h[t], wg, wu, wd, gt[:, None] * dy[t], dy[t], gt, us,
+                               m_gz[t, j], v_g[t, j])
         np.add.at(m_dh, t, Me["dx"])
         np.add.at(v_dh, t, Ve["dx"])
         m_dg[t, j] = Me["dg"]
@@ -248,6 +350,7 @@ def grad_scales(h, w_router, k, mode, weights_of, dy, b_router=None, b_select=No
         msh = (Ms["dw_gate"], Ms["dw_up"], Ms["dw_down"])
         vsh = (Vs["dw_gate"], Vs["dw_up"], Vs["dw_down"])
     m_dz, v_dz = router_scales(r, m_dg, disp.counts, k, mode, alpha, d_laux, d_zloss, v_dg)
+    m_dz = m_dz + m_dzz
     ah, awr = _a(h), _a(wr)
     m_dhr = m_dz @ awr
     m_dh += m_dhr
@@ -256,16 +359,17 @@ def grad_scales(h, w_router, k, mode, weights_of, dy, b_router=None, b_select=No
     if u_store is None:
         return M
     # the router's contributions: dz rounded to the stored dtype before it
-    # meets W_r and h; its dh rows stored; dh rounded once more
-    if ref is None:
-        ref = O.layer_backward(h, wr, k, mode, weights_of, dy, b_router, b_select, shared,
-                               alpha, None, capacity_factor, d_laux, d_zloss, ids=r.ids)
+    # meets W_r and h; its dh rows stored; dh rounded once more. A logit's
+    # error moves every entry of its token's dz row together, so its share
+    # of dz W_r is v_dhz, not the entry-wise sum.
     v_dzb = v_dz + rnd(ref.dz)
     dhr = ref.dz @ wr
-    v_dh = v_dh + v_dzb @ wr ** 2 + (U_F32 * math.sqrt(N) * m_dhr) ** 2 + rnd(dhr) + rnd(ref.dh)
+    v_dh = (v_dh + v_dzb @ wr ** 2 + v_dhz + (U_F32 * math.sqrt(N) * m_dhr) ** 2 + rnd(dhr)
+            + rnd(ref.dh))
+    v_dzb = v_dzb + v_dzz
     acc_t = lambda m: (U_F32 * math.sqrt(max(T, 1)) * m) ** 2
     Vv = GradScales(v_dh, v_dzb.T @ ah ** 2 + acc_t(M.dw_router),
-                    v_dz.sum(axis=0) + acc_t(M.db_router), np.stack(V_w["dw_gate"]),
+                    (v_dz + v_dzz).sum(axis=0) + acc_t(M.db_router), np.stack(V_w["dw_gate"]),
                     np.stack(V_w["dw_up"]), np.stack(V_w["dw_down"]), vsh, v_dg)
     S = GradScales(*(None if f is None else (tuple(np.sqrt(x) for x in f) if isinstance(f, tuple)
                                               else np.sqrt(f))

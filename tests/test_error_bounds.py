@@ -270,3 +270,103 @@ def test_check_ids_slot_order():
             with pytest.raises(AssertionError):
                 check_ids(swapped, r, k, O.MODE_SIGMOID_BIAS_RENORM, hh, w, None, b_sel)
         check_ids(r.ids, r, k, O.MODE_SIGMOID_BIAS_RENORM, hh, w, None, b_sel)
+
+
+def test_gates_of_matches_route():
+    """The gate step for a fixed selection gives the oracle's own gates."""
+    for mode in (O.MODE_SOFTMAX_RENORM, O.MODE_SOFTMAX_FULL, O.MODE_SIGMOID_BIAS_RENORM):
+        inp, _ = _inputs(11, 20, 32, 7, 3, 16, 0, mode)
+        r = O.route(inp["h"], inp["w_router"], 3, mode, inp["b_router"], inp["b_select"])
+        assert np.allclose(EB.gates_of(r.z, r.ids, mode), r.gates, rtol=1e-14, atol=0)
+
+
+def test_logit_jacobian_closed_form():
+    """The central-difference Jacobian of dL/dz in logit_propagation against
+    a closed form: with one expert, gate_backward is zero (the probability
+    is 1 whatever the logit) and the z-loss term is d_zloss (2/T) z, so
+    d dz / dz = 2 d_zloss / T and the propagated variance is that squared
+    times the logit's."""
+    T, d = 12, 16
+    inp, _ = _inputs(12, T, d, 1, 1, 16, 0, O.MODE_SOFTMAX_FULL)
+    r = O.route(inp["h"], inp["w_router"], 1, O.MODE_SOFTMAX_FULL, inp["b_router"])
+    m_z, v_z = EB.logit_scales(inp["h"], inp["w_router"], inp["b_router"])
+    dg = np.random.default_rng(3).standard_normal((T, 1))
+    m_g, v_g, m_dz, v_dz, v_dhr = EB.logit_propagation(
+        r, dg, np.array([T]), 1, O.MODE_SOFTMAX_FULL, 0.01, 0.5, 0.7, inp["w_router"], m_z, v_z)
+    c = 2.0 * 0.7 / T
+    assert not np.any(m_g) and not np.any(v_g)
+    assert np.allclose(m_dz, c * m_z, rtol=1e-6) and np.allclose(v_dz, c * c * v_z, rtol=1e-6)
+    wr = np.asarray(inp["w_router"], np.float64)
+    assert np.allclose(v_dhr, c * c * v_z * wr ** 2, rtol=1e-6)
+
+
+def _emulated_f32_logits_backward(inp, dy, k, mode, cf, d_laux, d_zloss):
+    """The oracle's backward with the router logits evaluated in fp32 (an
+    fp32 product of h and W_r, the bias added in fp32) and the gates rounded
+    to fp32; every other step exact. It isolates the logits' rounding, which
+    the other emulation leaves out."""
+    h = np.asarray(inp["h"], np.float64)
+    wr = np.asarray(inp["w_router"], np.float64)
+    T, d = h.shape
+    N = wr.shape[0]
+    z32 = np.asarray(inp["h"], np.float32) @ np.asarray(inp["w_router"], np.float32).T
+    if inp["b_router"] is not None:
+        z32 = z32 + np.asarray(inp["b_router"], np.float32)[None, :]
+    r = O.route(h, wr, k, mode, inp["b_router"], inp["b_select"])
+    z = z32.astype(np.float64)
+    g = EB.gates_of(z, r.ids, mode).astype(np.float32).astype(np.float64)
+    r = O.Routing(r.ids, g, z, r.sel, r.gap, r.stat_prob)
+    disp = O.dispatch(r.ids, N, O.expert_capacity(cf, T, k, N) if cf else None)
+    dh, dg = np.zeros((T, d)), np.zeros((T, k))
+    dwg, dwu, dwd = [], [], []
+    for e in range(N):
+        wg, wu, wd = (np.asarray(inp[key][e], np.float64) for key in ("w_gate", "w_up", "w_down"))
+        flats = disp.perm_src[disp.offsets[e]:disp.offsets[e + 1]]
+        t, j = flats // k, flats % k
+        dg[t, j] = np.sum(dy[t] * O.expert_ffn(h[t], wg, wu, wd), axis=-1)
+        dx, a, b, c = O.expert_ffn_backward(h[t], wg, wu, wd, g[t, j][:, None] * dy[t])
+        np.add.at(dh, t, dx)
+        dwg.append(a)
+        dwu.append(b)
+        dwd.append(c)
+    dz = O.gate_backward(r, dg, mode) + O.stats_backward(r, disp.counts, k, mode, 0.01, d_laux,
+                                                         d_zloss)
+    return O.LayerGrads(dh + dz @ wr, dz.T @ h, dz.sum(axis=0), np.stack(dwg), np.stack(dwu),
+                        np.stack(dwd), None, dg, dz)
+
+
+F32_LOGIT_CASES = [
+    # seed, T, d, N, k, d_ff, mode, capacity, d_laux, d_zloss
+    # one expert, half the tokens dropped: a dropped token's dh is the z-loss
+    # term alone, proportional to its logit, some of which nearly cancel
+    (33, 300, 32, 1, 1, 40, O.MODE_SOFTMAX_FULL, 0.5, 0.3, 0.3),
+    (22, 120, 48, 6, 2, 32, O.MODE_SOFTMAX_RENORM, 0.75, 1.0, 1.0),
+    (23, 90, 32, 9, 3, 24, O.MODE_SIGMOID_BIAS_RENORM, None, 0.3, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", F32_LOGIT_CASES, ids=[str(c[0]) for c in F32_LOGIT_CASES])
+def test_fp32_logit_error_inside_noise(case, monkeypatch):
+    """fp32 router logits stay inside the noise gate of the fp32 path; the
+    model without the logits' propagation fails the one-expert case."""
+    seed, T, d, N, k, dff, mode, cf, d_laux, d_zloss = case
+    inp = W.random_small(T, d, N, k, dff, 0, W.DTYPE_F32, mode, seed=seed, router_bias=True)
+    dy = np.random.default_rng(seed).standard_normal((T, d)).astype(np.float32).astype(np.float64)
+    args = _args(inp, dy, k, mode)
+    ids = ref_ids(inp, k, mode)
+    ref = O.layer_backward(*args, None, cf, d_laux, d_zloss, ids=ids)
+    emu = _emulated_f32_logits_backward(inp, dy, k, mode, cf, d_laux, d_zloss)
+    sc, nz = EB.grad_scales(*args, cf, d_laux, d_zloss, ids=ids, u_store=EB.U_F32, ref=ref)
+    R, S, Z, E = _fields(ref), _fields(sc), _fields(nz), _fields(emu)
+    for key in R:
+        check_grad(E[key], R[key], S[key], Z[key], GRAD_TOL[W.DTYPE_F32], key)
+    if N == 1:
+        def no_logits(r, dg, counts, k_, mode_, alpha, la, lz, wr, m_z, v_z, step=1e-6):
+            T_, N_ = r.z.shape
+            z_ = lambda *s: np.zeros(s)
+            return (z_(T_, r.ids.shape[1]), z_(T_, r.ids.shape[1]), z_(T_, N_), z_(T_, N_),
+                    z_(T_, np.asarray(wr).shape[1]))
+        monkeypatch.setattr(EB, "logit_propagation", no_logits)
+        _, nz0 = EB.grad_scales(*args, cf, d_laux, d_zloss, ids=ids, u_store=EB.U_F32, ref=ref)
+        with pytest.raises(AssertionError):
+            check_grad_noise(emu.dh, ref.dh, nz0.dh, "dh")
