@@ -350,6 +350,13 @@ moe_status dispatch_impl(const moe_shape* s, const int32_t* ids, int32_t* counts
                    "dispatch");
 }
 
+// bf16 with a shared expert as wide as the routed ones: the grouped
+// launchers run it as one more group of the routed experts' launch (or on
+// its own where the routed experts take the weight-streaming kernels).
+bool shared_in_routed(const moe_shape* s) {
+  return s->dtype == MOE_BF16 && s->d_ff_shared > 0 && s->d_ff_shared == s->d_ff;
+}
+
 moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32_t* perm_src,
                      const int32_t* offsets, const void* w_gate, const void* w_up,
                      const void* w_down, const void* sh_gate, const void* sh_up,
@@ -375,13 +382,23 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
     if (bf16) return gu ? moe::launch_gateup_bf16(p, ncu, st) : moe::launch_down_bf16(p, ncu, st);
     return gu ? moe::launch_gateup_f32(p, st) : moe::launch_down_f32(p, st);
   };
+  // the shared expert as one more group of the routed launches (same
+  // d_ff): its rows h[t] in order, its outputs at rows R + t
+  const bool merge = shared_in_routed(s);
   moe::GroupedProblem p{};
   if (gateup) {
     p = moe::GroupedProblem{h, d, perm_src, s->k, offsets, s->N, rows_all, rows_max, w_gate,
                             w_up, (int64_t)dff * d, d, dff, d, act, dff, 0, (uint32_t)(esz * T * d),
                             part, part_cnt, part_floats, preact, 2 * (int64_t)dff};
-    TRY(hip_check(run(p, true), "gate/up GEMM"));
-    if (dfs) {
+    if (merge) {
+      p.X0 = sh_gate;
+      p.X1 = sh_up;
+      p.x_rows = T;
+      p.x_a_row0 = 0;
+      p.x_c_row0 = R;
+    }
+    TRY(hip_check(run(p, true), merge ? "gate/up GEMM (routed and shared)" : "gate/up GEMM"));
+    if (dfs && !merge) {
       p = moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d, dfs, d,
                               act_sh, dfs, 0, (uint32_t)(esz * T * d),
                               part, part_cnt, part_floats,
@@ -402,6 +419,15 @@ moe_status ffn_stage(const moe_shape* s, bool gateup, const void* h, const int32
     if (fused) {
       if (dfs) TRY(hip_check(run(ps, false), "shared down GEMM"));
       return hip_check(moe::launch_down_combine_bf16(pr, *fuse, ncu, st), "down GEMM + combine");
+    }
+    if (merge) {
+      moe::GroupedProblem pm = pr;
+      pm.a_bytes = (uint32_t)(esz * ((size_t)R + T) * dff);
+      pm.X0 = sh_down;
+      pm.x_rows = T;
+      pm.x_a_row0 = R;
+      pm.x_c_row0 = R;
+      return hip_check(run(pm, false), "down GEMM (routed and shared)");
     }
     TRY(hip_check(run(pr, false), "down GEMM"));
     if (dfs) TRY(hip_check(run(ps, false), "shared down GEMM"));
@@ -570,11 +596,14 @@ BwdWs bwd_ws(const moe_shape* s) {
   w.dz = take(4 * T * N);
   w.colpart = take(4 * (size_t)moe::colsum_chunks((int)T) * N);
   w.dzb = take(es * T * w.Np);
-  w.gu = take(4 * R * 2 * dff);      // fp32 pre-activations and v
+  // fp32 pre-activations (the shared expert's right after the routed rows
+  // when one launch computes both) and v
+  const bool merge = shared_in_routed(s);
+  w.gu = take(4 * (R + (merge ? T : 0)) * 2 * dff);
   w.v = take(4 * R * dff);
   w.dgu = take(es * R * 2 * dff);
   w.act = take(es * R * dff);
-  w.gus = take(4 * T * 2 * dfs);
+  w.gus = merge ? w.gu + 4 * R * 2 * dff : take(4 * T * 2 * dfs);
   w.vs = take(4 * T * dfs);
   w.dgus = take(es * T * 2 * dfs);
   w.acts = take(es * T * dfs);
@@ -709,11 +738,21 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   // 2. gate/up pre-activations of the kept rows (and the shared expert),
   //    unless the forward kept them
   if (!preact) {
-    TRY(grouped(moe::GroupedProblem{h, d, perm, k, offsets, N, rows_all, rows_max, w_gate, w_up,
-                                    (int64_t)dff * d, d, dff, d, gu, 2 * dff, 0,
-                                    (uint32_t)(es * T * d), part, cnt, W.part_floats},
-                0, "gate/up recompute"));
-    if (dfs)
+    // the forward's launches: the shared expert's rows (at R + t, gus) in
+    // the routed launch when it ran there
+    moe::GroupedProblem pg{h, d, perm, k, offsets, N, rows_all, rows_max, w_gate, w_up,
+                           (int64_t)dff * d, d, dff, d, gu, 2 * dff, 0,
+                           (uint32_t)(es * T * d), part, cnt, W.part_floats};
+    const bool merge = shared_in_routed(s);
+    if (merge) {
+      pg.X0 = sh_gate;
+      pg.X1 = sh_up;
+      pg.x_rows = T;
+      pg.x_a_row0 = 0;
+      pg.x_c_row0 = R;
+    }
+    TRY(grouped(pg, 0, "gate/up recompute"));
+    if (dfs && !merge)
       TRY(grouped(moe::GroupedProblem{h, d, nullptr, 1, nullptr, 1, T, T, sh_gate, sh_up, 0, d,
                                       dfs, d, gus, 2 * dfs, 0, (uint32_t)(es * T * d), part,
                                       cnt, W.part_floats},

@@ -729,8 +729,13 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&aoff)[C::NAW], uint32_t (
 // where the experts average at most 1.5 m-tiles: then an expert's B columns
 // are read by one tile anyway, and the down-type GEMM is faster with groups
 // of GN = 8 n-tiles sharing the A rows (DeepSeek-V3 shape: 2.05 -> 1.94 ms).
+// Past the offsets' G groups, group G is the problem's extra group (X0):
+// its A rows x_a_row0 + r are read in order, its output rows are
+// x_c_row0 + r. c0 is the output row of the tile's first row.
 struct TileInfo {
   int g, m0, m_end, n0;
+  int64_t c0;
+  bool x;
 };
 template <class C>
 __device__ __forceinline__ int tile_group_width(int total_mt, int G) {
@@ -759,11 +764,21 @@ __device__ __forceinline__ TileInfo tile_info(const GroupedProblem& p, const int
   // so that descriptors and bounds live in scalar registers
   TileInfo ti;
   ti.g = __builtin_amdgcn_readfirstlane(lo);
+  const int lm0 = (mt - __builtin_amdgcn_readfirstlane(s_pref[ti.g])) * C::BM;
+  ti.n0 = nt * C::BN;
+  ti.x = p.X0 && ti.g == (p.offsets ? p.groups : 1);
+  if (ti.x) {
+    const int a0 = (int)p.x_a_row0;
+    ti.m0 = a0 + lm0;
+    ti.m_end = a0 + min(lm0 + C::BM, p.x_rows);
+    ti.c0 = p.x_c_row0 + lm0;
+    return ti;
+  }
   const int gbase = p.offsets ? __builtin_amdgcn_readfirstlane(p.offsets[ti.g]) : 0;
   const int gend = p.offsets ? __builtin_amdgcn_readfirstlane(p.offsets[ti.g + 1]) : p.M;
-  ti.m0 = gbase + (mt - __builtin_amdgcn_readfirstlane(s_pref[ti.g])) * C::BM;
+  ti.m0 = gbase + lm0;
   ti.m_end = min(ti.m0 + C::BM, gend);
-  ti.n0 = nt * C::BN;
+  ti.c0 = p.c_row0 + ti.m0;
   return ti;
 }
 
@@ -790,7 +805,8 @@ __device__ __forceinline__ void tile_mainloop(const GroupedProblem& p, const Til
                                               int k_begin, int k_len,
                                               f32x16 (&acc)[C::NB][C::FM][C::FN]) {
   uint32_t aoff[C::NAW], boff[C::NBW];
-  dma_offsets<C>(aoff, boff, p.perm, p.kdiv, p.lda, ti.m0, ti.m_end, p.ldb, ti.n0, p.Ncols);
+  dma_offsets<C>(aoff, boff, ti.x ? nullptr : p.perm, p.kdiv, p.lda, ti.m0, ti.m_end, p.ldb,
+                 ti.n0, p.Ncols);
   Rsrc rB0, rB1;
   if constexpr (C::NN) {
     // B0 holds K rows [0, k1) (all K when k1 = 0), B1 rows [k1, K)
@@ -803,8 +819,16 @@ __device__ __forceinline__ void tile_mainloop(const GroupedProblem& p, const Til
                      : rB0;
   } else {
     const uint32_t bbytes = (uint32_t)((int64_t)p.Ncols * p.ldb * 2);
-    rB0 = make_rsrc(static_cast<const bf16_t*>(p.B0) + (int64_t)ti.g * p.b_gstride, bbytes);
-    rB1 = C::DUAL ? make_rsrc(static_cast<const bf16_t*>(p.B1) + (int64_t)ti.g * p.b_gstride, bbytes) : rB0;
+    const bf16_t* b0 = ti.x ? static_cast<const bf16_t*>(p.X0)
+                            : static_cast<const bf16_t*>(p.B0) + (int64_t)ti.g * p.b_gstride;
+    rB0 = make_rsrc(b0, bbytes);
+    if constexpr (C::DUAL) {
+      const bf16_t* b1 = ti.x ? static_cast<const bf16_t*>(p.X1)
+                              : static_cast<const bf16_t*>(p.B1) + (int64_t)ti.g * p.b_gstride;
+      rB1 = make_rsrc(b1, bbytes);
+    } else {
+      rB1 = rB0;
+    }
   }
   zero_acc<C>(acc);
   // row blocks of this wave that hold rows of the group: the MFMAs of the
@@ -924,7 +948,9 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
   __shared__ int s_item;
   __shared__ int s_last;
   const int tid = threadIdx.x;
-  const int G = p.offsets ? p.groups : 1;
+  // the offsets' groups, then the extra group (launchers keep G <= kMaxGroups)
+  const int G0 = p.offsets ? p.groups : 1;
+  const int G = G0 + (p.X0 ? 1 : 0);
 
   if (tid < 64) {
     int loc[kMaxGroups / 64];
@@ -934,7 +960,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
       const int g = tid * (kMaxGroups / 64) + i;
       int c = 0;
       if (g < G) {
-        const int rows = p.offsets ? (p.offsets[g + 1] - p.offsets[g]) : p.M;
+        const int rows = g == G0 ? p.x_rows
+                                 : (p.offsets ? (p.offsets[g + 1] - p.offsets[g]) : p.M);
         c = (rows + C::BM - 1) / C::BM;
       }
       loc[i] = c;
@@ -1042,8 +1069,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void grouped_gemm_kernel(GroupedP
       }
     }
     if (write)
-      epilogue_bf16<C, EPI>(acc, p.C, p.ldc, p.c_row0 + ti.m0,
-                            ti.m_end - ti.m0, ti.n0, p.Ncols, p.C2, p.ldc2);
+      epilogue_bf16<C, EPI>(acc, p.C, p.ldc, ti.c0, ti.m_end - ti.m0, ti.n0, p.Ncols, p.C2,
+                            p.ldc2);
     if (dynamic) {
       __syncthreads();                 // every thread has read s_item / s_last
       if (tid == 0) s_item = nxt;
@@ -1457,7 +1484,9 @@ template <class C, int EPI>
 hipError_t launch_grouped(const GroupedProblem& p, int num_cu, hipStream_t st) {
   // Upper bound on tiles, to avoid idle blocks on tiny problems.
   const int G = p.offsets ? p.groups : 1;
-  const int64_t mt_bound = (int64_t)(p.M + C::BM - 1) / C::BM + (p.offsets ? G : 0);
+  const int64_t xr = p.X0 ? p.x_rows : 0;
+  const int64_t mt_bound = ((int64_t)p.M + xr + C::BM - 1) / C::BM + (p.offsets ? G : 0) +
+                           (p.X0 ? 1 : 0);
   const int64_t tiles = mt_bound * ((p.Ncols + C::BN - 1) / C::BN);
   // with a split-K workspace, small problems may use more blocks than tiles
   const int64_t units = p.part ? tiles * kMaxSplit : tiles;
@@ -1497,11 +1526,17 @@ using DownMid = TileCfg<128, 256, false, 3, 1, false, 64>;
 // per CU). A 256-row tile reads an expert's weight columns once for up to 256
 // of its rows, where 128-row tiles read them once per 128 rows and rely on L2
 // to share the rest; padding rows cost no loads and their MFMAs are skipped.
+// Rows and groups of a launch, its extra group included.
+static int64_t all_rows(const GroupedProblem& p) { return (int64_t)p.M + (p.X0 ? p.x_rows : 0); }
+static int64_t all_groups(const GroupedProblem& p) {
+  return (p.offsets ? p.groups : 1) + (p.X0 ? 1 : 0);
+}
+
 static bool tall_tiles(const GroupedProblem& p, int bn, int num_cu) {
-  const int G = p.offsets ? p.groups : 1;
-  if (p.M >= 1024 * G) return true;
+  const int64_t G = all_groups(p), M = all_rows(p);
+  if (M >= 1024 * G) return true;
   const int64_t nt = (p.Ncols + bn - 1) / bn;
-  const int64_t est = ((int64_t)p.M / 256 + G / 2) * nt;   // 256-row tiles, about
+  const int64_t est = (M / 256 + G / 2) * nt;   // 256-row tiles, about
   return est >= 4 * (int64_t)num_cu;
 }
 
@@ -1519,26 +1554,63 @@ static bool k64_tiles(const GroupedProblem& p) { return p.K % 64 == 0; }
 // Qwen3-30B shape, 512 Zipf-skewed: 3% faster; the Mixtral shape, 1,024:
 // 5% slower, so it keeps the 256-row tiles).
 static bool mid_tiles(const GroupedProblem& p) {
-  const int64_t G = p.offsets ? p.groups : 1;
-  return p.K % 64 == 0 && p.M < 768 * G;
+  return p.K % 64 == 0 && all_rows(p) < 768 * all_groups(p);
 }
 
-hipError_t launch_gateup_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
-  if (p.C2) {
+// The extra group (X0) runs in the launch of the other groups, on their
+// tiles, unless those take the weight-streaming kernels (at most 64 rows per
+// group; skinny = true) or there is no room for one more group: then it runs
+// after them as a launch of its own.
+static GroupedProblem without_extra(const GroupedProblem& p) {
+  GroupedProblem q = p;
+  q.X0 = q.X1 = nullptr;
+  q.x_rows = 0;
+  return q;
+}
+static GroupedProblem extra_alone(const GroupedProblem& p) {
+  GroupedProblem q = without_extra(p);
+  const int64_t skip = p.x_a_row0 * p.lda * 2;
+  q.A = static_cast<const char*>(p.A) + skip;
+  q.a_bytes = (uint32_t)(p.a_bytes - skip);
+  q.perm = nullptr;
+  q.kdiv = 1;
+  q.offsets = nullptr;
+  q.groups = 1;
+  q.M = q.max_rows = p.x_rows;
+  q.B0 = p.X0;
+  q.B1 = p.X1;
+  q.b_gstride = 0;
+  q.c_row0 = p.x_c_row0;
+  return q;
+}
+template <class F>
+static hipError_t with_extra(const GroupedProblem& p, bool skinny, F launch) {
+  if (!p.X0 || (!skinny && (p.offsets ? p.groups : 1) < kMaxGroups)) return launch(p);
+  const hipError_t e = launch(without_extra(p));
+  if (e != hipSuccess || p.x_rows == 0) return e;
+  return launch(extra_alone(p));
+}
+
+hipError_t launch_gateup_bf16(const GroupedProblem& p_, int num_cu, hipStream_t st) {
+  if (p_.C2) {
     // keeping the pre-activations: the grouped tiles at any row count, the
     // same tiles and schedule as the backward's recompute
-    if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_SWIGLU_SAVE>(p, num_cu, st);
-    if (tall_tiles(p, GateUp256::BN, num_cu))
-      return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_SWIGLU_SAVE>(p, num_cu, st)
-                          : launch_grouped<GateUp256, EPI_SWIGLU_SAVE>(p, num_cu, st);
-    return launch_grouped<GateUp128, EPI_SWIGLU_SAVE>(p, num_cu, st);
+    return with_extra(p_, false, [&](const GroupedProblem& p) {
+      if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_SWIGLU_SAVE>(p, num_cu, st);
+      if (tall_tiles(p, GateUp256::BN, num_cu))
+        return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_SWIGLU_SAVE>(p, num_cu, st)
+                            : launch_grouped<GateUp256, EPI_SWIGLU_SAVE>(p, num_cu, st);
+      return launch_grouped<GateUp128, EPI_SWIGLU_SAVE>(p, num_cu, st);
+    });
   }
-  if (p.max_rows <= 64) return launch_skinny_any<true>(p, num_cu, st);
-  if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_SWIGLU>(p, num_cu, st);
-  if (tall_tiles(p, GateUp256::BN, num_cu))
-    return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_SWIGLU>(p, num_cu, st)
-                        : launch_grouped<GateUp256, EPI_SWIGLU>(p, num_cu, st);
-  return launch_grouped<GateUp128, EPI_SWIGLU>(p, num_cu, st);
+  return with_extra(p_, p_.max_rows <= 64, [&](const GroupedProblem& p) {
+    if (p.max_rows <= 64) return launch_skinny_any<true>(p, num_cu, st);
+    if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_SWIGLU>(p, num_cu, st);
+    if (tall_tiles(p, GateUp256::BN, num_cu))
+      return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_SWIGLU>(p, num_cu, st)
+                          : launch_grouped<GateUp256, EPI_SWIGLU>(p, num_cu, st);
+    return launch_grouped<GateUp128, EPI_SWIGLU>(p, num_cu, st);
+  });
 }
 
 int combine_counters(int d) { return (d + 15) / 16; }
@@ -1555,13 +1627,15 @@ hipError_t launch_down_combine_bf16(const GroupedProblem& p, const CombineFuse& 
   return launch_skinny_any<false, true>(p, num_cu, st, cf);
 }
 
-hipError_t launch_down_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
-  if (p.max_rows <= 64) return launch_skinny_any<false>(p, num_cu, st);
-  if (mid_tiles(p)) return launch_grouped<DownMid, EPI_STORE_BF16>(p, num_cu, st);
-  if (tall_tiles(p, Down256::BN, num_cu))
-    return k64_tiles(p) ? launch_grouped<Down256K, EPI_STORE_BF16>(p, num_cu, st)
-                        : launch_grouped<Down256, EPI_STORE_BF16>(p, num_cu, st);
-  return launch_grouped<Down128, EPI_STORE_BF16>(p, num_cu, st);
+hipError_t launch_down_bf16(const GroupedProblem& p_, int num_cu, hipStream_t st) {
+  return with_extra(p_, p_.max_rows <= 64, [&](const GroupedProblem& p) {
+    if (p.max_rows <= 64) return launch_skinny_any<false>(p, num_cu, st);
+    if (mid_tiles(p)) return launch_grouped<DownMid, EPI_STORE_BF16>(p, num_cu, st);
+    if (tall_tiles(p, Down256::BN, num_cu))
+      return k64_tiles(p) ? launch_grouped<Down256K, EPI_STORE_BF16>(p, num_cu, st)
+                          : launch_grouped<Down256, EPI_STORE_BF16>(p, num_cu, st);
+    return launch_grouped<Down128, EPI_STORE_BF16>(p, num_cu, st);
+  });
 }
 
 // NN (B as [K rows][N columns]): the grouped tiles at more than 64 rows per
@@ -1590,12 +1664,14 @@ hipError_t launch_down_nn_f32out_bf16(const GroupedProblem& p, int num_cu, hipSt
 // Gate and up pre-activations of the routed rows as fp32, side by side in C
 // (ldc = 2 Ncols): the same tiles and schedule as the SwiGLU launch, any row
 // count.
-hipError_t launch_gateup_preact_bf16(const GroupedProblem& p, int num_cu, hipStream_t st) {
-  if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_STORE_DUAL_F32>(p, num_cu, st);
-  if (tall_tiles(p, GateUp256::BN, num_cu))
-    return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_STORE_DUAL_F32>(p, num_cu, st)
-                        : launch_grouped<GateUp256, EPI_STORE_DUAL_F32>(p, num_cu, st);
-  return launch_grouped<GateUp128, EPI_STORE_DUAL_F32>(p, num_cu, st);
+hipError_t launch_gateup_preact_bf16(const GroupedProblem& p_, int num_cu, hipStream_t st) {
+  return with_extra(p_, false, [&](const GroupedProblem& p) {
+    if (mid_tiles(p)) return launch_grouped<GateUpMid, EPI_STORE_DUAL_F32>(p, num_cu, st);
+    if (tall_tiles(p, GateUp256::BN, num_cu))
+      return k64_tiles(p) ? launch_grouped<GateUp256K, EPI_STORE_DUAL_F32>(p, num_cu, st)
+                          : launch_grouped<GateUp256, EPI_STORE_DUAL_F32>(p, num_cu, st);
+    return launch_grouped<GateUp128, EPI_STORE_DUAL_F32>(p, num_cu, st);
+  });
 }
 
 // C = A·B0^T stored as fp32, any row count (the grouped tiles only).

@@ -121,6 +121,16 @@ struct GroupedProblem {
   // B given as [K rows][ldb] (N contiguous; the down-type NN launchers
   // only): rows [0, b_k1) at B0, rows [b_k1, K) at B1 (b_k1 = 0: all at B0)
   int b_k1;
+  // One more group after the offsets' groups, nullable (the grouped bf16
+  // gate/up and down launchers only): x_rows rows with weights X0 (and X1,
+  // gate/up) of the same shape as one expert's, A rows x_a_row0 + r read in
+  // order (no perm), output rows x_c_row0 + r (in C, and C2 when given).
+  // The shared expert runs as this group in the routed experts' launch.
+  const void* X0;
+  const void* X1;
+  int x_rows;
+  int64_t x_a_row0;
+  int64_t x_c_row0;
 };
 
 constexpr int kSplitCounters = 1024;

@@ -142,6 +142,10 @@ BACKWARD_CASES = [
     # the auxiliary loss's alone, far below the scale of dL/dg
     ("bf16_C_top1_aux_only", 300, 1024, 2, 1, 128, 128, W.DTYPE_BF16, 2, None, 0.0, 1.0, 0.0),
     ("f32_A_top1_aux_only", 200, 64, 3, 1, 32, 0, W.DTYPE_F32, 0, None, 0.0, 1.0, 0.0),
+    # the shared expert's pre-activations recomputed in the routed launch,
+    # with its split-K tail
+    ("bf16_B_shared_in_routed_k4096", 128, 4096, 4, 1, 128, 128, W.DTYPE_BF16, 1, None, 0.0,
+     0.3, 0.1),
 ]
 
 
@@ -186,6 +190,8 @@ TRAIN_CASES = [
     # at most 64 rows per expert: the training forward takes the grouped tiles
     ("bf16_B_skinny_shared", 40, 128, 16, 4, 192, 128, W.DTYPE_BF16, 1, None, 0.0),
     ("bf16_A_split_k4096", 256, 4096, 2, 1, 256, 0, W.DTYPE_BF16, 0, None, 0.0),
+    # the shared expert in the routed launches (its kept pre-activations too)
+    ("bf16_B_shared_in_routed_k4096", 128, 4096, 4, 1, 128, 128, W.DTYPE_BF16, 1, None, 0.0),
 ]
 
 

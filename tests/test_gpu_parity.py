@@ -207,6 +207,13 @@ CASES = [
     ("bf16_N100_k6_switch", 300, 128, 100, 6, 128, 0, W.DTYPE_BF16, 1),
     ("bf16_N200_sigmoid_shared", 150, 64, 200, 8, 64, 64, W.DTYPE_BF16, 2),
     ("f32_N128_k8", 40, 32, 128, 8, 32, 0, W.DTYPE_F32, 0),
+    # d_ff_shared = d_ff: the shared expert runs as one more group of the
+    # routed experts' launches (three-stage 128-row tiles, 256-row tiles, a
+    # split-K tail in gate/up); with 512 routed experts it runs on its own
+    ("bf16_shared_in_routed_mid", 700, 256, 16, 4, 256, 256, W.DTYPE_BF16, 0),
+    ("bf16_shared_in_routed_bm256", 2304, 128, 2, 1, 320, 320, W.DTYPE_BF16, 1),
+    ("bf16_shared_in_routed_split_k4096", 128, 4096, 4, 1, 128, 128, W.DTYPE_BF16, 2),
+    ("bf16_shared_N512_alone", 300, 64, 512, 8, 64, 64, W.DTYPE_BF16, 2),
 ]
 
 
