@@ -555,10 +555,10 @@ struct BwdWs {
   int64_t Rp, Tp, Np;        // padded K spaces: routed rows, tokens, experts
   int64_t ta_rows, tb_rows;  // rows of the transposed-activation buffers
   size_t kofs, kofs_t, dg, dz, dzb, colpart;
-  size_t gu, v, dgu, act, gus, vs, dgus, acts;
+  size_t gu, v, dgu, dgpart, gus, vs, dgus, acts;
   size_t wdT, wguT, sdT, sguT, wrT;
   size_t dhr, dhs, dhrt;
-  size_t ta, tb, part, cnt, end;
+  size_t ta, tb, tc, part, cnt, end;
   int64_t part_floats;
 };
 // Rows per expert at most (all routed rows of a token set, or the capacity).
@@ -602,7 +602,7 @@ BwdWs bwd_ws(const moe_shape* s) {
   w.gu = take(4 * (R + (merge ? T : 0)) * 2 * dff);
   w.v = take(4 * R * dff);
   w.dgu = take(es * R * 2 * dff);
-  w.act = take(es * R * dff);
+  w.dgpart = take(4 * R * (size_t)moe::swiglu_bwd_t_tiles((int)dff));
   w.gus = merge ? w.gu + 4 * R * 2 * dff : take(4 * T * 2 * dfs);
   w.vs = take(4 * T * dfs);
   w.dgus = take(es * T * 2 * dfs);
@@ -618,6 +618,7 @@ BwdWs bwd_ws(const moe_shape* s) {
   w.dhrt = take(es * T * d);
   w.ta = take(es * w.ta_rows * w.Rp);
   w.tb = take(es * w.tb_rows * w.Rp);
+  w.tc = take(es * d * w.Rp);
   w.part_floats = 0;
   if (s->dtype == MOE_BF16) {
     int64_t f = std::max(moe::split_part_floats(R, s->N, s->d_ff, true),
@@ -673,7 +674,7 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   float* gu = preact ? const_cast<float*>(preact) : at<float>(ws, W.gu);
   float* v = at<float>(ws, W.v);
   char* dgu = at<char>(ws, W.dgu);
-  char* act = at<char>(ws, W.act);
+  float* dgpart = at<float>(ws, W.dgpart);
   float* gus = preact ? const_cast<float*>(preact) + (int64_t)R * 2 * dff : at<float>(ws, W.gus);
   float* vs = at<float>(ws, W.vs);
   char* dgus = at<char>(ws, W.dgus);
@@ -688,6 +689,7 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
   char* dhrt = at<char>(ws, W.dhrt);
   char* ta = at<char>(ws, W.ta);
   char* tb = at<char>(ws, W.tb);
+  char* tc = at<char>(ws, W.tc);
   int32_t* kofs = at<int32_t>(ws, W.kofs);
   int32_t* kofs_t = at<int32_t>(ws, W.kofs_t);
   float* dg = at<float>(ws, W.dg);
@@ -787,9 +789,13 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
                                     W.part_floats},
                 1, "shared v GEMM"));
   }
-  // 4. SwiGLU backward: act, [dgp | du] in place, dg per slot
-  TRY(hip_check(moe::launch_swiglu_bwd(gu, v, act, dgu, perm, gates, dg, offsets, N, rows_all,
-                                       dff, b, st), "SwiGLU backward"));
+  // 4. SwiGLU backward: [dgp | du] row-major for the h-row GEMM, act^T and
+  //    [dgp | du]^T in the weight-gradient GEMMs' padded K ranges (kofs),
+  //    dg per slot
+  TRY(hip_check(moe::launch_kofs(offsets, N, 0, kofs, st), "K ranges"));
+  TRY(hip_check(moe::launch_swiglu_bwd_t(gu, v, dgu, tb, ta, Rp, perm, gates, offsets, kofs, N,
+                                         Rp, rows_all, dff, dgpart, dg, b, st),
+                "SwiGLU backward"));
   if (dfs)
     TRY(hip_check(moe::launch_swiglu_bwd(gus, vs, acts, dgus, nullptr, nullptr, nullptr, nullptr,
                                          0, T, dfs, b, st), "shared SwiGLU backward"));
@@ -843,15 +849,11 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
               2, "router dh GEMM"));
   TRY(hip_check(moe::launch_dh_combine(dhr, row_of, dfs ? dhs : nullptr, dhrt, dh, T, k, d, b,
                                        st), "dh combine"));
-  // 7. expert weight gradients over each expert's kept rows (padded K ranges)
-  TRY(hip_check(moe::launch_kofs(offsets, N, 0, kofs, st), "K ranges"));
-  TRY(pack(dy, d, d, perm, k, gates, offsets, kofs, N, 0, Rp, ta, Rp, 1, 0, 0, "dOut transpose"));
-  TRY(pack(act, dff, dff, nullptr, 1, nullptr, offsets, kofs, N, 0, Rp, tb, Rp, 1, 0, 0,
-           "act transpose"));
-  TRY(kgroup(ta, Rp, d, tb, Rp, dff, kofs, N, d, dff, dw_down, (int64_t)d * dff, dff, false,
+  // 7. expert weight gradients over each expert's kept rows (padded K
+  //    ranges): act^T (tb) and [dgp | du]^T (ta) from step 4
+  TRY(pack(dy, d, d, perm, k, gates, offsets, kofs, N, 0, Rp, tc, Rp, 1, 0, 0, "dOut transpose"));
+  TRY(kgroup(tc, Rp, d, tb, Rp, dff, kofs, N, d, dff, dw_down, (int64_t)d * dff, dff, false,
              "W_down gradient"));
-  TRY(pack(dgu, 2 * dff, 2 * dff, nullptr, 1, nullptr, offsets, kofs, N, 0, Rp, ta, Rp, 1, 0, 0,
-           "dgu transpose"));
   TRY(pack(h, d, d, perm, k, nullptr, offsets, kofs, N, 0, Rp, tb, Rp, 1, 0, 0, "h transpose"));
   TRY(kgroup(ta, Rp, 2 * dff, tb, Rp, d, kofs, N, dff, d, dw_gate, (int64_t)dff * d, d, false,
              "W_gate gradient"));

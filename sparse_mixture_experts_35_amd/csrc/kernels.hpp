@@ -214,6 +214,17 @@ hipError_t launch_swiglu_bwd(const float* gu, const float* v, void* act,
                              void* dgu, const int32_t* perm, const float* gates,
                              float* dg_slot, const int32_t* offsets, int G,
                              int rows_bound, int d_ff, int bf16, hipStream_t st);
+// The routed rows' SwiGLU backward (launch_swiglu_bwd's values): dgu
+// [rows, 2 d_ff] row-major, and act^T [d_ff][ld_t] and [dgp | du]^T
+// [2 d_ff][ld_t] in launch_pack_t's transposed, padded layout (kofs; p_limit
+// a multiple of 64, ld_t of 8, 16-byte aligned); dg_slot[perm[r]] = <v_r,
+// act_r> through dg_part (swiglu_bwd_t_tiles(d_ff) x rows_bound floats).
+int swiglu_bwd_t_tiles(int d_ff);
+hipError_t launch_swiglu_bwd_t(const float* gu, const float* v, void* dgu, void* act_t,
+                               void* dgu_t, int64_t ld_t, const int32_t* perm,
+                               const float* gates, const int32_t* offsets, const int32_t* kofs,
+                               int G, int64_t p_limit, int rows_bound, int d_ff,
+                               float* dg_part, float* dg_slot, int bf16, hipStream_t st);
 hipError_t launch_route_bwd(const float* z_part, int splits,
                             const float* b_router, const int32_t* ids,
                             const float* gates, const float* dg_slot,
