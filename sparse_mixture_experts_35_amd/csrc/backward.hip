@@ -540,22 +540,48 @@ __global__ __launch_bounds__(kT) void colsum_final_kernel(const float* __restric
 }
 
 // dh[t] = sum_j rows[row_of[t k + j]] (kept slots, slot order) + shared[t]
-// + router[t], accumulated in fp32.
-template <typename TE>
+// + router[t], accumulated in fp32 in that order. The token's row indices
+// are read once into LDS; VEC: each thread takes 16 bytes of columns (d and
+// every pointer allow it; the launcher checks), else one column.
+constexpr int kMaxTopK = 16;
+template <typename TE, bool VEC>
 __global__ __launch_bounds__(kT) void dh_combine_kernel(
     const TE* __restrict__ rows, const int32_t* __restrict__ row_of,
     const TE* __restrict__ shared, const TE* __restrict__ router, TE* __restrict__ dh, int k,
     int d) {
+  constexpr int V = VEC ? 16 / sizeof(TE) : 1;
+  __shared__ int64_t s_r[kMaxTopK];
   const int64_t t = blockIdx.x;
-  for (int c = threadIdx.x; c < d; c += kT) {
-    float acc = 0.0f;
+  if (threadIdx.x < k) s_r[threadIdx.x] = row_of[t * k + threadIdx.x];
+  __syncthreads();
+  for (int c = threadIdx.x * V; c < d; c += kT * V) {
+    float acc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = 0.0f;
+    auto add = [&](const TE* src) {
+      if constexpr (VEC) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
+        const TE* x = reinterpret_cast<const TE*>(&raw);
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] += ld(x, e);
+      } else {
+        acc[0] += ld(src, 0);
+      }
+    };
     for (int j = 0; j < k; ++j) {
-      const int64_t r = row_of[t * k + j];
-      if (r >= 0) acc += ld(rows, r * d + c);
+      const int64_t r = s_r[j];
+      if (r >= 0) add(rows + r * d + c);
     }
-    if (shared) acc += ld(shared, t * d + c);
-    acc += ld(router, t * d + c);
-    st(dh, t * d + c, acc);
+    if (shared) add(shared + t * d + c);
+    add(router + t * d + c);
+    if constexpr (VEC) {
+      TE out[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) out[e] = from_f32<TE>(acc[e]);
+      *reinterpret_cast<u32x4*>(dh + t * d + c) = *reinterpret_cast<const u32x4*>(out);
+    } else {
+      st(dh, t * d + c, acc[0]);
+    }
   }
 }
 
@@ -671,15 +697,20 @@ hipError_t launch_dh_combine(const void* rows, const int32_t* row_of, const void
                              const void* router, void* dh, int T, int k, int d, int bf16,
                              hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (bf16)
-    hipLaunchKernelGGL(dh_combine_kernel<bf16_t>, dim3(T), dim3(kT), 0, st,
-                       static_cast<const bf16_t*>(rows), row_of,
-                       static_cast<const bf16_t*>(shared), static_cast<const bf16_t*>(router),
-                       static_cast<bf16_t*>(dh), k, d);
-  else
-    hipLaunchKernelGGL(dh_combine_kernel<float>, dim3(T), dim3(kT), 0, st,
-                       static_cast<const float*>(rows), row_of, static_cast<const float*>(shared),
-                       static_cast<const float*>(router), static_cast<float*>(dh), k, d);
+  if (k > kMaxTopK) return hipErrorInvalidValue;
+  const int V = bf16 ? 8 : 4;
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = d % V == 0 && al(rows) && al(router) && al(dh) && (!shared || al(shared));
+#define MOE_DHC(TE, VEC)                                                                       \
+  hipLaunchKernelGGL((dh_combine_kernel<TE, VEC>), dim3(T), dim3(kT), 0, st,                   \
+                     static_cast<const TE*>(rows), row_of, static_cast<const TE*>(shared),     \
+                     static_cast<const TE*>(router), static_cast<TE*>(dh), k, d)
+  if (bf16) {
+    if (vec) MOE_DHC(bf16_t, true); else MOE_DHC(bf16_t, false);
+  } else {
+    if (vec) MOE_DHC(float, true); else MOE_DHC(float, false);
+  }
+#undef MOE_DHC
   return hipGetLastError();
 }
 
