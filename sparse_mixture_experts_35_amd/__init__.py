@@ -120,6 +120,45 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _bytes_of(shape: Shape) -> dict:
+    """Bytes the library reads or writes through each array argument (the
+    layouts of include/moe.h)."""
+    es = 2 if shape.dtype == BF16 else 4
+    T, d, N, k = shape.T, shape.d, shape.N, shape.k
+    f, fs = shape.d_ff, shape.d_ff_shared
+    R = T * k
+    return dict(h=T * d * es, w_router=N * d * es, b_router=4 * N, b_select=4 * N,
+                topk_ids=4 * R, topk_gates=4 * R, p_mean=4 * N, p_out=4 * N, f_out=4 * N,
+                counts=4 * N, offsets=4 * (N + 1), perm_src=4 * R, row_of=4 * R, l_aux=4,
+                z_loss=4, entropy=4, cap_stats=8, w_gate=N * f * d * es, w_up=N * f * d * es,
+                w_down=N * d * f * es, sh_gate=fs * d * es, sh_up=fs * d * es,
+                sh_down=d * fs * es, out_rows=(R + (T if fs else 0)) * d * es, y=T * d * es,
+                dy=T * d * es, dh=T * d * es, preact=4 * preact_floats(shape),
+                dw_router=4 * N * d, db_router=4 * N, dw_gate=N * f * d * es,
+                dw_up=N * f * d * es, dw_down=N * d * f * es, dsh_gate=fs * d * es,
+                dsh_up=fs * d * es, dsh_down=d * fs * es, dgates=4 * R)
+
+
+def _args(shape: Shape, where: str, ws_bytes: int = 0):
+    """arg(t, name): the pointer of t. A tensor must be contiguous and hold
+    at least the bytes the call uses through it (a raw int pointer is passed
+    as it is): a short buffer raises MoEError instead of being overrun."""
+    need = _bytes_of(shape)
+    need["ws"] = int(ws_bytes)
+
+    def arg(t, name):
+        if t is None or isinstance(t, int):
+            return _ptr(t)
+        if not t.is_contiguous():
+            raise MoEError(ERR_INVALID_ARG, where, f"{name} is not contiguous")
+        have = t.numel() * t.element_size()
+        if have < need[name]:
+            raise MoEError(ERR_INVALID_ARG, where,
+                           f"{name} holds {have} bytes; this shape needs {need[name]}")
+        return t.data_ptr()
+    return arg
+
+
 def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -133,41 +172,52 @@ def workspace_bytes(shape: Shape) -> int:
 
 def route(shape, h, w_router, b_router, b_select, topk_ids, topk_gates, p_mean, ws,
           ws_bytes, stream=None, z_loss=None, entropy=None):
-    _check(lib().moe_route(ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router),
-                           _ptr(b_select), _ptr(topk_ids), _ptr(topk_gates), _ptr(p_mean),
-                           _ptr(z_loss), _ptr(entropy), _ptr(ws), ws_bytes, _stream(stream)),
-           "moe_route")
+    a = _args(shape, "moe_route", ws_bytes)
+    _check(lib().moe_route(ctypes.byref(shape), a(h, "h"), a(w_router, "w_router"),
+                           a(b_router, "b_router"), a(b_select, "b_select"),
+                           a(topk_ids, "topk_ids"), a(topk_gates, "topk_gates"),
+                           a(p_mean, "p_mean"), a(z_loss, "z_loss"), a(entropy, "entropy"),
+                           a(ws, "ws"), ws_bytes, _stream(stream)), "moe_route")
 
 
 def dispatch(shape, topk_ids, counts, offsets, perm_src, row_of, p_mean=None, f_out=None,
              l_aux=None, ws=None, ws_bytes=0, stream=None, cap_stats=None):
-    _check(lib().moe_dispatch(ctypes.byref(shape), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
-                              _ptr(perm_src), _ptr(row_of), _ptr(p_mean), _ptr(f_out),
-                              _ptr(l_aux), _ptr(cap_stats), _ptr(ws), ws_bytes, _stream(stream)),
-           "moe_dispatch")
+    a = _args(shape, "moe_dispatch", ws_bytes)
+    _check(lib().moe_dispatch(ctypes.byref(shape), a(topk_ids, "topk_ids"), a(counts, "counts"),
+                              a(offsets, "offsets"), a(perm_src, "perm_src"),
+                              a(row_of, "row_of"), a(p_mean, "p_mean"), a(f_out, "f_out"),
+                              a(l_aux, "l_aux"), a(cap_stats, "cap_stats"), a(ws, "ws"),
+                              ws_bytes, _stream(stream)), "moe_dispatch")
 
 
 def expert_ffn(shape, h, perm_src, offsets, w_gate, w_up, w_down, sh_gate, sh_up, sh_down,
                out_rows, ws, ws_bytes, stream=None):
-    _check(lib().moe_expert_ffn(ctypes.byref(shape), _ptr(h), _ptr(perm_src), _ptr(offsets),
-                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate),
-                                _ptr(sh_up), _ptr(sh_down), _ptr(out_rows), _ptr(ws), ws_bytes,
-                                _stream(stream)), "moe_expert_ffn")
+    a = _args(shape, "moe_expert_ffn", ws_bytes)
+    _check(lib().moe_expert_ffn(ctypes.byref(shape), a(h, "h"), a(perm_src, "perm_src"),
+                                a(offsets, "offsets"), a(w_gate, "w_gate"), a(w_up, "w_up"),
+                                a(w_down, "w_down"), a(sh_gate, "sh_gate"), a(sh_up, "sh_up"),
+                                a(sh_down, "sh_down"), a(out_rows, "out_rows"), a(ws, "ws"),
+                                ws_bytes, _stream(stream)), "moe_expert_ffn")
 
 
 def combine(shape, out_rows, row_of, topk_gates, y, stream=None):
-    _check(lib().moe_combine(ctypes.byref(shape), _ptr(out_rows), _ptr(row_of),
-                             _ptr(topk_gates), _ptr(y), _stream(stream)), "moe_combine")
+    a = _args(shape, "moe_combine")
+    _check(lib().moe_combine(ctypes.byref(shape), a(out_rows, "out_rows"), a(row_of, "row_of"),
+                             a(topk_gates, "topk_gates"), a(y, "y"), _stream(stream)),
+           "moe_combine")
 
 
 def layer_fused(shape, h, w_router, b_router, b_select, w_gate, w_up, w_down, sh_gate, sh_up,
                 sh_down, y, topk_ids=None, topk_gates=None, counts=None, f_out=None,
                 p_out=None, l_aux=None, ws=None, ws_bytes=0, stream=None, events=None,
                 z_loss=None, entropy=None, cap_stats=None):
-    args = (ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(b_select),
-            _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),
-            _ptr(y), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _ptr(f_out), _ptr(p_out),
-            _ptr(l_aux), _ptr(z_loss), _ptr(entropy), _ptr(cap_stats), _ptr(ws), ws_bytes,
+    a = _args(shape, "moe_layer_fused", ws_bytes)
+    args = (ctypes.byref(shape), a(h, "h"), a(w_router, "w_router"), a(b_router, "b_router"),
+            a(b_select, "b_select"), a(w_gate, "w_gate"), a(w_up, "w_up"), a(w_down, "w_down"),
+            a(sh_gate, "sh_gate"), a(sh_up, "sh_up"), a(sh_down, "sh_down"), a(y, "y"),
+            a(topk_ids, "topk_ids"), a(topk_gates, "topk_gates"), a(counts, "counts"),
+            a(f_out, "f_out"), a(p_out, "p_out"), a(l_aux, "l_aux"), a(z_loss, "z_loss"),
+            a(entropy, "entropy"), a(cap_stats, "cap_stats"), a(ws, "ws"), ws_bytes,
             _stream(stream))
     if events is None:
         _check(lib().moe_layer_fused(*args), "moe_layer_fused")
@@ -183,11 +233,14 @@ def layer_fused_noalloc(shape, h, w_router, b_router, b_select, w_gate, w_up, w_
                         entropy=None, cap_stats=None):
     """moe_layer_fused_noalloc: the fused layer on the library's static
     scratch (no workspace argument)."""
+    a = _args(shape, "moe_layer_fused_noalloc")
     _check(lib().moe_layer_fused_noalloc(
-        ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(b_select),
-        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),
-        _ptr(y), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _ptr(f_out), _ptr(p_out),
-        _ptr(l_aux), _ptr(z_loss), _ptr(entropy), _ptr(cap_stats), _stream(stream)),
+        ctypes.byref(shape), a(h, "h"), a(w_router, "w_router"), a(b_router, "b_router"),
+        a(b_select, "b_select"), a(w_gate, "w_gate"), a(w_up, "w_up"), a(w_down, "w_down"),
+        a(sh_gate, "sh_gate"), a(sh_up, "sh_up"), a(sh_down, "sh_down"), a(y, "y"),
+        a(topk_ids, "topk_ids"), a(topk_gates, "topk_gates"), a(counts, "counts"),
+        a(f_out, "f_out"), a(p_out, "p_out"), a(l_aux, "l_aux"), a(z_loss, "z_loss"),
+        a(entropy, "entropy"), a(cap_stats, "cap_stats"), _stream(stream)),
         "moe_layer_fused_noalloc")
 
 
@@ -195,12 +248,16 @@ def layer_forward_train(shape, h, w_router, b_router, b_select, w_gate, w_up, w_
                         sh_up, sh_down, y, topk_ids, topk_gates, counts, offsets, perm_src,
                         row_of, preact=None, p_out=None, l_aux=None, z_loss=None, entropy=None,
                         ws=None, ws_bytes=0, stream=None):
+    a = _args(shape, "moe_layer_forward_train", ws_bytes)
     _check(lib().moe_layer_forward_train(
-        ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(b_select),
-        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down),
-        _ptr(y), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _ptr(offsets), _ptr(perm_src),
-        _ptr(row_of), _ptr(preact), _ptr(p_out), _ptr(l_aux), _ptr(z_loss), _ptr(entropy),
-        _ptr(ws), ws_bytes, _stream(stream)), "moe_layer_forward_train")
+        ctypes.byref(shape), a(h, "h"), a(w_router, "w_router"), a(b_router, "b_router"),
+        a(b_select, "b_select"), a(w_gate, "w_gate"), a(w_up, "w_up"), a(w_down, "w_down"),
+        a(sh_gate, "sh_gate"), a(sh_up, "sh_up"), a(sh_down, "sh_down"), a(y, "y"),
+        a(topk_ids, "topk_ids"), a(topk_gates, "topk_gates"), a(counts, "counts"),
+        a(offsets, "offsets"), a(perm_src, "perm_src"), a(row_of, "row_of"),
+        a(preact, "preact"), a(p_out, "p_out"), a(l_aux, "l_aux"), a(z_loss, "z_loss"),
+        a(entropy, "entropy"), a(ws, "ws"), ws_bytes, _stream(stream)),
+        "moe_layer_forward_train")
 
 
 def preact_floats(shape: Shape) -> int:
@@ -218,14 +275,18 @@ def layer_backward(shape, h, w_router, b_router, w_gate, w_up, w_down, sh_gate, 
                    db_router, dw_gate, dw_up, dw_down, dsh_gate=None, dsh_up=None, dsh_down=None,
                    dgates=None, d_laux=0.0, d_zloss=0.0, ws=None, ws_bytes=0, stream=None,
                    preact=None):
+    a = _args(shape, "moe_layer_backward", ws_bytes)
     _check(lib().moe_layer_backward(
-        ctypes.byref(shape), _ptr(h), _ptr(w_router), _ptr(b_router), _ptr(w_gate), _ptr(w_up),
-        _ptr(w_down), _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down), _ptr(topk_ids),
-        _ptr(topk_gates), _ptr(counts), _ptr(offsets), _ptr(perm_src), _ptr(row_of),
-        _ptr(preact), _ptr(dy),
-        float(d_laux), float(d_zloss), _ptr(dh), _ptr(dw_router), _ptr(db_router), _ptr(dw_gate),
-        _ptr(dw_up), _ptr(dw_down), _ptr(dsh_gate), _ptr(dsh_up), _ptr(dsh_down), _ptr(dgates),
-        _ptr(ws), ws_bytes, _stream(stream)), "moe_layer_backward")
+        ctypes.byref(shape), a(h, "h"), a(w_router, "w_router"), a(b_router, "b_router"),
+        a(w_gate, "w_gate"), a(w_up, "w_up"), a(w_down, "w_down"), a(sh_gate, "sh_gate"),
+        a(sh_up, "sh_up"), a(sh_down, "sh_down"), a(topk_ids, "topk_ids"),
+        a(topk_gates, "topk_gates"), a(counts, "counts"), a(offsets, "offsets"),
+        a(perm_src, "perm_src"), a(row_of, "row_of"), a(preact, "preact"), a(dy, "dy"),
+        float(d_laux), float(d_zloss), a(dh, "dh"), a(dw_router, "dw_router"),
+        a(db_router, "db_router"), a(dw_gate, "dw_gate"), a(dw_up, "dw_up"),
+        a(dw_down, "dw_down"), a(dsh_gate, "dsh_gate"), a(dsh_up, "dsh_up"),
+        a(dsh_down, "dsh_down"), a(dgates, "dgates"), a(ws, "ws"), ws_bytes, _stream(stream)),
+        "moe_layer_backward")
 
 
 class MoELayer:

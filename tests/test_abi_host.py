@@ -262,3 +262,32 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
                                                          + [None] * 3 + [FAKE] + [None] * 9),
                                      None)
     assert st == M.ERR_INVALID_ARG
+
+
+def test_binding_rejects_short_and_strided_tensors():
+    """A tensor argument smaller than the bytes the call uses through it, or
+    not contiguous, raises MoEError in the binding before the library runs
+    (the C ABI takes bare pointers and cannot tell). out_rows holds T k rows
+    (and T more with a shared expert); one row short is refused."""
+    torch = pytest.importorskip("torch")
+    T, d, N, k, dff = 4, 64, 4, 2, 64
+    s = M.Shape(T, d, N, k, dff, 0, M.BF16)
+    bf = torch.bfloat16
+    h = torch.zeros((T, d), dtype=bf)
+    wg, wu = torch.zeros((N, dff, d), dtype=bf), torch.zeros((N, dff, d), dtype=bf)
+    wd = torch.zeros((N, d, dff), dtype=bf)
+    perm, off = torch.zeros(T * k, dtype=torch.int32), torch.zeros(N + 1, dtype=torch.int32)
+    ws = torch.zeros(64, dtype=torch.uint8)
+    short = torch.zeros((T * k - 1, d), dtype=bf)
+    with pytest.raises(M.MoEError, match="out_rows holds"):
+        M.expert_ffn(s, h, perm, off, wg, wu, wd, None, None, None, short, ws, 64)
+    strided = torch.zeros((T, 2 * d), dtype=bf)[:, ::2]
+    with pytest.raises(M.MoEError, match="h is not contiguous"):
+        M.expert_ffn(s, strided, perm, off, wg, wu, wd, None, None, None,
+                     torch.zeros((T * k, d), dtype=bf), ws, 64)
+    with pytest.raises(M.MoEError, match="ws holds"):
+        M.expert_ffn(s, h, perm, off, wg, wu, wd, None, None, None,
+                     torch.zeros((T * k, d), dtype=bf), ws, 65)
+    s2 = M.Shape(T, d, N, k, dff, 32, M.BF16)
+    with pytest.raises(M.MoEError, match="out_rows holds"):
+        M.combine(s2, torch.zeros((T * k, d), dtype=bf), perm, torch.zeros(T * k), h)
