@@ -1,17 +1,21 @@
-"""GPU parity of moe_layer_backward at the full Mixtral-8x7B prefill size
-(T = 4096, d = 4096, d_ff = 14336, 8 experts, top-2, bf16), in the launch
-configuration the benchmark times (inputs drawn on the device, the same
-seeded upstream gradient, d_laux = 1, d_zloss = 1e-3), against the float64
-oracle on sampled outputs it can compute one at a time:
-  * dL/dg and dh on sampled tokens: each token's experts forward and
-    backward on its own row (the oracle's expert_ffn / expert_ffn_backward),
-    its router-logit gradient from the oracle's gate_backward and
-    stats_backward rows (row-wise in the tokens, the L_aux term from the
-    counts of every token);
-  * sampled rows of dW_gate and dW_up of two experts: the oracle's expert
-    backward restricted to those hidden units is exact for them;
-  * sampled rows of dW_down of the smallest expert (the full expert
-    backward on its rows).
+"""GPU parity of moe_layer_backward at full size, in the launch configuration
+the benchmark times (inputs drawn on the device, the same seeded upstream
+gradient, d_laux = 1, d_zloss = 1e-3): the Mixtral-8x7B prefill (T = 4096,
+d = 4096, d_ff = 14336, 8 experts, top-2, softmax gates) and the
+DeepSeek-V3 shape (T = 4096, d = 7168, d_ff = 2048, 256 experts, top-8,
+sigmoid gates with a selection bias, a shared expert whose pre-activations
+come from the routed launches), against the float64 oracle on sampled
+outputs it can compute one at a time:
+  * dL/dg and dh on sampled tokens: each token's experts (and the shared
+    expert) forward and backward on its own row (the oracle's expert_ffn /
+    expert_ffn_backward), its router-logit gradient from the oracle's
+    gate_backward and stats_backward rows (row-wise in the tokens, the L_aux
+    term from the counts of every token);
+  * sampled rows of dW_gate and dW_up of the smallest, the largest and one
+    random expert, and of the shared expert over all tokens: the oracle's
+    expert backward restricted to those hidden units is exact for them;
+  * sampled rows of dW_down of the smallest expert and of the shared expert
+    (the full expert backward on its rows).
 The benchmark's training step (moe_layer_forward_train keeping the
 pre-activations, then the backward using them) must give the fused call's y
 and the checked gradients bit for bit. The router's weight gradients need
@@ -43,17 +47,22 @@ def _np(x):
     return x.float().cpu().numpy().astype(np.float64)
 
 
-def test_full_size_backward_mixtral_prefill():
+FULL_BACKWARD = [W.MIXTRAL_PREFILL, W.DEEPSEEK_V3]
+
+
+@pytest.mark.parametrize("w", FULL_BACKWARD, ids=[w.name for w in FULL_BACKWARD])
+def test_full_size_backward(w):
     t = torch()
-    w = W.MIXTRAL_PREFILL
-    T, d, N, k, dff = w.T, w.d, w.N, w.k, w.d_ff
+    T, d, N, k, dff, dfs = w.T, w.d, w.N, w.k, w.d_ff, w.d_ff_shared
     inp = W.device_inputs(w)
-    s = M.Shape(T, d, N, k, dff, 0, w.dtype, w.mode, w.aux_alpha)
+    sh = (inp["sh_gate"], inp["sh_up"], inp["sh_down"]) if dfs else (None, None, None)
+    s = M.Shape(T, d, N, k, dff, dfs, w.dtype, w.mode, w.aux_alpha)
     E = lambda shp, dt=t.bfloat16: t.empty(shp, dtype=dt, device="cuda")
     nws = M.workspace_bytes(s)
     ws = E(nws, t.uint8)
     ids, gates = E(T * k, t.int32), E(T * k, t.float32)
-    M.route(s, inp["h"], inp["w_router"], inp["b_router"], None, ids, gates, None, ws, nws)
+    M.route(s, inp["h"], inp["w_router"], inp["b_router"], inp["b_select"], ids, gates, None,
+            ws, nws)
     counts, offsets = E(N, t.int32), E(N + 1, t.int32)
     perm, row_of = E(T * k, t.int32), E(T * k, t.int32)
     M.dispatch(s, ids, counts, offsets, perm, row_of, ws=ws, ws_bytes=nws)
@@ -64,13 +73,21 @@ def test_full_size_backward_mixtral_prefill():
     g = dict(dh=E((T, d)), dw_router=E((N, d), t.float32), db_router=E(N, t.float32),
              dw_gate=E((N, dff, d)), dw_up=E((N, dff, d)), dw_down=E((N, d, dff)),
              dgates=E(T * k, t.float32))
+    if dfs:
+        g.update(dsh_gate=E((dfs, d)), dsh_up=E((dfs, d)), dsh_down=E((d, dfs)))
     nb = M.backward_workspace_bytes(s)
     bws = E(nb, t.uint8)
     print(f"\n[{w.name}] backward, workspace {nb / 1e9:.2f} GB", flush=True)
-    M.layer_backward(s, inp["h"], inp["w_router"], inp["b_router"], inp["w_gate"], inp["w_up"],
-                     inp["w_down"], None, None, None, ids, gates, counts, offsets, perm, row_of,
-                     dy, g["dh"], g["dw_router"], g["db_router"], g["dw_gate"], g["dw_up"],
-                     g["dw_down"], None, None, None, g["dgates"], D_LAUX, D_ZLOSS, bws, nb)
+
+    def backward(gr, ids_, gates_, counts_, off_, perm_, row_, preact=None):
+        M.layer_backward(s, inp["h"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                         inp["w_up"], inp["w_down"], *sh, ids_, gates_, counts_, off_, perm_,
+                         row_, dy, gr["dh"], gr["dw_router"], gr["db_router"], gr["dw_gate"],
+                         gr["dw_up"], gr["dw_down"], gr.get("dsh_gate"), gr.get("dsh_up"),
+                         gr.get("dsh_down"), gr["dgates"], D_LAUX, D_ZLOSS, bws, nb,
+                         preact=preact)
+
+    backward(g, ids, gates, counts, offsets, perm, row_of)
     t.cuda.synchronize()
 
     # the benchmark's training step: the training forward keeps the dispatch
@@ -81,11 +98,11 @@ def test_full_size_backward_mixtral_prefill():
     y_t, y_f = E((T, d)), E((T, d))
     ids_t, gates_t, counts_t = E(T * k, t.int32), E(T * k, t.float32), E(N, t.int32)
     off_t, perm_t, row_t = E(N + 1, t.int32), E(T * k, t.int32), E(T * k, t.int32)
-    M.layer_forward_train(s, inp["h"], inp["w_router"], inp["b_router"], None, inp["w_gate"],
-                          inp["w_up"], inp["w_down"], None, None, None, y_t, ids_t, gates_t,
+    M.layer_forward_train(s, inp["h"], inp["w_router"], inp["b_router"], inp["b_select"],
+                          inp["w_gate"], inp["w_up"], inp["w_down"], *sh, y_t, ids_t, gates_t,
                           counts_t, off_t, perm_t, row_t, preact=pre, ws=ws, ws_bytes=nws)
-    M.layer_fused(s, inp["h"], inp["w_router"], inp["b_router"], None, inp["w_gate"], inp["w_up"],
-                  inp["w_down"], None, None, None, y_f, ws=ws, ws_bytes=nws)
+    M.layer_fused(s, inp["h"], inp["w_router"], inp["b_router"], inp["b_select"], inp["w_gate"],
+                  inp["w_up"], inp["w_down"], *sh, y_f, ws=ws, ws_bytes=nws)
     t.cuda.synchronize()
     del ws
     kept = int(host(offsets)[-1])
@@ -93,11 +110,7 @@ def test_full_size_backward_mixtral_prefill():
     assert t.equal(ids_t, ids) and t.equal(gates_t, gates) and t.equal(counts_t, counts)
     assert t.equal(off_t, offsets) and t.equal(perm_t[:kept], perm[:kept]) and t.equal(row_t, row_of)
     g2 = {key: t.empty_like(v) for key, v in g.items()}
-    M.layer_backward(s, inp["h"], inp["w_router"], inp["b_router"], inp["w_gate"], inp["w_up"],
-                     inp["w_down"], None, None, None, ids_t, gates_t, counts_t, off_t, perm_t,
-                     row_t, dy, g2["dh"], g2["dw_router"], g2["db_router"], g2["dw_gate"],
-                     g2["dw_up"], g2["dw_down"], None, None, None, g2["dgates"], D_LAUX, D_ZLOSS,
-                     bws, nb, preact=pre)
+    backward(g2, ids_t, gates_t, counts_t, off_t, perm_t, row_t, preact=pre)
     t.cuda.synchronize()
     for key in g:
         assert t.equal(g[key], g2[key]), f"{key}: kept vs recomputed pre-activations"
@@ -106,10 +119,12 @@ def test_full_size_backward_mixtral_prefill():
     del bws, pre, g2
 
     h, wr, dyh = _np(inp["h"]), _np(inp["w_router"]), _np(dy)
+    br = None if inp["b_router"] is None else inp["b_router"].cpu().numpy()
+    bs = None if inp["b_select"] is None else inp["b_select"].cpu().numpy()
     g_ids = host(ids).reshape(T, k)
     g_cnt = host(counts)
     assert np.array_equal(g_cnt, np.bincount(g_ids.reshape(-1), minlength=N))
-    r = O.route(h, wr, k, w.mode, ids=g_ids)
+    r = O.route(h, wr, k, w.mode, br, bs, ids=g_ids)
     offs, pm = host(offsets), host(perm)
     rng = np.random.default_rng(99)
     tol = TOL[w.dtype]
@@ -121,7 +136,7 @@ def test_full_size_backward_mixtral_prefill():
             cache[e] = tuple(_np(inp[key][e]) for key in ("w_gate", "w_up", "w_down"))
         return cache[e]
 
-    # ---- dL/dg and dh on sampled tokens
+    # ---- dL/dg and dh on sampled tokens (the shared expert's rows too)
     toks = np.unique(np.concatenate([[0, 1, T - 1], rng.integers(0, T, 13)]))
     dg = np.zeros((T, k))
     dx = np.zeros((toks.size, d))
@@ -134,6 +149,10 @@ def test_full_size_backward_mixtral_prefill():
                 x = h[tt:tt + 1]
                 dg[tt, j] = float(np.sum(dyh[tt] * O.expert_ffn(x, wg, wu, wd)[0]))
                 dx[n] += O.expert_ffn_backward(x, wg, wu, wd, r.gates[tt, j] * dyh[tt:tt + 1])[0][0]
+    shw = None
+    if dfs:
+        shw = tuple(_np(x) for x in sh)
+        dx += O.expert_ffn_backward(h[toks], *shw, dyh[toks])[0]
     dz = O.gate_backward(r, dg, w.mode) + O.stats_backward(r, g_cnt, k, w.mode, w.aux_alpha,
                                                            D_LAUX, D_ZLOSS)
     dh_ref = dx + dz[toks] @ wr
@@ -148,8 +167,8 @@ def test_full_size_backward_mixtral_prefill():
         tk, sl = flats // k, flats % k
         return h[tk], r.gates[tk, sl][:, None] * dyh[tk]
 
-    small = int(np.argmin(g_cnt))
-    for e in sorted({small, int(rng.integers(0, N))}):
+    small = int(np.argmin(np.where(g_cnt > 0, g_cnt, 1 << 30)))
+    for e in sorted({small, int(np.argmax(g_cnt)), int(rng.integers(0, N))}):
         wg, wu, wd = weights_of(e)
         x, dout = expert_rows(e)
         js = np.unique(np.concatenate([[0, dff - 1], rng.integers(0, dff, 4)]))
@@ -169,3 +188,17 @@ def test_full_size_backward_mixtral_prefill():
     worst = check_close_rows(_np(g["dw_down"][small][t.from_numpy(cs).cuda()]), dwd, tol,
                              what=f"dW_down[{small}] rows")
     print(f"[{w.name}] dW_down rows of expert {small}: max row rel err {worst:.2e}", flush=True)
+
+    # ---- the shared expert's weight gradients over all T tokens (sampled rows)
+    if dfs:
+        js = np.unique(np.concatenate([[0, dfs - 1], rng.integers(0, dfs, 4)]))
+        _, dsg, dsu, _ = O.expert_ffn_backward(h, shw[0][js], shw[1][js], shw[2][:, js], dyh)
+        check_close_rows(_np(g["dsh_gate"][t.from_numpy(js).cuda()]), dsg, tol,
+                         what="dW_gate (shared) rows")
+        check_close_rows(_np(g["dsh_up"][t.from_numpy(js).cuda()]), dsu, tol,
+                         what="dW_up (shared) rows")
+        _, _, _, dsd = O.expert_ffn_backward(h, *shw[:2], shw[2][cs], dyh[:, cs])
+        worst = check_close_rows(_np(g["dsh_down"][t.from_numpy(cs).cuda()]), dsd, tol,
+                                 what="dW_down (shared) rows")
+        print(f"[{w.name}] shared expert's weight-gradient rows: max row rel err {worst:.2e}",
+              flush=True)
