@@ -1,8 +1,9 @@
 """GPU parity of moe_layer_backward at full size, in the launch configuration
 the benchmark times (inputs drawn on the device, the same seeded upstream
 gradient, d_laux = 1, d_zloss = 1e-3): the Mixtral-8x7B prefill (T = 4096,
-d = 4096, d_ff = 14336, 8 experts, top-2, softmax gates) and the
-DeepSeek-V3 shape (T = 4096, d = 7168, d_ff = 2048, 256 experts, top-8,
+d = 4096, d_ff = 14336, 8 experts, top-2, softmax gates), the Qwen3-30B-A3B
+shape (T = 8192, d = 2048, d_ff = 768, 128 experts, top-8, Zipf-skewed: 0 to
+7,928 rows per expert) and the DeepSeek-V3 shape (T = 4096, d = 7168, d_ff = 2048, 256 experts, top-8,
 sigmoid gates with a selection bias, a shared expert whose pre-activations
 come from the routed launches), against the float64 oracle on sampled
 outputs it can compute one at a time:
@@ -47,7 +48,7 @@ def _np(x):
     return x.float().cpu().numpy().astype(np.float64)
 
 
-FULL_BACKWARD = [W.MIXTRAL_PREFILL, W.DEEPSEEK_V3]
+FULL_BACKWARD = [W.MIXTRAL_PREFILL, W.QWEN3_30B, W.DEEPSEEK_V3]
 
 
 @pytest.mark.parametrize("w", FULL_BACKWARD, ids=[w.name for w in FULL_BACKWARD])
