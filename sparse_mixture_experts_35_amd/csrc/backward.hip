@@ -322,7 +322,9 @@ __global__ __launch_bounds__(kT) void swiglu_bwd_t_kernel(
   }
 }
 
-// The same outputs for bf16 layers with d_ff % 4 == 0, with 16-byte loads: a
+// The same outputs for bf16 layers (d_ff a multiple of 64) whose fp32
+// pre-activations and v are 16-byte aligned (the kernel above serves the
+// others and the fp32 layers), with 16-byte loads: a
 // lane takes four adjacent columns of a row (16 lanes per row of the 64-column
 // tile, four rows per wave and pass), so that each thread has twelve 16-byte
 // loads in flight instead of twelve 4-byte ones. The tile's partial
