@@ -719,7 +719,7 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
                     int64_t gstride, int ldc, bool f32out, const char* what) -> moe_status {
     if (bf16)
       return hip_check(moe::launch_kgroup_bf16(A, lda, a_rows, B, ldb, b_rows, ko, G, M, Ncols,
-                                               Cout, gstride, ldc, f32out, st), what);
+                                               Cout, gstride, ldc, f32out, ncu, st), what);
     return hip_check(moe::launch_kgroup_f32(static_cast<const float*>(A), lda,
                                             static_cast<const float*>(B), ldb, ko, G, M, Ncols,
                                             static_cast<float*>(Cout), gstride, ldc, st), what);

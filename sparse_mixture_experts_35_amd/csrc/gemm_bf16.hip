@@ -324,11 +324,14 @@ constexpr int na_k64(int V, int wn) {
   return n < 0 ? 0 : (n > C::NAW ? C::NAW : n);
 }
 
+// pre: the first slab's loads into S0 were issued already (first_slab_k64,
+// before the previous tile's epilogue).
 template <class C, int V, int NA>
 __device__ __forceinline__ void mainloop_k64(char* __restrict__ S0, char* __restrict__ S1, Rsrc A,
                                              const uint32_t* aoff, Rsrc B0, Rsrc B1,
                                              const uint32_t* boff, int k_begin, int k_len,
-                                             f32x16 (&acc)[C::NB][C::FM][C::FN]) {
+                                             f32x16 (&acc)[C::NB][C::FM][C::FN],
+                                             bool pre = false) {
   static_assert(C::BK == 64 && C::STAGES == 2 && !C::NN, "64-deep slabs: two stages");
   static_assert(C::NAW == C::NBW, "A blocks are the first half of a wave's loads");
   constexpr int STEP = C::BK * 2;
@@ -336,7 +339,7 @@ __device__ __forceinline__ void mainloop_k64(char* __restrict__ S0, char* __rest
   const int kb = k_begin * 2;
   auto kbyte = [&](int k) { return kb + min(k, KT - 1) * STEP; };
   Frags<C> f0, f1;
-  dma_slab<C, -1, NA>(S0, A, aoff, B0, B1, boff, kb, kb);
+  if (!pre) dma_slab<C, -1, NA>(S0, A, aoff, B0, B1, boff, kb, kb);
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   read_frags<C, V>(S0, 0, f0);
@@ -431,7 +434,7 @@ __device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict
                                          Rsrc A, const uint32_t* aoff, Rsrc B0, Rsrc B1,
                                          const uint32_t* boff, int k_begin, int k_len,
                                          f32x16 (&acc)[C::NB][C::FM][C::FN],
-                                         int ldb_bytes = 0, int nn_k1 = 0) {
+                                         int ldb_bytes = 0, int nn_k1 = 0, bool pre = false) {
   constexpr int STEP = C::BK * 2;
   const int KT = k_len / C::BK;
   const int kb = k_begin * 2;
@@ -460,9 +463,9 @@ __device__ __forceinline__ void mainloop(char* __restrict__ S0, char* __restrict
         mainloop_k64_3<C, V, NA1>(S0, S1, S2, A, aoff, B0, B1, boff, k_begin, k_len, acc);
     } else {
       if (first)
-        mainloop_k64<C, V, NA0>(S0, S1, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+        mainloop_k64<C, V, NA0>(S0, S1, A, aoff, B0, B1, boff, k_begin, k_len, acc, pre);
       else
-        mainloop_k64<C, V, NA1>(S0, S1, A, aoff, B0, B1, boff, k_begin, k_len, acc);
+        mainloop_k64<C, V, NA1>(S0, S1, A, aoff, B0, B1, boff, k_begin, k_len, acc, pre);
     }
     return;
   }
@@ -788,14 +791,16 @@ __device__ __forceinline__ void mainloop_rows(int v, char* S0, char* S1, char* S
                                               Rsrc A, const uint32_t* aoff, Rsrc B0, Rsrc B1,
                                               const uint32_t* boff, int k_begin, int k_len,
                                               f32x16 (&acc)[C::NB][C::FM][C::FN],
-                                              int ldb_bytes = 0, int nn_k1 = 0) {
+                                              int ldb_bytes = 0, int nn_k1 = 0,
+                                              bool pre = false) {
   if (v == W || W == 0) {
-    mainloop<C, W>(S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc, ldb_bytes, nn_k1);
+    mainloop<C, W>(S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc, ldb_bytes, nn_k1,
+                   pre);
     return;
   }
   if constexpr (W > 0)
     mainloop_rows<C, W - 1>(v, S0, S1, S2, S3, A, aoff, B0, B1, boff, k_begin, k_len, acc,
-                            ldb_bytes, nn_k1);
+                            ldb_bytes, nn_k1, pre);
 }
 
 // acc = A[tile rows] · B[tile columns]^T over k in [k_begin, k_begin + k_len).
@@ -1133,6 +1138,98 @@ __global__ __launch_bounds__(kThreads, C::OCC) void kgroup_gemm_kernel(
   } else {
     epilogue_bf16<C, EPI_STORE_BF16>(acc, static_cast<bf16_t*>(Cout) + (int64_t)g * c_gstride,
                                      ldc, m0, min(C::BM, M - m0), n0, Ncols);
+  }
+}
+
+// The weight gradients of kgroup_gemm_kernel (bf16 out) on two-stage 64-deep
+// tiles, persistent, one block per CU. An expert's K range is short (about
+// 16 slabs at the Mixtral prefill shape), so a tile's first-slab wait and a
+// block's start weigh on every tile: here the next tile's first slab goes out
+// into stage S0 as soon as the main loop has freed both stages (its closing
+// barrier; the epilogue stores from registers), ahead of the current tile's
+// stores. Block b runs on XCD x = b % 8. With mx > 0 (P blocks, a multiple of
+// 8, and at least mx m-tiles and 8 / mx n-tiles), XCD x takes, expert by
+// expert, the m-tiles m = x % mx (mod mx) and the n-tiles n = x / mx
+// (mod 8 / mx), m-tile major, its P / 8 blocks taking every (P / 8)-th of
+// them; mx = 1 is the order of the one-tile-per-block grid whenever the
+// n-tiles are a multiple of 8. Otherwise block b takes tiles b, b + P, ...
+// of that grid's order (group, m-tile, n-tile). Each output tile is computed
+// as in kgroup_gemm_kernel: the results are its results bit for bit.
+template <class C>
+__global__ __launch_bounds__(kThreads, 1) void kgroup_gemm_persist_kernel(
+    const bf16_t* __restrict__ A, int lda, uint32_t a_bytes, const bf16_t* __restrict__ B,
+    int ldb, uint32_t b_bytes, const int32_t* __restrict__ kofs, int G, int M, int Ncols,
+    bf16_t* __restrict__ Cout, int64_t c_gstride, int ldc, int mx) {
+  static_assert(C::BK == 64 && C::STAGES == 2 && !C::NN && !C::DUAL && !C::WAVE_ROWS,
+                "two-stage 64-deep tiles, every A block loaded");
+  __shared__ __attribute__((aligned(1024))) char S0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char S1[C::STAGE];
+  const int nt_m = (M + C::BM - 1) / C::BM;
+  const int nt_n = (Ncols + C::BN - 1) / C::BN;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int nx = mx > 0 ? kXcds / mx : 0;
+  const bool xg = mx > 0 && kXcds % mx == 0 && nblk % kXcds == 0 && nt_m >= mx && nt_n >= nx;
+  // tile sequence of this block: index u = u0, u0 + du, ... < un over
+  // (group, m class index, n class index)
+  int xm = 0, xn = 0, sm = 1, sn = 1, cm = nt_m, cn = nt_n;
+  int64_t u = b, du = nblk;
+  if (xg) {
+    const int x = b % kXcds;
+    xm = x % mx;
+    xn = x / mx;
+    sm = mx;
+    sn = nx;
+    cm = (nt_m - xm + mx - 1) / mx;
+    cn = (nt_n - xn + nx - 1) / nx;
+    u = b / kXcds;
+    du = nblk / kXcds;
+  }
+  const int per_g = cm * cn;
+  const int64_t un = (int64_t)per_g * G;
+  const Rsrc rA = make_rsrc(A, a_bytes), rB = make_rsrc(B, b_bytes);
+  const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / C::WN;
+  struct Tile {
+    int g, m0, n0, k_begin, k_len;
+  };
+  auto tile = [&](int64_t v) {
+    Tile t;
+    t.g = (int)(v / per_g);
+    const int r = (int)(v - (int64_t)t.g * per_g);
+    t.m0 = (xm + sm * (r / cn)) * C::BM;
+    t.n0 = (xn + sn * (r % cn)) * C::BN;
+    t.k_begin = __builtin_amdgcn_readfirstlane(kofs[t.g]);
+    t.k_len = __builtin_amdgcn_readfirstlane(kofs[t.g + 1]) - t.k_begin;
+    return t;
+  };
+  if (u >= un) return;
+  Tile cur = tile(u);
+  uint32_t aoff[C::NAW], boff[C::NBW];
+  dma_offsets<C>(aoff, boff, nullptr, 1, lda, cur.m0, M, ldb, cur.n0, Ncols);
+  bool pre = false;                    // the current tile's first slab is in flight
+  for (;;) {
+    f32x16 acc[C::NB][C::FM][C::FN];
+    zero_acc<C>(acc);
+    if (cur.k_len > 0) {
+      const int v = min(max((M - cur.m0 - wm * C::TM + 31) / 32, 0), C::FM);
+      mainloop_rows<C, C::FM>(v, S0, S1, S0, S0, rA, aoff, rB, rB, boff, cur.k_begin, cur.k_len,
+                              acc, 0, 0, pre);
+    }
+    const int64_t un_next = u + du;
+    Tile nxt = cur;
+    pre = false;
+    if (un_next < un) {
+      nxt = tile(un_next);
+      dma_offsets<C>(aoff, boff, nullptr, 1, lda, nxt.m0, M, ldb, nxt.n0, Ncols);
+      if (nxt.k_len > 0) {
+        dma_slab<C, -1, C::NAW>(S0, rA, aoff, rB, rB, boff, nxt.k_begin * 2, nxt.k_begin * 2);
+        pre = true;
+      }
+    }
+    epilogue_bf16<C, EPI_STORE_BF16>(acc, Cout + (int64_t)cur.g * c_gstride, ldc, cur.m0,
+                                     min(C::BM, M - cur.m0), cur.n0, Ncols);
+    if (un_next >= un) break;
+    u = un_next;
+    cur = nxt;
   }
 }
 
@@ -1685,7 +1782,8 @@ hipError_t launch_down_f32out_bf16(const GroupedProblem& p, int num_cu, hipStrea
 
 hipError_t launch_kgroup_bf16(const void* A_, int lda, int64_t a_rows, const void* B_, int ldb,
                               int64_t b_rows, const int32_t* kofs, int groups, int M, int Ncols,
-                              void* C, int64_t c_gstride, int ldc, bool f32out, hipStream_t st) {
+                              void* C, int64_t c_gstride, int ldc, bool f32out, int num_cu,
+                              hipStream_t st) {
   if (groups == 0 || M == 0 || Ncols == 0) return hipSuccess;
   const bf16_t* A = static_cast<const bf16_t*>(A_);
   const bf16_t* B = static_cast<const bf16_t*>(B_);
@@ -1697,11 +1795,16 @@ hipError_t launch_kgroup_bf16(const void* A_, int lda, int64_t a_rows, const voi
                        ldb, bb, kofs, M, Ncols, C, c_gstride, ldc);
   } else if (M >= 512) {
     // 256 x 256 tiles: half the operand traffic per flop of 128 x 256; the
-    // K ranges are whole 64-deep slabs
+    // K ranges are whole 64-deep slabs. Persistent, one block per CU.
     using K = Down256K;
-    dim3 grid((unsigned)(((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN)), groups);
-    hipLaunchKernelGGL((kgroup_gemm_kernel<K, false>), grid, dim3(kThreads), 0, st, A, lda, ab, B,
-                       ldb, bb, kofs, M, Ncols, C, c_gstride, ldc);
+    const int64_t tiles =
+        (int64_t)((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN) * groups;
+    int64_t nblk = std::min<int64_t>(tiles, num_cu > 0 ? num_cu : 256);
+    if (nblk >= kXcds) nblk -= nblk % kXcds;
+    const int mx = 2;
+    hipLaunchKernelGGL((kgroup_gemm_persist_kernel<K>), dim3((unsigned)nblk), dim3(kThreads), 0,
+                       st, A, lda, ab, B, ldb, bb, kofs, groups, M, Ncols,
+                       static_cast<bf16_t*>(C), c_gstride, ldc, mx);
   } else {
     using K = Down128;
     dim3 grid((unsigned)(((M + K::BM - 1) / K::BM) * ((Ncols + K::BN - 1) / K::BN)), groups);

@@ -180,11 +180,12 @@ hipError_t launch_down_nn_bf16(const GroupedProblem& p, int num_cu, hipStream_t 
 hipError_t launch_down_nn_f32out_bf16(const GroupedProblem& p, int num_cu, hipStream_t st);
 // C_g = A[:, kofs[g]:kofs[g+1]] · B[:, kofs[g]:kofs[g+1]]^T for g < groups
 // (A [a_rows, lda] and B [b_rows, ldb] bf16, K ranges multiples of 64);
-// C_g [M, Ncols] at C + g * c_gstride elements, bf16 or fp32 (f32out)
+// C_g [M, Ncols] at C + g * c_gstride elements, bf16 or fp32 (f32out);
+// num_cu sizes the persistent grid of the 256 x 256 tiles
 hipError_t launch_kgroup_bf16(const void* A, int lda, int64_t a_rows,
                               const void* B, int ldb, int64_t b_rows,
                               const int32_t* kofs, int groups, int M, int Ncols,
-                              void* C, int64_t c_gstride, int ldc, bool f32out,
+                              void* C, int64_t c_gstride, int ldc, bool f32out, int num_cu,
                               hipStream_t st);
 // fp32 versions (plain FMA kernels)
 hipError_t launch_gateup_f32(const GroupedProblem& p, hipStream_t st);
