@@ -146,6 +146,10 @@ BACKWARD_CASES = [
     # with its split-K tail
     ("bf16_B_shared_in_routed_k4096", 128, 4096, 4, 1, 128, 128, W.DTYPE_BF16, 1, None, 0.0,
      0.3, 0.1),
+    # weight gradients on the persistent 256 x 256 tiles with ragged edges:
+    # dW_gate / dW_up 576 x 1088 (3 x 5 tiles, split over the XCDs),
+    # dW_down 1088 x 576 (5 x 3 tiles, too few n-tiles for the split)
+    ("bf16_A_partial_tiles", 300, 1088, 4, 2, 576, 0, W.DTYPE_BF16, 0, None, 0.0, 0.2, 0.1),
 ]
 
 
