@@ -476,9 +476,15 @@ __global__ __launch_bounds__(64) void route_bwd_kernel(
     const int i = lane + 64 * q;
     float v = -INFINITY;
     if (i < N) {
+      // the forward's sum: slices in order, all loads issued first
       const float* zp = z_part + (int64_t)t * N + i;
+      float part[kRouterMaxSplits];
+#pragma unroll
+      for (int s = 0; s < kRouterMaxSplits; ++s) part[s] = s < splits ? zp[s * TN] : 0.0f;
       v = 0.0f;
-      for (int s = 0; s < splits; ++s) v += zp[s * TN];
+#pragma unroll
+      for (int s = 0; s < kRouterMaxSplits; ++s)
+        if (s < splits) v += part[s];
       if (b_router) v += b_router[i];
     }
     z[q] = v;
@@ -787,6 +793,7 @@ hipError_t launch_route_bwd(const float* z_part, int splits, const float* b_rout
                             int mode, float alpha, float d_laux, float d_zloss, float* dz,
                             void* dzb, int ldzb, int bf16, float* dg_out, hipStream_t st) {
   if (T == 0) return hipSuccess;
+  if (splits < 1 || splits > kRouterMaxSplits) return hipErrorInvalidValue;
   if (bf16)
     hipLaunchKernelGGL(route_bwd_kernel<bf16_t>, dim3(T), dim3(64), 0, st, z_part, splits,
                        b_router, ids, gates, dg_slot, row_of, counts, T, N, k, mode, alpha,

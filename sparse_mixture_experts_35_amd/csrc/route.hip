@@ -114,8 +114,15 @@ __device__ __forceinline__ void route_select_block(
       cand[i] = in;
       float v = 0.0f;
       if (in) {
+        // every slice's load issued before the first add (splits <=
+        // kRouterMaxSplits); the sum still runs in slice order
         const float* zp = z_part + (int64_t)t * N + e;
-        for (int s = 0; s < splits; ++s) v += zp[s * TN];
+        float part[kRouterMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kRouterMaxSplits; ++s) part[s] = s < splits ? zp[s * TN] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < kRouterMaxSplits; ++s)
+          if (s < splits) v += part[s];
         if (b_router) v += b_router[e];
       }
       zv[i] = v;
@@ -556,6 +563,7 @@ hipError_t launch_route_select(const float* z_part, int splits, const float* b_r
   const SelectCfg c = select_cfg(T, N);
   const int blocks = (T + c.tpb - 1) / c.tpb;
   if (blocks == 0) return hipSuccess;
+  if (splits < 1 || splits > kRouterMaxSplits) return hipErrorInvalidValue;
   if (k > c.lpt) return hipErrorInvalidValue;   // a lane per selected slot (k <= 16 <= LPT, or k <= N <= LPT)
   fin.on = fin.on && blocks == 1;
   if (dq) {
