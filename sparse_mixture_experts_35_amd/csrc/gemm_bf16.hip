@@ -1291,7 +1291,7 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(
 // loads 32 contiguous bytes of weight row i at k = 64c + 16q, so each group
 // of four lanes reads one full 128-byte line; the A fragments use the same
 // k mapping.
-template <int MT, int CT, bool DUAL, bool CMB>
+template <int MT, int CT, bool DUAL, bool CMB, int PD>
 __device__ __forceinline__ void skinny_tile(const GroupedProblem& p, int g, int cb, int r0,
                                             int cnt,
                                             f32x4 (&red)[4][(DUAL ? 2 : 1) * MT * CT][64]) {
@@ -1331,8 +1331,6 @@ __device__ __forceinline__ void skinny_tile(const GroupedProblem& p, int g, int 
       for (int ct = 0; ct < CT; ++ct) acc[nb][mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = p.K / 64;
-  u32x4 bc[NB][CT][2], bn[NB][CT][2];
-  u32x4 ac[MT][2], an[MT][2];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   auto loadB = [&](u32x4 (&dst)[NB][CT][2], int c) {
 #pragma unroll
@@ -1350,19 +1348,7 @@ __device__ __forceinline__ void skinny_tile(const GroupedProblem& p, int g, int 
       for (int s = 0; s < 2; ++s)
         dst[mt][s] = aval[mt] ? *reinterpret_cast<const u32x4*>(arow[mt] + c * 64 + s * 8) : zero4;
   };
-  // A and B of chunk c + 4 are loaded together, one chunk ahead of the
-  // MFMAs: loads complete in issue order, so the MFMAs' wait for chunk c
-  // leaves all of chunk c + 4 in flight
-  int c = w;
-  if (c < KT) {
-    loadB(bc, c);
-    loadA(ac, c);
-  }
-  for (; c < KT; c += 4) {
-    if (c + 4 < KT) {
-      loadB(bn, c + 4);
-      loadA(an, c + 4);
-    }
+  auto chunk_mfma = [&](const u32x4 (&a)[MT][2], const u32x4 (&b)[NB][CT][2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -1371,17 +1357,66 @@ __device__ __forceinline__ void skinny_tile(const GroupedProblem& p, int g, int 
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
-            acc[nb][mt][ct] = mfma_16x16x32(ac[mt][s], bc[nb][ct][s], acc[nb][mt][ct]);
+            acc[nb][mt][ct] = mfma_16x16x32(a[mt][s], b[nb][ct][s], acc[nb][mt][ct]);
+  };
+  if constexpr (PD == 1) {
+    // A and B of chunk c + 4 are loaded together, one chunk ahead of the
+    // MFMAs: loads complete in issue order, so the MFMAs' wait for chunk c
+    // leaves all of chunk c + 4 in flight
+    u32x4 bc[NB][CT][2], bn[NB][CT][2];
+    u32x4 ac[MT][2], an[MT][2];
+    int c = w;
+    if (c < KT) {
+      loadB(bc, c);
+      loadA(ac, c);
+    }
+    for (; c < KT; c += 4) {
+      if (c + 4 < KT) {
+        loadB(bn, c + 4);
+        loadA(an, c + 4);
+      }
+      chunk_mfma(ac, bc);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) bc[nb][ct][s] = bn[nb][ct][s];
+          for (int s = 0; s < 2; ++s) bc[nb][ct][s] = bn[nb][ct][s];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) ac[mt][s] = an[mt][s];
+        for (int s = 0; s < 2; ++s) ac[mt][s] = an[mt][s];
+    }
+  } else {
+    // a ring of PD + 1 register sets: while a wave computes chunk c, chunks
+    // c + 4, ..., c + 4 PD are in flight. The loop is unrolled over the ring,
+    // so every slot is a fixed register set (copying from a slot whose loads
+    // are in flight would wait for them), at the cost of more live
+    // registers; used for 16-column blocks, whose chunks are small.
+    u32x4 bq[PD + 1][NB][CT][2];
+    u32x4 aq[PD + 1][MT][2];
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      const int cj = w + 4 * j;
+      if (cj < KT) {
+        loadB(bq[j], cj);
+        loadA(aq[j], cj);
+      }
+    }
+    for (int c0 = w; c0 < KT; c0 += 4 * (PD + 1)) {
+#pragma unroll
+      for (int j = 0; j <= PD; ++j) {
+        const int c = c0 + 4 * j;
+        if (c < KT) {
+          const int cl = c + 4 * PD;
+          if (cl < KT) {
+            loadB(bq[(j + PD) % (PD + 1)], cl);
+            loadA(aq[(j + PD) % (PD + 1)], cl);
+          }
+          chunk_mfma(aq[j], bq[j]);
+        }
+      }
+    }
   }
 
 #pragma unroll
@@ -1486,7 +1521,7 @@ __device__ __forceinline__ void skinny_combine(const GroupedProblem& p, const Co
 // range's arrival counter (the blocks of experts without rows too); the
 // last to arrive sums each token's rows over those columns into y, with the
 // separate combine kernel's arithmetic and order (same bits).
-template <int MT, int CT, bool DUAL, bool CMB>
+template <int MT, int CT, bool DUAL, bool CMB, int PD>
 __global__ __launch_bounds__(kThreads) void skinny_gemm_kernel(GroupedProblem p, CombineFuse cf) {
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int NACC = NB * MT * CT;
@@ -1533,18 +1568,23 @@ __global__ __launch_bounds__(kThreads) void skinny_gemm_kernel(GroupedProblem p,
   // expert twice for a token (the row bound of the launch assumes not)
   for (int base = 0; base < cnt; base += 16 * MT) {
     if (base > 0) __syncthreads();          // the previous pass's LDS reads are done
-    skinny_tile<MT, CT, DUAL, CMB>(p, g, cb, r0 + base, min(cnt - base, 16 * MT), red);
+    skinny_tile<MT, CT, DUAL, CMB, PD>(p, g, cb, r0 + base, min(cnt - base, 16 * MT), red);
   }
   if constexpr (CMB) skinny_combine<CT>(p, cf, cb, ngroups);
 }
 
+// PD chunks in flight per wave: 3 for 16-column blocks (a wave's chunk is
+// 2 or 4 KB of weights, and one token's down GEMM has two blocks per CU),
+// else 1.
 template <int MT, int CT, bool DUAL, bool CMB>
 hipError_t launch_skinny_ct(const GroupedProblem& p, hipStream_t st, const CombineFuse& cf) {
   const int G = p.offsets ? p.groups : (p.M + 16 * MT - 1) / (16 * MT);
   if (G == 0) return hipSuccess;
   const int64_t items = (int64_t)G * ((p.Ncols + 16 * CT - 1) / (16 * CT));
   const dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds));
-  hipLaunchKernelGGL((skinny_gemm_kernel<MT, CT, DUAL, CMB>), grid, dim3(kThreads), 0, st, p, cf);
+  constexpr int PD = CT == 1 ? 3 : 1;
+  hipLaunchKernelGGL((skinny_gemm_kernel<MT, CT, DUAL, CMB, PD>), grid, dim3(kThreads), 0, st, p,
+                     cf);
   return hipGetLastError();
 }
 
