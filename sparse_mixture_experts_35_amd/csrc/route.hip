@@ -48,12 +48,25 @@ __global__ __launch_bounds__(256) void router_gemv_bf16_kernel(const bf16_t* __r
   const bf16_t* a = h + (int64_t)t * d;
   const bf16_t* b = w + (int64_t)e * d;
   float s = 0.0f;
-  for (int c = lane * 8; c < d; c += 512) {
-    float x[8], y[8];
-    unpack_bf16x8(*reinterpret_cast<const u32x4*>(a + c), x);
-    unpack_bf16x8(*reinterpret_cast<const u32x4*>(b + c), y);
+  // four 512-element steps per pass, their loads issued before the first
+  // fmaf; the products still add in order of c
+  for (int c0 = lane * 8; c0 < d; c0 += 4 * 512) {
+    u32x4 va[4], vb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s = fmaf(x[i], y[i], s);
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + j * 512;
+      va[j] = c < d ? *reinterpret_cast<const u32x4*>(a + c) : u32x4{0u, 0u, 0u, 0u};
+      vb[j] = c < d ? *reinterpret_cast<const u32x4*>(b + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (c0 + j * 512 >= d) break;
+      float x[8], y[8];
+      unpack_bf16x8(va[j], x);
+      unpack_bf16x8(vb[j], y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = fmaf(x[i], y[i], s);
+    }
   }
   s = wave_sum(s);
   if (lane == 0) z[wv] = s;
