@@ -192,9 +192,13 @@ CASES = [
     # weight-streaming down GEMM (bf16)
     ("bf16_decode_T1", 1, 128, 8, 2, 128, 0, W.DTYPE_BF16, 0),
     # one token: the weight-streaming kernels narrow their column blocks so
-    # that the two experts' work covers the CUs (32 columns for gate/up
-    # here, 16 for down)
+    # that the two experts' work covers the CUs (16 columns for both here,
+    # with three chunks in flight per wave: eight turns of the ring of
+    # register sets over the down GEMM's K = 8192)
     ("bf16_decode_T1_wide", 1, 256, 8, 2, 8192, 0, W.DTYPE_BF16, 0),
+    # the ring stopping part-way through a turn: K of 23 (gate/up) and 11
+    # (down) 64-deep chunks over four waves
+    ("bf16_decode_T1_ring_tail", 1, 1472, 8, 2, 704, 0, W.DTYPE_BF16, 0),
     ("bf16_decode_T32_shared", 32, 256, 8, 2, 384, 128, W.DTYPE_BF16, 0),
     ("bf16_decode_T16_N64_sigmoid", 16, 128, 64, 6, 128, 0, W.DTYPE_BF16, 2),
     ("bf16_decode_T5_N512_k16_shared", 5, 64, 512, 16, 64, 64, W.DTYPE_BF16, 1),
