@@ -150,6 +150,12 @@ BACKWARD_CASES = [
     # dW_gate / dW_up 576 x 1088 (3 x 5 tiles, split over the XCDs),
     # dW_down 1088 x 576 (5 x 3 tiles, too few n-tiles for the split)
     ("bf16_A_partial_tiles", 300, 1088, 4, 2, 576, 0, W.DTYPE_BF16, 0, None, 0.0, 0.2, 0.1),
+    # both weight-gradient shapes split over the XCDs with ragged edges and
+    # classes of unequal size (5 x 6 and 6 x 5 tiles)
+    ("bf16_B_xcd_split_ragged", 400, 1536, 3, 2, 1088, 0, W.DTYPE_BF16, 1, None, 0.0, 0.1, 0.0),
+    # the shared expert's weight gradients on the persistent tiles too
+    ("bf16_C_xcd_split_shared", 300, 1024, 4, 2, 1024, 1024, W.DTYPE_BF16, 2, None, 0.0, 0.3,
+     0.1),
 ]
 
 
