@@ -841,14 +841,22 @@ moe_status backward_impl(const moe_shape* s, const void* h, const void* w_router
                                     part, cnt, W.part_floats},
                 2, "shared dh GEMM"));
   }
-  TRY(pack(w_router, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, N, Np, wrT, Np, 1, 0, 0,
-           "W_r transpose"));
-  TRY(grouped(moe::GroupedProblem{dzb, Np, nullptr, 1, nullptr, 1, T, T, wrT, nullptr, 0, Np, d,
-                                  Np, dhrt, d, 0, (uint32_t)(es * T * Np), part, cnt,
-                                  W.part_floats},
-              2, "router dh GEMM"));
-  TRY(hip_check(moe::launch_dh_combine(dhr, row_of, dfs ? dhs : nullptr, dhrt, dh, T, k, d, b,
-                                       st), "dh combine"));
+  // the router's term dz W_r: for a few experts inside the combine (N fp32
+  // products per element), else a GEMM over the padded dz
+  const bool router_in_combine = N <= moe::kMaxRouterFused;
+  if (!router_in_combine) {
+    TRY(pack(w_router, d, d, nullptr, 1, nullptr, nullptr, nullptr, 0, N, Np, wrT, Np, 1, 0, 0,
+             "W_r transpose"));
+    TRY(grouped(moe::GroupedProblem{dzb, Np, nullptr, 1, nullptr, 1, T, T, wrT, nullptr, 0, Np,
+                                    d, Np, dhrt, d, 0, (uint32_t)(es * T * Np), part, cnt,
+                                    W.part_floats},
+                2, "router dh GEMM"));
+  }
+  TRY(hip_check(moe::launch_dh_combine(dhr, row_of, dfs ? dhs : nullptr,
+                                       router_in_combine ? nullptr : dhrt,
+                                       router_in_combine ? dz : nullptr, w_router, N, dh, T, k,
+                                       d, b, st),
+                "dh combine"));
   // 7. expert weight gradients over each expert's kept rows (padded K
   //    ranges): act^T (tb) and [dgp | du]^T (ta) from step 4
   TRY(pack(dy, d, d, perm, k, gates, offsets, kofs, N, 0, Rp, tc, Rp, 1, 0, 0, "dOut transpose"));

@@ -658,16 +658,21 @@ __global__ __launch_bounds__(kT) void colsum_final_kernel(const float* __restric
 // + router[t], accumulated in fp32 in that order. The token's row indices
 // are read once into LDS; VEC: each thread takes 16 bytes of columns (d and
 // every pointer allow it; the launcher checks), else one column.
+// With dz (N <= kMaxRouterFused experts) the router's term is formed here
+// instead of read: sum over i < N, in order, of dz[t][i] · W_r[i][c] in fp32
+// (no bf16 rounding of the term or of dz, and no separate GEMM).
 constexpr int kMaxTopK = 16;
 template <typename TE, bool VEC>
 __global__ __launch_bounds__(kT) void dh_combine_kernel(
     const TE* __restrict__ rows, const int32_t* __restrict__ row_of,
-    const TE* __restrict__ shared, const TE* __restrict__ router, TE* __restrict__ dh, int k,
-    int d) {
+    const TE* __restrict__ shared, const TE* __restrict__ router, const float* __restrict__ dz,
+    const TE* __restrict__ wr, int N, TE* __restrict__ dh, int k, int d) {
   constexpr int V = VEC ? 16 / sizeof(TE) : 1;
   __shared__ int64_t s_r[kMaxTopK];
+  __shared__ float s_dz[kMaxRouterFused];
   const int64_t t = blockIdx.x;
   if (threadIdx.x < k) s_r[threadIdx.x] = row_of[t * k + threadIdx.x];
+  if (dz && threadIdx.x < N) s_dz[threadIdx.x] = dz[t * N + threadIdx.x];
   __syncthreads();
   for (int c = threadIdx.x * V; c < d; c += kT * V) {
     float acc[V];
@@ -688,7 +693,26 @@ __global__ __launch_bounds__(kT) void dh_combine_kernel(
       if (r >= 0) add(rows + r * d + c);
     }
     if (shared) add(shared + t * d + c);
-    add(router + t * d + c);
+    if (dz) {
+      float rr[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) rr[e] = 0.0f;
+      for (int i = 0; i < N; ++i) {
+        const float z = s_dz[i];
+        if constexpr (VEC) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(wr + (int64_t)i * d + c);
+          const TE* x = reinterpret_cast<const TE*>(&raw);
+#pragma unroll
+          for (int e = 0; e < V; ++e) rr[e] = fmaf(z, ld(x, e), rr[e]);
+        } else {
+          rr[0] = fmaf(z, ld(wr, (int64_t)i * d + c), rr[0]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += rr[e];
+    } else {
+      add(router + t * d + c);
+    }
     if constexpr (VEC) {
       TE out[V];
 #pragma unroll
@@ -818,17 +842,21 @@ hipError_t launch_colsum(const float* dz, int T, int N, float* part, float* db, 
 }
 
 hipError_t launch_dh_combine(const void* rows, const int32_t* row_of, const void* shared,
-                             const void* router, void* dh, int T, int k, int d, int bf16,
-                             hipStream_t st) {
+                             const void* router, const float* dz, const void* w_router, int N,
+                             void* dh, int T, int k, int d, int bf16, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (k > kMaxTopK) return hipErrorInvalidValue;
+  if ((dz != nullptr) == (router != nullptr) || (dz && (N > kMaxRouterFused || !w_router)))
+    return hipErrorInvalidValue;                 // exactly one form of the router's term
   const int V = bf16 ? 8 : 4;
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  const bool vec = d % V == 0 && al(rows) && al(router) && al(dh) && (!shared || al(shared));
+  const bool vec = d % V == 0 && al(rows) && al(dh) && (!shared || al(shared)) &&
+                   (router ? al(router) : al(w_router));
 #define MOE_DHC(TE, VEC)                                                                       \
   hipLaunchKernelGGL((dh_combine_kernel<TE, VEC>), dim3(T), dim3(kT), 0, st,                   \
                      static_cast<const TE*>(rows), row_of, static_cast<const TE*>(shared),     \
-                     static_cast<const TE*>(router), static_cast<TE*>(dh), k, d)
+                     static_cast<const TE*>(router), dz, static_cast<const TE*>(w_router), N,  \
+                     static_cast<TE*>(dh), k, d)
   if (bf16) {
     if (vec) MOE_DHC(bf16_t, true); else MOE_DHC(bf16_t, false);
   } else {

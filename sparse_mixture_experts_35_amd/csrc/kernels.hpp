@@ -237,8 +237,12 @@ hipError_t launch_route_bwd(const float* z_part, int splits,
 int colsum_chunks(int T);
 hipError_t launch_colsum(const float* dz, int T, int N, float* part, float* db,
                          hipStream_t st);
+// the router's term either as rows (router, [T, d]) or formed from the
+// fp32 dz [T, N] and w_router [N, d] (N <= kMaxRouterFused); exactly one
+constexpr int kMaxRouterFused = 16;
 hipError_t launch_dh_combine(const void* rows, const int32_t* row_of,
-                             const void* shared, const void* router, void* dh,
+                             const void* shared, const void* router, const float* dz,
+                             const void* w_router, int N, void* dh,
                              int T, int k, int d, int bf16, hipStream_t st);
 hipError_t launch_kgroup_f32(const float* A, int lda, const float* B, int ldb,
                              const int32_t* kofs, int groups, int M, int Ncols,
