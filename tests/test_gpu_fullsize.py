@@ -28,8 +28,12 @@ pytestmark = pytest.mark.gpu
 
 import sparse_mixture_experts_35_amd as M  # noqa: E402
 
-FULL = [W.MIXTRAL_PREFILL, W.MIXTRAL_PREFILL_R1, W.MIXTRAL_DECODE, W.QWEN3_30B, W.QWEN3_30B_CAP,
-        W.DEEPSEEK_V3, W.DEEPSEEK_V3_GROUPED]
+# the decode layer at one and four tokens too: 16-column weight-streaming
+# blocks with three chunks in flight per wave over K = 4,096 and 14,336
+DECODE_T1 = W.MIXTRAL_DECODE.replace(name="mixtral_8x7b_decode_T1", T=1)
+DECODE_T4 = W.MIXTRAL_DECODE.replace(name="mixtral_8x7b_decode_T4", T=4)
+FULL = [W.MIXTRAL_PREFILL, W.MIXTRAL_PREFILL_R1, W.MIXTRAL_DECODE, DECODE_T1, DECODE_T4,
+        W.QWEN3_30B, W.QWEN3_30B_CAP, W.DEEPSEEK_V3, W.DEEPSEEK_V3_GROUPED]
 # sampled tokens for the end-to-end y check (every token at decode)
 Y_TOKENS = {2: 64, 3: 16, 4: 64, 5: 64}
 
